@@ -1,0 +1,300 @@
+"""Plain CPU oracle for the BitNet b1.58 W1.58A8 ternary linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The product
+path (the HIP library and its Python binding) never touches it, and this module
+imports nothing from the product package: the two share no code.
+
+Every step is the plain definition written out with numpy (fp32 where the step
+is a floating-point rounding, exact Python integers where the step is an exact
+sum or an integer contraction).  Nothing is blocked, fused or reordered.
+
+Sources (web pages, cited by title and section)
+-----------------------------------------------
+[OV]  onedollarvps.pages.dev, "如何在本地運行 BitNet B1.58（1-Bit LLM）"
+      (How to run BitNet B1.58 locally), section 2 "技術背景" (technical
+      background), sub-section on 1-bit vs 1.58-bit quantisation: weights are
+      scaled by the reciprocal of their mean absolute value, then rounded and
+      clipped to the three values -1, 0, +1.
+[DT]  dashen-tech.com, "BitNet.cpp 深度解析：1-bit LLM 推論、CPU 上運行 100B
+      模型速度提升 6 倍" (BitNet.cpp deep dive), section 2.3 "I2_S 格式" (2 bits
+      per stored weight, eight weights in 16 bits) and section 3.1 "計算核心：
+      整數矩陣乘法" (integer matmul; the product with ternary weights splits into
+      the sum over +1 weights minus the sum over -1 weights).
+[CM]  communeify.com, "微軟 BitNet b1.58 震撼登場：跑更快、更省電的 1 位元 AI
+      模型來了？", section introducing BitNet b1.58 2B4T, item "量化細節"
+      (quantisation details: W1.58A8, i.e. ternary weights, 8-bit integer
+      activations).
+[GN]  th.news.hada.io, "BitNet - เฟรมเวิร์กการอนุมานสำหรับ LLM แบบ 1 บิต"
+      (GeekNews summary), Hacker News comments: the stored 2-bit field can hold
+      the four values -1, 0, 1, 2.
+
+Readings taken where the pages are silent (each is also listed in the design doc)
+----------------------------------------------------------------------------
+O1  weight scale: one per-tensor scale; the mean |W| is taken exactly and
+    rounded once to fp32 (RN32, ties to even); gamma* = max(gamma, RN32(1e-5)).
+O2  ternarise: t = RN32(W / gamma*) (correctly rounded fp32 division), then
+    round half to even, then clip to [-1, 1].
+O3  pack: code = q + 1 in {0, 1, 2}; four codes per byte, least significant bit
+    pair first; row n occupies bytes [n*K/4, (n+1)*K/4); K % 4 == 0.
+O4  activations: per token (row) absmax a, a* = max(a, RN32(1e-5)),
+    s = RN32(127 / a*), xq = clip(rne(RN32(x * s)), -128, 127), d = RN32(a* / 127).
+O5  contraction: acc[m, n] = sum_k q[n, k] * xq[m, k] exactly (int32 range).
+O6  rescale: y = RN32(float(acc) * RN32(gamma* * d[m])); bf16 output = RNE(y).
+
+bf16 inputs are upcast to fp32 exactly (bit pattern shifted left by 16) before
+any step, so every function here takes fp32 arrays.
+
+Parity pins: every function below is checked in tests/test_oracle_pins.py
+against values that do not come from this module (hand-worked examples in
+tests/golden/, Python ``fractions`` exact arithmetic, numpy's IEEE fp32
+division, torch's fp32->bf16 conversion, brute-force enumeration of all
+ternary rows, the Gaussian closed form of the zero fraction, and invariants).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F32 = np.float32
+EPS = F32(1e-5)          # RN32(1e-5): the floor of both scales (readings O1, O4)
+QB = F32(127.0)          # symmetric int8 activation range (reading O4)
+_FLT_MAX_UNITS_EXP = 104  # largest finite fp32 = (2**24 - 1) * 2**104
+
+
+# ---------------------------------------------------------------------------
+# bf16 <-> fp32 bit helpers (bf16 held as uint16 bit patterns)
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bit patterns (uint16) to fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def f32_to_bf16_bits(y: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); returns uint16 bits.
+
+    A finite value keeps its top 16 bits after adding half of the dropped
+    field's range, with the kept field's lowest bit deciding exact ties.
+    NaN stays a quiet NaN with its sign.
+    """
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    u = y.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(y)
+    if nan.any():
+        sign = ((u >> np.uint64(16)) & np.uint64(0x8000)).astype(np.uint16)
+        r = np.where(nan, sign | np.uint16(0x7FC0), r)
+    return r
+
+
+# ---------------------------------------------------------------------------
+# O1: exact absolute-mean weight scale
+# ---------------------------------------------------------------------------
+
+def exact_abs_sum_units(w: np.ndarray):
+    """Exact sum of |w| over fp32 ``w``, as an integer count of 2**-149 units.
+
+    Every finite fp32 value is an integer multiple of 2**-149 (the subnormal
+    spacing): a normal value with biased exponent e and fraction f equals
+    (2**23 + f) * 2**(e - 1) units, a subnormal equals f units.  The sum is
+    formed per distinct exponent in int64 (each partial sum stays below 2**63
+    for fewer than 2**39 elements) and combined in Python integers, so no
+    rounding occurs anywhere.  Returns None if any element is Inf or NaN.
+    """
+    bits = np.ascontiguousarray(w, dtype=np.float32).reshape(-1).view(np.uint32)
+    e = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64)
+    if np.any(e == 0xFF):
+        return None
+    frac = (bits & np.uint32(0x7FFFFF)).astype(np.int64)
+    mant = np.where(e > 0, frac | (1 << 23), frac)
+    shift = np.where(e > 0, e - 1, 0)
+    total = 0
+    for s in np.unique(shift):
+        total += int(mant[shift == s].sum(dtype=np.int64)) << int(s)
+    return total
+
+
+def rn32_ratio(num: int, den: int) -> np.float32:
+    """Round the non-negative rational num/den to fp32, ties to even.
+
+    Exact integer arithmetic: choose the power of two 2**e that puts the
+    quotient's integer part q in [2**23, 2**24) (or e = -149 in the subnormal
+    range), then round q using the remainder.
+    """
+    if num < 0 or den <= 0:
+        raise ValueError("rn32_ratio needs num >= 0 and den > 0")
+    if num == 0:
+        return F32(0.0)
+    e = num.bit_length() - den.bit_length() - 24
+    while True:
+        n2, d2 = (num, den << e) if e >= 0 else (num << -e, den)
+        q, r = divmod(n2, d2)
+        if q >= (1 << 24):
+            e += 1
+        elif q < (1 << 23):
+            e -= 1
+        else:
+            break
+    if e < -149:                      # below 2**-126: fixed subnormal spacing
+        e = -149
+        n2, d2 = num << 149, den
+        q, r = divmod(n2, d2)
+    if 2 * r > d2 or (2 * r == d2 and (q & 1)):
+        q += 1
+    if q == (1 << 24):                # rounding carried into the next binade
+        q >>= 1
+        e += 1
+    if e > _FLT_MAX_UNITS_EXP:
+        return F32(np.inf)
+    return F32(math.ldexp(q, e))
+
+
+def weight_scale(w: np.ndarray) -> np.float32:
+    """gamma* per reading O1 ([OV] section 2: divide by the mean absolute value).
+
+    gamma = RN32(exact sum|W| / (N*K)); gamma* = max(gamma, RN32(1e-5)).
+    NaN if W holds any Inf or NaN.
+    """
+    count = int(np.asarray(w).size)
+    if count == 0:
+        raise ValueError("weight_scale needs at least one weight")
+    units = exact_abs_sum_units(w)
+    if units is None:
+        return F32(np.nan)
+    gamma = rn32_ratio(units, count << 149)
+    return gamma if gamma > EPS else EPS
+
+
+# ---------------------------------------------------------------------------
+# O2 / O3: ternarise and pack
+# ---------------------------------------------------------------------------
+
+def ternarize(w: np.ndarray, gamma: np.float32) -> np.ndarray:
+    """q = clip(rne(RN32(w / gamma)), -1, 1) as int8 ([OV] section 2: round, clip)."""
+    t = np.ascontiguousarray(w, dtype=np.float32) / F32(gamma)
+    return np.clip(np.rint(t), -1.0, 1.0).astype(np.int8)
+
+
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """Pack ternary q [N, K] into uint8 [N, K/4] per reading O3 ([DT] section 2.3).
+
+    Byte j of row n holds codes q[n, 4j + i] + 1 at bits 2i..2i+1.
+    """
+    q = np.asarray(q, dtype=np.int8)
+    n_rows, k = q.shape
+    if k % 4:
+        raise ValueError("K must be a multiple of 4")
+    codes = (q.astype(np.int16) + 1).astype(np.uint8).reshape(n_rows, k // 4, 4)
+    out = np.zeros((n_rows, k // 4), dtype=np.uint8)
+    for i in range(4):
+        out |= codes[:, :, i] << np.uint8(2 * i)
+    return out
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_codes: uint8 [N, K/4] -> int8 q [N, K].  Code 3 is invalid."""
+    p = np.asarray(packed, dtype=np.uint8)
+    n_rows, kb = p.shape
+    codes = np.empty((n_rows, kb, 4), dtype=np.uint8)
+    for i in range(4):
+        codes[:, :, i] = (p >> np.uint8(2 * i)) & np.uint8(3)
+    if np.any(codes == 3):
+        raise ValueError("packed weights hold the unused code 3")
+    return (codes.astype(np.int8) - 1).reshape(n_rows, 4 * kb)
+
+
+def quantize_weights(w: np.ndarray):
+    """Readings O1-O3 in sequence: returns (packed uint8 [N, K/4], gamma*).
+
+    If W holds a non-finite value, gamma* is NaN and packed is None.
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    gamma = weight_scale(w)
+    if not np.isfinite(gamma):
+        return None, gamma
+    return pack_codes(ternarize(w, gamma)), gamma
+
+
+# ---------------------------------------------------------------------------
+# O4: per-token absmax int8 activations ([CM] quantisation details: A8)
+# ---------------------------------------------------------------------------
+
+def quantize_acts(x: np.ndarray):
+    """Per token m: a = max|x|, a* = max(a, eps), s = RN32(127/a*),
+    xq = clip(rne(RN32(x*s)), -128, 127), d = RN32(a*/127).
+
+    Returns (xq int8 [M, K], d fp32 [M]).  Activations must be finite.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    m_rows, k = x.shape
+    a = np.abs(x).max(axis=1) if k > 0 else np.zeros(m_rows, dtype=np.float32)
+    a_star = np.maximum(a, EPS)
+    s = QB / a_star
+    xq = np.clip(np.rint(x * s[:, None]), -128.0, 127.0).astype(np.int8)
+    d = (a_star / QB).astype(np.float32)
+    return xq, d
+
+
+# ---------------------------------------------------------------------------
+# O5: exact integer contraction ([DT] section 3.1)
+# ---------------------------------------------------------------------------
+
+def integer_matmul(q: np.ndarray, xq: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k q[n, k] * xq[m, k] in exact integers -> int32 [M, N]."""
+    acc = np.asarray(xq, dtype=np.int64) @ np.asarray(q, dtype=np.int64).T
+    if acc.size and np.abs(acc).max() >= 2 ** 31:
+        raise OverflowError("accumulator leaves the int32 range")
+    return acc.astype(np.int32)
+
+
+def sum_pos_minus_sum_neg(q_row: np.ndarray, x_row: np.ndarray) -> int:
+    """The pages' form of one output ([DT] section 3.1): the sum of the inputs
+    met by +1 weights minus the sum of the inputs met by -1 weights."""
+    q_row = np.asarray(q_row)
+    x_row = np.asarray(x_row, dtype=np.int64)
+    return int(x_row[q_row == 1].sum()) - int(x_row[q_row == -1].sum())
+
+
+# ---------------------------------------------------------------------------
+# O6: rescale to fp32 / bf16
+# ---------------------------------------------------------------------------
+
+def dequantize(acc: np.ndarray, gamma: np.float32, d: np.ndarray) -> np.ndarray:
+    """y[m, n] = RN32(float(acc[m, n]) * RN32(gamma* * d[m])) as fp32 [M, N]."""
+    scale = (F32(gamma) * np.asarray(d, dtype=np.float32)).astype(np.float32)
+    return np.asarray(acc, dtype=np.int32).astype(np.float32) * scale[:, None]
+
+
+def ternary_linear(packed: np.ndarray, gamma: np.float32, xq: np.ndarray,
+                   d: np.ndarray):
+    """Whole layer on pre-quantised inputs: returns (acc int32 [M, N], y fp32 [M, N])."""
+    q = unpack_codes(packed)
+    acc = integer_matmul(q, xq)
+    return acc, dequantize(acc, gamma, d)
+
+
+def ternary_linear_at(packed: np.ndarray, gamma: np.float32, xq: np.ndarray,
+                      d: np.ndarray, m_idx, n_idx):
+    """Selected outputs only: acc and y at the pairs (m_idx[i], n_idx[i])."""
+    m_idx = np.asarray(m_idx, dtype=np.int64)
+    n_idx = np.asarray(n_idx, dtype=np.int64)
+    q_rows = unpack_codes(np.asarray(packed)[n_idx]).astype(np.int64)
+    x_rows = np.asarray(xq)[m_idx].astype(np.int64)
+    acc = (q_rows * x_rows).sum(axis=1)
+    if acc.size and np.abs(acc).max() >= 2 ** 31:
+        raise OverflowError("accumulator leaves the int32 range")
+    acc = acc.astype(np.int32)
+    scale = (F32(gamma) * np.asarray(d, dtype=np.float32)[m_idx]).astype(np.float32)
+    return acc, acc.astype(np.float32) * scale
+
+
+def quant_linear(packed: np.ndarray, gamma: np.float32, x: np.ndarray):
+    """Act-quant followed by the layer: returns (xq, d, acc, y)."""
+    xq, d = quantize_acts(x)
+    acc, y = ternary_linear(packed, gamma, xq, d)
+    return xq, d, acc, y

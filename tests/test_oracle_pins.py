@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names the mistake it would catch.  None of them calls the HIP library.
+"""
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import bitnet_oracle as O
+
+F32 = np.float32
+
+
+def f32_from_hex(h):
+    return np.array([int(h, 16)], dtype=np.uint32).view(np.float32)[0]
+
+
+def frac_of(v):
+    return Fraction(float(v))
+
+
+# ---------------------------------------------------------------------------
+# hand-worked examples (tests/golden/worked_examples.json)
+# ---------------------------------------------------------------------------
+
+def test_golden_worked_examples(golden):
+    """Full layer on hand-derived examples: catches any wrong step end to end."""
+    for ex in golden["examples"]:
+        w = np.array(ex["W"], dtype=np.float32)
+        x = np.array(ex["X"], dtype=np.float32)
+        packed, gamma = O.quantize_weights(w)
+        want_gamma = f32_from_hex(ex["gamma_bits"]) if "gamma_bits" in ex else F32(ex["gamma"])
+        assert gamma.view(np.uint32) == want_gamma.view(np.uint32), ex["name"]
+        np.testing.assert_array_equal(O.ternarize(w, gamma), np.array(ex["q"], dtype=np.int8))
+        np.testing.assert_array_equal(packed, np.array(ex["packed"], dtype=np.uint8))
+        xq, d = O.quantize_acts(x)
+        np.testing.assert_array_equal(xq, np.array(ex["xq"], dtype=np.int8))
+        np.testing.assert_array_equal(d.view(np.uint32),
+                                      np.array([int(h, 16) for h in ex["d_bits"]], dtype=np.uint32))
+        acc, y = O.ternary_linear(packed, gamma, xq, d)
+        np.testing.assert_array_equal(acc, np.array(ex["acc"], dtype=np.int32))
+        want_y = np.array([[int(h, 16) for h in r] for r in ex["y_bits"]], dtype=np.uint32)
+        np.testing.assert_array_equal(y.view(np.uint32), want_y)
+        want_b = np.array([[int(h, 16) for h in r] for r in ex["y_bf16_bits"]], dtype=np.uint16)
+        np.testing.assert_array_equal(O.f32_to_bf16_bits(y), want_b)
+
+
+def test_golden_byte_layout(golden):
+    """Bit order and code map: catches MSB-first packing, two's-complement codes."""
+    for case in golden["byte_layout"]["cases"]:
+        q = np.array([case["q"]], dtype=np.int8)
+        assert int(O.pack_codes(q)[0, 0]) == case["byte"], case
+        np.testing.assert_array_equal(O.unpack_codes(np.array([[case["byte"]]], np.uint8)), q)
+
+
+def test_golden_size_arithmetic(golden):
+    """Two bits per weight: eight weights in 16 bits, 100B weights in ~25 GB."""
+    for n, k, nbytes in golden["size_arithmetic"]["cases"]:
+        assert n * k // 4 == nbytes
+        if n * k <= 1 << 20:
+            assert O.pack_codes(np.zeros((n, k), np.int8)).nbytes == nbytes
+
+
+# ---------------------------------------------------------------------------
+# exact rounding of a rational to fp32
+# ---------------------------------------------------------------------------
+
+def test_rn32_ratio_matches_ieee_division():
+    """numpy's fp32 division is correctly rounded: for fp32 operands the exact
+    rational a/b must round to the same value.  Catches truncation, off-by-one
+    exponent choice and wrong tie handling (sub-normal quotients included)."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    a = (rng.standard_normal(4000) * np.exp2(rng.integers(-60, 60, 4000))).astype(np.float32)
+    b = (rng.standard_normal(4000) * np.exp2(rng.integers(-60, 60, 4000))).astype(np.float32)
+    a = np.abs(a)
+    b = np.abs(b)
+    # push a few quotients into the sub-normal range
+    a[:200] = np.abs(rng.standard_normal(200)).astype(np.float32) * F32(2.0 ** -120)
+    b[:200] = np.abs(rng.standard_normal(200)).astype(np.float32) * F32(2.0 ** 20)
+    with np.errstate(under="ignore"):
+        want = a / b
+    for ai, bi, wi in zip(a, b, want):
+        fa, fb = Fraction(float(ai)), Fraction(float(bi))
+        r = fa / fb
+        got = O.rn32_ratio(r.numerator, r.denominator)
+        assert got.view(np.uint32) == wi.view(np.uint32), (ai, bi)
+
+
+def test_rn32_ratio_nearest_and_ties_to_even():
+    """Checks the defining property with exact Fractions on constructed ties and
+    random large rationals (catches ties-away and double rounding)."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    for _ in range(300):
+        q = int(rng.integers(1 << 23, 1 << 24))
+        e = int(rng.integers(-140, 90))
+        tie = Fraction(2 * q + 1, 2) * Fraction(2) ** e
+        got = O.rn32_ratio(tie.numerator, tie.denominator)
+        want_q = q + (q & 1)
+        assert Fraction(float(got)) == Fraction(want_q) * Fraction(2) ** e
+    for _ in range(300):
+        num = int(rng.integers(1, 1 << 62)) << int(rng.integers(0, 60))
+        den = int(rng.integers(1, 1 << 40))
+        r = Fraction(num, den)
+        got = O.rn32_ratio(num, den)
+        up = np.nextafter(got, F32(np.inf), dtype=np.float32)
+        dn = np.nextafter(got, F32(0), dtype=np.float32)
+        err = abs(r - frac_of(got))
+        assert err <= abs(r - frac_of(up)) and err <= abs(r - frac_of(dn))
+
+
+# ---------------------------------------------------------------------------
+# O1: weight scale
+# ---------------------------------------------------------------------------
+
+def _mixed_weights(seed, n):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 10, n))).astype(np.float32)
+    w[:5] = np.array([0.0, -0.0, 1e-45, -3e-42, 2.0 ** -126], dtype=np.float32)
+    return w
+
+
+def test_exact_abs_sum_equals_fraction_sum():
+    """Python Fractions hold every float exactly: catches dropped sub-normals,
+    a wrong hidden bit or a wrong exponent offset in the integer decomposition."""
+    for seed in range(6):
+        w = _mixed_weights(seed, 3000)
+        units = O.exact_abs_sum_units(w)
+        want = sum((abs(Fraction(float(v))) for v in w), Fraction(0))
+        assert Fraction(units) * Fraction(2) ** -149 == want
+
+
+def test_weight_scale_is_nearest_fp32_of_exact_mean():
+    """gamma must be the fp32 nearest to the exact mean (checked against both
+    neighbours with Fractions), including a case where a naive fp32 sum differs."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    for n, k in [(3, 4), (17, 64), (64, 256)]:
+        w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        gamma = O.weight_scale(w)
+        mean = sum((abs(Fraction(float(v))) for v in w.reshape(-1)), Fraction(0)) / (n * k)
+        up = np.nextafter(gamma, F32(np.inf), dtype=np.float32)
+        dn = np.nextafter(gamma, F32(0), dtype=np.float32)
+        err = abs(mean - frac_of(gamma))
+        assert err <= abs(mean - frac_of(up)) and err <= abs(mean - frac_of(dn))
+    # one large value and many tiny ones: an fp32 running sum loses the tiny ones
+    w = np.full(1 << 14, 2.0 ** -25, dtype=np.float32)
+    w[0] = 1.0
+    gamma = O.weight_scale(w)
+    mean = (Fraction(1) + (w.size - 1) * Fraction(2) ** -25) / w.size
+    assert abs(mean - frac_of(gamma)) <= abs(mean - frac_of(np.nextafter(gamma, F32(1))))
+    naive = F32(np.float32(0))
+    for v in w:
+        naive = F32(naive + v)
+    assert F32(naive / F32(w.size)) != gamma
+
+
+def test_weight_scale_invariants():
+    """Sign, order and power-of-two invariance; constant W; floor; non-finite."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    w = (rng.standard_normal((32, 64)) * 0.02).astype(np.float32)
+    g = O.weight_scale(w)
+    assert O.weight_scale(-w) == g
+    assert O.weight_scale(w[::-1, ::-1].copy()) == g
+    assert O.weight_scale(rng.permutation(w.reshape(-1))) == g
+    for j in (-3, 5):
+        assert O.weight_scale(w * F32(2.0 ** j)) == g * F32(2.0 ** j)
+    c = F32(0.0123)
+    assert O.weight_scale(np.full((7, 12), c, np.float32)) == c
+    assert O.weight_scale(np.full((3, 4), -c, np.float32)) == c
+    assert O.weight_scale(np.zeros((4, 8), np.float32)) == F32(1e-5)
+    assert O.weight_scale(np.full((4, 8), 1e-7, np.float32)) == F32(1e-5)
+    for bad in (np.inf, -np.inf, np.nan):
+        wb = w.copy()
+        wb[3, 5] = bad
+        assert np.isnan(O.weight_scale(wb))
+        packed, gb = O.quantize_weights(wb)
+        assert packed is None and np.isnan(gb)
+
+
+# ---------------------------------------------------------------------------
+# O2: ternarise
+# ---------------------------------------------------------------------------
+
+def test_ternarize_ties_and_clip():
+    """t = +-0.5 -> 0 and t = +-1.5 -> +-1 (round half even, then clip): catches
+    round-half-away-from-zero, floor/truncation and a missing clip."""
+    w = np.array([[0.5, 1.5, -0.5, -1.5, 0.7, -0.3, 3.0, -9.0]], np.float32)
+    gamma = F32(1.0)
+    np.testing.assert_array_equal(O.ternarize(w, gamma), [[0, 1, 0, -1, 1, 0, 1, -1]])
+    # just above / below the 0.5 threshold after the fp32 division
+    g = F32(0.8125)
+    half = F32(0.40625)                     # exactly g/2
+    above = np.nextafter(half, F32(1), dtype=np.float32)
+    below = np.nextafter(half, F32(0), dtype=np.float32)
+    np.testing.assert_array_equal(O.ternarize(np.array([half, above, below, -above]), g),
+                                  [0, 1, 0, -1])
+
+
+def test_ternarize_gaussian_closed_form():
+    """For W ~ N(0, s^2), gamma -> s*sqrt(2/pi) and q = 0 iff |W| < gamma/2, so
+    P(q = 0) = erf(1/(2*sqrt(pi))) = 0.31006 and P(+1) = P(-1) = 0.34497.
+    Catches dividing by absmax or RMS instead of the absolute mean."""
+    w = np.random.Generator(np.random.PCG64(21)).standard_normal(1 << 22, dtype=np.float32)
+    w *= F32(0.02)
+    q = O.ternarize(w, O.weight_scale(w))
+    p0 = math.erf(1.0 / (2.0 * math.sqrt(math.pi)))
+    n = w.size
+    sigma0 = math.sqrt(p0 * (1 - p0) / n)
+    assert abs(np.mean(q == 0) - p0) < 5 * sigma0
+    p1 = (1 - p0) / 2
+    sigma1 = math.sqrt(p1 * (1 - p1) / n)
+    assert abs(np.mean(q == 1) - p1) < 5 * sigma1
+    assert abs(np.mean(q == -1) - p1) < 5 * sigma1
+    assert set(np.unique(q).tolist()) <= {-1, 0, 1}
+
+
+def test_ternarize_symmetry_and_scale():
+    rng = np.random.Generator(np.random.PCG64(3))
+    w = (rng.standard_normal((16, 64)) * 0.02).astype(np.float32)
+    g = O.weight_scale(w)
+    q = O.ternarize(w, g)
+    np.testing.assert_array_equal(O.ternarize(-w, O.weight_scale(-w)), -q)
+    w2 = w * F32(8.0)
+    np.testing.assert_array_equal(O.ternarize(w2, O.weight_scale(w2)), q)
+
+
+# ---------------------------------------------------------------------------
+# O3: pack / unpack
+# ---------------------------------------------------------------------------
+
+def test_pack_roundtrip_all_valid_bytes():
+    """All 81 bytes built from codes {0,1,2} survive unpack->pack; code 3 is rejected."""
+    valid = [c0 | c1 << 2 | c2 << 4 | c3 << 6
+             for c0, c1, c2, c3 in itertools.product(range(3), repeat=4)]
+    b = np.array([valid], dtype=np.uint8)
+    np.testing.assert_array_equal(O.pack_codes(O.unpack_codes(b)), b)
+    with pytest.raises(ValueError):
+        O.unpack_codes(np.array([[0xFF]], np.uint8))
+    rng = np.random.Generator(np.random.PCG64(4))
+    q = rng.integers(-1, 2, (13, 40)).astype(np.int8)
+    np.testing.assert_array_equal(O.unpack_codes(O.pack_codes(q)), q)
+    assert O.pack_codes(q).shape == (13, 10)
+
+
+# ---------------------------------------------------------------------------
+# O4: activations
+# ---------------------------------------------------------------------------
+
+def test_act_quant_invariants():
+    """Range, exact 127 at the row maximum, sign symmetry, power-of-two scaling,
+    per-token independence and the half-step error bound."""
+    rng = np.random.Generator(np.random.PCG64(9))
+    x = rng.standard_normal((257, 96)).astype(np.float32)
+    x[5] *= F32(1e4)
+    x[6] *= F32(1e-3)
+    xq, d = O.quantize_acts(x)
+    assert xq.min() >= -127 and xq.max() <= 127
+    np.testing.assert_array_equal(np.abs(xq.astype(np.int32)).max(axis=1), 127)
+    xn, dn = O.quantize_acts(-x)
+    np.testing.assert_array_equal(xn, -xq)
+    np.testing.assert_array_equal(dn, d)
+    for j in (-7, 4):
+        xs, ds = O.quantize_acts(x * F32(2.0 ** j))
+        np.testing.assert_array_equal(xs, xq)
+        np.testing.assert_array_equal(ds, d * F32(2.0 ** j))
+    # a row's result does not depend on the other rows (per-token, not per-tensor)
+    xr, dr = O.quantize_acts(x[5:6])
+    np.testing.assert_array_equal(xr[0], xq[5])
+    assert dr[0] == d[5]
+    # |xq*d - x| <= d/2 (plus fp32 slack) everywhere: catches d = a/128 or Qb = 128
+    err = np.abs(xq.astype(np.float64) * d[:, None] - x.astype(np.float64))
+    assert np.all(err <= d[:, None].astype(np.float64) * (0.5 + 1e-5))
+
+
+def test_act_quant_ties_and_zero_row():
+    """Row with absmax 127 has s = 1 exactly, so xq = round-half-even(x)."""
+    x = np.array([[127.0, 2.5, -0.5, 3.5, 126.5, -1.5, 0.49, -127.0],
+                  [0.0] * 8], np.float32)
+    xq, d = O.quantize_acts(x)
+    np.testing.assert_array_equal(xq[0], [127, 2, 0, 4, 126, -2, 0, -127])
+    assert d[0] == F32(1.0)
+    np.testing.assert_array_equal(xq[1], 0)
+    assert d[1].view(np.uint32) == 0x33A917DC          # RN32(RN32(1e-5)/127)
+
+
+def test_act_quant_rounding_of_product_matches_fraction():
+    """xq = rne(RN32(x*s)): compare with exact Fractions, rounding the product
+    to fp32 by hand through rn32_ratio's independent check above."""
+    rng = np.random.Generator(np.random.PCG64(10))
+    x = rng.standard_normal((4, 33)).astype(np.float32)
+    xq, d = O.quantize_acts(x)
+    for m in range(4):
+        a = max(abs(Fraction(float(v))) for v in x[m])
+        s = F32(127.0) / F32(float(a))
+        for k in range(33):
+            prod = Fraction(float(x[m, k])) * Fraction(float(s))
+            p32 = O.rn32_ratio(abs(prod.numerator), prod.denominator)
+            p = Fraction(float(p32)) * (1 if prod >= 0 else -1)
+            fl = math.floor(p)
+            rem = p - fl
+            r = fl + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2) else 0)
+            assert int(xq[m, k]) == max(-128, min(127, r))
+
+
+# ---------------------------------------------------------------------------
+# O5: integer contraction
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [4, 8])
+def test_matmul_brute_force_every_ternary_row(k):
+    """W enumerates all 3^K ternary rows; every output is checked against a
+    pure-Python integer dot product.  Catches transposed operands, a wrong sign,
+    a wrong unpack order and any dropped term."""
+    rows = np.array(list(itertools.product((-1, 0, 1), repeat=k)), dtype=np.int8)
+    rng = np.random.Generator(np.random.PCG64(k))
+    xq = rng.integers(-128, 128, (3, k)).astype(np.int8)
+    xq[0, 0] = -128
+    xq[1, :] = 127
+    packed = O.pack_codes(rows)
+    acc, _ = O.ternary_linear(packed, F32(1.0), xq, np.ones(3, np.float32))
+    for m in range(3):
+        for n in range(rows.shape[0]):
+            want = 0
+            for j in range(k):
+                want += int(rows[n, j]) * int(xq[m, j])
+            assert int(acc[m, n]) == want
+
+
+def test_matmul_equals_sum_pos_minus_sum_neg():
+    """The pages' form (sum over +1 weights minus sum over -1 weights)."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    q = rng.integers(-1, 2, (37, 100)).astype(np.int8)
+    xq = rng.integers(-127, 128, (5, 100)).astype(np.int8)
+    acc = O.integer_matmul(q, xq)
+    for m in range(5):
+        for n in range(37):
+            assert int(acc[m, n]) == O.sum_pos_minus_sum_neg(q[n], xq[m])
+    np.testing.assert_array_equal(O.integer_matmul(-q, xq), -acc)
+
+
+def test_identity_weights_reproduce_activations():
+    """W = I: gamma = RN32(1/K), every diagonal t ~ K >= 1.5 -> q = I, acc = xq."""
+    k = 64
+    packed, gamma = O.quantize_weights(np.eye(k, dtype=np.float32))
+    assert gamma == F32(1.0 / k)
+    np.testing.assert_array_equal(O.unpack_codes(packed), np.eye(k, dtype=np.int8))
+    x = np.random.Generator(np.random.PCG64(2)).standard_normal((3, k)).astype(np.float32)
+    xq, d, acc, y = O.quant_linear(packed, gamma, x)
+    np.testing.assert_array_equal(acc, xq.astype(np.int32))
+    np.testing.assert_array_equal(y, xq.astype(np.float32) * (gamma * d)[:, None])
+
+
+def test_sampled_outputs_match_full():
+    rng = np.random.Generator(np.random.PCG64(14))
+    w = (rng.standard_normal((40, 128)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((6, 128)).astype(np.float32)
+    packed, gamma = O.quantize_weights(w)
+    xq, d, acc, y = O.quant_linear(packed, gamma, x)
+    mi = rng.integers(0, 6, 50)
+    ni = rng.integers(0, 40, 50)
+    a2, y2 = O.ternary_linear_at(packed, gamma, xq, d, mi, ni)
+    np.testing.assert_array_equal(a2, acc[mi, ni])
+    np.testing.assert_array_equal(y2.view(np.uint32), y[mi, ni].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# O6: rescale
+# ---------------------------------------------------------------------------
+
+def test_dequant_error_bound_and_zero():
+    """y is within two fp32 roundings of acc*gamma*d (exact rationals), and acc=0 -> +0."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    acc = rng.integers(-(1 << 20), 1 << 20, (7, 50)).astype(np.int32)
+    acc[0, :3] = 0
+    d = (np.abs(rng.standard_normal(7)) * 0.05).astype(np.float32)
+    gamma = F32(0.0159587)
+    y = O.dequantize(acc, gamma, d)
+    assert np.all(y[0, :3] == 0) and not np.any(np.signbit(y[0, :3]))
+    for m in range(7):
+        for n in range(50):
+            exact = Fraction(int(acc[m, n])) * Fraction(float(gamma)) * Fraction(float(d[m]))
+            if exact == 0:
+                continue
+            rel = abs((Fraction(float(y[m, n])) - exact) / exact)
+            assert rel <= Fraction(2 * 2 ** -24 + 2 ** -47)
+
+
+def test_bf16_rounding_matches_torch():
+    """The oracle's fp32->bf16 rounding against torch's conversion (RNE)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.Generator(np.random.PCG64(16))
+    y = (rng.standard_normal(20000) * np.exp2(rng.integers(-40, 40, 20000))).astype(np.float32)
+    ties = (rng.integers(0, 1 << 15, 2000).astype(np.uint32) << np.uint32(16)) | np.uint32(0x8000)
+    y = np.concatenate([y, ties.view(np.float32),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 3.4e38, -3.4e38, 1e-40], np.float32)])
+    y = y[np.isfinite(y) | np.isinf(y)]
+    got = O.f32_to_bf16_bits(y)
+    want = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    nan = O.f32_to_bf16_bits(np.array([np.nan], np.float32))
+    assert (int(nan[0]) & 0x7F80) == 0x7F80 and (int(nan[0]) & 0x7F) != 0
+
+
+def test_bf16_upcast_is_exact():
+    torch = pytest.importorskip("torch")
+    x = torch.randn(1000, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.bf16_bits_to_f32(bits), x.float().numpy())
