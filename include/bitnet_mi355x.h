@@ -1,0 +1,159 @@
+/*
+ * bitnet_mi355x.h - C ABI of the BitNet b1.58 W1.58A8 ternary linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (web pages, cited by title and section):
+ *  - onedollarvps.pages.dev, "如何在本地運行 BitNet B1.58（1-Bit LLM）", section 2
+ *    (technical background, 1-bit vs 1.58-bit quantisation): weights are divided by
+ *    their mean absolute value, then rounded and clipped to {-1, 0, +1}.
+ *  - dashen-tech.com, "BitNet.cpp 深度解析", section 2.3 (I2_S format): two bits per
+ *    stored weight; section 3.1 (integer matmul): with ternary weights the product
+ *    is the sum of inputs under +1 weights minus the sum under -1 weights.
+ *  - communeify.com, "微軟 BitNet b1.58 震撼登場", 2B4T section, quantisation
+ *    details: W1.58A8, i.e. ternary weights and 8-bit integer activations.
+ *
+ * Readings where the pages are silent (the CPU oracle uses the same ones):
+ *  gamma  = RN32(exact sum|W| / (N*K)), gamma* = max(gamma, RN32(1e-5));
+ *  q      = clip(round_half_even(RN32(W / gamma*)), -1, 1);
+ *  packed = code q+1 in {0,1,2}, four codes per byte, least significant pair
+ *           first, row n at bytes [n*K/4, (n+1)*K/4);
+ *  per token m: astar = max(max_k |x[m,k]|, RN32(1e-5)), s = RN32(127 / astar),
+ *           xq = clip(round_half_even(RN32(x*s)), -128, 127), d[m] = RN32(astar / 127);
+ *  acc[m,n] = sum_k q[n,k] * xq[m,k] (exact int32);
+ *  y[m,n]   = RN32(float(acc) * RN32(gamma* * d[m])); bf16 y = round-to-nearest-even.
+ * Every integer result (packed bytes, gamma*, xq, d, acc) is bit-identical to the
+ * CPU oracle, and so is y under the rescale order above.
+ *
+ * Conventions for every call:
+ *  - All array pointers are DEVICE pointers owned by the caller.  Row-major,
+ *    contiguous, no strides.  No call allocates, frees, synchronises or keeps a
+ *    pointer after it returns.
+ *  - All work is enqueued on `stream` (0 = the legacy default stream); results are
+ *    ready when the caller's own synchronisation on that stream completes.
+ *  - Arguments are validated before any HIP call; a bad argument returns its
+ *    status and enqueues nothing.  A failed launch returns BITNET_ERR_HIP.  A fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ *  - 16-byte aligned packed weights / int8 activations with K % 64 == 0 take the
+ *    fast kernels; any other K % 4 == 0 layout takes a slower generic kernel with
+ *    identical results.
+ *  - The library keeps no mutable global state: calls are thread-safe.  Calls that
+ *    share an output buffer on different streams race, as with any kernel.
+ */
+#ifndef BITNET_MI355X_H
+#define BITNET_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bitnet_status {
+  BITNET_OK = 0,
+  BITNET_ERR_NULL = 1,      /* a required pointer is NULL */
+  BITNET_ERR_SHAPE = 2,     /* a size is negative, K % 4 != 0, or a size limit is exceeded */
+  BITNET_ERR_DTYPE = 3,     /* unknown bitnet_dtype value */
+  BITNET_ERR_ALIGN = 4,     /* an fp32/bf16 pointer is not aligned to its element size */
+  BITNET_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the queried size */
+  BITNET_ERR_HIP = 6        /* a HIP launch failed (hipGetLastError) */
+} bitnet_status;
+
+typedef enum bitnet_dtype { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
+
+/* Largest N*K accepted by bitnet_quantize_weights (exact-sum limit): 2^38 - 1. */
+#define BITNET_MAX_WEIGHTS ((int64_t)1 << 38)
+/* Largest K accepted by the linear calls: |acc| <= 127*K stays below 2^24, so
+ * float(acc) is exact. */
+#define BITNET_MAX_K ((int64_t)131072)
+
+/* Human-readable name of a status value (static string, never NULL). */
+const char *bitnet_status_string(int status);
+
+/* Bytes of the packed weight matrix: N * (K / 4).  0 for invalid sizes. */
+size_t bitnet_packed_bytes(int64_t N, int64_t K);
+
+/* Bytes of device workspace bitnet_quantize_weights needs (a constant 4096). */
+size_t bitnet_quantize_weights_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * Weight quantisation: the absolute-mean scale and the ternary 2-bit packing
+ * (onedollarvps, section 2; dashen-tech, section 2.3).
+ *   w        [N][K] fp32 or bf16 master weights (w_dtype), element-aligned.
+ *   N, K     N >= 1, K >= 4, K % 4 == 0, N*K < BITNET_MAX_WEIGHTS.
+ *   w_packed [N][K/4] uint8 out (layout above).
+ *   w_scale  [1] fp32 out: gamma*.  If W holds Inf or NaN, *w_scale = NaN and
+ *            w_packed is unspecified (detected by the caller after its sync).
+ *   workspace >= bitnet_quantize_weights_workspace_bytes() bytes of device memory,
+ *            8-byte aligned; clobbered; may be reused once the call's work is done.
+ * The sum of |W| is exact (integer per-exponent buckets), so gamma* does not
+ * depend on the launch configuration.
+ */
+bitnet_status bitnet_quantize_weights(const void *w, int w_dtype, int64_t N, int64_t K,
+                                      uint8_t *w_packed, float *w_scale, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-token absmax int8 activation quantisation (communeify, quantisation
+ * details: 8-bit activations; the scheme is the per-token reading above).
+ *   x        [M][K] fp32 or bf16 (x_dtype), finite values, element-aligned.
+ *   M, K     M >= 0 (M == 0 is a no-op), K >= 0 (K == 0: d = RN32(RN32(1e-5)/127)).
+ *   x_q      [M][K] int8 out, values in [-127, 127].
+ *   x_scale  [M] fp32 out: d[m].
+ */
+bitnet_status bitnet_quantize_acts(const void *x, int x_dtype, int64_t M, int64_t K,
+                                   int8_t *x_q, float *x_scale, hipStream_t stream);
+
+/*
+ * Ternary linear layer on quantised inputs: integer contraction and rescale
+ * (dashen-tech, section 3.1).
+ *   w_packed [N][K/4] uint8 from bitnet_quantize_weights.
+ *   w_scale  [1] fp32 gamma* (device).
+ *   x_q      [M][K] int8; x_scale [M] fp32 d[m].
+ *   M, N, K  M >= 0, N >= 0 (0 = no-op), K % 4 == 0, 0 <= K <= BITNET_MAX_K.
+ *   y        [M][N] out, fp32 or bf16 (y_dtype), element-aligned.
+ *   acc_out  optional [M][N] int32 out (NULL to skip): the exact accumulator.
+ * M <= 16 runs the HBM-streaming decode kernel, larger M the int8-MFMA prefill
+ * kernel; both produce identical integers.
+ */
+bitnet_status bitnet_ternary_linear(const uint8_t *w_packed, const float *w_scale,
+                                    const int8_t *x_q, const float *x_scale, int64_t M,
+                                    int64_t N, int64_t K, void *y, int y_dtype,
+                                    int32_t *acc_out, hipStream_t stream);
+
+/*
+ * Measurement variant of bitnet_ternary_linear: the same validation, kernel choice
+ * and results; in addition the kernel's dispatch records `start` when the kernel
+ * begins and `stop` when it ends (either may be NULL), so
+ * hipEventElapsedTime(start, stop) is the kernel's own duration, free of launch
+ * gaps.  The events must come from hipEventCreate on the current device.
+ */
+bitnet_status bitnet_ternary_linear_timed(const uint8_t *w_packed, const float *w_scale,
+                                          const int8_t *x_q, const float *x_scale, int64_t M,
+                                          int64_t N, int64_t K, void *y, int y_dtype,
+                                          int32_t *acc_out, hipEvent_t start, hipEvent_t stop,
+                                          hipStream_t stream);
+
+/*
+ * Activation quantisation fused into the layer, for chaining layers without a
+ * separate quantisation launch (one chained step: y = linear(quant(x))).
+ *   x        [M][K] fp32 or bf16 (x_dtype), finite values.
+ *   x_q, x_scale  [M][K] int8 and [M] fp32 out: the same values
+ *            bitnet_quantize_acts(x) writes (so further layers that share this
+ *            input can call bitnet_ternary_linear on them).
+ *   other arguments as bitnet_ternary_linear.
+ * For M <= 16 (when M*K fits the decode kernel's on-chip buffer) each workgroup
+ * quantises the activations itself; otherwise this is bitnet_quantize_acts
+ * followed by bitnet_ternary_linear on the same stream.
+ */
+bitnet_status bitnet_quant_linear(const uint8_t *w_packed, const float *w_scale,
+                                  const void *x, int x_dtype, int64_t M, int64_t N, int64_t K,
+                                  int8_t *x_q, float *x_scale, void *y, int y_dtype,
+                                  int32_t *acc_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_MI355X_H */

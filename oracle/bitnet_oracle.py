@@ -101,21 +101,28 @@ def exact_abs_sum_units(w: np.ndarray):
 
     Every finite fp32 value is an integer multiple of 2**-149 (the subnormal
     spacing): a normal value with biased exponent e and fraction f equals
-    (2**23 + f) * 2**(e - 1) units, a subnormal equals f units.  The sum is
-    formed per distinct exponent in int64 (each partial sum stays below 2**63
-    for fewer than 2**39 elements) and combined in Python integers, so no
-    rounding occurs anywhere.  Returns None if any element is Inf or NaN.
+    (2**23 + f) * 2**(e - 1) units, a subnormal equals f units.  The 24-bit
+    significands are summed per exponent, split into two 12-bit halves so that
+    every partial sum is an integer below 4096 * 2**38 < 2**53; numpy's bincount
+    adds them in float64, where such integers and their sums are exact.  The
+    per-exponent sums are combined in Python integers, so no rounding occurs
+    anywhere.  Needs fewer than 2**38 elements.  Returns None if any element is
+    Inf or NaN.
     """
     bits = np.ascontiguousarray(w, dtype=np.float32).reshape(-1).view(np.uint32)
-    e = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64)
+    if bits.size >= (1 << 38):
+        raise ValueError("exact sum supports fewer than 2**38 elements")
+    e = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.intp)
     if np.any(e == 0xFF):
         return None
-    frac = (bits & np.uint32(0x7FFFFF)).astype(np.int64)
-    mant = np.where(e > 0, frac | (1 << 23), frac)
-    shift = np.where(e > 0, e - 1, 0)
+    frac = bits & np.uint32(0x7FFFFF)
+    mant = np.where(e > 0, frac | np.uint32(1 << 23), frac)
+    hi = np.bincount(e, weights=(mant >> np.uint32(12)).astype(np.float64), minlength=256)
+    lo = np.bincount(e, weights=(mant & np.uint32(0xFFF)).astype(np.float64), minlength=256)
     total = 0
-    for s in np.unique(shift):
-        total += int(mant[shift == s].sum(dtype=np.int64)) << int(s)
+    for ex in range(255):
+        part = (int(hi[ex]) << 12) + int(lo[ex])
+        total += part << (ex - 1 if ex > 0 else 0)
     return total
 
 

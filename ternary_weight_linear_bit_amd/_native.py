@@ -1,0 +1,180 @@
+"""ctypes binding of libbitnet_mi355x.so: argument marshalling only.
+
+Function names match the C ABI in include/bitnet_mi355x.h.  torch supplies the
+device memory (``data_ptr()``) and the stream (``torch.cuda.current_stream()``);
+every step of the layer runs in the HIP kernels behind these calls.  If the
+library is missing, the first call raises: there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbitnet_mi355x.so")
+
+BITNET_OK = 0
+BITNET_F32 = 0
+BITNET_BF16 = 1
+STATUS = {0: "BITNET_OK", 1: "BITNET_ERR_NULL", 2: "BITNET_ERR_SHAPE", 3: "BITNET_ERR_DTYPE",
+          4: "BITNET_ERR_ALIGN", 5: "BITNET_ERR_WORKSPACE", 6: "BITNET_ERR_HIP"}
+
+# exported symbol -> (restype, argtypes); kept in the order of the public header
+_P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "bitnet_status_string": (ctypes.c_char_p, [_I]),
+    "bitnet_packed_bytes": (_SZ, [_I64, _I64]),
+    "bitnet_quantize_weights_workspace_bytes": (_SZ, [_I64, _I64]),
+    "bitnet_quantize_weights": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bitnet_quantize_acts": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
+    "bitnet_ternary_linear": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P]),
+    "bitnet_ternary_linear_timed": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _P,
+                                         _P]),
+    "bitnet_quant_linear": (_I, [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P]),
+}
+
+_lib = None
+
+
+class BitnetError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run python -m ternary_weight_linear_bit_amd.build)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn, status):
+    if status != BITNET_OK:
+        raise BitnetError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt):
+    import torch
+    if dt == torch.float32:
+        return BITNET_F32
+    if dt == torch.bfloat16:
+        return BITNET_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA tensors")
+
+
+def bitnet_packed_bytes(n: int, k: int) -> int:
+    return lib().bitnet_packed_bytes(n, k)
+
+
+def bitnet_quantize_weights(w, packed=None, scale=None, workspace=None, stream=None):
+    """w: [N, K] fp32/bf16 -> (packed uint8 [N, K/4], gamma* fp32 [1])."""
+    import torch
+    _need_cuda(w)
+    n, k = w.shape
+    dev = w.device
+    if packed is None:
+        packed = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_bytes = lib().bitnet_quantize_weights_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _need_cuda(packed, scale, workspace)
+    _check("bitnet_quantize_weights", lib().bitnet_quantize_weights(
+        _ptr(w), _dtype_code(w.dtype), n, k, _ptr(packed), _ptr(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return packed, scale
+
+
+def bitnet_quantize_acts(x, x_q=None, x_scale=None, stream=None):
+    """x: [M, K] fp32/bf16 -> (x_q int8 [M, K], d fp32 [M])."""
+    import torch
+    _need_cuda(x)
+    m, k = x.shape
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need_cuda(x_q, x_scale)
+    _check("bitnet_quantize_acts", lib().bitnet_quantize_acts(
+        _ptr(x), _dtype_code(x.dtype), m, k, _ptr(x_q), _ptr(x_scale), _stream(stream)))
+    return x_q, x_scale
+
+
+def bitnet_ternary_linear(w_packed, w_scale, x_q, x_scale, y=None, y_dtype=None,
+                          acc_out=None, stream=None):
+    """Packed W [N, K/4] x int8 X [M, K] -> y [M, N] (fp32 or bf16)."""
+    import torch
+    _need_cuda(w_packed, w_scale, x_q, x_scale, acc_out)
+    m, k = x_q.shape
+    n = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != k:
+        raise ValueError("w_packed and x_q disagree on K")
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype or torch.float32, device=x_q.device)
+    _need_cuda(y)
+    _check("bitnet_ternary_linear", lib().bitnet_ternary_linear(
+        _ptr(w_packed), _ptr(w_scale), _ptr(x_q), _ptr(x_scale), m, n, k, _ptr(y),
+        _dtype_code(y.dtype), _ptr(acc_out), _stream(stream)))
+    return y
+
+
+def bitnet_ternary_linear_timed(w_packed, w_scale, x_q, x_scale, y, start, stop, acc_out=None,
+                                stream=None):
+    """bitnet_ternary_linear whose kernel dispatch records the torch.cuda.Event
+    pair (start, stop), which must have been recorded once so that they exist."""
+    m, k = x_q.shape
+    n = w_packed.shape[0]
+    _check("bitnet_ternary_linear_timed", lib().bitnet_ternary_linear_timed(
+        _ptr(w_packed), _ptr(w_scale), _ptr(x_q), _ptr(x_scale), m, n, k, _ptr(y),
+        _dtype_code(y.dtype), _ptr(acc_out), ctypes.c_void_p(start.cuda_event),
+        ctypes.c_void_p(stop.cuda_event), _stream(stream)))
+    return y
+
+
+def bitnet_quant_linear(w_packed, w_scale, x, x_q=None, x_scale=None, y=None, y_dtype=None,
+                        acc_out=None, stream=None):
+    """Act-quant fused into the layer: returns (y, x_q, x_scale)."""
+    import torch
+    _need_cuda(w_packed, w_scale, x, acc_out)
+    m, k = x.shape
+    n = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != k:
+        raise ValueError("w_packed and x disagree on K")
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype or torch.float32, device=x.device)
+    _need_cuda(x_q, x_scale, y)
+    _check("bitnet_quant_linear", lib().bitnet_quant_linear(
+        _ptr(w_packed), _ptr(w_scale), _ptr(x), _dtype_code(x.dtype), m, n, k, _ptr(x_q),
+        _ptr(x_scale), _ptr(y), _dtype_code(y.dtype), _ptr(acc_out), _stream(stream)))
+    return y, x_q, x_scale

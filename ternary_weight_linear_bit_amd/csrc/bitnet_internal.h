@@ -1,0 +1,152 @@
+// Internal declarations shared by the HIP translation units of libbitnet_mi355x.
+// Not part of the public ABI (include/bitnet_mi355x.h is).
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bitnet {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr float kEps = 1e-5f;   // floor of both scales; the literal rounds to RN32(1e-5)
+constexpr float kQb = 127.0f;   // symmetric int8 activation range
+
+// Exact bf16 -> fp32 upcast.
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN -> quiet NaN with its sign.
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Wave64 reductions (butterfly over all 64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// 4x4 byte transpose of four dwords: out[i].byte[b] = in[b].byte[i].
+__device__ __forceinline__ void transpose4x4_bytes(const uint32_t in[4], uint32_t out[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[i] = ((in[0] >> (8 * i)) & 0xffu) | (((in[1] >> (8 * i)) & 0xffu) << 8) |
+             (((in[2] >> (8 * i)) & 0xffu) << 16) | (((in[3] >> (8 * i)) & 0xffu) << 24);
+  }
+}
+
+// Quantise four activations with the token's factor s = RN32(127 / a*):
+// clip(rne(RN32(x * s)), -128, 127), packed little-endian into one dword.
+__device__ __forceinline__ uint32_t quant4(const float* v, float s) {
+  uint32_t out = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float q = rintf(v[i] * s);
+    q = fminf(fmaxf(q, -128.0f), 127.0f);
+    out |= ((uint32_t)(int32_t)q & 0xffu) << (8 * i);
+  }
+  return out;
+}
+
+// 16 consecutive fp32 or bf16 activations from a 16-byte aligned address
+// (i16 counts groups of 16 elements).
+template <bool BF16>
+__device__ __forceinline__ void load16_act(const void* x, int64_t i16, float v[16]) {
+  if (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * i16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 a = p[h];
+      const uint32_t d[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * h + 2 * j] = __uint_as_float(d[j] << 16);
+        v[8 * h + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(x) + 4 * i16;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float4 a = p[h];
+      v[4 * h] = a.x;
+      v[4 * h + 1] = a.y;
+      v[4 * h + 2] = a.z;
+      v[4 * h + 3] = a.w;
+    }
+  }
+}
+
+// Raw buffer resource over [base, base + bytes).  Loads at offsets >= bytes
+// return zeros (hardware range check), which pads ragged rows and tails without
+// branches.  Word 3 selects 32-bit data format as gfx9 buffer loads require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every range used with make_rsrc
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// Wait for this wave's LDS operations, then workgroup barrier.  Unlike
+// __syncthreads() this does not wait for outstanding global loads, so weight
+// prefetches stay in flight across it; the "memory" clobber keeps the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Where a linear-layer kernel is launched.  With a start or stop event the
+// dispatch itself records them (hipExtLaunchKernelGGL), so their elapsed time is
+// the kernel's own duration.
+struct Launch {
+  hipStream_t stream;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+template <typename F, typename... Args>
+void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, const Launch& l, Args... args) {
+  if (l.start != nullptr || l.stop != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, l.stream, l.start, l.stop, 0u,
+                          args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, l.stream, args...);
+}
+
+// Host-side launchers (one per kernel family); each returns a hipError_t from
+// hipGetLastError() after its launches.
+hipError_t launch_wq(const void* w, bool w_bf16, int64_t n_weights, uint8_t* w_packed,
+                     float* w_scale, void* workspace, hipStream_t s);
+hipError_t launch_aq(const void* x, bool x_bf16, int64_t M, int64_t K, int8_t* x_q,
+                     float* x_scale, hipStream_t s);
+// Decode (skinny) kernel: returns hipErrorInvalidValue when the shape does not fit it.
+bool gemv_fits(int64_t M, int64_t K);
+bool gemv_fused_fits(int64_t M, int64_t K);  // fused activation quantisation, small M
+hipError_t launch_gemv(const uint8_t* wp, const float* w_scale, const int8_t* xq,
+                       const float* x_scale, const void* xf, int xf_dtype, int8_t* xq_out,
+                       float* xs_out, int M, int N, int K, void* y, bool y_bf16,
+                       int32_t* acc_out, const Launch& l);
+hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
+                       const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
+                       int32_t* acc_out, const Launch& l);
+hipError_t launch_generic_linear(const uint8_t* wp, const float* w_scale, const int8_t* xq,
+                                 const float* x_scale, int64_t M, int64_t N, int64_t K,
+                                 void* y, bool y_bf16, int32_t* acc_out, const Launch& l);
+
+}  // namespace bitnet

@@ -1,0 +1,265 @@
+// Weight quantisation: exact absolute-mean scale and ternary 2-bit packing.
+//
+// Method: onedollarvps.pages.dev, "如何在本地運行 BitNet B1.58（1-Bit LLM）",
+// section 2 (technical background): weights are divided by their mean absolute
+// value, then rounded and clipped to {-1, 0, +1}.  Storage: dashen-tech.com,
+// "BitNet.cpp 深度解析", section 2.3 (I2_S): two bits per weight.
+//
+// gamma is RN32 of the EXACT mean: a 1-ulp change of gamma flips some of the
+// ~10^8 weights of a large matrix, so the sum must not depend on summation order.
+// Every finite fp32 |w| is an integer count of 2^-149 units: (2^23 + frac) shifted
+// left by (biased exponent - 1), or frac for sub-normals.  Pass 1 adds the 24-bit
+// significands into 256 uint64 buckets keyed by biased exponent (integer atomics:
+// exact and order-free).  Pass 2 (one thread) forms the exact sum in a 320-bit
+// integer, divides by N*K and rounds once to fp32.  Pass 3 ternarises and packs.
+//
+// Workspace layout (device, caller-owned, >= kWsBytes):
+//   [0, 2048)    uint64 buckets[256]   (bucket 255 counts Inf/NaN weights)
+//   [2048, 2052) float  threshold      (see wq_finish)
+#include "bitnet_internal.h"
+
+namespace bitnet {
+namespace {
+
+constexpr int kHistThreads = 256;
+constexpr int kPackThreads = 256;
+
+__global__ __launch_bounds__(256) void wq_clear(unsigned long long* __restrict__ buckets) {
+  buckets[threadIdx.x] = 0ull;
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_bits(const void* w, int64_t i) {
+  if (BF16) return (uint32_t)(reinterpret_cast<const uint16_t*>(w)[i]) << 16;
+  return reinterpret_cast<const uint32_t*>(w)[i];
+}
+
+__device__ __forceinline__ void hist_add(unsigned long long* sb, uint32_t bits) {
+  const uint32_t e = (bits >> 23) & 0xffu;
+  const uint32_t f = bits & 0x7fffffu;
+  if (e == 0xffu) {
+    atomicAdd(&sb[255], 1ull);                      // non-finite flag
+  } else {
+    const uint32_t m = e ? (f | 0x800000u) : f;     // units of 2^(max(e,1)-1-149)
+    if (m) atomicAdd(&sb[e], (unsigned long long)m);
+  }
+}
+
+// Pass 1: per-exponent integer sums of the significands of |w|.
+template <bool BF16>
+__global__ __launch_bounds__(kHistThreads) void wq_hist(const void* __restrict__ w,
+                                                        int64_t count, bool vec,
+                                                        unsigned long long* __restrict__ gb) {
+  __shared__ unsigned long long sb[256];
+  sb[threadIdx.x] = 0ull;
+  __syncthreads();
+  // 16-byte vectors: 4 fp32 or 8 bf16 elements.
+  constexpr int kVec = BF16 ? 8 : 4;
+  const int64_t nvec = vec ? count / kVec : 0;
+  const int64_t stride = (int64_t)gridDim.x * kHistThreads;
+  const uint4* wv = reinterpret_cast<const uint4*>(w);
+  for (int64_t v = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; v < nvec; v += stride) {
+    const uint4 p = wv[v];
+    const uint32_t d[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (BF16) {
+        hist_add(sb, d[j] << 16);
+        hist_add(sb, d[j] & 0xffff0000u);
+      } else {
+        hist_add(sb, d[j]);
+      }
+    }
+  }
+  for (int64_t i = nvec * kVec + (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < count;
+       i += stride)
+    hist_add(sb, load_bits<BF16>(w, i));
+  __syncthreads();
+  const unsigned long long s = sb[threadIdx.x];
+  if (s) atomicAdd(&gb[threadIdx.x], s);
+}
+
+__device__ __forceinline__ void add_u64(uint64_t L[5], uint64_t x) {
+  uint64_t prev = L[0];
+  L[0] += x;
+  uint64_t carry = L[0] < prev;
+#pragma unroll
+  for (int i = 1; i < 5; ++i) {
+    prev = L[i];
+    L[i] += carry;
+    carry = (L[i] < prev);
+  }
+}
+
+// Pass 2 (one thread): gamma* = max(RN32(S * 2^-149 / count), RN32(1e-5)) and the
+// ternarisation threshold.
+//
+// Threshold: q = +1 exactly when RN32(w / gamma*) > 0.5.  The fp32 values next to
+// 0.5 are 0.5 - 2^-25 and 0.5 + 2^-24, and a tie at 0.5 + 2^-25 rounds to 0.5
+// (even significand), so RN32(v) > 0.5 iff v > 0.5 + 2^-25, i.e. iff
+// w > T = gamma* * (0.5 + 2^-25).  T is exact in fp64 (24-bit times 25-bit
+// significands), and for fp32 w the test w > T equals w >= thr with thr the
+// smallest fp32 above T.  q = -1 is the mirror image.  This gives the quotient's
+// correctly rounded decision without a per-weight division.
+__global__ void wq_finish(const unsigned long long* __restrict__ b, unsigned long long count,
+                          float* __restrict__ w_scale, float* __restrict__ thr_out) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  if (b[255] != 0ull) {
+    *w_scale = __uint_as_float(0x7fc00000u);
+    *thr_out = __uint_as_float(0x7fc00000u);
+    return;
+  }
+  // S = sum_{e>=1} b[e] * 2^(e-1) + b[0]  (Horner from the top exponent down)
+  uint64_t L[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
+  for (int e = 254; e >= 1; --e) {
+    uint64_t carry = 0ull;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const uint64_t v = L[i];
+      L[i] = (v << 1) | carry;
+      carry = v >> 63;
+    }
+    add_u64(L, b[e]);
+  }
+  add_u64(L, b[0]);
+
+  float gamma = 0.0f;
+  int top = -1;
+  for (int i = 4; i >= 0; --i)
+    if (L[i] != 0ull) { top = i; break; }
+  if (top >= 0) {
+    const int bitlen = 64 * top + (64 - __clzll(L[top]));
+    const int p = bitlen - 64;  // S = H * 2^p + (lower bits)
+    uint64_t H;
+    bool sticky = false;
+    if (p <= 0) {
+      H = L[0] << (-p);
+    } else {
+      const int li = p >> 6, off = p & 63;
+      H = L[li] >> off;
+      if (off) H |= L[li + 1] << (64 - off);
+      if (off && (L[li] & ((1ull << off) - 1ull))) sticky = true;
+      for (int j = 0; j < li; ++j)
+        if (L[j]) sticky = true;
+    }
+    // mean = (H + frac) * 2^(p-149) / count; count < 2^38 so q has >= 26 bits
+    const uint64_t q = H / count;
+    const uint64_t r = H - q * count;
+    const int qb = 64 - __clzll(q);
+    int sh = qb - 24;
+    uint64_t kept = q >> sh;
+    const uint64_t rem = q & ((1ull << sh) - 1ull);
+    const uint64_t half = 1ull << (sh - 1);
+    const bool inexact = sticky || (r != 0ull);
+    if (rem > half || (rem == half && (inexact || (kept & 1ull)))) kept += 1ull;
+    if (kept == (1ull << 24)) { kept >>= 1; sh += 1; }
+    const int biased = sh + p - 149 + 150;  // value = kept * 2^(sh+p-149)
+    if (biased >= 255) {
+      gamma = __uint_as_float(0x7f800000u);
+    } else if (biased >= 1) {
+      gamma = __uint_as_float(((uint32_t)biased << 23) | (uint32_t)(kept & 0x7fffffull));
+    } else {
+      gamma = 0.0f;  // below 2^-126: the floor below takes over
+    }
+  }
+  const float gstar = gamma > kEps ? gamma : kEps;
+  *w_scale = gstar;
+  const double T = (double)gstar * (0.5 + 0x1p-25);
+  const float f = (float)T;
+  *thr_out = ((double)f > T) ? f : __uint_as_float(__float_as_uint(f) + 1u);
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t code_of(uint32_t bits, float thr) {
+  const float a = __uint_as_float(bits & 0x7fffffffu);
+  return a >= thr ? ((bits >> 31) ? 0u : 2u) : 1u;
+}
+
+// Pass 3: 16 weights -> one packed dword (weights 4j..4j+3 in byte j, first weight
+// in the lowest bit pair).  Groups of four consecutive weights never straddle a row
+// because K % 4 == 0, so the packed matrix is the flat row-major sequence of groups.
+template <bool BF16>
+__global__ __launch_bounds__(kPackThreads) void wq_pack(const void* __restrict__ w,
+                                                        int64_t count,
+                                                        bool vec, const float* __restrict__ thr_p,
+                                                        uint8_t* __restrict__ out) {
+  const float thr = *thr_p;
+  const int64_t n16 = vec ? count / 16 : 0;
+  const int64_t stride = (int64_t)gridDim.x * kPackThreads;
+  for (int64_t v = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; v < n16; v += stride) {
+    uint32_t bits[16];
+    if (BF16) {
+      const uint4* p = reinterpret_cast<const uint4*>(w) + 2 * v;
+      const uint4 a = p[0], b = p[1];
+      const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        bits[2 * j] = d[j] << 16;
+        bits[2 * j + 1] = d[j] & 0xffff0000u;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(w) + 4 * v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 a = p[j];
+        bits[4 * j] = a.x;
+        bits[4 * j + 1] = a.y;
+        bits[4 * j + 2] = a.z;
+        bits[4 * j + 3] = a.w;
+      }
+    }
+    uint32_t word = 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) word |= code_of<BF16>(bits[j], thr) << (2 * j);
+    reinterpret_cast<uint32_t*>(out)[v] = word;
+  }
+  // tail: whole groups of four left after the last full 16
+  const int64_t groups = count / 4;
+  for (int64_t g = n16 * 4 + (int64_t)blockIdx.x * kPackThreads + threadIdx.x; g < groups;
+       g += stride) {
+    uint32_t byte = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) byte |= code_of<BF16>(load_bits<BF16>(w, 4 * g + i), thr) << (2 * i);
+    out[g] = (uint8_t)byte;
+  }
+}
+
+int grid_for(int64_t work_items, int threads, int max_blocks) {
+  int64_t b = (work_items + threads - 1) / threads;
+  if (b < 1) b = 1;
+  if (b > max_blocks) b = max_blocks;
+  return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_wq(const void* w, bool w_bf16, int64_t n, uint8_t* w_packed, float* w_scale,
+                     void* workspace, hipStream_t s) {
+  auto* buckets = reinterpret_cast<unsigned long long*>(workspace);
+  float* thr = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + 2048);
+  hipLaunchKernelGGL(wq_clear, dim3(1), dim3(256), 0, s, buckets);
+  // 16-byte vector loads need a 16-byte aligned base; otherwise every element
+  // takes the scalar loop.  Packed dword stores need a 4-byte aligned output.
+  const bool w_vec = ((uintptr_t)w & 15u) == 0;
+  const bool pack_vec = w_vec && (((uintptr_t)w_packed & 3u) == 0);
+  const int64_t per = w_bf16 ? 8 : 4;
+  const int hist_blocks = grid_for(n / per + 1, kHistThreads, 2048);
+  if (w_bf16)
+    hipLaunchKernelGGL(wq_hist<true>, dim3(hist_blocks), dim3(kHistThreads), 0, s, w, n, w_vec,
+                       buckets);
+  else
+    hipLaunchKernelGGL(wq_hist<false>, dim3(hist_blocks), dim3(kHistThreads), 0, s, w, n, w_vec,
+                       buckets);
+  hipLaunchKernelGGL(wq_finish, dim3(1), dim3(64), 0, s, buckets, (unsigned long long)n, w_scale,
+                     thr);
+  const int pack_blocks = grid_for(n / 16 + 1, kPackThreads, 8192);
+  if (w_bf16)
+    hipLaunchKernelGGL(wq_pack<true>, dim3(pack_blocks), dim3(kPackThreads), 0, s, w, n,
+                       pack_vec, thr, w_packed);
+  else
+    hipLaunchKernelGGL(wq_pack<false>, dim3(pack_blocks), dim3(kPackThreads), 0, s, w, n,
+                       pack_vec, thr, w_packed);
+  return hipGetLastError();
+}
+
+}  // namespace bitnet

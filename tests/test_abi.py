@@ -1,0 +1,108 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+public header declares, and rejects bad arguments before making any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_weight_linear_bit_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitnet_mi355x.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS = 0, 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(0x10002)    # 2-byte aligned only
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitnet_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(N.LIB_PATH):
+        pytest.skip("libbitnet_mi355x.so not built")
+    return N.lib()
+
+
+def test_header_declares_expected_calls():
+    names = header_functions()
+    for want in ("bitnet_quantize_weights", "bitnet_quantize_acts", "bitnet_ternary_linear"):
+        assert want in names
+
+
+def test_library_exports_every_header_function(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert name in N.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings_and_sizes(lib):
+    for s in range(0, 8):
+        assert lib.bitnet_status_string(s)
+    assert lib.bitnet_packed_bytes(2560, 6912) == 2560 * 6912 // 4
+    assert lib.bitnet_packed_bytes(3, 6) == 0
+    assert lib.bitnet_packed_bytes(-1, 8) == 0
+    assert lib.bitnet_quantize_weights_workspace_bytes(1, 4) >= 2048 + 4
+
+
+def test_quantize_weights_validation(lib):
+    f = lib.bitnet_quantize_weights
+    assert f(None, 0, 4, 8, FAKE, FAKE, FAKE, 4096, None) == ENULL
+    assert f(FAKE, 0, 4, 8, None, FAKE, FAKE, 4096, None) == ENULL
+    assert f(FAKE, 9, 4, 8, FAKE, FAKE, FAKE, 4096, None) == EDTYPE
+    assert f(FAKE, 0, 0, 8, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
+    assert f(FAKE, 0, 4, 6, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
+    assert f(FAKE, 0, 4, 0, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
+    assert f(FAKE, 0, 1 << 20, 1 << 18, FAKE, FAKE, FAKE, 4096, None) == ESHAPE  # N*K = 2^38
+    assert f(FAKE, 0, 4, 8, FAKE, FAKE, None, 4096, None) == EWS
+    assert f(FAKE, 0, 4, 8, FAKE, FAKE, FAKE, 100, None) == EWS
+    assert f(FAKE_ODD, 0, 4, 8, FAKE, FAKE, FAKE, 4096, None) == EALIGN     # fp32 at 2 bytes
+    assert f(FAKE, 0, 4, 8, FAKE, FAKE, FAKE_ODD, 4096, None) == EALIGN
+
+
+def test_quantize_acts_validation(lib):
+    f = lib.bitnet_quantize_acts
+    assert f(FAKE, 5, 2, 8, FAKE, FAKE, None) == EDTYPE
+    assert f(FAKE, 0, -1, 8, FAKE, FAKE, None) == ESHAPE
+    assert f(None, 0, 0, 8, None, None, None) == OK          # M == 0: nothing to do
+    assert f(None, 0, 2, 8, FAKE, FAKE, None) == ENULL
+    assert f(FAKE, 0, 2, 8, FAKE, None, None) == ENULL
+    assert f(FAKE_ODD, 0, 2, 8, FAKE, FAKE, None) == EALIGN
+
+
+def test_ternary_linear_validation(lib):
+    f = lib.bitnet_ternary_linear
+    assert f(FAKE, FAKE, None, FAKE, 2, 3, 8, FAKE, 0, None, None) == ENULL
+    assert f(FAKE, None, FAKE, FAKE, 2, 3, 8, FAKE, 0, None, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 3, 8, None, 0, None, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 3, 8, FAKE, 2, None, None) == EDTYPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 3, 6, FAKE, 0, None, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, -2, 3, 8, FAKE, 0, None, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 3, 1 << 20, FAKE, 0, None, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 3, 8, FAKE_ODD, 0, None, None) == EALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 3, 8, FAKE, 0, FAKE_ODD, None) == EALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 3, 8, FAKE, 0, None, None) == OK   # empty batch
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 0, 8, FAKE, 0, None, None) == OK   # no outputs
+
+
+def test_quant_linear_validation(lib):
+    f = lib.bitnet_quant_linear
+    assert f(FAKE, FAKE, None, 0, 1, 3, 8, FAKE, FAKE, FAKE, 0, None, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, 0, 1, 3, 8, None, FAKE, FAKE, 0, None, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, 4, 1, 3, 8, FAKE, FAKE, FAKE, 0, None, None) == EDTYPE
+    assert f(FAKE, FAKE, FAKE, 0, 1, 3, 10, FAKE, FAKE, FAKE, 0, None, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE_ODD, 0, 1, 3, 8, FAKE, FAKE, FAKE, 0, None, None) == EALIGN
+    assert f(FAKE, FAKE, FAKE, 0, 0, 3, 8, FAKE, FAKE, FAKE, 0, None, None) == OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(N, "_lib", None)
+    monkeypatch.setattr(N, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        N.lib()

@@ -1,0 +1,66 @@
+"""Parity at the full benchmark shapes, through the same calls the bench times.
+
+For every distinct (K, N) of the 2B-, 8B- and 100B-shaped layer sets: gamma* and
+the packed bytes of the whole matrix (bit-exact), and the accumulators
+and outputs at sampled (token, row) pairs plus one full output row, at the token
+counts of each configuration (decode M = 1 / 16, prefill M = 512 / 2048 / 4096).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bitnet_oracle as O
+from ternary_weight_linear_bit_amd import _native as N
+from ternary_weight_linear_bit_amd import inputs as I
+
+from gpu_helpers import DEV, f32_bits, host
+
+pytestmark = pytest.mark.gpu
+
+# (K, N, token counts) -- every distinct matrix shape of the configurations
+FULL = [
+    (2560, 2560, (1, 512, 4096)), (2560, 640, (1, 4096)), (2560, 6912, (1, 512, 4096)),
+    (6912, 2560, (1, 4096)),
+    (4096, 4096, (1, 16, 2048)), (4096, 1024, (1, 16)), (4096, 14336, (1, 16, 2048)),
+    (14336, 4096, (1, 16, 2048)),
+    (8192, 8192, (1,)), (8192, 28672, (1,)), (28672, 8192, (1,)),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    N.lib()
+
+
+@pytest.mark.parametrize("k,n,ms", FULL, ids=[f"{k}x{n}" for k, n, _ in FULL])
+def test_full_size(k, n, ms):
+    print(f"full-size K={k} N={n} M={ms}", flush=True)
+    seed = I.weight_seed(0, (k * 7 + n) % 7)
+    w = I.master_weights(n, k, seed)
+    w_d = torch.from_numpy(w).to(DEV)
+    packed_d, scale_d = N.bitnet_quantize_weights(w_d)
+    gamma = O.weight_scale(w)
+    assert f32_bits(host(scale_d))[0] == f32_bits(gamma)
+    rng = np.random.Generator(np.random.PCG64(k + n))
+    packed_o = O.pack_codes(O.ternarize(w, gamma))
+    del w, w_d
+    np.testing.assert_array_equal(host(packed_d), packed_o)
+    for m in ms:
+        x = I.activations(m, k, I.ACT_SEED + m)
+        xq_d, xs_d = N.bitnet_quantize_acts(torch.from_numpy(x).to(DEV))
+        xq, d = O.quantize_acts(x)
+        np.testing.assert_array_equal(host(xq_d), xq)
+        np.testing.assert_array_equal(f32_bits(host(xs_d)), f32_bits(d))
+        acc_d = torch.empty((m, n), dtype=torch.int32, device=DEV)
+        y_d = N.bitnet_ternary_linear(packed_d, scale_d, xq_d, xs_d, acc_out=acc_d)
+        acc_h, y_h = host(acc_d), host(y_d)
+        mi = np.concatenate([rng.integers(0, m, 256), np.zeros(n, np.int64)])
+        ni = np.concatenate([rng.integers(0, n, 256), np.arange(n)])
+        acc_w, y_w = O.ternary_linear_at(packed_o, gamma, xq, d, mi, ni)
+        np.testing.assert_array_equal(acc_h[mi, ni], acc_w)
+        np.testing.assert_array_equal(f32_bits(y_h[mi, ni]), f32_bits(y_w))
+    del packed_d
+    torch.cuda.empty_cache()

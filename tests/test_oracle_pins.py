@@ -133,6 +133,23 @@ def test_exact_abs_sum_equals_fraction_sum():
         assert Fraction(units) * Fraction(2) ** -149 == want
 
 
+def test_exact_abs_sum_equals_plain_integer_sum():
+    """Bucketed float64 sums against a plain per-element Python-integer sum on a
+    wide exponent range (catches an inexact bucket sum or a wrong exponent shift)."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    w = (rng.standard_normal(200000) * np.exp2(rng.integers(-140, 120, 200000))).astype(np.float32)
+    bits = w.view(np.uint32)
+    want = 0
+    for b in bits.tolist():
+        e = (b >> 23) & 0xFF
+        f = b & 0x7FFFFF
+        want += ((f | (1 << 23)) << (e - 1)) if e else f
+    assert O.exact_abs_sum_units(w) == want
+    # many equal large significands in one exponent bucket
+    w = np.full(1 << 21, np.nextafter(np.float32(2.0), np.float32(0)), dtype=np.float32)
+    assert O.exact_abs_sum_units(w) == w.size * ((2 ** 24 - 1) << 126)   # biased exponent 127
+
+
 def test_weight_scale_is_nearest_fp32_of_exact_mean():
     """gamma must be the fp32 nearest to the exact mean (checked against both
     neighbours with Fractions), including a case where a naive fp32 sum differs."""
