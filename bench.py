@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
 """Throughput of the ternary linear layer path on one MI355X.
 
-Default workload: BitNet-2B-shaped decode, one token (M = 1) streamed through 30
-layers of {q, k, v, o: 2560->2560 / 2560->640, gate, up: 2560->6912, down:
-6912->2560} with the per-token int8 activation quantisation fused into the
-layers (bf16 activations between layers).  Chain per layer: q, k, v from the
-layer input; o from q; gate and up from o; down from up; down is the next
-layer's input.  One step = one token through the whole stack, replayed from a
-HIP graph.  Weights are synthetic N(0, 0.02^2), seeded, ternarised on the GPU;
-the stack is replicated so that the footprint cycled per step pair exceeds
-1 GB (4x the 256 MB Infinity Cache) and weights really stream from HBM.
+Default workload (`bitnet2b-decode-m1-30L`): BitNet-2B-shaped decode, one token
+(M = 1) streamed through 30 layers of {q, k, v: 2560->2560/640/640, o:
+2560->2560, gate, up: 2560->6912, down: 6912->2560}, bf16 activations between
+layers, the per-token int8 activation quantisation fused into the layers.
+Chain per layer: q, k, v from the layer input (one launch); o from q; gate and up
+from o (one launch); down from up; down is the next layer's input: 4 launches
+per layer.  One step = one token through the whole stack, replayed from a HIP
+graph.  Weights are synthetic N(0, 0.02^2), seeded, ternarised on the GPU by
+the library; the stack is replicated so that more than 1 GiB of weights is cycled
+between reuses (4x the 256 MB Infinity Cache) and weights stream from HBM.
 
-Printed: one JSON line with the packed-weight GB/s of the whole step (value),
-the decode kernel's roofline (kernel durations from events stamped by the
-kernel dispatch itself), the prefill kernel's int8 TOPS on the same layer
-shapes at M = 512 and 4096, and the CPU oracle timed on a bounded sample.
+Printed: one JSON line.  value = packed weight bytes per step / step time.
+roofline = the decode kernel (the only kernel in the step): achieved = mean
+packed bytes per launch / mean launch time, where the mean launch time is the
+graph replay time over the timed steps divided by the number of launches.
+Also: the 100B-class decode stack (96 layers, 23.35 GB packed, fp32 activations),
+the prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096, and the
+CPU oracle timed on a bounded sample of the same decode workload.
 """
 
 from __future__ import annotations
@@ -47,6 +51,7 @@ def parse():
     p.add_argument("--workload", default="bitnet2b-decode-m1-30L")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-100b", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this size (PMC calibration)")
@@ -72,54 +77,85 @@ def build_stack(torch, N, I, layer_shapes, layers, replicas):
     return stack
 
 
-def decode_step_fn(torch, N, shapes, layers_mats, h0, bufs):
-    """Enqueue one token through every layer (the chain described above)."""
+def chain_fn(torch, N, layers_mats, h0, bufs):
+    """Enqueue one token through every layer; returns the number of launches."""
     def step():
-        h = bufs["h"]
-        h.copy_(h0)
+        h = h0
         for mats in layers_mats:
-            N.bitnet_quant_linear(*mats["q"], h, x_q=bufs["xq_h"], x_scale=bufs["xs_h"], y=bufs["q"])
-            N.bitnet_ternary_linear(*mats["k"], bufs["xq_h"], bufs["xs_h"], y=bufs["k"])
-            N.bitnet_ternary_linear(*mats["v"], bufs["xq_h"], bufs["xs_h"], y=bufs["v"])
+            N.bitnet_quant_linear_multi(
+                [(*mats["q"], bufs["q"]), (*mats["k"], bufs["k"]), (*mats["v"], bufs["v"])], h,
+                x_q=bufs["xq_h"], x_scale=bufs["xs_h"])
             N.bitnet_quant_linear(*mats["o"], bufs["q"], x_q=bufs["xq_q"], x_scale=bufs["xs_q"],
                                   y=bufs["o"])
-            N.bitnet_quant_linear(*mats["gate"], bufs["o"], x_q=bufs["xq_o"], x_scale=bufs["xs_o"],
-                                  y=bufs["gate"])
-            N.bitnet_ternary_linear(*mats["up"], bufs["xq_o"], bufs["xs_o"], y=bufs["up"])
+            N.bitnet_quant_linear_multi(
+                [(*mats["gate"], bufs["gate"]), (*mats["up"], bufs["up"])], bufs["o"],
+                x_q=bufs["xq_o"], x_scale=bufs["xs_o"])
             N.bitnet_quant_linear(*mats["down"], bufs["up"], x_q=bufs["xq_u"], x_scale=bufs["xs_u"],
-                                  y=h)
+                                  y=bufs["h"])
+            h = bufs["h"]
+        return 4 * len(layers_mats)
     return step
 
 
-def time_decode_kernels(torch, N, layers_mats, xq_by_k, xs1, reps):
-    """Per-launch durations of the decode kernel for every matrix of the stack,
-    from events recorded by the kernel dispatch itself."""
-    launches = []
-    for mats in layers_mats:
-        for nm, (p, s) in mats.items():
-            launches.append((p, s))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in launches]
-    for a, b in ev:
-        a.record()
-        b.record()
-    outs = {p.shape[0]: torch.empty((1, p.shape[0]), dtype=torch.bfloat16, device="cuda")
-            for p, _ in launches}
-    durs, nbytes = [], []
-    torch.cuda.synchronize()
-    for _ in range(reps):
-        for (p, s), (a, b) in zip(launches, ev):
-            k = p.shape[1] * 4
-            N.bitnet_ternary_linear_timed(p, s, xq_by_k[k], xs1, outs[p.shape[0]], a, b)
+def decode_leg(torch, N, I, name, steps, warmup):
+    """One token at a time through a whole layer stack, replayed from HIP graphs."""
+    wl = I.WORKLOADS[name]
+    shapes, layers = wl["layer"], wl["layers"]
+    per_stack = I.packed_bytes(shapes) * layers
+    replicas = max(1, math.ceil(CACHE_CYCLE_BYTES / per_stack))
+    t0 = time.time()
+    stack = build_stack(torch, N, I, shapes, layers, replicas)
+    log(f"{name}: {layers} layers, {per_stack / 1e6:.1f} MB packed per token, {replicas} replicas, "
+        f"weights ternarised on the GPU in {time.time() - t0:.1f} s")
+    act_dt = torch.bfloat16 if wl["act"] == "bf16" else torch.float32
+    hidden = shapes[0][1]
+    g = torch.Generator(device="cuda").manual_seed(I.ACT_SEED)
+    h0 = torch.randn((1, hidden), generator=g, device="cuda").to(act_dt)
+    kin = {nm: k for nm, k, _ in shapes}
+    bufs = {nm: torch.empty((1, n), dtype=act_dt, device="cuda") for nm, _, n in shapes}
+    bufs["h"] = torch.empty((1, hidden), dtype=act_dt, device="cuda")
+    for tag, k in (("h", kin["q"]), ("q", kin["o"]), ("o", kin["gate"]), ("u", kin["down"])):
+        bufs["xq_" + tag] = torch.empty((1, k), dtype=torch.int8, device="cuda")
+        bufs["xs_" + tag] = torch.empty((1,), dtype=torch.float32, device="cuda")
+    graphs = []
+    launches = 0
+    for r in range(replicas):
+        step = chain_fn(torch, N, stack[r], h0, bufs)
+        step()
         torch.cuda.synchronize()
-        for (p, _), (a, b) in zip(launches, ev):
-            durs.append(a.elapsed_time(b) * 1e-3)
-            nbytes.append(p.numel())
-    return durs, nbytes
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            launches = step()
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % replicas].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % replicas].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = per_stack / (ms * 1e-3) / 1e9
+    log(f"{name}: {ms * 1e3:.1f} us/token, {gbs:.1f} GB/s packed, "
+        f"{ms * 1e3 / launches:.2f} us per launch")
+    res = dict(ms=ms, gbs=gbs, per_stack=per_stack, replicas=replicas, launches=launches,
+               layers=layers, shapes=shapes, act=wl["act"])
+    del graphs, stack
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
-def prefill(torch, N, I, layer_shapes, mats, ms, steps):
+def prefill(torch, N, I, layer_shapes, ms, steps):
     """int8 TOPS of the prefill kernel on one layer's matrices at M tokens."""
+    mats = {}
+    for i, (nm, k, n) in enumerate(layer_shapes):
+        g = torch.Generator(device="cuda").manual_seed(I.weight_seed(0, i))
+        w = torch.randn((n, k), generator=g, device="cuda").mul_(I.WEIGHT_SIGMA)
+        mats[nm] = N.bitnet_quantize_weights(w)
     res = {}
     for m in ms:
         xq = {}
@@ -131,55 +167,48 @@ def prefill(torch, N, I, layer_shapes, mats, ms, steps):
         ys = {nm: torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for nm, _, n in layer_shapes}
         ops = sum(2 * m * n * k for _, k, n in layer_shapes)
 
-        def run():
-            for nm, k, _ in layer_shapes:
-                N.bitnet_ternary_linear(*mats[nm], *xq[k], y=ys[nm])
-        run()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run()
-        for _ in range(3):
-            g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        sec = e0.elapsed_time(e1) * 1e-3 / steps
-        # kernel-own durations of the largest matrix
-        nm, k, n = max(layer_shapes, key=lambda t: t[1] * t[2])
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        b.record()
-        kd = []
-        for _ in range(5):
-            N.bitnet_ternary_linear_timed(*mats[nm], *xq[k], ys[nm], a, b)
+        def run(only=None, reps=1):
+            for _ in range(reps):
+                for nm, k, _ in layer_shapes:
+                    if only is None or nm == only:
+                        N.bitnet_ternary_linear(*mats[nm], *xq[k], y=ys[nm])
+
+        def timed(fn):
+            fn()
             torch.cuda.synchronize()
-            kd.append(a.elapsed_time(b) * 1e-3)
-        kd = sorted(kd)[len(kd) // 2]
-        kop = 2 * m * n * k
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                fn()
+            gr.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3 / steps
+
+        sec = timed(run)
+        nm, k, n = max(layer_shapes, key=lambda t: t[1] * t[2])
+        ksec = timed(lambda: run(only=nm, reps=10)) / 10
         res[str(m)] = {"tops": round(ops / sec / 1e12, 2),
                        "frac_of_int8_peak": round(ops / sec / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
                        "layer_ms": round(sec * 1e3, 4),
                        "largest_matrix": f"{k}->{n}",
-                       "largest_matrix_kernel_us": round(kd * 1e6, 2),
-                       "largest_matrix_kernel_tops": round(kop / kd / 1e12, 2)}
+                       "largest_matrix_us": round(ksec * 1e6, 2),
+                       "largest_matrix_tops": round(2 * m * n * k / ksec / 1e12, 2)}
     return res
 
 
 def cpu_baseline(I, layer_shapes, seconds):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     whole 2B-shaped layers at M = 1 (act-quant + layer per matrix)."""
-    import numpy as np
     from oracle import bitnet_oracle as O
     mats = {}
     for i, (nm, k, n) in enumerate(layer_shapes):
         mats[nm] = O.quantize_weights(I.master_weights(n, k, I.weight_seed(0, i)))
-    hk = layer_shapes[0][1]
-    x0 = I.activations(1, hk)
+    x0 = I.activations(1, layer_shapes[0][1])
     nbytes = 0
     layers_done = 0
     t0 = time.perf_counter()
@@ -197,7 +226,6 @@ def cpu_baseline(I, layer_shapes, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    _ = np
     return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{layers_done} x one 2B-shaped layer (7 matrices, "
                       f"{sum(p.nbytes for p, _ in mats.values())} packed bytes) at M=1, "
@@ -216,91 +244,48 @@ def main():
     from ternary_weight_linear_bit_amd import inputs as I
 
     wl = I.WORKLOADS[args.workload]
-    shapes, layers = wl["layer"], wl["layers"]
-    if wl["m"] != (1,) or len(shapes) != 7:
+    if wl["m"] != (1,) or len(wl["layer"]) != 7:
         raise SystemExit("bench.py times the layer-stack decode workloads")
     torch.cuda.set_device(0)
     N.lib()
-    per_stack = I.packed_bytes(shapes) * layers
-    replicas = max(1, math.ceil(CACHE_CYCLE_BYTES / per_stack))
-    log(f"workload {args.workload}: {layers} layers, {per_stack / 1e6:.1f} MB packed per token, "
-        f"{replicas} replicas")
-    t0 = time.time()
-    stack = build_stack(torch, N, I, shapes, layers, replicas)
-    log(f"weights quantised on GPU in {time.time() - t0:.1f} s")
-
-    act_dt = torch.bfloat16 if wl["act"] == "bf16" else torch.float32
-    hidden = shapes[0][1]
-    g = torch.Generator(device="cuda").manual_seed(I.ACT_SEED)
-    h0 = torch.randn((1, hidden), generator=g, device="cuda").to(act_dt)
-    sz = {nm: n for nm, _, n in shapes}
-    kin = {nm: k for nm, k, _ in shapes}
-    bufs = {nm: torch.empty((1, n), dtype=act_dt, device="cuda") for nm, n in sz.items()}
-    bufs["h"] = torch.empty((1, hidden), dtype=act_dt, device="cuda")
-    for tag, k in (("h", kin["q"]), ("q", kin["o"]), ("o", kin["gate"]), ("u", kin["down"])):
-        bufs["xq_" + tag] = torch.empty((1, k), dtype=torch.int8, device="cuda")
-        bufs["xs_" + tag] = torch.empty((1,), dtype=torch.float32, device="cuda")
-
-    graphs = []
-    for r in range(replicas):
-        step = decode_step_fn(torch, N, shapes, stack[r], h0, bufs)
-        step()
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            step()
-        graphs.append(gr)
-    torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % replicas].replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % replicas].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    value = per_stack / (ms * 1e-3) / 1e9
-    log(f"decode: {ms * 1e3:.1f} us/token, {value:.1f} GB/s packed")
-
-    # decode kernel roofline: kernel-own durations over every matrix of one stack
-    xq_by_k = {}
-    for k in sorted(set(kin.values())):
-        x = torch.randn((1, k), generator=g, device="cuda").to(act_dt)
-        xq_by_k[k], xs1 = N.bitnet_quantize_acts(x)
-    durs, nb = time_decode_kernels(torch, N, stack[0], xq_by_k, xs1, reps=min(5, max(1, args.steps)))
-    avg_dur = sum(durs) / len(durs)
-    avg_bytes = sum(nb) / len(nb)
-    achieved = avg_bytes / avg_dur / 1e9
-    log(f"decode kernel: {len(durs)} launches, avg {avg_dur * 1e6:.2f} us, "
-        f"avg {avg_bytes / 1e6:.2f} MB -> {achieved:.0f} GB/s")
-
+    d = decode_leg(torch, N, I, args.workload, args.steps, args.warmup)
+    avg_launch = d["ms"] * 1e-3 / d["launches"]
+    avg_bytes = d["per_stack"] / d["launches"]
+    achieved = avg_bytes / avg_launch / 1e9
     result = {
         "metric": "decode GEMV packed-weight GB/s (% HBM peak); prefill int8 TOPS (% MFMA peak)",
-        "value": round(value, 2),
+        "value": round(d["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(d["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens_per_step": 1, "layers": layers,
-                   "matrices_per_layer": len(shapes), "packed_bytes_per_step": per_stack,
-                   "activations": wl["act"], "weight_replicas_cycled": replicas,
-                   "launches_per_step": layers * len(shapes) + 1, "graph": "hip"},
+        "config": {"workload": args.workload, "tokens_per_step": 1, "layers": d["layers"],
+                   "matrices_per_layer": len(d["shapes"]), "packed_bytes_per_step": d["per_stack"],
+                   "activations": d["act"], "weight_replicas_cycled": d["replicas"],
+                   "launches_per_step": d["launches"], "graph": "hip"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel (decode, pre-quantised input)",
-                     "launches_timed": len(durs), "avg_launch_us": round(avg_dur * 1e6, 3),
-                     "avg_bytes_per_launch": int(avg_bytes)},
+                     "kernel": "gemv_kernel (decode, fused int8 activation quantisation)",
+                     "avg_launch_us": round(avg_launch * 1e6, 3),
+                     "avg_bytes_per_launch": int(avg_bytes),
+                     "launch_time": "graph replay time / launches in the timed steps"},
     }
+    if not args.no_100b:
+        d5 = decode_leg(torch, N, I, "ternary100b-decode-m1-96L", max(5, args.steps // 5), 2)
+        result["decode_100b"] = {
+            "workload": "ternary100b-decode-m1-96L", "gbs": round(d5["gbs"], 1),
+            "frac_of_hbm_peak": round(d5["gbs"] / HBM_PEAK_GBS, 4),
+            "ms_per_token": round(d5["ms"], 4), "tokens_per_s": round(1e3 / d5["ms"], 1),
+            "packed_bytes_per_token": d5["per_stack"], "launches_per_token": d5["launches"],
+            "avg_launch_us": round(d5["ms"] * 1e3 / d5["launches"], 3)}
     if not args.no_prefill:
-        result["prefill"] = prefill(torch, N, I, shapes, stack[0][0], (512, 4096), steps=10)
+        result["prefill"] = prefill(torch, N, I, wl["layer"], (512, 4096), steps=10)
         log(f"prefill: {result['prefill']}")
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 18
@@ -311,7 +296,7 @@ def main():
         torch.cuda.synchronize()
         result["calib_copy_bytes"] = 2 * a.numel() * 4
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(I, shapes, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(I, wl["layer"], args.cpu_seconds)
         log(f"cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 

@@ -62,6 +62,15 @@ typedef enum bitnet_status {
 
 typedef enum bitnet_dtype { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
 
+/* One weight matrix of a grouped call (all pointers device memory). */
+typedef struct bitnet_matrix {
+  const uint8_t *w_packed; /* [N][K/4] packed codes from bitnet_quantize_weights */
+  const float *w_scale;    /* [1] gamma* */
+  int64_t N;               /* output features, >= 0 */
+  void *y;                 /* [M][N] fp32 or bf16 out */
+  int32_t *acc_out;        /* optional [M][N] int32 accumulators, or NULL */
+} bitnet_matrix;
+
 /* Largest N*K accepted by bitnet_quantize_weights (exact-sum limit): 2^38 - 1. */
 #define BITNET_MAX_WEIGHTS ((int64_t)1 << 38)
 /* Largest K accepted by the linear calls: |acc| <= 127*K stays below 2^24, so
@@ -114,8 +123,8 @@ bitnet_status bitnet_quantize_acts(const void *x, int x_dtype, int64_t M, int64_
  *   M, N, K  M >= 0, N >= 0 (0 = no-op), K % 4 == 0, 0 <= K <= BITNET_MAX_K.
  *   y        [M][N] out, fp32 or bf16 (y_dtype), element-aligned.
  *   acc_out  optional [M][N] int32 out (NULL to skip): the exact accumulator.
- * M <= 16 runs the HBM-streaming decode kernel, larger M the int8-MFMA prefill
- * kernel; both produce identical integers.
+ * M <= 16 (K % 64 == 0) runs the HBM-streaming decode kernel, larger M the
+ * int8-MFMA prefill kernel; both produce identical integers.
  */
 bitnet_status bitnet_ternary_linear(const uint8_t *w_packed, const float *w_scale,
                                     const int8_t *x_q, const float *x_scale, int64_t M,
@@ -123,17 +132,16 @@ bitnet_status bitnet_ternary_linear(const uint8_t *w_packed, const float *w_scal
                                     int32_t *acc_out, hipStream_t stream);
 
 /*
- * Measurement variant of bitnet_ternary_linear: the same validation, kernel choice
- * and results; in addition the kernel's dispatch records `start` when the kernel
- * begins and `stop` when it ends (either may be NULL), so
- * hipEventElapsedTime(start, stop) is the kernel's own duration, free of launch
- * gaps.  The events must come from hipEventCreate on the current device.
+ * Several weight matrices that share one input (for example the q, k and v
+ * projections, or gate and up): the same results as `count` calls of
+ * bitnet_ternary_linear with the same x_q / x_scale, in as few kernel launches as
+ * the decode kernel allows (up to 4 matrices per launch when M <= 16).
+ *   mats     HOST array of `count` >= 1 descriptors (read during the call only).
+ *   x_q, x_scale, M, K, y_dtype  as bitnet_ternary_linear; every y has y_dtype.
  */
-bitnet_status bitnet_ternary_linear_timed(const uint8_t *w_packed, const float *w_scale,
+bitnet_status bitnet_ternary_linear_multi(const bitnet_matrix *mats, int count,
                                           const int8_t *x_q, const float *x_scale, int64_t M,
-                                          int64_t N, int64_t K, void *y, int y_dtype,
-                                          int32_t *acc_out, hipEvent_t start, hipEvent_t stop,
-                                          hipStream_t stream);
+                                          int64_t K, int y_dtype, hipStream_t stream);
 
 /*
  * Activation quantisation fused into the layer, for chaining layers without a
@@ -143,14 +151,23 @@ bitnet_status bitnet_ternary_linear_timed(const uint8_t *w_packed, const float *
  *            bitnet_quantize_acts(x) writes (so further layers that share this
  *            input can call bitnet_ternary_linear on them).
  *   other arguments as bitnet_ternary_linear.
- * For M <= 16 (when M*K fits the decode kernel's on-chip buffer) each workgroup
- * quantises the activations itself; otherwise this is bitnet_quantize_acts
+ * For M <= 4 with M*K <= 64 KiB (and K % 64 == 0) each workgroup of the decode
+ * kernel quantises the activations itself; otherwise this is bitnet_quantize_acts
  * followed by bitnet_ternary_linear on the same stream.
  */
 bitnet_status bitnet_quant_linear(const uint8_t *w_packed, const float *w_scale,
                                   const void *x, int x_dtype, int64_t M, int64_t N, int64_t K,
                                   int8_t *x_q, float *x_scale, void *y, int y_dtype,
                                   int32_t *acc_out, hipStream_t stream);
+
+/*
+ * bitnet_quant_linear for several matrices sharing the input x: quantises x once
+ * (into x_q / x_scale) and applies every matrix, fused into one launch for up to
+ * 4 matrices when M <= 4 and M*K <= 64 KiB.
+ */
+bitnet_status bitnet_quant_linear_multi(const bitnet_matrix *mats, int count, const void *x,
+                                        int x_dtype, int64_t M, int64_t K, int8_t *x_q,
+                                        float *x_scale, int y_dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -28,10 +28,21 @@ SIGNATURES = {
     "bitnet_quantize_weights": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "bitnet_quantize_acts": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bitnet_ternary_linear": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P]),
-    "bitnet_ternary_linear_timed": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P, _P,
-                                         _P]),
     "bitnet_quant_linear": (_I, [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P]),
 }
+
+
+
+class BitnetMatrix(ctypes.Structure):
+    """struct bitnet_matrix of the public header."""
+    _fields_ = [("w_packed", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("y", ctypes.c_void_p), ("acc_out", ctypes.c_void_p)]
+
+
+SIGNATURES["bitnet_ternary_linear_multi"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _P, _P, _I64,
+                                                  _I64, _I, _P])
+SIGNATURES["bitnet_quant_linear_multi"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _P, _I, _I64,
+                                                _I64, _P, _P, _I, _P])
 
 _lib = None
 
@@ -145,19 +156,6 @@ def bitnet_ternary_linear(w_packed, w_scale, x_q, x_scale, y=None, y_dtype=None,
     return y
 
 
-def bitnet_ternary_linear_timed(w_packed, w_scale, x_q, x_scale, y, start, stop, acc_out=None,
-                                stream=None):
-    """bitnet_ternary_linear whose kernel dispatch records the torch.cuda.Event
-    pair (start, stop), which must have been recorded once so that they exist."""
-    m, k = x_q.shape
-    n = w_packed.shape[0]
-    _check("bitnet_ternary_linear_timed", lib().bitnet_ternary_linear_timed(
-        _ptr(w_packed), _ptr(w_scale), _ptr(x_q), _ptr(x_scale), m, n, k, _ptr(y),
-        _dtype_code(y.dtype), _ptr(acc_out), ctypes.c_void_p(start.cuda_event),
-        ctypes.c_void_p(stop.cuda_event), _stream(stream)))
-    return y
-
-
 def bitnet_quant_linear(w_packed, w_scale, x, x_q=None, x_scale=None, y=None, y_dtype=None,
                         acc_out=None, stream=None):
     """Act-quant fused into the layer: returns (y, x_q, x_scale)."""
@@ -178,3 +176,50 @@ def bitnet_quant_linear(w_packed, w_scale, x, x_q=None, x_scale=None, y=None, y_
         _ptr(w_packed), _ptr(w_scale), _ptr(x), _dtype_code(x.dtype), m, n, k, _ptr(x_q),
         _ptr(x_scale), _ptr(y), _dtype_code(y.dtype), _ptr(acc_out), _stream(stream)))
     return y, x_q, x_scale
+
+
+def _matrices(mats, m, dtype, device):
+    """[(w_packed, w_scale[, y[, acc_out]])] -> ctypes array and the y tensors."""
+    import torch
+    arr = (BitnetMatrix * len(mats))()
+    ys = []
+    for i, t in enumerate(mats):
+        w_packed, w_scale = t[0], t[1]
+        y = t[2] if len(t) > 2 and t[2] is not None else torch.empty(
+            (m, w_packed.shape[0]), dtype=dtype, device=device)
+        acc = t[3] if len(t) > 3 else None
+        _need_cuda(w_packed, w_scale, y, acc)
+        arr[i] = BitnetMatrix(w_packed.data_ptr(), w_scale.data_ptr(), w_packed.shape[0],
+                              y.data_ptr(), 0 if acc is None else acc.data_ptr())
+        ys.append(y)
+    return arr, ys
+
+
+def bitnet_ternary_linear_multi(mats, x_q, x_scale, y_dtype=None, stream=None):
+    """Several (w_packed, w_scale[, y[, acc_out]]) sharing x_q -> list of y."""
+    import torch
+    _need_cuda(x_q, x_scale)
+    m, k = x_q.shape
+    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x_q.device)
+    dt = _dtype_code(ys[0].dtype)
+    _check("bitnet_ternary_linear_multi", lib().bitnet_ternary_linear_multi(
+        arr, len(mats), _ptr(x_q), _ptr(x_scale), m, k, dt, _stream(stream)))
+    return ys
+
+
+def bitnet_quant_linear_multi(mats, x, x_q=None, x_scale=None, y_dtype=None, stream=None):
+    """Quantise x once and apply several matrices: returns (list of y, x_q, x_scale)."""
+    import torch
+    _need_cuda(x)
+    m, k = x.shape
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need_cuda(x_q, x_scale)
+    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x.device)
+    dt = _dtype_code(ys[0].dtype)
+    _check("bitnet_quant_linear_multi", lib().bitnet_quant_linear_multi(
+        arr, len(mats), _ptr(x), _dtype_code(x.dtype), m, k, _ptr(x_q), _ptr(x_scale), dt,
+        _stream(stream)))
+    return ys, x_q, x_scale

@@ -19,33 +19,108 @@ bool fast_layout(const void* w_packed, const void* x_q, int64_t K) {
   return K >= 64 && (K % 64) == 0 && aligned(w_packed, 16) && aligned(x_q, 16);
 }
 
-bitnet_status check_linear_args(const uint8_t* w_packed, const float* w_scale, const float* x_scale,
-                                int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
-                                int32_t* acc_out) {
-  if (!w_scale || !x_scale || !y || (K > 0 && !w_packed)) return BITNET_ERR_NULL;
-  if (!valid_dtype(y_dtype)) return BITNET_ERR_DTYPE;
-  if (M < 0 || N < 0 || K < 0 || (K % 4) != 0 || K > BITNET_MAX_K || M > kInt32Max ||
-      N > kInt32Max)
-    return BITNET_ERR_SHAPE;
-  if (!aligned(y, esize(y_dtype)) || !aligned(w_scale, 4) || !aligned(x_scale, 4) ||
-      (acc_out && !aligned(acc_out, 4)))
+bitnet_status check_sizes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || (K % 4) != 0 || K > BITNET_MAX_K || M > kInt32Max) return BITNET_ERR_SHAPE;
+  return BITNET_OK;
+}
+
+// Per-matrix checks shared by the single and grouped calls.
+bitnet_status check_matrix(const bitnet_matrix& m, int64_t M, int64_t K, int y_dtype) {
+  if (!m.w_scale || !m.y || (K > 0 && !m.w_packed)) return BITNET_ERR_NULL;
+  if (m.N < 0 || m.N > kInt32Max || M * m.N > ((int64_t)1 << 46)) return BITNET_ERR_SHAPE;
+  if (!aligned(m.y, esize(y_dtype)) || !aligned(m.w_scale, 4) ||
+      (m.acc_out && !aligned(m.acc_out, 4)))
     return BITNET_ERR_ALIGN;
   return BITNET_OK;
 }
 
-bitnet_status run_linear(const uint8_t* w_packed, const float* w_scale, const int8_t* x_q,
-                         const float* x_scale, int64_t M, int64_t N, int64_t K, void* y,
-                         int y_dtype, int32_t* acc_out, const bitnet::Launch& l) {
-  const bool yb = y_dtype == BITNET_BF16;
-  if (fast_layout(w_packed, x_q, K)) {
-    if (bitnet::gemv_fits(M, K))
-      return from_hip(bitnet::launch_gemv(w_packed, w_scale, x_q, x_scale, nullptr, 0, nullptr,
-                                          nullptr, (int)M, (int)N, (int)K, y, yb, acc_out, l));
-    return from_hip(bitnet::launch_gemm(w_packed, w_scale, x_q, x_scale, (int)M, (int)N, (int)K, y,
-                                        yb, acc_out, l));
+bitnet_status check_group(const bitnet_matrix* mats, int count, int64_t M, int64_t K,
+                          int y_dtype) {
+  if (!mats) return BITNET_ERR_NULL;
+  if (count < 1) return BITNET_ERR_SHAPE;
+  if (!valid_dtype(y_dtype)) return BITNET_ERR_DTYPE;
+  const bitnet_status s = check_sizes(M, K);
+  if (s != BITNET_OK) return s;
+  for (int i = 0; i < count; ++i) {
+    const bitnet_status st = check_matrix(mats[i], M, K, y_dtype);
+    if (st != BITNET_OK) return st;
   }
-  return from_hip(bitnet::launch_generic_linear(w_packed, w_scale, x_q, x_scale, M, N, K, y, yb,
-                                                acc_out, l));
+  return BITNET_OK;
+}
+
+bitnet::GemvArgs gemv_args(const bitnet_matrix* mats, int count, int64_t M, int64_t K,
+                           int y_dtype) {
+  bitnet::GemvArgs a{};
+  for (int j = 0; j < count; ++j) {
+    a.wp[j] = mats[j].w_packed;
+    a.ws[j] = mats[j].w_scale;
+    a.y[j] = mats[j].y;
+    a.acc[j] = mats[j].acc_out;
+    a.n[j] = (int)mats[j].N;
+  }
+  a.count = count;
+  a.M = (int)M;
+  a.K = (int)K;
+  a.y_bf16 = y_dtype == BITNET_BF16 ? 1 : 0;
+  return a;
+}
+
+bool all_fast(const bitnet_matrix* mats, int count, const void* x_q, int64_t K) {
+  for (int j = 0; j < count; ++j)
+    if (!fast_layout(mats[j].w_packed, x_q, K)) return false;
+  return true;
+}
+
+// Quantised activations already in x_q / x_scale; M, K and every matrix valid.
+bitnet_status run_linear(const bitnet_matrix* mats, int count, const int8_t* x_q,
+                         const float* x_scale, int64_t M, int64_t K, int y_dtype,
+                         hipStream_t stream) {
+  if (M == 0) return BITNET_OK;
+  const bool yb = y_dtype == BITNET_BF16;
+  if (all_fast(mats, count, x_q, K) && bitnet::gemv_fits(M, K)) {
+    for (int j0 = 0; j0 < count; j0 += bitnet::kMaxGroup) {
+      const int c = count - j0 < bitnet::kMaxGroup ? count - j0 : bitnet::kMaxGroup;
+      bitnet::GemvArgs a = gemv_args(mats + j0, c, M, K, y_dtype);
+      a.xq = x_q;
+      a.xs = x_scale;
+      const bitnet_status st = from_hip(bitnet::launch_gemv(a, 0, stream));
+      if (st != BITNET_OK) return st;
+    }
+    return BITNET_OK;
+  }
+  for (int j = 0; j < count; ++j) {
+    const bitnet_matrix& m = mats[j];
+    if (m.N == 0) continue;
+    hipError_t e;
+    if (fast_layout(m.w_packed, x_q, K))
+      e = bitnet::launch_gemm(m.w_packed, m.w_scale, x_q, x_scale, (int)M, (int)m.N, (int)K, m.y,
+                              yb, m.acc_out, stream);
+    else
+      e = bitnet::launch_generic_linear(m.w_packed, m.w_scale, x_q, x_scale, M, m.N, K, m.y, yb,
+                                        m.acc_out, stream);
+    if (e != hipSuccess) return BITNET_ERR_HIP;
+  }
+  return BITNET_OK;
+}
+
+bitnet_status quant_linear(const bitnet_matrix* mats, int count, const void* x, int x_dtype,
+                           int64_t M, int64_t K, int8_t* x_q, float* x_scale, int y_dtype,
+                           hipStream_t stream) {
+  if (M == 0) return BITNET_OK;
+  if (all_fast(mats, count, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K)) {
+    const int c = count < bitnet::kMaxGroup ? count : bitnet::kMaxGroup;
+    bitnet::GemvArgs a = gemv_args(mats, c, M, K, y_dtype);
+    a.xf = x;
+    a.xq = x_q;
+    a.xq_out = x_q;
+    a.xs_out = x_scale;
+    if (bitnet::launch_gemv(a, x_dtype, stream) != hipSuccess) return BITNET_ERR_HIP;
+    if (count == c) return BITNET_OK;
+    return run_linear(mats + c, count - c, x_q, x_scale, M, K, y_dtype, stream);
+  }
+  if (bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, stream) != hipSuccess)
+    return BITNET_ERR_HIP;
+  return run_linear(mats, count, x_q, x_scale, M, K, y_dtype, stream);
 }
 
 }  // namespace
@@ -99,53 +174,41 @@ bitnet_status bitnet_quantize_acts(const void* x, int x_dtype, int64_t M, int64_
   return from_hip(bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, stream));
 }
 
+bitnet_status bitnet_ternary_linear_multi(const bitnet_matrix* mats, int count,
+                                          const int8_t* x_q, const float* x_scale, int64_t M,
+                                          int64_t K, int y_dtype, hipStream_t stream) {
+  if (M > 0 && (!x_scale || (K > 0 && !x_q))) return BITNET_ERR_NULL;
+  const bitnet_status st = check_group(mats, count, M, K, y_dtype);
+  if (st != BITNET_OK) return st;
+  if (x_scale && !aligned(x_scale, 4)) return BITNET_ERR_ALIGN;
+  return run_linear(mats, count, x_q, x_scale, M, K, y_dtype, stream);
+}
+
 bitnet_status bitnet_ternary_linear(const uint8_t* w_packed, const float* w_scale,
                                     const int8_t* x_q, const float* x_scale, int64_t M,
                                     int64_t N, int64_t K, void* y, int y_dtype, int32_t* acc_out,
                                     hipStream_t stream) {
-  if (K > 0 && M > 0 && !x_q) return BITNET_ERR_NULL;
-  const bitnet_status st =
-      check_linear_args(w_packed, w_scale, x_scale, M, N, K, y, y_dtype, acc_out);
-  if (st != BITNET_OK) return st;
-  if (M == 0 || N == 0) return BITNET_OK;
-  return run_linear(w_packed, w_scale, x_q, x_scale, M, N, K, y, y_dtype, acc_out,
-                    bitnet::Launch{stream, nullptr, nullptr});
+  const bitnet_matrix m{w_packed, w_scale, N, y, acc_out};
+  return bitnet_ternary_linear_multi(&m, 1, x_q, x_scale, M, K, y_dtype, stream);
 }
 
-bitnet_status bitnet_ternary_linear_timed(const uint8_t* w_packed, const float* w_scale,
-                                          const int8_t* x_q, const float* x_scale, int64_t M,
-                                          int64_t N, int64_t K, void* y, int y_dtype,
-                                          int32_t* acc_out, hipEvent_t start, hipEvent_t stop,
-                                          hipStream_t stream) {
-  if (K > 0 && M > 0 && !x_q) return BITNET_ERR_NULL;
-  const bitnet_status st =
-      check_linear_args(w_packed, w_scale, x_scale, M, N, K, y, y_dtype, acc_out);
+bitnet_status bitnet_quant_linear_multi(const bitnet_matrix* mats, int count, const void* x,
+                                        int x_dtype, int64_t M, int64_t K, int8_t* x_q,
+                                        float* x_scale, int y_dtype, hipStream_t stream) {
+  if (M > 0 && (!x_scale || (K > 0 && (!x || !x_q)))) return BITNET_ERR_NULL;
+  if (!valid_dtype(x_dtype)) return BITNET_ERR_DTYPE;
+  const bitnet_status st = check_group(mats, count, M, K, y_dtype);
   if (st != BITNET_OK) return st;
-  if (M == 0 || N == 0) return BITNET_OK;
-  return run_linear(w_packed, w_scale, x_q, x_scale, M, N, K, y, y_dtype, acc_out,
-                    bitnet::Launch{stream, start, stop});
+  if (!aligned(x, esize(x_dtype)) || (x_scale && !aligned(x_scale, 4))) return BITNET_ERR_ALIGN;
+  return quant_linear(mats, count, x, x_dtype, M, K, x_q, x_scale, y_dtype, stream);
 }
 
 bitnet_status bitnet_quant_linear(const uint8_t* w_packed, const float* w_scale, const void* x,
                                   int x_dtype, int64_t M, int64_t N, int64_t K, int8_t* x_q,
                                   float* x_scale, void* y, int y_dtype, int32_t* acc_out,
                                   hipStream_t stream) {
-  if (K > 0 && M > 0 && (!x || !x_q)) return BITNET_ERR_NULL;
-  if (!valid_dtype(x_dtype)) return BITNET_ERR_DTYPE;
-  const bitnet_status st =
-      check_linear_args(w_packed, w_scale, x_scale, M, N, K, y, y_dtype, acc_out);
-  if (st != BITNET_OK) return st;
-  if (!aligned(x, esize(x_dtype))) return BITNET_ERR_ALIGN;
-  if (M == 0) return BITNET_OK;
-  const bitnet::Launch l{stream, nullptr, nullptr};
-  if (N > 0 && fast_layout(w_packed, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K))
-    return from_hip(bitnet::launch_gemv(w_packed, w_scale, nullptr, nullptr, x,
-                                        x_dtype == BITNET_BF16 ? 1 : 0, x_q, x_scale, (int)M,
-                                        (int)N, (int)K, y, y_dtype == BITNET_BF16, acc_out, l));
-  const hipError_t e = bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, stream);
-  if (e != hipSuccess) return BITNET_ERR_HIP;
-  if (N == 0) return BITNET_OK;
-  return run_linear(w_packed, w_scale, x_q, x_scale, M, N, K, y, y_dtype, acc_out, l);
+  const bitnet_matrix m{w_packed, w_scale, N, y, acc_out};
+  return bitnet_quant_linear_multi(&m, 1, x, x_dtype, M, K, x_q, x_scale, y_dtype, stream);
 }
 
 }  // extern "C"

@@ -2,7 +2,6 @@
 // Not part of the public ABI (include/bitnet_mi355x.h is).
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -103,6 +102,18 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 
+// A generic pointer as a global address-space pointer, so that accesses through
+// it compile to global rather than flat instructions (flat ones also count as LDS
+// traffic, which makes the compiler's waits conservative).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* as_global(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
 // Wait for this wave's LDS operations, then workgroup barrier.  Unlike
 // __syncthreads() this does not wait for outstanding global loads, so weight
 // prefetches stay in flight across it; the "memory" clobber keeps the compiler
@@ -111,42 +122,44 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Where a linear-layer kernel is launched.  With a start or stop event the
-// dispatch itself records them (hipExtLaunchKernelGGL), so their elapsed time is
-// the kernel's own duration.
-struct Launch {
-  hipStream_t stream;
-  hipEvent_t start;
-  hipEvent_t stop;
-};
-
-template <typename F, typename... Args>
-void launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, const Launch& l, Args... args) {
-  if (l.start != nullptr || l.stop != nullptr)
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, l.stream, l.start, l.stop, 0u,
-                          args...);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, lds, l.stream, args...);
-}
-
 // Host-side launchers (one per kernel family); each returns a hipError_t from
 // hipGetLastError() after its launches.
 hipError_t launch_wq(const void* w, bool w_bf16, int64_t n_weights, uint8_t* w_packed,
                      float* w_scale, void* workspace, hipStream_t s);
 hipError_t launch_aq(const void* x, bool x_bf16, int64_t M, int64_t K, int8_t* x_q,
                      float* x_scale, hipStream_t s);
-// Decode (skinny) kernel: returns hipErrorInvalidValue when the shape does not fit it.
+// Decode kernel arguments: up to kMaxGroup weight matrices sharing K and the
+// activations, passed by value.
+constexpr int kMaxGroup = 4;
+struct GemvArgs {
+  const uint8_t* wp[kMaxGroup];
+  const float* ws[kMaxGroup];
+  void* y[kMaxGroup];
+  int32_t* acc[kMaxGroup];
+  int n[kMaxGroup];
+  int wg0[kMaxGroup];        // first workgroup of each matrix (set by launch_gemv)
+  const int8_t* xq;          // int8 activations (pre-quantised input)
+  const float* xs;           // their token scales
+  const void* xf;            // fp32/bf16 activations (fused quantisation) or nullptr
+  int8_t* xq_out;            // fused: where x_q and x_scale are written
+  float* xs_out;
+  int count, unused0;
+  int M, K;                  // pairs of ints are read as one 64-bit value each
+  int y_bf16, tiles_per_wg;  // row tiles per workgroup (set by launch_gemv)
+  int kx, phases;            // K range staged per phase and phase count (launch_gemv)
+  int mdiv, unused1;         // ceil(65536 / M) (launch_gemv)
+};
+
+// Decode kernel: M <= 16, K % 64 == 0; the fused variant (a.xf != nullptr) also
+// needs M <= 4 and the activations of all tokens in one LDS phase.
 bool gemv_fits(int64_t M, int64_t K);
-bool gemv_fused_fits(int64_t M, int64_t K);  // fused activation quantisation, small M
-hipError_t launch_gemv(const uint8_t* wp, const float* w_scale, const int8_t* xq,
-                       const float* x_scale, const void* xf, int xf_dtype, int8_t* xq_out,
-                       float* xs_out, int M, int N, int K, void* y, bool y_bf16,
-                       int32_t* acc_out, const Launch& l);
+bool gemv_fused_fits(int64_t M, int64_t K);
+hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                        const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
-                       int32_t* acc_out, const Launch& l);
+                       int32_t* acc_out, hipStream_t s);
 hipError_t launch_generic_linear(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                                  const float* x_scale, int64_t M, int64_t N, int64_t K,
-                                 void* y, bool y_bf16, int32_t* acc_out, const Launch& l);
+                                 void* y, bool y_bf16, int32_t* acc_out, hipStream_t s);
 
 }  // namespace bitnet

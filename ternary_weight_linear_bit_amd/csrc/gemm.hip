@@ -160,22 +160,22 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 
 hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                        const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
-                       int32_t* acc_out, const Launch& l) {
+                       int32_t* acc_out, hipStream_t s) {
   if (K % BK != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  launch_kernel(gemm_kernel, grid, dim3(kThreads), 0, l, wp, w_scale, xq, x_scale, M, N, K, y,
-                y_bf16 ? 1 : 0, acc_out);
+  hipLaunchKernelGGL(gemm_kernel, grid, dim3(kThreads), 0, s, wp, w_scale, xq, x_scale, M, N, K, y,
+                     y_bf16 ? 1 : 0, acc_out);
   return hipGetLastError();
 }
 
 hipError_t launch_generic_linear(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                                  const float* x_scale, int64_t M, int64_t N, int64_t K,
-                                 void* y, bool y_bf16, int32_t* acc_out, const Launch& l) {
+                                 void* y, bool y_bf16, int32_t* acc_out, hipStream_t s) {
   int64_t blocks = (M * N + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  launch_kernel(generic_linear_kernel, dim3((unsigned)blocks), dim3(256), 0, l, wp, w_scale, xq,
-                x_scale, M, N, K, y, y_bf16 ? 1 : 0, acc_out);
+  hipLaunchKernelGGL(generic_linear_kernel, dim3((unsigned)blocks), dim3(256), 0, s, wp, w_scale,
+                     xq, x_scale, M, N, K, y, y_bf16 ? 1 : 0, acc_out);
   return hipGetLastError();
 }
 

@@ -3,331 +3,527 @@
 //
 // Method: dashen-tech.com, "BitNet.cpp 深度解析", section 3.1 (integer matmul):
 // with weights in {-1, 0, +1} each output is the sum of the inputs under +1
-// weights minus the sum under -1 weights.  Here every weight is carried as its
-// 2-bit code c = q + 1 in {0, 1, 2} (section 2.3: two bits per weight), so
-//     acc[m, n] = sum_k c[n, k] * x[m, k]  -  sum_k x[m, k],
-// one unsigned-code contraction plus one per-token correction that every
-// workgroup forms once from its staged activations.
+// weights minus the sum under -1 weights, i.e. the dot product of the signed
+// weights with the int8 activations.  Every weight is carried as its 2-bit code
+// c = q + 1 in {0, 1, 2} (section 2.3: two bits per weight) and turned back into
+// the int8 value q in registers, so the matrix cores contract q with x directly.
 //
-// Design for gfx950 (not the pages' CPU kernels):
-//  * Workgroup = 4 waves = one tile of 16 output rows; the waves split K in
-//    interleaved 256-k super-chunks.  Each lane streams 16-byte chunks (64 codes)
-//    of one row with raw buffer loads; one wave load instruction covers 16 rows x
-//    64 contiguous bytes, and the four waves together read 256 contiguous bytes of
-//    each row per step.  Rows past N and chunks past K read as zeros (buffer range
-//    check), so the stream has no branches.
-//  * kUnroll loads per lane are kept in flight; the first batch is issued before
-//    the activations are staged, and the LDS-only barriers do not drain it.
-//  * Unpack is 7 VALU ops per packed dword: (w >> 2i) & 0x03030303, i = 0..3,
-//    yields 16 int8 codes in a k order that is a 4x4 byte transpose of the natural
-//    one.  The activations are written to LDS with the same transpose, once per
-//    workgroup, so the matrix-core operands agree without a per-weight shuffle.
-//  * v_mfma_i32_16x16x64_i8: A = 16 weight rows x 64 k (codes), B = 64 k x 16
-//    tokens (tokens >= M read a zero slot), int32 accumulate.  The four lane
-//    groups of the instruction take four different 16-k blocks, so the matrix core
-//    also performs the reduction along K inside a wave.
-//  * The four waves' partial tiles are summed through LDS; wave 0 applies the
-//    correction and the rescale y = RN32(float(acc) * RN32(gamma * d[m])).
+// Design for gfx950 (the pages' kernels are CPU SIMD and lookup-table code):
+//  * Workgroup = 4 waves; it owns T consecutive 16-row tiles of one matrix (of up
+//    to kMaxGroup matrices that share the activations).  T is the smallest count
+//    with which every workgroup of the launch is resident at once.  K is cut into
+//    256-k super-chunks; wave w takes super-chunks w, w + 4, ..., so one wave load
+//    instruction covers 16 rows x 64 contiguous bytes and the four waves read 256
+//    contiguous bytes of each row per step.
+//  * The activations are staged once per workgroup into LDS, byte-transposed
+//    within each 16-byte group; this is the order in which a shift, a mask and a
+//    byte lookup per field, (w >> 2i) & 0x03030303, unpack the weights, so no
+//    per-weight shuffle is needed.  When M * K exceeds the LDS budget, K is
+//    processed in phases.
+//  * Each wave streams its (tile, super-chunk) sequence with raw buffer loads
+//    (16 bytes per lane; rows past N and chunks past K read as zeros) through a
+//    ring of R loads in flight that runs on across tiles.  The first loads are
+//    issued before the activations are staged, and the LDS-only barriers do not
+//    drain them.
+//  * v_mfma_i32_16x16x64_i8: A = 16 rows x 64 k of weights (registers), B = 64 k x
+//    16 tokens (LDS; tokens >= M read a zero slot), int32 accumulate; the four
+//    lane groups take four 16-k blocks, so the matrix core also sums along k.
+//  * When a wave finishes a tile it adds its partial tile into LDS with integer
+//    atomics (exact in any order); after one barrier the workgroup applies
+//    y = RN32(float(acc) * RN32(gamma * d[m])).
 //
-// XMODE 1/2 (M <= kMaxFusedM) fuse the per-token absmax activation quantisation
-// (fp32 / bf16 input) into the staging step: every workgroup quantises the
-// activations with the same arithmetic as the standalone kernel, and workgroup 0
-// also writes x_q and x_scale.
+// XMODE 1/2 fuse the per-token absmax activation quantisation (fp32 / bf16 input,
+// M <= kMaxFusedM, one phase): the workgroup quantises the activations with the
+// same arithmetic as the standalone kernel while staging them (one read of the
+// input; the first kHold groups of each thread stay in registers between the
+// absmax and the quantise pass), and workgroup 0 also writes x_q and x_scale.
 #include "bitnet_internal.h"
 
 namespace bitnet {
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kRows = 16;      // output rows per workgroup (one MFMA tile)
-constexpr int kUnroll = 8;     // 16-byte weight loads in flight per lane
-constexpr int kStageBatch = 8; // 16-byte activation loads in flight per thread when staging
+constexpr int kThreads = 256;              // 4 waves
+constexpr int kMaxTiles = 16;              // row tiles per workgroup
 constexpr int kMaxM = 16;
 constexpr int kMaxFusedM = 4;
-constexpr int kLdsLimit = 64 * 1024;
+constexpr int kXBudget = 46 * 1024;        // LDS bytes of staged activations per phase
+                                           // (with 16 tiles of partials: < 64 KiB in all)
+constexpr int kStageBatch = 8;             // 16-byte activation loads per thread per batch
+constexpr int kHold = 2;                   // fused: groups per thread held in registers
 
-// LDS layout after the activations (offsets from zero_off = M * (K + 16)):
-constexpr int kZeroBytes = 64;                   // four zero 16-byte groups
-constexpr int kSumxOff = kZeroBytes;             // int   sumx[16]
-constexpr int kSclOff = kSumxOff + 64;           // float scl[16]
-constexpr int kRedOff = kSclOff + 64;            // v4i   red[3][64]
-constexpr int kWredOff = kRedOff + 3 * 64 * 16;  // float wred[2][4]
-constexpr int kExtra = kWredOff + 32;
+// K range staged per phase: a multiple of 256 with M * (kx + 16) <= kXBudget and
+// at most 16 activation pieces (token, 4096-k block), i.e. two staging batches.
+int phase_k(int M, int K) {
+  int kx = ((kXBudget / M - 16) / 256) * 256;
+  const int cap = 4096 * (16 / M);
+  if (kx > cap) kx = cap;
+  return kx >= K ? K : kx;
+}
 
-int lds_bytes(int64_t M, int64_t K) { return (int)(M * (K + 16)) + kExtra; }
+// LDS: X [M][kx + 16] | zero[64] | part[T][16][16] int | dsc[16] | wred[16]
+int lds_bytes(int tiles, int M, int K) {
+  return M * (phase_k(M, K) + 16) + 64 + tiles * 1024 + 64 + 64;
+}
+
+// This workgroup's matrix and the launch's scalars.  Everything the kernel needs
+// from its arguments is fetched in one round of scalar loads: the empty asm makes
+// the values materialise before the matrix is selected (selecting by index first
+// would fetch the chosen matrix's fields in a second, dependent round, and a
+// field first touched in the epilogue would cost a round trip there).  Pairs of
+// ints travel as one 64-bit value to stay within the asm operand limit.
+// Matrices j >= count have wg0[j] = grid size and are never selected.
+struct Prologue {
+  const uint8_t* wp;
+  const float* ws;
+  void* y;
+  int32_t* acc;
+  int n, wg0;
+  const int8_t* xq;
+  const float* xs;
+  const void* xf;
+  int M, K, y_bf16, T, kx, phases, mdiv;
+};
+__device__ __forceinline__ uint64_t arg_pair(const int* p) {
+  return *reinterpret_cast<const uint64_t*>(p);
+}
+__device__ __forceinline__ Prologue load_prologue(const GemvArgs& a) {
+  static_assert(kMaxGroup == 4, "load_prologue lists four matrices");
+  static_assert(offsetof(GemvArgs, n) % 8 == 0 && offsetof(GemvArgs, wg0) % 8 == 0 &&
+                    offsetof(GemvArgs, M) % 8 == 0 && offsetof(GemvArgs, y_bf16) % 8 == 0 &&
+                    offsetof(GemvArgs, kx) % 8 == 0 && offsetof(GemvArgs, mdiv) % 8 == 0,
+                "64-bit aligned int pairs");
+  const uint8_t *wp0 = a.wp[0], *wp1 = a.wp[1], *wp2 = a.wp[2], *wp3 = a.wp[3];
+  const float *ws0 = a.ws[0], *ws1 = a.ws[1], *ws2 = a.ws[2], *ws3 = a.ws[3];
+  void *y0 = a.y[0], *y1 = a.y[1], *y2 = a.y[2], *y3 = a.y[3];
+  int32_t *c0 = a.acc[0], *c1 = a.acc[1], *c2 = a.acc[2], *c3 = a.acc[3];
+  uint64_t n01 = arg_pair(&a.n[0]), n23 = arg_pair(&a.n[2]);
+  uint64_t g01 = arg_pair(&a.wg0[0]), g23 = arg_pair(&a.wg0[2]);
+  uint64_t mk = arg_pair(&a.M), bt = arg_pair(&a.y_bf16), kp = arg_pair(&a.kx);
+  uint64_t md = arg_pair(&a.mdiv);
+  const int8_t* xq = a.xq;
+  const float* xs = a.xs;
+  const void* xf = a.xf;
+  asm volatile(""
+               : "+s"(wp0), "+s"(wp1), "+s"(wp2), "+s"(wp3), "+s"(ws0), "+s"(ws1), "+s"(ws2),
+                 "+s"(ws3), "+s"(y0), "+s"(y1), "+s"(y2), "+s"(y3), "+s"(c0), "+s"(c1),
+                 "+s"(c2), "+s"(c3), "+s"(n01), "+s"(n23), "+s"(g01), "+s"(g23), "+s"(mk),
+                 "+s"(bt), "+s"(kp), "+s"(md), "+s"(xq), "+s"(xs), "+s"(xf));
+  const int b = (int)blockIdx.x;
+  const int g1 = (int)(g01 >> 32), g2 = (int)g23, g3 = (int)(g23 >> 32);
+  Prologue v{wp0, ws0, y0, c0, (int)n01, 0, xq, xs, xf,
+             (int)mk, (int)(mk >> 32), (int)bt, (int)(bt >> 32), (int)kp, (int)(kp >> 32),
+             (int)md};
+  if (b >= g1) { v.wp = wp1; v.ws = ws1; v.y = y1; v.acc = c1; v.n = (int)(n01 >> 32); v.wg0 = g1; }
+  if (b >= g2) { v.wp = wp2; v.ws = ws2; v.y = y2; v.acc = c2; v.n = (int)n23; v.wg0 = g2; }
+  if (b >= g3) { v.wp = wp3; v.ws = ws3; v.y = y3; v.acc = c3; v.n = (int)(n23 >> 32); v.wg0 = g3; }
+  return v;
+}
+
+__device__ __forceinline__ int ceil_log2(int m) { return m > 1 ? 32 - __builtin_clz(m - 1) : 0; }
 
 // One packed dword (codes of k-offsets 0..15, byte b holding 4b..4b+3) -> the
-// 16-byte operand whose byte 4i + b is the code of k-offset 4b + i.
-__device__ __forceinline__ v4i unpack_codes_transposed(uint32_t w) {
+// 16-byte operand whose byte 4i + b is the weight q = c - 1 of k-offset 4b + i.
+// Each field is isolated with a mask and mapped through a byte lookup (v_perm:
+// selector byte c picks byte c of kCodeLut: 0 -> -1, 1 -> 0, 2 -> +1).
+constexpr uint32_t kCodeLut = 0x000100ffu;
+__device__ __forceinline__ v4i unpack_weights_transposed(uint32_t w) {
   v4i a;
-  a.x = (int)(w & 0x03030303u);
-  a.y = (int)((w >> 2) & 0x03030303u);
-  a.z = (int)((w >> 4) & 0x03030303u);
-  a.w = (int)((w >> 6) & 0x03030303u);
+  a.x = (int)__builtin_amdgcn_perm(0u, kCodeLut, w & 0x03030303u);
+  a.y = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 2) & 0x03030303u);
+  a.z = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 4) & 0x03030303u);
+  a.w = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 6) & 0x03030303u);
   return a;
 }
 
-__device__ __forceinline__ void store_transposed(uint8_t* smem, int off, const uint32_t xd[4]) {
-  uint32_t pd[4];
-  transpose4x4_bytes(xd, pd);
-  *reinterpret_cast<uint4*>(smem + off) = make_uint4(pd[0], pd[1], pd[2], pd[3]);
+__device__ __forceinline__ void store_transposed(uint8_t* dst, uint4 v) {
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+  transpose4x4_bytes(in, o);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Stage activation groups [i0, i0 + kThreads * kStageBatch) of the flattened
-// [M][K/16] group index: transpose each 16-byte group into LDS.
-__device__ __forceinline__ void stage_groups(uint8_t* smem, const uint4* v, int i0, int tid,
-                                             int total, int K16, int stride) {
+// The 16 activations of one group from its raw 16-byte words (2 words of bf16 or
+// 4 of fp32); bf16 -> fp32 is exact.
+template <bool BF>
+__device__ __forceinline__ void raw_to_f32(const uint4* w, float v[16]) {
+  if (BF) {
 #pragma unroll
-  for (int b = 0; b < kStageBatch; ++b) {
-    const int i = i0 + tid + kThreads * b;
-    if (i < total) {
-      const int t = i / K16, c = i - t * K16;
-      const uint32_t xd[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
-      store_transposed(smem, t * stride + 16 * c, xd);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t d[4] = {w[h].x, w[h].y, w[h].z, w[h].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * h + 2 * j] = __uint_as_float(d[j] << 16);
+        v[8 * h + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[4 * h] = __uint_as_float(w[h].x);
+      v[4 * h + 1] = __uint_as_float(w[h].y);
+      v[4 * h + 2] = __uint_as_float(w[h].z);
+      v[4 * h + 3] = __uint_as_float(w[h].w);
     }
   }
 }
 
-template <int XMODE, int UNROLL>  // XMODE 0: int8 x_q; 1: fp32 input; 2: bf16 input
-__global__ __launch_bounds__(kThreads) void gemv_kernel(
-    const uint8_t* __restrict__ wp, const float* __restrict__ w_scale,
-    const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
-    const void* __restrict__ xf, int8_t* __restrict__ xq_out, float* __restrict__ xs_out,
-    int M, int N, int K, void* __restrict__ y, int y_bf16, int32_t* __restrict__ acc_out) {
+template <int XMODE, int R>  // XMODE 0: int8 x_q; 1: fp32 input; 2: bf16 input
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr bool BF = XMODE == 2;
+  constexpr int NV = BF ? 2 : 4;             // fused: 16-byte words per 16-element group
+  constexpr uint32_t ES = BF ? 2u : 4u;      // fused: input element size
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int r = lane & 15;  // A operand: weight row of the tile; B operand: token
-  const int g = lane >> 4;  // 16-k block of the operand within the instruction
-  const int stride = K + 16;
-  const int zero_off = M * stride;
-  int* sumx = reinterpret_cast<int*>(smem + zero_off + kSumxOff);
-  float* scl = reinterpret_cast<float*>(smem + zero_off + kSclOff);
-  v4i* red = reinterpret_cast<v4i*>(smem + zero_off + kRedOff);
-  float* wred = reinterpret_cast<float*>(smem + zero_off + kWredOff);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
+  const int r = lane & 15;  // A operand: row of the tile; B operand: token
+  const int g = lane >> 4;  // 16-k block of the operand within a 64-k chunk
+  // this workgroup's matrix (each workgroup's tiles belong to one matrix)
+  const Prologue pro = load_prologue(a);
+  const int M = pro.M, K = pro.K, T = pro.T;
+  const uint32_t rowb = (uint32_t)K >> 2;  // packed bytes per row
+  const uint8_t* wmat = pro.wp;
+  const int nrows = pro.n;
+  const int tl0 = ((int)blockIdx.x - pro.wg0) * T;   // first tile in the matrix
+  const int ntiles = min(T, (nrows + 15) / 16 - tl0);
+  const int kx = pro.kx;
+  const int stride = kx + 16;
 
-  const int n0 = blockIdx.x * kRows;
-  const int C = K >> 6;                                 // 16-byte chunks per row
-  const int S = (C + 3) >> 2;                           // 256-k super-chunks
-  const int J = (S > wave) ? (S - wave + 3) >> 2 : 0;  // super-chunks of this wave
-  const uint32_t rowb = (uint32_t)K >> 2;               // packed bytes per row
-  const int rows_here = min(kRows, N - n0);
-  const auto wr = make_rsrc(wp + (size_t)n0 * rowb, (uint32_t)rows_here * rowb);
-  const uint32_t wbase = (uint32_t)r * rowb;            // out of range when r >= rows_here
-  // Chunk of iteration j for this lane; iterations j >= J (and chunks past the
-  // row) read zeros, so a batch may run past J without changing the result.
-  auto woff = [&](int j) -> uint32_t {
-    const int c = 4 * (wave + 4 * j) + g;
-    return c < C ? wbase + 16u * (uint32_t)c : kOob;
+  uint8_t* xs = smem;                                    // [M][stride]
+  uint8_t* zero = smem + M * stride;                     // 64 zero bytes
+  int* part = reinterpret_cast<int*>(zero + 64);         // [T][16 rows][16 tokens]
+  float* dsc = reinterpret_cast<float*>(part + T * 256);  // [16]
+  float* wred = dsc + 16;                                // [16]
+
+  // Buffer descriptor of local tile tl (wave-uniform; readfirstlane keeps it in
+  // scalar registers so the loads need no per-lane legalisation loop).
+  auto tile_rsrc = [&](int tl) {
+    const int row0 = (tl0 + tl) * 16;
+    const int rows = max(0, min(16, nrows - row0));
+    const uint64_t base = (uint64_t)(wmat + (size_t)row0 * rowb);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)rows * rowb);
+    return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), bytes);
   };
-  const int K16 = K >> 4;
-  const int total = M * K16;  // 16-byte activation groups, all tokens
 
-  // 1. token scales and the first batch of int8 activation loads, then the first
-  //    weight loads, so that waiting for the former does not wait for the latter
-  const float xs_t = (XMODE == 0) ? x_scale[min(tid, M - 1)] : 0.0f;
-  uint4 xv[kStageBatch];
-  const auto xr = make_rsrc(xq, (uint32_t)M * (uint32_t)K);
-  if (XMODE == 0) {
-#pragma unroll
-    for (int b = 0; b < kStageBatch; ++b) {
-      const int i = tid + kThreads * b;
-      xv[b] = bload16(xr, i < total ? 16u * (uint32_t)i : kOob);
-    }
-  }
-  uint4 buf[UNROLL];
-#pragma unroll
-  for (int u = 0; u < UNROLL; ++u) buf[u] = bload16(wr, woff(u));
+  // clear the partial tiles and the zero slot; scalars the epilogue needs are
+  // loaded now so that their latency hides behind the stream
+  for (int i = tid; i < T * 64; i += kThreads) reinterpret_cast<uint4*>(part)[i] = make_uint4(0, 0, 0, 0);
+  if (tid < 16) reinterpret_cast<uint32_t*>(zero)[tid] = 0u;
+  // (buffer loads: the pointers come out of the asm above as generic pointers,
+  // and generic loads would make the compiler's waits for every load conservative)
+  const float xs_t = XMODE == 0 ? __uint_as_float(bload4(make_rsrc(pro.xs, 4u * (uint32_t)M),
+                                                         4u * (uint32_t)min(tid, M - 1)))
+                                : 0.0f;
+  const float gamma = __uint_as_float(bload4(make_rsrc(pro.ws, 4u), 0u));
 
-  // 2. small LDS state
-  if (tid < kMaxM) sumx[tid] = 0;
-  if (tid >= 64 && tid < 68)
-    reinterpret_cast<uint4*>(smem + zero_off)[tid - 64] = make_uint4(0u, 0u, 0u, 0u);
+  // token groups: G consecutive threads per token (G = 256 / 2^ceil(log2 M));
+  // threads of tokens >= M idle in the per-token passes
+  const int lgG = 8 - ceil_log2(M);
+  const int G = 1 << lgG;
+  const int tk = tid >> lgG;
+  const int jg = tid & (G - 1);
 
-  // 3. stage the activations, transposed within each 16-byte group
-  const float gamma = *w_scale;
-  if (XMODE == 0) {
-    stage_groups(smem, xv, 0, tid, total, K16, stride);
-    for (int i0 = kThreads * kStageBatch; i0 < total; i0 += kThreads * kStageBatch) {
-#pragma unroll
-      for (int b = 0; b < kStageBatch; ++b) {
-        const int i = i0 + tid + kThreads * b;
-        xv[b] = bload16(xr, i < total ? 16u * (uint32_t)i : kOob);
+  for (int p = 0; p < pro.phases; ++p) {
+    const int k0 = p * kx;
+    const int klen = min(kx, K - k0);
+    const int C = klen >> 6;                       // 64-k chunks in this phase
+    const int S = (C + 3) >> 2;                    // 256-k super-chunks
+    const int J = S > wave ? (S - wave + 3) >> 2 : 0;
+    const int Q = ntiles * J;                      // loads per lane in this phase
+    const uint32_t kb0 = (uint32_t)k0 >> 2;        // phase start within a packed row
+    const int K16 = klen >> 4;
+
+    // 1. first activation loads of this phase, then the first weight loads.
+    // int8 activations come in pieces (token t, 4096-k block j): lane tid loads
+    // 16-byte group c = 256 j + tid of the piece (zeros past the phase); the piece
+    // counters are uniform, so no per-lane division is needed
+    const int J16 = (K16 + 255) >> 8;              // blocks per token
+    uint4 xv[kStageBatch];
+    const auto xr = make_rsrc(pro.xq, (uint32_t)M * (uint32_t)K);
+    int lt = 0, lj = 0;                            // next piece to load
+    auto xload = [&]() -> uint4 {
+      const int c = 256 * lj + tid;
+      const uint4 v = bload16(xr, (lt < M && c < K16) ? (uint32_t)lt * (uint32_t)K +
+                                                            (uint32_t)k0 + 16u * (uint32_t)c
+                                                      : kOob);
+      if (++lj == J16) {
+        lj = 0;
+        ++lt;
       }
-      stage_groups(smem, xv, i0, tid, total, K16, stride);
+      return v;
+    };
+    // fused: group c of this thread's token (zeros past the end or for idle threads)
+    const auto fr = make_rsrc(pro.xf, (uint32_t)M * (uint32_t)K * ES);
+    auto foff = [&](int c, int h) -> uint32_t {
+      return (tk < M && c < K16) ? ((uint32_t)tk * (uint32_t)K + 16u * (uint32_t)c) * ES + 16u * h
+                                 : kOob;
+    };
+    uint4 hold[kHold][NV];
+    if constexpr (XMODE == 0) {
+#pragma unroll
+      for (int b = 0; b < kStageBatch; ++b) xv[b] = xload();
+    } else {
+#pragma unroll
+      for (int b = 0; b < kHold; ++b)
+#pragma unroll
+        for (int h = 0; h < NV; ++h) hold[b][h] = bload16(fr, foff(jg + G * b, h));
     }
-    if (tid < M) scl[tid] = gamma * xs_t;
-  } else {
-    constexpr bool BF = XMODE == 2;
-    constexpr uint32_t esz = BF ? 2u : 4u;
-    constexpr int L = BF ? 2 : 4;  // 16-byte loads per 16 activations
-    const auto fr = make_rsrc(xf, (uint32_t)M * (uint32_t)K * esz);
-    for (int t = 0; t < M; ++t) {
-      const uint32_t rowoff = (uint32_t)t * (uint32_t)K * esz;
-      float a = 0.0f;
-      for (int c0 = 0; c0 < K16; c0 += kThreads * 4) {
-        uint4 v[4][L];
+    // producer position of the ring: tile tp, step jp of this wave's super-chunks
+    // (past the last tile or chunk the offset is out of range and the load reads
+    // zeros; a wave without super-chunks never advances past its first tile)
+    int tp = 0, jp = 0;
+    auto rs = tile_rsrc(0);
+    auto next_load = [&]() -> uint4 {
+      const int c = 4 * (wave + 4 * jp) + g;
+      const uint4 v = bload16(rs, (tp < ntiles && c < C)
+                                      ? (uint32_t)r * rowb + kb0 + 16u * (uint32_t)c
+                                      : kOob);
+      if (++jp == J) {
+        jp = 0;
+        ++tp;
+        rs = tile_rsrc(tp);
+      }
+      return v;
+    };
+    uint4 ring[R];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int c = c0 + tid + kThreads * b;
+    for (int u = 0; u < R; ++u) {
+      ring[u] = next_load();
+      asm volatile("" ::: "memory");  // keep the ring's loads in slot order
+    }
+
+    // 2. stage the activations, transposed within each 16-byte group
+    if constexpr (XMODE == 0) {
+      // at most two batches (phase_k keeps the pieces <= 2 * kStageBatch);
+      // written out rather than as a loop so that the wait for the ring's loads
+      // at the top of the stream loop stays a partial one.  Every lane stores
+      // (groups past the end read as zeros and go to the zero slot): a store under
+      // a lane mask would leave its load's wait inside a skippable block, and the
+      // compiler then drains all loads in flight later.
+      static_assert(2 * kStageBatch == 16, "phase_k allows 16 pieces");
+      int st = 0, sj = 0;                          // next piece to store
+      auto store_batch = [&]() {
 #pragma unroll
-          for (int h = 0; h < L; ++h)
-            v[b][h] = bload16(fr, c < K16 ? rowoff + 16u * (uint32_t)(L * c + h) : kOob);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int h = 0; h < L; ++h) {
-            const uint32_t d[4] = {v[b][h].x, v[b][h].y, v[b][h].z, v[b][h].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (BF) {
-                a = fmaxf(a, fabsf(__uint_as_float(d[e] << 16)));
-                a = fmaxf(a, fabsf(__uint_as_float(d[e] & 0xffff0000u)));
-              } else {
-                a = fmaxf(a, fabsf(__uint_as_float(d[e])));
-              }
-            }
+        for (int b = 0; b < kStageBatch; ++b) {
+          const int c = 256 * sj + tid;
+          store_transposed((st < M && c < K16) ? xs + st * stride + 16 * c : zero, xv[b]);
+          if (++sj == J16) {
+            sj = 0;
+            ++st;
           }
+        }
+      };
+      store_batch();
+      if (M * J16 > kStageBatch) {
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b) xv[b] = xload();
+        store_batch();
       }
-      a = wave_max(a);
-      float* wrd = wred + 4 * (t & 1);
-      if (lane == 0) wrd[wave] = a;
-      lds_barrier();
-      a = fmaxf(fmaxf(wrd[0], wrd[1]), fmaxf(wrd[2], wrd[3]));
-      const float astar = fmaxf(a, kEps);
-      const float s_t = kQb / astar;
-      if (tid == 0) {
-        const float d = astar / kQb;
-        scl[t] = gamma * d;
-        if (blockIdx.x == 0) xs_out[t] = d;
-      }
-      const void* xrow = BF ? (const void*)(reinterpret_cast<const uint16_t*>(xf) + (size_t)t * K)
-                            : (const void*)(reinterpret_cast<const float*>(xf) + (size_t)t * K);
-      for (int c = tid; c < K16; c += kThreads) {
+    } else {
+      // absmax of the token over its G threads (G >= 64: one token per wave)
+      const int nb = (K16 + G - 1) >> lgG;       // groups per thread, uniform
+      float amax = 0.0f;
+#pragma unroll
+      for (int b = 0; b < kHold; ++b) {
         float v[16];
-        load16_act<BF>(xrow, c, v);
-        uint32_t xd[4];
+        raw_to_f32<BF>(hold[b], v);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xd[i] = quant4(v + 4 * i, s_t);
-        if (blockIdx.x == 0)
-          reinterpret_cast<uint4*>(xq_out + (size_t)t * K)[c] = make_uint4(xd[0], xd[1], xd[2], xd[3]);
-        store_transposed(smem, t * stride + 16 * c, xd);
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      }
+      for (int b = kHold; b < nb; ++b) {
+        uint4 w[NV];
+#pragma unroll
+        for (int h = 0; h < NV; ++h) w[h] = bload16(fr, foff(jg + G * b, h));
+        float v[16];
+        raw_to_f32<BF>(w, v);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      }
+      amax = wave_max(amax);
+      if (lane == 0) wred[wave] = amax;
+      lds_barrier();
+      const int nw = G >> 6;                     // waves per token
+      float tmax = 0.0f;
+      for (int i = 0; i < nw; ++i) tmax = fmaxf(tmax, wred[(tk * nw + i) & 3]);
+      const float astar = fmaxf(tmax, kEps);
+      const float s_t = kQb / astar;
+      if (jg == 0 && tk < M) {
+        const float d = astar / kQb;
+        dsc[tk] = d;
+        if (blockIdx.x == 0) a.xs_out[tk] = d;
+      }
+      // quantise; every lane stores (idle lanes and groups past the end hold
+      // zeros, which quantise to zeros and go to the zero slot)
+      auto put = [&](int c, const float* v) {
+        const uint4 q = make_uint4(quant4(v, s_t), quant4(v + 4, s_t), quant4(v + 8, s_t),
+                                   quant4(v + 12, s_t));
+        const bool in = tk < M && c < K16;
+        if (in && blockIdx.x == 0) reinterpret_cast<uint4*>(a.xq_out + (size_t)tk * K)[c] = q;
+        store_transposed(in ? xs + tk * stride + 16 * c : zero, q);
+      };
+#pragma unroll
+      for (int b = 0; b < kHold; ++b) {
+        float v[16];
+        raw_to_f32<BF>(hold[b], v);
+        put(jg + G * b, v);
+      }
+      for (int b = kHold; b < nb; ++b) {
+        uint4 w[NV];
+#pragma unroll
+        for (int h = 0; h < NV; ++h) w[h] = bload16(fr, foff(jg + G * b, h));
+        float v[16];
+        raw_to_f32<BF>(w, v);
+        put(jg + G * b, v);
       }
     }
-  }
-  lds_barrier();
+    if (XMODE == 0 && p == 0 && tid < M) dsc[tid] = xs_t;
+    lds_barrier();
 
-  // 4. per-token sums of the staged activations (the code-offset correction)
-  for (int t = 0; t < M; ++t) {
-    int sx = 0;
-    for (int c = tid; c < K16; c += kThreads) {
-      const v4i v = *reinterpret_cast<const v4i*>(smem + t * stride + 16 * c);
-      sx = __builtin_amdgcn_sdot4(v.x, 0x01010101, sx, false);
-      sx = __builtin_amdgcn_sdot4(v.y, 0x01010101, sx, false);
-      sx = __builtin_amdgcn_sdot4(v.z, 0x01010101, sx, false);
-      sx = __builtin_amdgcn_sdot4(v.w, 0x01010101, sx, false);
-    }
-    sx = wave_sum(sx);
-    if (lane == 0) atomicAdd(&sumx[t], sx);
-  }
-
-  // 5. stream the weights: batches of UNROLL iterations with a branch-free body
-  v4i acc = {0, 0, 0, 0};
-  const int bt = (r < M) ? r * stride : -1;
-  for (int j0 = 0; j0 < J; j0 += UNROLL) {
+    // 3. stream: consumer position (tc, jc); flush a tile's partial when it ends
+    const int bt = r < M ? r * stride : -1;
+    int tc = 0, jc = 0;
+    v4i acc = {0, 0, 0, 0};
+    for (int q0 = 0; q0 < Q; q0 += R) {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int j = j0 + u;
-      const int c = 4 * (wave + 4 * j) + g;
-      // unpack the whole chunk before refilling its slot, so the refill can land in
-      // the same registers (no loop-carried copy that would wait for the load)
-      const v4i a0 = unpack_codes_transposed(buf[u].x);
-      const v4i a1 = unpack_codes_transposed(buf[u].y);
-      const v4i a2 = unpack_codes_transposed(buf[u].z);
-      const v4i a3 = unpack_codes_transposed(buf[u].w);
-      buf[u] = bload16(wr, woff(j + UNROLL));
-      const int bbase = (bt >= 0 && c < C) ? bt + 64 * c : zero_off;
-      const v4i* bp = reinterpret_cast<const v4i*>(smem + bbase);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bp[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bp[1], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, bp[2], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, bp[3], acc, 0, 0, 0);
-    }
-  }
-
-  // 6. sum the four waves' partial tiles, correct, rescale, store
-  if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
-  lds_barrier();
-  if (wave == 0) {
-    acc += red[lane] + red[64 + lane] + red[128 + lane];
-    const int t = r;  // D layout: the lane holds rows 4g..4g+3 of the tile for token r
-    if (t < M) {
-      const int sxt = sumx[t];
-      const float sc = scl[t];
+      for (int u = 0; u < R; ++u) {
+        // unpack the whole chunk before refilling its slot, so the refill can land
+        // in the same registers (no loop-carried copy that would wait for the load)
+        v4i a0 = unpack_weights_transposed(ring[u].x);
+        v4i a1 = unpack_weights_transposed(ring[u].y);
+        v4i a2 = unpack_weights_transposed(ring[u].z);
+        v4i a3 = unpack_weights_transposed(ring[u].w);
+        // the empty asm takes the unpacked operands and orders memory reads after
+        // itself, so the scheduler cannot hoist the refill above the unpack
+        asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)::"memory");
+        ring[u] = next_load();
+        const int c = 4 * (wave + 4 * jc) + g;
+        const int bb = (bt >= 0 && c < C) ? bt + 64 * c : M * stride;
+        const v4i* bp = reinterpret_cast<const v4i*>(xs + bb);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bp[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bp[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, bp[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, bp[3], acc, 0, 0, 0);
+        if (++jc == J) {
+          // D layout: the lane holds rows 4g..4g+3 of the tile for token r
+          if (tc < ntiles && r < M) {
+            int* pt = part + tc * 256 + (4 * g) * 16 + r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int n = n0 + 4 * g + v;
-        if (n < N) {
-          const int a = acc[v] - sxt;
-          const float yv = (float)a * sc;
-          const size_t o = (size_t)t * N + n;
-          if (acc_out) acc_out[o] = a;
-          if (y_bf16)
-            reinterpret_cast<uint16_t*>(y)[o] = float_to_bf16_rne(yv);
-          else
-            reinterpret_cast<float*>(y)[o] = yv;
+            for (int v = 0; v < 4; ++v) atomicAdd(pt + 16 * v, acc[v]);
+          }
+          acc = (v4i){0, 0, 0, 0};
+          jc = 0;
+          ++tc;
         }
       }
     }
+    if (p + 1 < pro.phases) lds_barrier();  // the next phase overwrites the staged activations
   }
+  lds_barrier();
+
+  // 4. rescale, store: index = ((tile * M) + token) * 16 + row
+  int32_t* accp = pro.acc;
+  void* yp = pro.y;
+  for (int i = tid; i < ntiles * M * 16; i += kThreads) {
+    const int row = i & 15;
+    const int tt = i >> 4;
+    const int tl = (int)(((uint32_t)tt * (uint32_t)pro.mdiv) >> 16);  // tt / M
+    const int t = tt - tl * M;
+    const int n = (tl0 + tl) * 16 + row;
+    if (n < nrows) {
+      const int accv = part[tl * 256 + row * 16 + t];
+      const float yv = (float)accv * (gamma * dsc[t]);
+      const size_t o = (size_t)t * nrows + n;
+      if (accp) as_global(accp)[o] = accv;
+      if (pro.y_bf16)
+        as_global(reinterpret_cast<uint16_t*>(yp))[o] = float_to_bf16_rne(yv);
+      else
+        as_global(reinterpret_cast<float*>(yp))[o] = yv;
+    }
+  }
+}
+
+// Kernel for activation mode XMODE and ring depth 4, 8 or 16 (smallest >= R).
+template <int XMODE>
+const void* ring_kernel(int R) {
+  if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4>);
+  if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8>);
+  return reinterpret_cast<const void*>(gemv_kernel<XMODE, 16>);
+}
+
+const void* select_kernel(int xmode, int R) {
+  return xmode == 0 ? ring_kernel<0>(R) : xmode == 1 ? ring_kernel<1>(R) : ring_kernel<2>(R);
+}
+
+// Workgroups of `kernel` with `lds` bytes of LDS that the current device holds at
+// once (falls back to one per compute unit if the runtime cannot say).
+int resident_wgs(const void* kernel, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1) {
+    (void)hipGetLastError();
+    cus = 1;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) !=
+          hipSuccess ||
+      per_cu < 1) {
+    (void)hipGetLastError();
+    per_cu = 1;
+  }
+  return cus * per_cu;
 }
 
 }  // namespace
 
 bool gemv_fits(int64_t M, int64_t K) {
-  return M >= 1 && M <= kMaxM && K >= 64 && (K % 64) == 0 && lds_bytes(M, K) <= kLdsLimit;
+  return M >= 1 && M <= kMaxM && K >= 64 && (K % 64) == 0;
 }
 
-bool gemv_fused_fits(int64_t M, int64_t K) { return M <= kMaxFusedM && gemv_fits(M, K); }
-
-template <int XMODE>
-void launch_mode(dim3 grid, size_t lds, const Launch& l, int unroll, const uint8_t* wp,
-                 const float* w_scale, const int8_t* xq, const float* x_scale, const void* xf,
-                 int8_t* xq_out, float* xs_out, int M, int N, int K, void* y, int yb,
-                 int32_t* acc_out) {
-  if (unroll <= 2)
-    launch_kernel(gemv_kernel<XMODE, 2>, grid, dim3(kThreads), lds, l, wp, w_scale, xq,
-                       x_scale, xf, xq_out, xs_out, M, N, K, y, yb, acc_out);
-  else if (unroll <= 4)
-    launch_kernel(gemv_kernel<XMODE, 4>, grid, dim3(kThreads), lds, l, wp, w_scale, xq,
-                       x_scale, xf, xq_out, xs_out, M, N, K, y, yb, acc_out);
-  else
-    launch_kernel(gemv_kernel<XMODE, 8>, grid, dim3(kThreads), lds, l, wp, w_scale, xq,
-                       x_scale, xf, xq_out, xs_out, M, N, K, y, yb, acc_out);
+bool gemv_fused_fits(int64_t M, int64_t K) {
+  return gemv_fits(M, K) && M <= kMaxFusedM && phase_k((int)M, (int)K) == K;
 }
 
-hipError_t launch_gemv(const uint8_t* wp, const float* w_scale, const int8_t* xq,
-                       const float* x_scale, const void* xf, int xf_dtype, int8_t* xq_out,
-                       float* xs_out, int M, int N, int K, void* y, bool y_bf16,
-                       int32_t* acc_out, const Launch& l) {
-  if (!gemv_fits(M, K) || (xf != nullptr && M > kMaxFusedM)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((N + kRows - 1) / kRows));
-  const size_t lds = (size_t)lds_bytes(M, K);
-  const int yb = y_bf16 ? 1 : 0;
-  // loop depth: the largest per-wave iteration count, rounded up to 2, 4 or 8
-  const int jmax = ((K / 64 + 3) / 4 + 3) / 4;
-  if (xf == nullptr)
-    launch_mode<0>(grid, lds, l, jmax, wp, w_scale, xq, x_scale, xf, xq_out, xs_out, M, N, K, y,
-                   yb, acc_out);
-  else if (xf_dtype == 1)
-    launch_mode<2>(grid, lds, l, jmax, wp, w_scale, xq, x_scale, xf, xq_out, xs_out, M, N, K, y,
-                   yb, acc_out);
-  else
-    launch_mode<1>(grid, lds, l, jmax, wp, w_scale, xq, x_scale, xf, xq_out, xs_out, M, N, K, y,
-                   yb, acc_out);
-  return hipGetLastError();
+hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s) {
+  const bool fused = a.xf != nullptr;
+  if (a.count < 1 || a.count > kMaxGroup || !gemv_fits(a.M, a.K) ||
+      (fused && !gemv_fused_fits(a.M, a.K)))
+    return hipErrorInvalidValue;
+  const int xmode = !fused ? 0 : xf_dtype == 1 ? 2 : 1;
+  int tiles[kMaxGroup] = {0, 0, 0, 0};
+  int total_tiles = 0;
+  for (int j = 0; j < a.count; ++j) total_tiles += tiles[j] = (a.n[j] + 15) / 16;
+  if (total_tiles == 0) return hipSuccess;
+  // loads per lane of one tile in the first phase (the busiest wave)
+  const int kx = phase_k(a.M, a.K);
+  const int per_tile = ((kx / 64 + 3) / 4 + 3) / 4;
+  // tiles per workgroup: the fewest with which the whole grid is resident at once
+  int tpw = 1, wgs = 0;
+  const void* kernel = nullptr;
+  size_t lds = 0;
+  for (;;) {
+    kernel = select_kernel(xmode, tpw * per_tile);
+    lds = (size_t)lds_bytes(tpw, a.M, a.K);
+    wgs = 0;
+    for (int j = 0; j < a.count; ++j) wgs += (tiles[j] + tpw - 1) / tpw;
+    const int slots = resident_wgs(kernel, lds);
+    if (wgs <= slots || tpw == kMaxTiles) break;
+    int next = (total_tiles + slots - 1) / slots;
+    next = next > tpw ? next : tpw + 1;
+    tpw = next < kMaxTiles ? next : kMaxTiles;
+  }
+  a.tiles_per_wg = tpw;
+  a.kx = kx;
+  a.phases = (a.K + kx - 1) / kx;
+  a.mdiv = (65536 + a.M - 1) / a.M;  // tt / M == (tt * mdiv) >> 16 for tt < 256, M <= 16
+  int w0 = 0;
+  for (int j = 0; j < kMaxGroup; ++j) {
+    a.wg0[j] = w0;
+    if (j < a.count) w0 += (tiles[j] + tpw - 1) / tpw;
+  }
+  void* args[] = {&a};
+  return hipLaunchKernel(kernel, dim3((unsigned)wgs), dim3(kThreads), args, lds, s);
 }
 
 }  // namespace bitnet

@@ -152,6 +152,9 @@ LINEAR_SHAPES = [
     # prefill kernel: ragged M and N, several 128 x 128 tiles
     (17, 100, 256), (100, 130, 2560), (300, 257, 192), (128, 128, 64), (513, 640, 512),
     (16, 50, 4096),
+    # decode kernel: several K phases, multi-tile workgroups, M = 16 at large K
+    (16, 100, 14336), (1, 40, 28672), (3, 24, 65536), (1, 20, 131072), (2, 9000, 256),
+    (1, 70000, 64), (16, 300, 1088),
 ]
 
 
@@ -238,7 +241,8 @@ def test_end_to_end_gpu_quantisers():
 @pytest.mark.parametrize("m,n,k,dt", [(1, 2560, 2560, "bf16"), (1, 640, 6912, "f32"),
                                       (2, 100, 256, "f32"), (4, 48, 1024, "bf16"),
                                       (5, 64, 512, "f32"), (1, 20, 100, "f32"),
-                                      (1, 130, 28672, "f32"), (300, 64, 256, "bf16")])
+                                      (1, 130, 28672, "f32"), (300, 64, 256, "bf16"),
+                                      (3, 50, 12288, "bf16"), (2, 70, 8192, "f32")])
 def test_quant_linear_fused(m, n, k, dt):
     packed, gamma = O.quantize_weights(I.master_weights(n, k, 700 + n))
     xt, x_or = acts(m, k, 800 + m, dt)
@@ -305,3 +309,41 @@ def test_repeatable_and_stream_ordered():
     np.testing.assert_array_equal(f32_bits(y1), f32_bits(y2.cpu().numpy()))
     _, want = O.ternary_linear(packed, gamma, xq, d)
     np.testing.assert_array_equal(f32_bits(y1), f32_bits(want))
+
+
+def _group(ns, k, seed):
+    return [O.quantize_weights(I.master_weights(n, k, seed + i)) for i, n in enumerate(ns)]
+
+
+@pytest.mark.parametrize("m,k,ns", [(1, 2560, (2560, 640, 640)), (5, 256, (100, 37, 16, 64, 200)),
+                                    (16, 1024, (48, 33)), (40, 512, (100, 130, 17)),
+                                    (1, 64, (30000, 20000, 7))])
+def test_ternary_linear_multi(m, k, ns):
+    """Grouped matrices sharing x_q, including more than 4 (split into launches) and
+    M beyond the decode kernel (one prefill launch per matrix)."""
+    mats = _group(ns, k, 900)
+    xq, d = O.quantize_acts(I.activations(m, k, 901))
+    accs = [torch.empty((m, n), dtype=torch.int32, device=DEV) for n in ns]
+    dm = [(dev(p), dev(np.array([g], np.float32)), None, a) for (p, g), a in zip(mats, accs)]
+    ys = N.bitnet_ternary_linear_multi(dm, dev(xq), dev(d))
+    for (p, g), y, acc in zip(mats, ys, accs):
+        acc_w, y_w = O.ternary_linear(p, g, xq, d)
+        np.testing.assert_array_equal(host(acc), acc_w)
+        np.testing.assert_array_equal(f32_bits(host(y)), f32_bits(y_w))
+
+
+@pytest.mark.parametrize("m,k,ns,dt", [(1, 2560, (2560, 640, 640), "bf16"),
+                                       (1, 2560, (6912, 6912), "bf16"),
+                                       (3, 512, (100, 37, 16, 64, 200), "f32"),
+                                       (1, 28672, (40, 24), "f32"), (8, 256, (16, 20), "f32")])
+def test_quant_linear_multi(m, k, ns, dt):
+    mats = _group(ns, k, 950)
+    xt, x_or = acts(m, k, 951, dt)
+    dm = [(dev(p), dev(np.array([g], np.float32))) for p, g in mats]
+    ys, xq, xs = N.bitnet_quant_linear_multi(dm, xt, y_dtype=torch.bfloat16)
+    want_q, want_d = O.quantize_acts(x_or)
+    np.testing.assert_array_equal(host(xq), want_q)
+    np.testing.assert_array_equal(f32_bits(host(xs)), f32_bits(want_d))
+    for (p, g), y in zip(mats, ys):
+        _, y_w = O.ternary_linear(p, g, want_q, want_d)
+        np.testing.assert_array_equal(bf16_bits(y), O.f32_to_bf16_bits(y_w))
