@@ -10,8 +10,8 @@
 //
 // Design for gfx950 (the pages' kernels are CPU SIMD and lookup-table code):
 //  * Workgroup = 4 waves; it owns T consecutive 16-row tiles of one matrix (of up
-//    to kMaxGroup matrices that share the activations).  T is the smallest count
-//    with which every workgroup of the launch is resident at once.  K is cut into
+//    to kMaxGroup matrices that share the activations).  T = 1 for small launches;
+//    large ones spread equal tile counts over two workgroups per CU.  K is cut into
 //    256-k super-chunks; wave w takes super-chunks w, w + 4, ..., so one wave load
 //    instruction covers 16 rows x 64 contiguous bytes and the four waves read 256
 //    contiguous bytes of each row per step.
@@ -50,6 +50,9 @@ constexpr int kXBudget = 46 * 1024;        // LDS bytes of staged activations pe
                                            // (with 16 tiles of partials: < 64 KiB in all)
 constexpr int kStageBatch = 8;             // 16-byte activation loads per thread per batch
 constexpr int kHold = 2;                   // fused: groups per thread held in registers
+constexpr int64_t kLatencyBytes = 6000000; // launches above this use the bandwidth regime
+constexpr int kWgsPerCu = 2;               // bandwidth regime: workgroups per compute unit
+constexpr int kFlightLoads = 8192;         // target 1 KiB loads in flight over the chip
 
 // K range staged per phase: a multiple of 256 with M * (kx + 16) <= kXBudget and
 // at most 16 activation pieces (token, 4096-k block), i.e. two staging batches.
@@ -456,23 +459,16 @@ const void* select_kernel(int xmode, int R) {
   return xmode == 0 ? ring_kernel<0>(R) : xmode == 1 ? ring_kernel<1>(R) : ring_kernel<2>(R);
 }
 
-// Workgroups of `kernel` with `lds` bytes of LDS that the current device holds at
-// once (falls back to one per compute unit if the runtime cannot say).
-int resident_wgs(const void* kernel, size_t lds) {
-  int dev = 0, cus = 0, per_cu = 0;
+// Compute units of the current device (1 if the runtime cannot say).
+int device_cus() {
+  int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1) {
     (void)hipGetLastError();
     cus = 1;
   }
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) !=
-          hipSuccess ||
-      per_cu < 1) {
-    (void)hipGetLastError();
-    per_cu = 1;
-  }
-  return cus * per_cu;
+  return cus;
 }
 
 }  // namespace
@@ -498,21 +494,31 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s) {
   // loads per lane of one tile in the first phase (the busiest wave)
   const int kx = phase_k(a.M, a.K);
   const int per_tile = ((kx / 64 + 3) / 4 + 3) / 4;
-  // tiles per workgroup: the fewest with which the whole grid is resident at once
-  int tpw = 1, wgs = 0;
-  const void* kernel = nullptr;
-  size_t lds = 0;
-  for (;;) {
-    kernel = select_kernel(xmode, tpw * per_tile);
-    lds = (size_t)lds_bytes(tpw, a.M, a.K);
-    wgs = 0;
-    for (int j = 0; j < a.count; ++j) wgs += (tiles[j] + tpw - 1) / tpw;
-    const int slots = resident_wgs(kernel, lds);
-    if (wgs <= slots || tpw == kMaxTiles) break;
-    int next = (total_tiles + slots - 1) / slots;
-    next = next > tpw ? next : tpw + 1;
-    tpw = next < kMaxTiles ? next : kMaxTiles;
+  // Two regimes (measured on the decode shapes): a launch of at most
+  // kLatencyBytes of packed weights gives every tile its own workgroup, so all
+  // loads issue at once; a larger one is spread as kWgsPerCu workgroups per
+  // compute unit with equal tile counts.  The ring depth targets kFlightLoads
+  // 1 KiB loads in flight over the whole chip: deeper rings measured slower
+  // (more requests queue without more throughput).
+  const int cus = device_cus();
+  auto count_wgs = [&](int t) {
+    int w = 0;
+    for (int j = 0; j < a.count; ++j) w += (tiles[j] + t - 1) / t;
+    return w;
+  };
+  int tpw = 1;
+  if ((int64_t)total_tiles * 16 * (a.K / 4) > kLatencyBytes) {
+    for (int k = kWgsPerCu;; ++k) {
+      tpw = (total_tiles + cus * k - 1) / (cus * k);
+      if (tpw <= kMaxTiles) break;
+    }
   }
+  const int wgs = count_wgs(tpw);
+  int ring = 4;
+  while (ring < 16 && 2 * ring * 4 * wgs <= kFlightLoads) ring *= 2;
+  if (ring > tpw * per_tile) ring = tpw * per_tile;
+  const void* kernel = select_kernel(xmode, ring);
+  const size_t lds = (size_t)lds_bytes(tpw, a.M, a.K);
   a.tiles_per_wg = tpw;
   a.kx = kx;
   a.phases = (a.K + kx - 1) / kx;
