@@ -15,7 +15,9 @@ between reuses (4x the 256 MB Infinity Cache) and weights stream from HBM.
 Printed: one JSON line.  value = packed weight bytes per step / step time.
 roofline = the decode kernel (the only kernel in the step): achieved = mean
 packed bytes per launch / mean launch time, where the mean launch time is the
-graph replay time over the timed steps divided by the number of launches.
+graph replay time over the timed steps divided by the number of launches (so it
+includes the gap between dependent launches); traffic = HBM bytes per launch from
+the PMC summary in profiles/, when it was taken on the current kernel sources.
 Also: the 100B-class decode stack (96 layers, 23.35 GB packed, fp32 activations),
 the prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096, and the
 CPU oracle timed on a bounded sample of the same decode workload.
@@ -28,6 +30,7 @@ import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -41,6 +44,24 @@ CACHE_CYCLE_BYTES = 1 << 30      # cycle at least 1 GiB of weights between reuse
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed PMC summary, or None when the
+    decode kernel's sources differ from the ones the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_bitnet2b_decode_chain.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-record:"):
+            csrc = os.path.join(ROOT, "ternary_weight_linear_bit_amd", "csrc")
+            for name, digest in re.findall(r"(\S+) sha256=([0-9a-f]{64})", line):
+                data = open(os.path.join(csrc, name), "rb").read()
+                if hashlib.sha256(data).hexdigest() != digest:
+                    return None
+            return int(re.search(r"bytes_per_launch=(\d+)", line).group(1))
+    return None
 
 
 def parse():
@@ -131,18 +152,21 @@ def decode_leg(torch, N, I, name, steps, warmup):
     for i in range(warmup):
         graphs[i % replicas].replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
     for i in range(steps):
         graphs[i % replicas].replay()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    pct = {q: per[min(steps - 1, int(q / 100 * steps))] for q in (10, 50, 90)}
     gbs = per_stack / (ms * 1e-3) / 1e9
     log(f"{name}: {ms * 1e3:.1f} us/token, {gbs:.1f} GB/s packed, "
         f"{ms * 1e3 / launches:.2f} us per launch")
     res = dict(ms=ms, gbs=gbs, per_stack=per_stack, replicas=replicas, launches=launches,
-               layers=layers, shapes=shapes, act=wl["act"])
+               layers=layers, shapes=shapes, act=wl["act"],
+               ms_p10=pct[10], ms_median=pct[50], ms_p90=pct[90])
     del graphs, stack
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -269,8 +293,11 @@ def main():
                    "matrices_per_layer": len(d["shapes"]), "packed_bytes_per_step": d["per_stack"],
                    "activations": d["act"], "weight_replicas_cycled": d["replicas"],
                    "launches_per_step": d["launches"], "graph": "hip"},
+        "ms_per_step_p10_median_p90": [round(d["ms_p10"], 5), round(d["ms_median"], 5),
+                                       round(d["ms_p90"], 5)],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(),
                      "kernel": "gemv_kernel (decode, fused int8 activation quantisation)",
                      "avg_launch_us": round(avg_launch * 1e6, 3),
                      "avg_bytes_per_launch": int(avg_bytes),
