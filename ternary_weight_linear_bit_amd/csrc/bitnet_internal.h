@@ -37,13 +37,18 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// 4x4 byte transpose of four dwords: out[i].byte[b] = in[b].byte[i].
+// 4x4 byte transpose of four dwords: out[i].byte[b] = in[b].byte[i], as eight
+// byte permutes (v_perm: selector bytes 0-3 pick from the second operand, 4-7
+// from the first).
 __device__ __forceinline__ void transpose4x4_bytes(const uint32_t in[4], uint32_t out[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    out[i] = ((in[0] >> (8 * i)) & 0xffu) | (((in[1] >> (8 * i)) & 0xffu) << 8) |
-             (((in[2] >> (8 * i)) & 0xffu) << 16) | (((in[3] >> (8 * i)) & 0xffu) << 24);
-  }
+  const uint32_t t0 = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);  // in0.b0 in1.b0 in0.b1 in1.b1
+  const uint32_t t1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);  // in0.b2 in1.b2 in0.b3 in1.b3
+  const uint32_t t2 = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
 // Quantise four activations with the token's factor s = RN32(127 / a*):
@@ -96,6 +101,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every range used with make_rsrc
+
+// make_rsrc for a base and size that are the same in every lane of the wave: the
+// readfirstlanes keep the descriptor in scalar registers, so the loads need no
+// per-lane legalisation loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_uniform_rsrc(const void* base,
+                                                                    uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);

@@ -2,119 +2,192 @@
 //
 // Method: dashen-tech.com, "BitNet.cpp 深度解析", section 3.1: ternary weights turn
 // the float matmul into an integer one.  At many tokens the contraction is
-// compute-bound (hundreds of int8 ops per weight byte), so the ternary tiles are
-// expanded to signed int8 in LDS and fed to v_mfma_i32_16x16x64_i8.
+// compute-bound (hundreds of int8 ops per packed weight byte), so it runs on
+// v_mfma_i32_32x32x32_i8 with the ternary weights expanded to int8 in registers.
 //
-// Tile: 128 tokens x 128 output rows per workgroup, K step 64; 4 waves as 2 x 2,
-// each owning a 64 x 64 sub-tile (4 x 4 instructions, 64 int32 accumulators per
-// lane).  Per K step each thread loads 32 activation bytes and 8 packed weight
-// bytes (32 codes) from global memory into registers one step ahead, expands the
-// codes to signed int8 in natural k order and writes both tiles to LDS (row
-// stride 80 bytes so the 16-byte operand reads of 8 consecutive rows hit distinct
-// banks).  The rescale y = RN32(float(acc) * RN32(gamma * d[m])) is fused into the
+// Workgroup tile: BM tokens x 128 output rows, 4 waves as 2 (tokens) x 2 (rows);
+// a wave owns (BM / 2) tokens x 64 rows = (BM / 64) x 2 blocks of 32 x 32 int32
+// accumulators.  K advances in steps of 128:
+//  * activations: the workgroup stages the BM x 128 int8 tile into LDS (double
+//    buffered, one barrier per step), byte-transposed within each 16-byte group;
+//  * weights: each wave loads its 64 rows x 128 k of packed codes straight from
+//    global memory (16 bytes per lane) and expands them in registers with the same
+//    shift / mask / byte-lookup as the decode kernel, whose k order matches the
+//    transposed activations, so neither operand needs a per-element shuffle;
+//  * loads run kDepth steps ahead of the matrix cores.
+// Lane (r, h) of a 32 x 32 x 32 operand holds row r and 16 k: with the 16 bytes
+// lane h loads per row (k0 + 64h .. k0 + 64h + 63), MFMA j of a step sums over
+// k0 + 64h + 16j + (0..15) for h = 0, 1; the A operand reads the matching LDS
+// group.  The rescale y = RN32(float(acc) * RN32(gamma * d[m])) is fused into the
 // store.
 #include "bitnet_internal.h"
 
 namespace bitnet {
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int kThreads = 256;
-constexpr int kLds = BK + 16;   // row stride in bytes
+typedef int v16i __attribute__((ext_vector_type(16)));
 
-// One packed dword (codes of k-offsets 0..15) -> four dwords of signed int8 in
-// natural order (dword b holds k-offsets 4b..4b+3).
-__device__ __forceinline__ void unpack_signed_natural(uint32_t w, uint32_t out[4]) {
-  uint32_t m[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m[i] = (w >> (2 * i)) & 0x03030303u;   // byte b = code(4b + i)
-  transpose4x4_bytes(m, out);                                         // byte i = code(4b + i)
-#pragma unroll
-  for (int b = 0; b < 4; ++b) out[b] = (out[b] + 0x7f7f7f7fu) ^ 0x80808080u;  // c -> c - 1
+constexpr int BN = 128;         // output rows per workgroup
+constexpr int BK = 128;         // k per step
+constexpr int kThreads = 256;
+constexpr int kStride = BK;       // LDS bytes per staged token row (groups XOR-swizzled)
+
+// LDS byte offset of 16-byte group kg of staged token row t (128-byte rows).  The
+// group index is XORed with the low bits of t so that consecutive tokens reading
+// the same group (the A operand) and the 8 groups of one row (staging writes)
+// fall in distinct banks.
+__device__ __forceinline__ int lds_group(int t, int kg) {
+  return t * kStride + 16 * (kg ^ (t & 7));
+}
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, each with its own L2
+constexpr int kDepth = 2;         // steps of global loads in flight
+
+// Packed dword (16 codes) -> signed int8 operand in the 4x4-byte-transposed k
+// order (byte 4i + b = weight of k-offset 4b + i): mask each 2-bit field and map
+// code c to c - 1 with a byte lookup.
+constexpr uint32_t kCodeLut = 0x000100ffu;
+__device__ __forceinline__ v4i expand_weights(uint32_t w) {
+  v4i a;
+  a.x = (int)__builtin_amdgcn_perm(0u, kCodeLut, w & 0x03030303u);
+  a.y = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 2) & 0x03030303u);
+  a.z = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 4) & 0x03030303u);
+  a.w = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 6) & 0x03030303u);
+  return a;
 }
 
+template <int BM>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint8_t* __restrict__ wp, const float* __restrict__ w_scale,
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale, int M, int N, int K,
     void* __restrict__ y, int y_bf16, int32_t* __restrict__ acc_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[BM * kLds];
-  __shared__ __attribute__((aligned(16))) uint8_t ws[BN * kLds];
+  constexpr int TB = BM / 64;               // 32-token blocks per wave
+  constexpr int XG = BM * (BK / 16) / kThreads;  // 16-byte activation groups per thread per step
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * kStride];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 1, wr = wave & 1;
+  const int r = lane & 31, h = lane >> 5;
+  // XCD-aware tile order: workgroup b runs on XCD b % 8 (round-robin dispatch);
+  // each XCD takes a contiguous run of tiles in token-major order, so the
+  // workgroups that share an activation tile share one XCD's L2
+  const int nb = (N + BN - 1) / BN;
+  const int tiles = nb * ((M + BM - 1) / BM);
+  const int per_xcd = (tiles + kXcds - 1) / kXcds;
+  const int t = ((int)blockIdx.x % kXcds) * per_xcd + (int)blockIdx.x / kXcds;
+  if (t >= tiles) return;
+  const int m0 = (t / nb) * BM;
+  const int n0 = (t % nb) * BN;
+  const uint32_t rowb = (uint32_t)K >> 2;
+  const int steps = (K + BK - 1) / BK;   // K % 64 == 0; a last step of 64 k reads zeros past K
 
-  // global -> register assignment: row tid/2, half tid%2 of the K step
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const bool xrow_ok = m0 + lrow < M;
-  const bool wrow_ok = n0 + lrow < N;
-  const int8_t* xptr = xq + (size_t)(xrow_ok ? m0 + lrow : 0) * K + 32 * lhalf;
-  const uint8_t* wptr = wp + (size_t)(wrow_ok ? n0 + lrow : 0) * (size_t)(K >> 2) + 8 * lhalf;
-  uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
-  uint2 wv = make_uint2(0u, 0u);
-  auto gload = [&](int k0) {
-    if (xrow_ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(xptr + k0);
-      xa = p[0];
-      xb = p[1];
-    }
-    if (wrow_ok) wv = *reinterpret_cast<const uint2*>(wptr + (k0 >> 2));
+  // activations: group g = tid + 256 i of the BM x 128 tile (token g / 8, k-group g % 8);
+  // tokens past M read zeros (range-checked buffer)
+  const int mrows = min(BM, M - m0);
+  const auto xr = make_uniform_rsrc(xq + (size_t)m0 * K, (uint32_t)mrows * (uint32_t)K);
+  auto xoff = [&](int i, int k0) -> uint32_t {
+    const int g = tid + kThreads * i;
+    const int k = k0 + 16 * (g & 7);
+    return k < K ? (uint32_t)(g >> 3) * (uint32_t)K + (uint32_t)k : kOob;
+  };
+  // weights: this wave's 64 rows; rows past N read zeros
+  const int wrow0 = n0 + wr * 64;
+  const int wrows = max(0, min(64, N - wrow0));
+  const auto wrs = make_uniform_rsrc(wp + (size_t)wrow0 * rowb, (uint32_t)wrows * rowb);
+  auto woff = [&](int b, int k0) -> uint32_t {
+    const int k = k0 + 64 * h;
+    return k < K ? (uint32_t)(32 * b + r) * rowb + ((uint32_t)k >> 2) : kOob;
   };
 
-  v4i acc[4][4];
+  // (past the last step the offsets leave the buffers and the loads read zeros:
+  // no branch around the loads, whose waits would then sit in a skippable block)
+  // (the past-the-end bit is ORed in arithmetically: a select on it is turned
+  // into a branch, which also drains every load in flight at the loop top)
+  auto gload = [&](uint4 (&xv)[XG], uint4 (&wv)[2], int s) {
+    const int k0 = s * BK;
+    const uint32_t past = (uint32_t)(s >= steps) << 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < XG; ++i) xv[i] = bload16(xr, xoff(i, k0) | past);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+    for (int b = 0; b < 2; ++b) wv[b] = bload16(wrs, woff(b, k0) | past);
+  };
 
-  const int orow = lane & 15, ocol = 16 * (lane >> 4);
-  gload(0);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-    {
-      uint8_t* xd = xs + lrow * kLds + 32 * lhalf;
-      *reinterpret_cast<uint4*>(xd) = xa;
-      *reinterpret_cast<uint4*>(xd + 16) = xb;
-      uint32_t o[8];
-      unpack_signed_natural(wv.x, o);
-      unpack_signed_natural(wv.y, o + 4);
-      uint8_t* wd = ws + lrow * kLds + 32 * lhalf;
-      *reinterpret_cast<uint4*>(wd) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(wd + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+  uint4 xv_[kDepth][XG];
+  uint4 wv_[kDepth][2];
+  v16i acc[TB][2];
+#pragma unroll
+  for (int i = 0; i < TB; ++i)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[i][b] = (v16i){};
+
+  auto body = [&](uint4 (&xv)[XG], uint4 (&wv)[2], int s) {
+    uint8_t* buf = xs[s & 1];
+    // stage this step's activations (transposed within each 16-byte group)
+#pragma unroll
+    for (int i = 0; i < XG; ++i) {
+      const int g = tid + kThreads * i;
+      const uint32_t in[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+      uint32_t o[4];
+      transpose4x4_bytes(in, o);
+      *reinterpret_cast<uint4*>(buf + lds_group(g >> 3, g & 7)) =
+          make_uint4(o[0], o[1], o[2], o[3]);
     }
-    __syncthreads();
-    if (k0 + BK < K) gload(k0 + BK);
-    v4i af[4], bf[4];
+    // expand this step's weights before their registers are refilled
+    v4i bop[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[i] = *reinterpret_cast<const v4i*>(xs + (wm * 64 + i * 16 + orow) * kLds + ocol);
-      bf[i] = *reinterpret_cast<const v4i*>(ws + (wn * 64 + i * 16 + orow) * kLds + ocol);
+    for (int b = 0; b < 2; ++b) {
+      bop[b][0] = expand_weights(wv[b].x);
+      bop[b][1] = expand_weights(wv[b].y);
+      bop[b][2] = expand_weights(wv[b].z);
+      bop[b][3] = expand_weights(wv[b].w);
     }
+    // the empty asm takes the expanded operands, so the expansion cannot sink
+    // below the refill of the registers it reads (which would force copies and a
+    // full wait for every load in flight at each loop trip)
+    asm volatile("" : "+v"(bop[0][0]), "+v"(bop[0][1]), "+v"(bop[0][2]), "+v"(bop[0][3]),
+                 "+v"(bop[1][0]), "+v"(bop[1][1]), "+v"(bop[1][2]), "+v"(bop[1][3])::"memory");
+    lds_barrier();  // staged tile visible; the other buffer is no longer read
+    gload(xv, wv, s + kDepth);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < TB; ++i) {
+        const v4i a = *reinterpret_cast<const v4i*>(
+            buf + lds_group(wt * (BM / 2) + 32 * i + r, 4 * h + j));
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[i][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop[b][j], acc[i][b], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    gload(xv_[d], wv_[d], d);
+    asm volatile("" ::: "memory");  // issue the sets in order, as the loop refills them
+  }
+  // register set d holds step s + d; steps past the end (when kDepth does not
+  // divide the step count) only stage zeros and add zero products
+  for (int s = 0; s < steps; s += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) body(xv_[d], wv_[d], s + d);
   }
 
-  // D layout: lane holds tokens 4*(lane/16) + v of each 16 x 16 block, row lane % 16
+  // D layout (32 x 32): lane l holds output row (n) l % 32 and tokens
+  // 8 (v / 4) + 4 (l / 32) + v % 4 for its 16 values v
   const float gamma = *w_scale;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TB; ++i) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + v;
+    for (int v = 0; v < 16; ++v) {
+      const int m = m0 + wt * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
       if (m < M) {
         const float sc = gamma * x_scale[m];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 64 + j * 16 + (lane & 15);
+        for (int b = 0; b < 2; ++b) {
+          const int n = wrow0 + 32 * b + r;
           if (n < N) {
-            const int a = acc[i][j][v];
+            const int a = acc[i][b][v];
             const float yv = (float)a * sc;
             const size_t o = (size_t)m * N + n;
             if (acc_out) acc_out[o] = a;
@@ -161,10 +234,14 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                        const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
                        int32_t* acc_out, hipStream_t s) {
-  if (K % BK != 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(kThreads), 0, s, wp, w_scale, xq, x_scale, M, N, K, y,
-                     y_bf16 ? 1 : 0, acc_out);
+  if (K % 64 != 0) return hipErrorInvalidValue;
+  // 128-token tiles: 256-token ones (2 x 2 waves of 128 x 64) measured slower on
+  // every prefill shape (more registers, fewer waves to hide latency)
+  const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + 127) / 128);
+  if (tiles > (int64_t)1 << 30) return hipErrorInvalidValue;  // grid and tile index limits
+  const dim3 grid((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds));
+  hipLaunchKernelGGL(gemm_kernel<128>, grid, dim3(kThreads), 0, s, wp, w_scale, xq, x_scale, M, N,
+                     K, y, y_bf16 ? 1 : 0, acc_out);
   return hipGetLastError();
 }
 
