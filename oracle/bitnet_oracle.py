@@ -42,6 +42,20 @@ O4  activations: per token (row) absmax a, a* = max(a, RN32(1e-5)),
 O5  contraction: acc[m, n] = sum_k q[n, k] * xq[m, k] exactly (int32 range).
 O6  rescale: y = RN32(float(acc) * RN32(gamma* * d[m])); bf16 output = RNE(y).
 
+Neighbours of the layer ([CM], section introducing BitNet b1.58 2B4T, item
+"架構" (architecture): squared-ReLU activation, sub-layer normalisation, no bias
+terms anywhere):
+N1  squared-ReLU gating: u = RN32(RN32(max(g, 0) * max(g, 0)) * up), elementwise,
+    where g and up are the gate and up projections of the same input.
+N2  sub-layer RMS normalisation (no bias) of the input v of a BitLinear layer:
+    RMSNorm(v)[k] = v[k] * w[k] * r with r = 1 / sqrt(mean_k v[k]^2 + eps).
+    ms = RN32(exact sum_k v^2 / K); r = RN32(1 / sqrt(RN32(ms + eps))) with the
+    square root and the division taken in float64.
+N3  normalise-then-quantise: r is a positive per-token factor and absmax
+    quantisation is invariant under such factors, so the layer quantises
+    v * w (fp32 products) with O4 and folds r into the token scale:
+    xq = O4(v * w).xq, d = RN32(O4(v * w).d * r).
+
 bf16 inputs are upcast to fp32 exactly (bit pattern shifted left by 16) before
 any step, so every function here takes fp32 arrays.
 
@@ -298,6 +312,74 @@ def ternary_linear_at(packed: np.ndarray, gamma: np.float32, xq: np.ndarray,
     acc = acc.astype(np.int32)
     scale = (F32(gamma) * np.asarray(d, dtype=np.float32)[m_idx]).astype(np.float32)
     return acc, acc.astype(np.float32) * scale
+
+
+# ---------------------------------------------------------------------------
+# N1-N3: the layer's neighbours fused into its input ([CM] architecture item)
+# ---------------------------------------------------------------------------
+
+def relu2_glu(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """N1: u = RN32(RN32(a * a) * up) with a = max(gate, 0), all fp32."""
+    a = np.maximum(np.asarray(gate, dtype=np.float32), F32(0.0))
+    return ((a * a).astype(np.float32) * np.asarray(up, dtype=np.float32)).astype(np.float32)
+
+
+def exact_square_sum_units(v: np.ndarray) -> int:
+    """Exact sum of v**2 over fp32 ``v`` as an integer count of 2**-298 units.
+
+    v = m * 2**(e - 150) for a normal value (m the 24-bit significand, e the
+    biased exponent), m * 2**-149 for a subnormal, so v**2 = m**2 * 2**(2e - 300)
+    (normal) or m**2 * 2**-298 (subnormal).  m**2 < 2**48 is split into two
+    24-bit halves that numpy sums exactly in float64 per exponent; the
+    per-exponent sums are combined in Python integers.  Needs fewer than 2**29
+    elements and finite values.
+    """
+    bits = np.ascontiguousarray(v, dtype=np.float32).reshape(-1).view(np.uint32)
+    if bits.size >= (1 << 29):
+        raise ValueError("exact square sum supports fewer than 2**29 elements")
+    e = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.intp)
+    if np.any(e == 0xFF):
+        raise ValueError("exact square sum needs finite values")
+    frac = (bits & np.uint32(0x7FFFFF)).astype(np.uint64)
+    mant = np.where(e > 0, frac | np.uint64(1 << 23), frac)
+    sq = mant * mant
+    hi = np.bincount(e, weights=(sq >> np.uint64(24)).astype(np.float64), minlength=256)
+    lo = np.bincount(e, weights=(sq & np.uint64(0xFFFFFF)).astype(np.float64), minlength=256)
+    total = 0
+    for ex in range(255):
+        part = (int(hi[ex]) << 24) + int(lo[ex])
+        total += part << (2 * ex - 2 if ex > 0 else 0)
+    return total
+
+
+def rms_factor(v: np.ndarray, eps: float) -> np.ndarray:
+    """N2: per row, r = RN32(1 / sqrt(RN32(RN32(exact sum v^2 / K) + eps)))."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    m_rows, k = v.shape
+    eps32 = F32(eps)
+    out = np.empty(m_rows, dtype=np.float32)
+    for m in range(m_rows):
+        ms = rn32_ratio(exact_square_sum_units(v[m]), k << 298)
+        t = F32(ms + eps32)
+        out[m] = F32(1.0 / math.sqrt(float(t)))
+    return out
+
+
+def prologue_quantize_acts(x: np.ndarray, up=None, norm_weight=None, eps: float = 1e-5):
+    """The layer input after its neighbours, quantised (N1-N3, then O4).
+
+    x is the layer input, or the gate projection when ``up`` is given (N1);
+    with ``norm_weight`` the input is RMS-normalised first (N2), quantised as
+    v * w and rescaled by r (N3).  Returns (xq int8 [M, K], d fp32 [M]).
+    """
+    v = np.ascontiguousarray(x, dtype=np.float32)
+    if up is not None:
+        v = relu2_glu(v, up)
+    if norm_weight is None:
+        return quantize_acts(v)
+    w = np.asarray(norm_weight, dtype=np.float32)
+    xq, d = quantize_acts((v * w[None, :]).astype(np.float32))
+    return xq, (d * rms_factor(v, eps)).astype(np.float32)
 
 
 def quant_linear(packed: np.ndarray, gamma: np.float32, x: np.ndarray):

@@ -426,3 +426,110 @@ def test_bf16_upcast_is_exact():
     x = torch.randn(1000, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
     bits = x.view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(O.bf16_bits_to_f32(bits), x.float().numpy())
+
+
+# ---------------------------------------------------------------------------
+# N1-N3: squared-ReLU gating and the sub-layer RMS norm in front of the layer
+# ---------------------------------------------------------------------------
+
+def _f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+def test_relu2_glu_hand_worked_rounding():
+    """Worked by hand: a = 1 + 2^-12, a^2 = 1 + 2^-11 + 2^-24 is a tie between
+    1 + 2^-11 (even) and the next fp32, so RN32(a^2) = 1 + 2^-11 (0x3F801000);
+    times up = 1 + 2^-23 the exact product 1 + 2^-11 + 2^-23 + 2^-34 rounds to
+    0x3F801001.  Rounding once at the end instead would give 0x3F801002."""
+    gate = np.array([_f32(0x3F800800), -2.0, 3.0, 0.0], dtype=np.float32)
+    up = np.array([_f32(0x3F800001), 5.0, 0.5, -7.0], dtype=np.float32)
+    u = O.relu2_glu(gate, up)
+    assert u.view(np.uint32)[0] == 0x3F801001
+    assert u[1] == 0.0 and u[2] == np.float32(4.5) and u[3] == 0.0
+
+
+def test_relu2_glu_matches_exact_rational_steps():
+    rng = np.random.default_rng(11)
+    g = rng.standard_normal(2000).astype(np.float32)
+    up = rng.standard_normal(2000).astype(np.float32)
+    u = O.relu2_glu(g, up)
+    for i in range(0, 2000, 7):
+        a = max(Fraction(float(g[i])), Fraction(0))
+        a2 = O.rn32_ratio((a * a).numerator, (a * a).denominator)
+        prod = Fraction(float(a2)) * Fraction(float(up[i]))
+        want = O.rn32_ratio(abs(prod).numerator, prod.denominator) if prod != 0 else np.float32(0)
+        want = -want if prod < 0 else want
+        assert np.float32(u[i]) == np.float32(want)
+
+
+def test_exact_square_sum_equals_fraction_sum():
+    rng = np.random.default_rng(12)
+    v = (rng.standard_normal(3000) * np.exp(rng.uniform(-60, 60, 3000))).astype(np.float32)
+    v[:5] = np.array([0x1, 0x7FFFFF, 0x00800000, 0x3F800000, 0x80000003], dtype=np.uint32).view(np.float32)
+    exact = sum(Fraction(float(t)) ** 2 for t in v)
+    assert Fraction(O.exact_square_sum_units(v), 1 << 298) == exact
+
+
+def test_rms_factor_closed_form_integer_rows():
+    """Rows 1..n (eps = 0): sum k^2 = n(n+1)(2n+1)/6, so mean = (n+1)(2n+1)/6."""
+    for n in (1, 3, 64, 1000, 4096):
+        v = np.arange(1, n + 1, dtype=np.float32)[None, :]
+        mean = Fraction((n + 1) * (2 * n + 1), 6)
+        ms = O.rn32_ratio(mean.numerator, mean.denominator)
+        want = np.float32(1.0 / math.sqrt(float(ms)))
+        assert O.rms_factor(v, 0.0)[0] == want
+
+
+def test_rms_factor_power_of_two_scaling_and_float64():
+    rng = np.random.default_rng(13)
+    v = rng.standard_normal((6, 700)).astype(np.float32)
+    r0 = O.rms_factor(v, 0.0)
+    for j in (-5, 3, 9):
+        rj = O.rms_factor((v * np.float32(2.0 ** j)).astype(np.float32), 0.0)
+        np.testing.assert_array_equal(rj, (r0 * np.float32(2.0 ** -j)).astype(np.float32))
+    r = O.rms_factor(v, 1e-5)
+    ref = 1.0 / np.sqrt((v.astype(np.float64) ** 2).mean(axis=1) + 1e-5)
+    assert np.all(np.abs(r / ref - 1.0) < 3e-7)
+
+
+def test_prologue_quantize_matches_normalise_then_quantise():
+    """N3 against the textbook order (normalise in float64, then O4 in float64):
+    the int8 codes agree except where a product lands within rounding of a
+    half-integer, the token scale to float rounding."""
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((8, 2560)).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(2560)).astype(np.float32)
+    xq, d = O.prologue_quantize_acts(x, norm_weight=w, eps=1e-5)
+    x64 = x.astype(np.float64)
+    y = x64 / np.sqrt((x64 ** 2).mean(axis=1, keepdims=True) + 1e-5) * w.astype(np.float64)
+    a = np.abs(y).max(axis=1)
+    q64 = np.clip(np.rint(y * (127.0 / a)[:, None]), -128, 127)
+    assert np.mean(xq == q64) > 0.999
+    assert np.all(np.abs(d / (a / 127.0) - 1.0) < 1e-6)
+
+
+def test_prologue_quantize_invariants():
+    rng = np.random.default_rng(15)
+    g = rng.standard_normal((5, 512)).astype(np.float32)
+    up = rng.standard_normal((5, 512)).astype(np.float32)
+    w = (1.0 + 0.2 * rng.standard_normal(512)).astype(np.float32)
+    xq, d = O.prologue_quantize_acts(g, up=up, norm_weight=w, eps=0.0)
+    # scaling the up projection of a row by 2^j leaves the normalised input, so
+    # the codes and the token scale, unchanged (eps = 0)
+    for j in (-7, 4):
+        xq2, d2 = O.prologue_quantize_acts(g, up=(up * np.float32(2.0 ** j)).astype(np.float32),
+                                           norm_weight=w, eps=0.0)
+        np.testing.assert_array_equal(xq2, xq)
+        np.testing.assert_array_equal(d2, d)
+    # a gate that is negative everywhere zeroes the row: codes 0, and the scale
+    # is the zero-row act-quant scale times 1/sqrt(eps)
+    gz = -np.abs(g)
+    xq0, d0 = O.prologue_quantize_acts(gz, up=up, norm_weight=w, eps=1e-5)
+    assert not np.any(xq0)
+    base = np.float32(O.EPS / O.QB)
+    assert np.all(d0 == np.float32(base * np.float32(1.0 / math.sqrt(float(np.float32(1e-5))))))
+    # without a norm the prologue is plain O4 of the gated input
+    xq1, d1 = O.prologue_quantize_acts(g, up=up)
+    xq2, d2 = O.quantize_acts(O.relu2_glu(g, up))
+    np.testing.assert_array_equal(xq1, xq2)
+    np.testing.assert_array_equal(d1, d2)
