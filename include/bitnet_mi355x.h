@@ -151,9 +151,9 @@ bitnet_status bitnet_ternary_linear_multi(const bitnet_matrix *mats, int count,
  *            bitnet_quantize_acts(x) writes (so further layers that share this
  *            input can call bitnet_ternary_linear on them).
  *   other arguments as bitnet_ternary_linear.
- * For M <= 4 with M*K <= 64 KiB (and K % 64 == 0) each workgroup of the decode
- * kernel quantises the activations itself; otherwise this is bitnet_quantize_acts
- * followed by bitnet_ternary_linear on the same stream.
+ * For M <= 4 with M*(K+16) <= 46 KiB (and K % 64 == 0) each workgroup of the
+ * decode kernel quantises the activations itself; otherwise this is
+ * bitnet_quantize_acts followed by bitnet_ternary_linear on the same stream.
  */
 bitnet_status bitnet_quant_linear(const uint8_t *w_packed, const float *w_scale,
                                   const void *x, int x_dtype, int64_t M, int64_t N, int64_t K,
@@ -163,11 +163,56 @@ bitnet_status bitnet_quant_linear(const uint8_t *w_packed, const float *w_scale,
 /*
  * bitnet_quant_linear for several matrices sharing the input x: quantises x once
  * (into x_q / x_scale) and applies every matrix, fused into one launch for up to
- * 4 matrices when M <= 4 and M*K <= 64 KiB.
+ * 4 matrices when M <= 4 and M*(K+16) <= 46 KiB.
  */
 bitnet_status bitnet_quant_linear_multi(const bitnet_matrix *mats, int count, const void *x,
                                         int x_dtype, int64_t M, int64_t K, int8_t *x_q,
                                         float *x_scale, int y_dtype, hipStream_t stream);
+
+/*
+ * Input prologue of a layer: its neighbours on the path, applied before the
+ * int8 quantisation (communeify.com, section on BitNet b1.58 2B4T, architecture
+ * item: squared-ReLU activation, subln normalisation, no bias terms).
+ *   up           NULL, or the up projection [M][K] (same dtype and alignment as
+ *                x): x is then the gate projection and the layer input is
+ *                v = RN32(RN32(max(x, 0)^2) * up), elementwise.
+ *   norm_weight  NULL, or the RMS norm weight w [K] fp32 (device, 4-byte
+ *                aligned): the layer input v is normalised, which the layer
+ *                computes by quantising RN32(v * w) per token and multiplying
+ *                the token scale by r = RN32(1 / sqrt(RN32(RN32(mean v^2) + eps)))
+ *                (square root and division in float64; absmax quantisation is
+ *                invariant under the positive per-token factor r).  mean v^2 is
+ *                accumulated in float64 (exact products): it may differ from the
+ *                exactly rounded mean by one fp32 ulp, so x_scale (and y) match
+ *                the exact reading to within a few ulp; x_q is unaffected.
+ *                Needs K >= 1.
+ *   norm_eps     eps >= 0, finite.
+ */
+typedef struct bitnet_act_prologue {
+  const void *up;
+  const float *norm_weight;
+  float norm_eps;
+} bitnet_act_prologue;
+
+/*
+ * bitnet_quantize_acts with the input prologue `pro` (NULL: none).  With
+ * norm_weight, x_scale[m] includes the factor r.
+ */
+bitnet_status bitnet_quantize_acts_ex(const void *x, int x_dtype, const bitnet_act_prologue *pro,
+                                      int64_t M, int64_t K, int8_t *x_q, float *x_scale,
+                                      hipStream_t stream);
+
+/*
+ * bitnet_quant_linear_multi with the input prologue `pro` (NULL: none): the
+ * layers see the gated and / or normalised input, quantised as
+ * bitnet_quantize_acts_ex writes it (also into x_q / x_scale).  Fused into the
+ * decode kernel under the same conditions as bitnet_quant_linear_multi when x,
+ * up and norm_weight are 16-byte aligned.
+ */
+bitnet_status bitnet_quant_linear_ex(const bitnet_matrix *mats, int count, const void *x,
+                                     int x_dtype, const bitnet_act_prologue *pro, int64_t M,
+                                     int64_t K, int8_t *x_q, float *x_scale, int y_dtype,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

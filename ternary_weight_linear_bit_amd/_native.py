@@ -44,6 +44,19 @@ SIGNATURES["bitnet_ternary_linear_multi"] = (_I, [ctypes.POINTER(BitnetMatrix), 
 SIGNATURES["bitnet_quant_linear_multi"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _P, _I, _I64,
                                                 _I64, _P, _P, _I, _P])
 
+
+class BitnetActPrologue(ctypes.Structure):
+    """struct bitnet_act_prologue of the public header."""
+    _fields_ = [("up", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
+
+
+SIGNATURES["bitnet_quantize_acts_ex"] = (_I, [_P, _I, ctypes.POINTER(BitnetActPrologue), _I64,
+                                              _I64, _P, _P, _P])
+SIGNATURES["bitnet_quant_linear_ex"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _P, _I,
+                                             ctypes.POINTER(BitnetActPrologue), _I64, _I64, _P,
+                                             _P, _I, _P])
+
 _lib = None
 
 
@@ -123,8 +136,23 @@ def bitnet_quantize_weights(w, packed=None, scale=None, workspace=None, stream=N
     return packed, scale
 
 
-def bitnet_quantize_acts(x, x_q=None, x_scale=None, stream=None):
-    """x: [M, K] fp32/bf16 -> (x_q int8 [M, K], d fp32 [M])."""
+def _prologue(x, up, norm_weight, eps):
+    """struct bitnet_act_prologue for (up, norm_weight, eps), or None for none."""
+    if up is None and norm_weight is None:
+        return None
+    _need_cuda(up, norm_weight)
+    if up is not None and (up.shape != x.shape or up.dtype != x.dtype):
+        raise ValueError("up must match x in shape and dtype")
+    return ctypes.byref(BitnetActPrologue(0 if up is None else up.data_ptr(),
+                                          0 if norm_weight is None else norm_weight.data_ptr(),
+                                          float(eps)))
+
+
+def bitnet_quantize_acts(x, x_q=None, x_scale=None, stream=None, up=None, norm_weight=None,
+                         eps=1e-5):
+    """x: [M, K] fp32/bf16 -> (x_q int8 [M, K], d fp32 [M]).  With ``up`` x is the
+    gate projection (squared-ReLU gating); with ``norm_weight`` the input is
+    RMS-normalised (bitnet_quantize_acts_ex)."""
     import torch
     _need_cuda(x)
     m, k = x.shape
@@ -133,8 +161,14 @@ def bitnet_quantize_acts(x, x_q=None, x_scale=None, stream=None):
     if x_scale is None:
         x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
     _need_cuda(x_q, x_scale)
-    _check("bitnet_quantize_acts", lib().bitnet_quantize_acts(
-        _ptr(x), _dtype_code(x.dtype), m, k, _ptr(x_q), _ptr(x_scale), _stream(stream)))
+    pro = _prologue(x, up, norm_weight, eps)
+    if pro is None:
+        _check("bitnet_quantize_acts", lib().bitnet_quantize_acts(
+            _ptr(x), _dtype_code(x.dtype), m, k, _ptr(x_q), _ptr(x_scale), _stream(stream)))
+    else:
+        _check("bitnet_quantize_acts_ex", lib().bitnet_quantize_acts_ex(
+            _ptr(x), _dtype_code(x.dtype), pro, m, k, _ptr(x_q), _ptr(x_scale),
+            _stream(stream)))
     return x_q, x_scale
 
 
@@ -207,8 +241,10 @@ def bitnet_ternary_linear_multi(mats, x_q, x_scale, y_dtype=None, stream=None):
     return ys
 
 
-def bitnet_quant_linear_multi(mats, x, x_q=None, x_scale=None, y_dtype=None, stream=None):
-    """Quantise x once and apply several matrices: returns (list of y, x_q, x_scale)."""
+def bitnet_quant_linear_multi(mats, x, x_q=None, x_scale=None, y_dtype=None, stream=None,
+                              up=None, norm_weight=None, eps=1e-5):
+    """Quantise x once and apply several matrices: returns (list of y, x_q, x_scale).
+    ``up`` / ``norm_weight`` / ``eps``: the input prologue (bitnet_quant_linear_ex)."""
     import torch
     _need_cuda(x)
     m, k = x.shape
@@ -219,7 +255,13 @@ def bitnet_quant_linear_multi(mats, x, x_q=None, x_scale=None, y_dtype=None, str
     _need_cuda(x_q, x_scale)
     arr, ys = _matrices(mats, m, y_dtype or torch.float32, x.device)
     dt = _dtype_code(ys[0].dtype)
-    _check("bitnet_quant_linear_multi", lib().bitnet_quant_linear_multi(
-        arr, len(mats), _ptr(x), _dtype_code(x.dtype), m, k, _ptr(x_q), _ptr(x_scale), dt,
-        _stream(stream)))
+    pro = _prologue(x, up, norm_weight, eps)
+    if pro is None:
+        _check("bitnet_quant_linear_multi", lib().bitnet_quant_linear_multi(
+            arr, len(mats), _ptr(x), _dtype_code(x.dtype), m, k, _ptr(x_q), _ptr(x_scale), dt,
+            _stream(stream)))
+    else:
+        _check("bitnet_quant_linear_ex", lib().bitnet_quant_linear_ex(
+            arr, len(mats), _ptr(x), _dtype_code(x.dtype), pro, m, k, _ptr(x_q), _ptr(x_scale),
+            dt, _stream(stream)))
     return ys, x_q, x_scale

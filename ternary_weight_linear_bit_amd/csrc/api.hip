@@ -103,22 +103,48 @@ bitnet_status run_linear(const bitnet_matrix* mats, int count, const int8_t* x_q
   return BITNET_OK;
 }
 
+bitnet::ActPrologue act_prologue(const bitnet_act_prologue* pro) {
+  bitnet::ActPrologue p{nullptr, nullptr, 0.0f};
+  if (pro) {
+    p.up = pro->up;
+    p.w = pro->norm_weight;
+    p.eps = pro->norm_eps;
+  }
+  return p;
+}
+
+// The prologue's own operands (x, M, K already checked).
+bitnet_status check_prologue(const bitnet_act_prologue* pro, int x_dtype, int64_t M, int64_t K) {
+  if (!pro || M == 0) return BITNET_OK;
+  if (pro->norm_weight) {
+    if (K < 1) return BITNET_ERR_SHAPE;
+    if (!aligned(pro->norm_weight, 4)) return BITNET_ERR_ALIGN;
+    if (!(pro->norm_eps >= 0.0f) || pro->norm_eps > 3.4e38f) return BITNET_ERR_SHAPE;
+  }
+  if (pro->up && !aligned(pro->up, esize(x_dtype))) return BITNET_ERR_ALIGN;
+  return BITNET_OK;
+}
+
 bitnet_status quant_linear(const bitnet_matrix* mats, int count, const void* x, int x_dtype,
-                           int64_t M, int64_t K, int8_t* x_q, float* x_scale, int y_dtype,
-                           hipStream_t stream) {
+                           const bitnet::ActPrologue& pro, int64_t M, int64_t K, int8_t* x_q,
+                           float* x_scale, int y_dtype, hipStream_t stream) {
   if (M == 0) return BITNET_OK;
-  if (all_fast(mats, count, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K)) {
+  if (all_fast(mats, count, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K) &&
+      (!pro.up || aligned(pro.up, 16)) && (!pro.w || aligned(pro.w, 16))) {
     const int c = count < bitnet::kMaxGroup ? count : bitnet::kMaxGroup;
     bitnet::GemvArgs a = gemv_args(mats, c, M, K, y_dtype);
     a.xf = x;
     a.xq = x_q;
     a.xq_out = x_q;
     a.xs_out = x_scale;
+    a.xup = pro.up;
+    a.gnorm = pro.w;
+    a.eps = pro.eps;
     if (bitnet::launch_gemv(a, x_dtype, stream) != hipSuccess) return BITNET_ERR_HIP;
     if (count == c) return BITNET_OK;
     return run_linear(mats + c, count - c, x_q, x_scale, M, K, y_dtype, stream);
   }
-  if (bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, stream) != hipSuccess)
+  if (bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, pro, stream) != hipSuccess)
     return BITNET_ERR_HIP;
   return run_linear(mats, count, x_q, x_scale, M, K, y_dtype, stream);
 }
@@ -164,14 +190,23 @@ bitnet_status bitnet_quantize_weights(const void* w, int w_dtype, int64_t N, int
                                     stream));
 }
 
-bitnet_status bitnet_quantize_acts(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* x_q,
-                                   float* x_scale, hipStream_t stream) {
+bitnet_status bitnet_quantize_acts_ex(const void* x, int x_dtype, const bitnet_act_prologue* pro,
+                                      int64_t M, int64_t K, int8_t* x_q, float* x_scale,
+                                      hipStream_t stream) {
   if (!valid_dtype(x_dtype)) return BITNET_ERR_DTYPE;
   if (M < 0 || K < 0 || M > kInt32Max) return BITNET_ERR_SHAPE;
   if (M == 0) return BITNET_OK;
   if (!x_scale || (K > 0 && (!x || !x_q))) return BITNET_ERR_NULL;
   if (!aligned(x, esize(x_dtype)) || !aligned(x_scale, 4)) return BITNET_ERR_ALIGN;
-  return from_hip(bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, stream));
+  const bitnet_status st = check_prologue(pro, x_dtype, M, K);
+  if (st != BITNET_OK) return st;
+  return from_hip(bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale,
+                                    act_prologue(pro), stream));
+}
+
+bitnet_status bitnet_quantize_acts(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* x_q,
+                                   float* x_scale, hipStream_t stream) {
+  return bitnet_quantize_acts_ex(x, x_dtype, nullptr, M, K, x_q, x_scale, stream);
 }
 
 bitnet_status bitnet_ternary_linear_multi(const bitnet_matrix* mats, int count,
@@ -192,15 +227,26 @@ bitnet_status bitnet_ternary_linear(const uint8_t* w_packed, const float* w_scal
   return bitnet_ternary_linear_multi(&m, 1, x_q, x_scale, M, K, y_dtype, stream);
 }
 
+bitnet_status bitnet_quant_linear_ex(const bitnet_matrix* mats, int count, const void* x,
+                                     int x_dtype, const bitnet_act_prologue* pro, int64_t M,
+                                     int64_t K, int8_t* x_q, float* x_scale, int y_dtype,
+                                     hipStream_t stream) {
+  if (M > 0 && (!x_scale || (K > 0 && (!x || !x_q)))) return BITNET_ERR_NULL;
+  if (!valid_dtype(x_dtype)) return BITNET_ERR_DTYPE;
+  bitnet_status st = check_group(mats, count, M, K, y_dtype);
+  if (st != BITNET_OK) return st;
+  if (!aligned(x, esize(x_dtype)) || (x_scale && !aligned(x_scale, 4))) return BITNET_ERR_ALIGN;
+  st = check_prologue(pro, x_dtype, M, K);
+  if (st != BITNET_OK) return st;
+  return quant_linear(mats, count, x, x_dtype, act_prologue(pro), M, K, x_q, x_scale, y_dtype,
+                      stream);
+}
+
 bitnet_status bitnet_quant_linear_multi(const bitnet_matrix* mats, int count, const void* x,
                                         int x_dtype, int64_t M, int64_t K, int8_t* x_q,
                                         float* x_scale, int y_dtype, hipStream_t stream) {
-  if (M > 0 && (!x_scale || (K > 0 && (!x || !x_q)))) return BITNET_ERR_NULL;
-  if (!valid_dtype(x_dtype)) return BITNET_ERR_DTYPE;
-  const bitnet_status st = check_group(mats, count, M, K, y_dtype);
-  if (st != BITNET_OK) return st;
-  if (!aligned(x, esize(x_dtype)) || (x_scale && !aligned(x_scale, 4))) return BITNET_ERR_ALIGN;
-  return quant_linear(mats, count, x, x_dtype, M, K, x_q, x_scale, y_dtype, stream);
+  return bitnet_quant_linear_ex(mats, count, x, x_dtype, nullptr, M, K, x_q, x_scale, y_dtype,
+                                stream);
 }
 
 bitnet_status bitnet_quant_linear(const uint8_t* w_packed, const float* w_scale, const void* x,

@@ -1,14 +1,21 @@
-// Per-token absmax int8 activation quantisation.
+// Per-token absmax int8 activation quantisation, with the layer's optional input
+// prologue (squared-ReLU gating, RMS norm).
 //
 // Method: communeify.com, "微軟 BitNet b1.58 震撼登場", section on BitNet b1.58
 // 2B4T, quantisation details: activations are 8-bit integers (W1.58A8).  The pages
 // give no scheme; the reading here is per token (row) absmax to the symmetric
 // range [-127, 127]:  a* = max(max|x|, RN32(1e-5)), s = RN32(127/a*),
 // xq = clip(rne(RN32(x*s)), -128, 127), d = RN32(a*/127).
+// Prologue (same page, architecture item: ReLU^2 activation, subln norm, no
+// biases): with gating the input is v = RN32(RN32(relu(x)^2) * up); with a norm
+// weight w the row is quantised as RN32(v * w) and the token scale becomes
+// RN32(d * r), r = RN32(1/sqrt(RN32(RN32(mean v^2) + eps))) -- absmax
+// quantisation is invariant under the positive per-token factor r.
 //
-// One workgroup per token row.  Pass 1 reduces max|x| (exact in any order) with
-// wave butterflies and a cross-wave step in LDS; pass 2 re-reads the row (now in
-// L1/L2) and writes 16 int8 per 16-byte store.
+// One workgroup per token row.  Pass 1 reduces max|v*w| (exact in any order) and
+// sum v^2 (float64; the products are exact) with wave butterflies and a
+// cross-wave step in LDS; pass 2 re-reads the row (now in L1/L2) and writes 16
+// int8 per 16-byte store.
 #include "bitnet_internal.h"
 
 namespace bitnet {
@@ -22,38 +29,99 @@ __device__ __forceinline__ float load_act(const void* x, int64_t i) {
   return reinterpret_cast<const float*>(x)[i];
 }
 
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// 16 consecutive prologue values (the quantised ones, q) of group c; adds v^2
+// to ss when the norm is on.
+template <bool BF16>
+__device__ __forceinline__ void prologue16(const void* row, const void* urow, const float* w,
+                                           int64_t c, float q[16], double& ss) {
+  load16_act<BF16>(row, c, q);
+  if (urow) {
+    float u[16];
+    load16_act<BF16>(urow, c, u);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[j] = glu_value(q[j], u[j]);
+  }
+  if (w) {
+    const float4* wp = reinterpret_cast<const float4*>(w) + 4 * c;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float4 g = wp[h];
+      const float gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = q[4 * h + j];
+        ss += (double)v * (double)v;
+        q[4 * h + j] = __fmul_rn(v, gv[j]);
+      }
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float prologue1(const void* row, const void* urow, const float* w,
+                                           int64_t i, double& ss) {
+  float v = load_act<BF16>(row, i);
+  if (urow) v = glu_value(v, load_act<BF16>(urow, i));
+  if (w) {
+    ss += (double)v * (double)v;
+    v = __fmul_rn(v, w[i]);
+  }
+  return v;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kAqThreads) void aq_kernel(const void* __restrict__ x, int64_t K,
                                                        bool vec, int8_t* __restrict__ xq,
-                                                       float* __restrict__ xs) {
+                                                       float* __restrict__ xs,
+                                                       const ActPrologue pro) {
   __shared__ float wmax[kAqThreads / 64];
+  __shared__ double wss[kAqThreads / 64];
   const int64_t m = blockIdx.x;
-  const void* row = BF16 ? (const void*)(reinterpret_cast<const uint16_t*>(x) + m * K)
-                         : (const void*)(reinterpret_cast<const float*>(x) + m * K);
+  const size_t esz = BF16 ? 2 : 4;
+  const void* row = reinterpret_cast<const uint8_t*>(x) + (size_t)m * K * esz;
+  const void* urow = pro.up ? reinterpret_cast<const uint8_t*>(pro.up) + (size_t)m * K * esz
+                            : nullptr;
   int8_t* qrow = xq + m * K;
   const int tid = threadIdx.x;
   const int64_t n16 = vec ? K / 16 : 0;
 
   float a = 0.0f;
+  double ss = 0.0;
   for (int64_t c = tid; c < n16; c += kAqThreads) {
     float v[16];
-    load16_act<BF16>(row, c, v);
+    prologue16<BF16>(row, urow, pro.w, c, v, ss);
 #pragma unroll
     for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
   }
-  for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads) a = fmaxf(a, fabsf(load_act<BF16>(row, i)));
+  for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads)
+    a = fmaxf(a, fabsf(prologue1<BF16>(row, urow, pro.w, i, ss)));
   a = wave_max(a);
-  if ((tid & 63) == 0) wmax[tid >> 6] = a;
+  ss = wave_sum_f64(ss);
+  if ((tid & 63) == 0) {
+    wmax[tid >> 6] = a;
+    wss[tid >> 6] = ss;
+  }
   __syncthreads();
   a = wmax[0];
+  ss = wss[0];
 #pragma unroll
-  for (int w = 1; w < kAqThreads / 64; ++w) a = fmaxf(a, wmax[w]);
+  for (int w = 1; w < kAqThreads / 64; ++w) {
+    a = fmaxf(a, wmax[w]);
+    ss += wss[w];
+  }
 
   const float astar = fmaxf(a, kEps);
   const float s = kQb / astar;   // correctly rounded fp32 division
   for (int64_t c = tid; c < n16; c += kAqThreads) {
     float v[16];
-    load16_act<BF16>(row, c, v);
+    double unused = 0.0;
+    prologue16<BF16>(row, urow, pro.w, c, v, unused);
     uint4 o;
     o.x = quant4(v, s);
     o.y = quant4(v + 4, s);
@@ -62,26 +130,33 @@ __global__ __launch_bounds__(kAqThreads) void aq_kernel(const void* __restrict__
     reinterpret_cast<uint4*>(qrow)[c] = o;
   }
   for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads) {
-    float q = rintf(load_act<BF16>(row, i) * s);
+    double unused = 0.0;
+    float q = rintf(prologue1<BF16>(row, urow, pro.w, i, unused) * s);
     qrow[i] = (int8_t)(int32_t)fminf(fmaxf(q, -128.0f), 127.0f);
   }
-  if (tid == 0) xs[m] = astar / kQb;
+  if (tid == 0) {
+    float d = astar / kQb;
+    if (pro.w) d = __fmul_rn(d, rms_factor(ss, K, pro.eps));
+    xs[m] = d;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_aq(const void* x, bool x_bf16, int64_t M, int64_t K, int8_t* x_q,
-                     float* x_scale, hipStream_t s) {
-  // 16-element vectors need 16-byte aligned rows in both the input and the output.
+                     float* x_scale, const ActPrologue& pro, hipStream_t s) {
+  // 16-element vectors need 16-byte aligned rows in the input, the output and
+  // the prologue operands.
   const size_t esz = x_bf16 ? 2 : 4;
-  const bool vec = (K % 16 == 0) && (((uintptr_t)x & 15u) == 0) && (((uintptr_t)x_q & 15u) == 0) &&
+  const auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
+  const bool vec = (K % 16 == 0) && a16(x) && a16(x_q) && a16(pro.up) && a16(pro.w) &&
                    ((K * esz) % 16 == 0);
   if (x_bf16)
     hipLaunchKernelGGL(aq_kernel<true>, dim3((unsigned)M), dim3(kAqThreads), 0, s, x, K, vec, x_q,
-                       x_scale);
+                       x_scale, pro);
   else
     hipLaunchKernelGGL(aq_kernel<false>, dim3((unsigned)M), dim3(kAqThreads), 0, s, x, K, vec, x_q,
-                       x_scale);
+                       x_scale, pro);
   return hipGetLastError();
 }
 

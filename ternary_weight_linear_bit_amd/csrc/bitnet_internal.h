@@ -143,8 +143,31 @@ __device__ __forceinline__ void lds_barrier() {
 // hipGetLastError() after its launches.
 hipError_t launch_wq(const void* w, bool w_bf16, int64_t n_weights, uint8_t* w_packed,
                      float* w_scale, void* workspace, hipStream_t s);
+// Input prologue of a layer (squared-ReLU gating and RMS norm), already validated.
+struct ActPrologue {
+  const void* up;       // gating: up projection, same dtype and shape as x; else nullptr
+  const float* w;       // RMS norm weight [K]; else nullptr
+  float eps;
+};
+
+// Elementwise part of the prologue for one activation: the gated value
+// v = RN32(RN32(a * a) * up) with a = max(x, 0) (or v = x), and the value that is
+// quantised, RN32(v * w) (or v).  Two separate roundings; no fused multiply-add.
+__device__ __forceinline__ float glu_value(float x, float up) {
+  const float a = fmaxf(x, 0.0f);
+  return __fmul_rn(__fmul_rn(a, a), up);
+}
+
+// RMS norm factor of a row from its float64 sum of squares ss over K values:
+// r = RN32(1 / sqrt(RN32(RN32(ss / K) + eps))), square root and division in float64.
+__device__ __forceinline__ float rms_factor(double ss, int64_t K, float eps) {
+  const float ms = (float)(ss / (double)K);
+  const float t = __fadd_rn(ms, eps);
+  return (float)(1.0 / sqrt((double)t));
+}
+
 hipError_t launch_aq(const void* x, bool x_bf16, int64_t M, int64_t K, int8_t* x_q,
-                     float* x_scale, hipStream_t s);
+                     float* x_scale, const ActPrologue& pro, hipStream_t s);
 // Decode kernel arguments: up to kMaxGroup weight matrices sharing K and the
 // activations, passed by value.
 constexpr int kMaxGroup = 4;
@@ -165,6 +188,9 @@ struct GemvArgs {
   int y_bf16, tiles_per_wg;  // row tiles per workgroup (set by launch_gemv)
   int kx, phases;            // K range staged per phase and phase count (launch_gemv)
   int mdiv, unused1;         // ceil(65536 / M) (launch_gemv)
+  const void* xup;           // fused prologue: up projection (gating) or nullptr
+  const float* gnorm;        // fused prologue: RMS norm weight or nullptr
+  float eps, unused2;
 };
 
 // Decode kernel: M <= 16, K % 64 == 0; the fused variant (a.xf != nullptr) also

@@ -32,11 +32,17 @@
 //    atomics (exact in any order); after one barrier the workgroup applies
 //    y = RN32(float(acc) * RN32(gamma * d[m])).
 //
-// XMODE 1/2 fuse the per-token absmax activation quantisation (fp32 / bf16 input,
+// XMODE 1-8 fuse the per-token absmax activation quantisation (fp32 / bf16 input,
 // M <= kMaxFusedM, one phase): the workgroup quantises the activations with the
 // same arithmetic as the standalone kernel while staging them (one read of the
 // input; the first kHold groups of each thread stay in registers between the
 // absmax and the quantise pass), and workgroup 0 also writes x_q and x_scale.
+// XMODE 3-8 add the layer's input prologue (communeify.com page on BitNet b1.58
+// 2B4T, architecture item: squared-ReLU activation, subln norm, no biases): the
+// input may be the gate projection, gated as RN32(RN32(relu(x)^2) * up), and / or
+// RMS-normalised, quantised as RN32(v * w) with the factor
+// r = RN32(1/sqrt(RN32(RN32(mean v^2) + eps))) folded into the token scale (the
+// sum of squares in float64 over the token's threads).
 #include "bitnet_internal.h"
 
 namespace bitnet {
@@ -63,9 +69,9 @@ int phase_k(int M, int K) {
   return kx >= K ? K : kx;
 }
 
-// LDS: X [M][kx + 16] | zero[64] | part[T][16][16] int | dsc[16] | wred[16]
+// LDS: X [M][kx + 16] | zero[64] | part[T][16][16] int | dsc[16] | wred[16] | wss[4] double
 int lds_bytes(int tiles, int M, int K) {
-  return M * (phase_k(M, K) + 16) + 64 + tiles * 1024 + 64 + 64;
+  return M * (phase_k(M, K) + 16) + 64 + tiles * 1024 + 64 + 64 + 32;
 }
 
 // This workgroup's matrix and the launch's scalars.  Everything the kernel needs
@@ -170,10 +176,17 @@ __device__ __forceinline__ void raw_to_f32(const uint4* w, float v[16]) {
   }
 }
 
-template <int XMODE, int R>  // XMODE 0: int8 x_q; 1: fp32 input; 2: bf16 input
+// XMODE 0: int8 x_q.  XMODE 1 + f, f = bf16 (1) | gated by a.xup (2) | RMS norm
+// with a.gnorm (4): fp32 / bf16 input quantised in the kernel.  The prologue
+// options are compile-time so that no load sits behind a runtime branch.
+template <int XMODE, int R>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr bool BF = XMODE == 2;
+  constexpr int F = XMODE > 0 ? XMODE - 1 : 0;
+  constexpr bool BF = (F & 1) != 0;
+  constexpr bool GLU = XMODE > 0 && (F & 2) != 0;
+  constexpr bool NRM = XMODE > 0 && (F & 4) != 0;
+  constexpr bool PRO = GLU || NRM;
   constexpr int NV = BF ? 2 : 4;             // fused: 16-byte words per 16-element group
   constexpr uint32_t ES = BF ? 2u : 4u;      // fused: input element size
   const int tid = threadIdx.x;
@@ -197,6 +210,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   int* part = reinterpret_cast<int*>(zero + 64);         // [T][16 rows][16 tokens]
   float* dsc = reinterpret_cast<float*>(part + T * 256);  // [16]
   float* wred = dsc + 16;                                // [16]
+  double* wss = reinterpret_cast<double*>(wred + 16);    // [4]
 
   // Buffer descriptor of local tile tl (wave-uniform; readfirstlane keeps it in
   // scalar registers so the loads need no per-lane legalisation loop).
@@ -263,15 +277,30 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
       return (tk < M && c < K16) ? ((uint32_t)tk * (uint32_t)K + 16u * (uint32_t)c) * ES + 16u * h
                                  : kOob;
     };
-    uint4 hold[kHold][NV];
+    // prologue operands: the up projection (same layout as the input) and the
+    // norm weight (fp32 [K], 64 bytes per group)
+    constexpr bool glu = GLU, nrm = NRM;
+    const auto ur = make_rsrc(glu ? a.xup : pro.xf, (uint32_t)M * (uint32_t)K * ES);
+    const auto gr = make_rsrc(nrm ? (const void*)a.gnorm : pro.xf, nrm ? 4u * (uint32_t)K : 0u);
+    auto goff = [&](int c, int h) -> uint32_t {
+      return (tk < M && c < K16) ? 64u * (uint32_t)c + 16u * (uint32_t)h : kOob;
+    };
+    uint4 hold[kHold][NV], holdu[kHold][NV], holdg[kHold][4];
     if constexpr (XMODE == 0) {
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) xv[b] = xload();
     } else {
 #pragma unroll
-      for (int b = 0; b < kHold; ++b)
+      for (int b = 0; b < kHold; ++b) {
 #pragma unroll
         for (int h = 0; h < NV; ++h) hold[b][h] = bload16(fr, foff(jg + G * b, h));
+        if (PRO) {
+#pragma unroll
+          for (int h = 0; h < NV; ++h) holdu[b][h] = glu ? bload16(ur, foff(jg + G * b, h)) : hold[b][h];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) holdg[b][h] = nrm ? bload16(gr, goff(jg + G * b, h)) : make_uint4(0, 0, 0, 0);
+        }
+      }
     }
     // producer position of the ring: tile tp, step jp of this wave's super-chunks
     // (past the last tile or chunk the offset is out of range and the load reads
@@ -325,35 +354,79 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         store_batch();
       }
     } else {
-      // absmax of the token over its G threads (G >= 64: one token per wave)
+      // the values that are quantised, from the raw input (and up projection and
+      // norm weight) of one group; adds the squares of the gated values to ss
+      auto values = [&](const uint4* xw, const uint4* uw, const uint4* gw, float q[16],
+                        double& ss) {
+        raw_to_f32<BF>(xw, q);
+        if (PRO) {
+          if (glu) {
+            float u[16];
+            raw_to_f32<BF>(uw, u);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) q[j] = glu_value(q[j], u[j]);
+          }
+          if (nrm) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const uint4 g4 = gw[j >> 2];
+              const uint32_t gb = (j & 3) == 0 ? g4.x : (j & 3) == 1 ? g4.y : (j & 3) == 2 ? g4.z : g4.w;
+              ss += (double)q[j] * (double)q[j];
+              q[j] = __fmul_rn(q[j], __uint_as_float(gb));
+            }
+          }
+        }
+      };
+      auto reload = [&](int c, float q[16], double& ss) {
+        uint4 xw[NV], uw[NV], gw[4];
+#pragma unroll
+        for (int h = 0; h < NV; ++h) xw[h] = bload16(fr, foff(c, h));
+        if (PRO) {
+#pragma unroll
+          for (int h = 0; h < NV; ++h) uw[h] = glu ? bload16(ur, foff(c, h)) : xw[h];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) gw[h] = nrm ? bload16(gr, goff(c, h)) : make_uint4(0, 0, 0, 0);
+        }
+        values(xw, uw, gw, q, ss);
+      };
+      // absmax of the token over its G threads (G >= 64: one token per wave); the
+      // held groups keep their values for the quantise pass
       const int nb = (K16 + G - 1) >> lgG;       // groups per thread, uniform
       float amax = 0.0f;
+      double ss = 0.0;
+      float qh[kHold][16];
 #pragma unroll
       for (int b = 0; b < kHold; ++b) {
-        float v[16];
-        raw_to_f32<BF>(hold[b], v);
+        values(hold[b], holdu[b], holdg[b], qh[b], ss);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(qh[b][j]));
       }
       for (int b = kHold; b < nb; ++b) {
-        uint4 w[NV];
-#pragma unroll
-        for (int h = 0; h < NV; ++h) w[h] = bload16(fr, foff(jg + G * b, h));
         float v[16];
-        raw_to_f32<BF>(w, v);
+        reload(jg + G * b, v, ss);
 #pragma unroll
         for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
       }
       amax = wave_max(amax);
       if (lane == 0) wred[wave] = amax;
+      if (PRO) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        if (lane == 0) wss[wave] = ss;
+      }
       lds_barrier();
       const int nw = G >> 6;                     // waves per token
       float tmax = 0.0f;
-      for (int i = 0; i < nw; ++i) tmax = fmaxf(tmax, wred[(tk * nw + i) & 3]);
+      double tss = 0.0;
+      for (int i = 0; i < nw; ++i) {
+        tmax = fmaxf(tmax, wred[(tk * nw + i) & 3]);
+        if (PRO) tss += wss[(tk * nw + i) & 3];
+      }
       const float astar = fmaxf(tmax, kEps);
       const float s_t = kQb / astar;
       if (jg == 0 && tk < M) {
-        const float d = astar / kQb;
+        float d = astar / kQb;
+        if (nrm) d = __fmul_rn(d, rms_factor(tss, K, a.eps));
         dsc[tk] = d;
         if (blockIdx.x == 0) a.xs_out[tk] = d;
       }
@@ -367,17 +440,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         store_transposed(in ? xs + tk * stride + 16 * c : zero, q);
       };
 #pragma unroll
-      for (int b = 0; b < kHold; ++b) {
-        float v[16];
-        raw_to_f32<BF>(hold[b], v);
-        put(jg + G * b, v);
-      }
+      for (int b = 0; b < kHold; ++b) put(jg + G * b, qh[b]);
       for (int b = kHold; b < nb; ++b) {
-        uint4 w[NV];
-#pragma unroll
-        for (int h = 0; h < NV; ++h) w[h] = bload16(fr, foff(jg + G * b, h));
         float v[16];
-        raw_to_f32<BF>(w, v);
+        double unused = 0.0;
+        reload(jg + G * b, v, unused);
         put(jg + G * b, v);
       }
     }
@@ -456,7 +523,17 @@ const void* ring_kernel(int R) {
 }
 
 const void* select_kernel(int xmode, int R) {
-  return xmode == 0 ? ring_kernel<0>(R) : xmode == 1 ? ring_kernel<1>(R) : ring_kernel<2>(R);
+  switch (xmode) {
+    case 0: return ring_kernel<0>(R);
+    case 1: return ring_kernel<1>(R);
+    case 2: return ring_kernel<2>(R);
+    case 3: return ring_kernel<3>(R);
+    case 4: return ring_kernel<4>(R);
+    case 5: return ring_kernel<5>(R);
+    case 6: return ring_kernel<6>(R);
+    case 7: return ring_kernel<7>(R);
+    default: return ring_kernel<8>(R);
+  }
 }
 
 // Compute units of the current device (1 if the runtime cannot say).
@@ -486,7 +563,9 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s) {
   if (a.count < 1 || a.count > kMaxGroup || !gemv_fits(a.M, a.K) ||
       (fused && !gemv_fused_fits(a.M, a.K)))
     return hipErrorInvalidValue;
-  const int xmode = !fused ? 0 : xf_dtype == 1 ? 2 : 1;
+  if ((a.xup != nullptr || a.gnorm != nullptr) && !fused) return hipErrorInvalidValue;
+  const int xmode = !fused ? 0
+                           : 1 + (xf_dtype == 1 ? 1 : 0) + (a.xup ? 2 : 0) + (a.gnorm ? 4 : 0);
   int tiles[kMaxGroup] = {0, 0, 0, 0};
   int total_tiles = 0;
   for (int j = 0; j < a.count; ++j) total_tiles += tiles[j] = (a.n[j] + 15) / 16;

@@ -38,6 +38,13 @@ def activations(m: int, k: int, seed: int = ACT_SEED) -> np.ndarray:
     return rng.standard_normal((m, k), dtype=np.float32)
 
 
+def norm_weight(k: int, seed: int) -> np.ndarray:
+    """Seeded RMS norm weights [K] fp32: 1 + 0.1 * N(0, 1) (synthetic stand-ins for
+    trained ones)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32)
+
+
 def to_bf16(x_f32: np.ndarray):
     """Round an fp32 array to a torch bf16 CPU tensor (torch's own conversion)."""
     import torch

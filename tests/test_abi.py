@@ -106,3 +106,21 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(N, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         N.lib()
+
+
+def test_prologue_validation(lib):
+    """The activation prologue's operands are checked before any HIP call."""
+    P = N.BitnetActPrologue
+    q = lib.bitnet_quantize_acts_ex
+    assert q(FAKE, 0, ctypes.byref(P(None, 0x10000, 1e-5)), 2, 0, FAKE, FAKE, None) == ESHAPE  # norm needs K >= 1
+    assert q(FAKE, 0, ctypes.byref(P(None, 0x10000, -1.0)), 2, 8, FAKE, FAKE, None) == ESHAPE
+    assert q(FAKE, 0, ctypes.byref(P(None, 0x10000, float("nan"))), 2, 8, FAKE, FAKE, None) == ESHAPE
+    assert q(FAKE, 0, ctypes.byref(P(None, 0x10002, 1e-5)), 2, 8, FAKE, FAKE, None) == EALIGN
+    assert q(FAKE, 0, ctypes.byref(P(0x10002, None, 1e-5)), 2, 8, FAKE, FAKE, None) == EALIGN
+    assert q(FAKE, 0, ctypes.byref(P(0x10002, None, 1e-5)), 0, 8, FAKE, FAKE, None) == OK  # M == 0
+    mats = (N.BitnetMatrix * 1)(N.BitnetMatrix(0x10000, 0x10000, 3, 0x10000, None))
+    f = lib.bitnet_quant_linear_ex
+    assert f(mats, 1, FAKE, 0, ctypes.byref(P(None, 0x10002, 1e-5)), 1, 8, FAKE, FAKE, 0, None) == EALIGN
+    assert f(mats, 1, FAKE, 0, ctypes.byref(P(None, 0x10000, float("inf"))), 1, 8, FAKE, FAKE, 0,
+             None) == ESHAPE
+    assert f(mats, 1, FAKE, 7, ctypes.byref(P(None, 0x10000, 1e-5)), 1, 8, FAKE, FAKE, 0, None) == EDTYPE
