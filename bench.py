@@ -18,9 +18,12 @@ packed bytes per launch / mean launch time, where the mean launch time is the
 graph replay time over the timed steps divided by the number of launches (so it
 includes the gap between dependent launches); traffic = HBM bytes per launch from
 the PMC summary in profiles/, when it was taken on the current kernel sources.
-Also: the 100B-class decode stack (96 layers, 23.35 GB packed, fp32 activations),
-the prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096, and the
-CPU oracle timed on a bounded sample of the same decode workload.
+Also: the same 2B chain as full layers (RMS norms and squared-ReLU gating fused
+into the launches), the 8B-shaped stack (32 layers) at M = 1 and M = 16, the
+100B-class decode stack (96 layers, 23.35 GB packed, fp32 activations), the
+prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096 and on the
+8B shapes at M = 2048, and the CPU oracle timed on a bounded sample of the same
+decode workload.
 """
 
 from __future__ import annotations
@@ -73,6 +76,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-100b", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the full-layer 2B chain and the 8B-shaped chains")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this size (PMC calibration)")
@@ -98,50 +103,76 @@ def build_stack(torch, N, I, layer_shapes, layers, replicas):
     return stack
 
 
-def chain_fn(torch, N, layers_mats, h0, bufs):
-    """Enqueue one token through every layer; returns the number of launches."""
+def chain_fn(torch, N, layers_mats, h0, bufs, norms=None, eps=1e-5):
+    """Enqueue one step (M tokens) through every layer; returns the number of
+    launches.  Plain chain: q, k, v from the layer input; o from q (attention is
+    out of scope); gate and up from o; down from up.  Full layer (``norms``): an
+    RMS norm in front of q/k/v and of gate/up, the sub-layer norm in front of o
+    and of down, and down consumes ReLU(gate)^2 * up (the layer's neighbours as
+    the BitNet b1.58 2B4T architecture names them), all fused into the launches."""
+    m = h0.shape[0]
+    per_multi = 1 if m <= 4 else 2   # fused act-quant, or act-quant + linear launches
+
     def step():
         h = h0
-        for mats in layers_mats:
+        for li, mats in enumerate(layers_mats):
+            nw = norms[li] if norms else None
+
+            def pro(key, up=None):
+                if nw is None:
+                    return {}
+                return dict(norm_weight=nw[key], eps=eps, up=up)
             N.bitnet_quant_linear_multi(
                 [(*mats["q"], bufs["q"]), (*mats["k"], bufs["k"]), (*mats["v"], bufs["v"])], h,
-                x_q=bufs["xq_h"], x_scale=bufs["xs_h"])
-            N.bitnet_quant_linear(*mats["o"], bufs["q"], x_q=bufs["xq_q"], x_scale=bufs["xs_q"],
-                                  y=bufs["o"])
+                x_q=bufs["xq_h"], x_scale=bufs["xs_h"], **pro("in"))
+            N.bitnet_quant_linear_multi([(*mats["o"], bufs["o"])], bufs["q"], x_q=bufs["xq_q"],
+                                        x_scale=bufs["xs_q"], **pro("attn_sub"))
             N.bitnet_quant_linear_multi(
                 [(*mats["gate"], bufs["gate"]), (*mats["up"], bufs["up"])], bufs["o"],
-                x_q=bufs["xq_o"], x_scale=bufs["xs_o"])
-            N.bitnet_quant_linear(*mats["down"], bufs["up"], x_q=bufs["xq_u"], x_scale=bufs["xs_u"],
-                                  y=bufs["h"])
+                x_q=bufs["xq_o"], x_scale=bufs["xs_o"], **pro("ffn_in"))
+            if nw is None:
+                N.bitnet_quant_linear_multi([(*mats["down"], bufs["h"])], bufs["up"],
+                                            x_q=bufs["xq_u"], x_scale=bufs["xs_u"])
+            else:
+                N.bitnet_quant_linear_multi([(*mats["down"], bufs["h"])], bufs["gate"],
+                                            x_q=bufs["xq_u"], x_scale=bufs["xs_u"],
+                                            **pro("ffn_sub", up=bufs["up"]))
             h = bufs["h"]
-        return 4 * len(layers_mats)
+        return 4 * per_multi * len(layers_mats)
     return step
 
 
-def decode_leg(torch, N, I, name, steps, warmup):
-    """One token at a time through a whole layer stack, replayed from HIP graphs."""
+def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycle=None):
+    """M tokens at a time through a whole layer stack, replayed from HIP graphs."""
     wl = I.WORKLOADS[name]
     shapes, layers = wl["layer"], wl["layers"]
     per_stack = I.packed_bytes(shapes) * layers
-    replicas = max(1, math.ceil(CACHE_CYCLE_BYTES / per_stack))
+    replicas = max(1, math.ceil((min_cycle or CACHE_CYCLE_BYTES) / per_stack))
     t0 = time.time()
     stack = build_stack(torch, N, I, shapes, layers, replicas)
-    log(f"{name}: {layers} layers, {per_stack / 1e6:.1f} MB packed per token, {replicas} replicas, "
+    log(f"{name}: {layers} layers, {per_stack / 1e6:.1f} MB packed per step, {replicas} replicas, "
         f"weights ternarised on the GPU in {time.time() - t0:.1f} s")
     act_dt = torch.bfloat16 if wl["act"] == "bf16" else torch.float32
     hidden = shapes[0][1]
     g = torch.Generator(device="cuda").manual_seed(I.ACT_SEED)
-    h0 = torch.randn((1, hidden), generator=g, device="cuda").to(act_dt)
+    h0 = torch.randn((m, hidden), generator=g, device="cuda").to(act_dt)
     kin = {nm: k for nm, k, _ in shapes}
-    bufs = {nm: torch.empty((1, n), dtype=act_dt, device="cuda") for nm, _, n in shapes}
-    bufs["h"] = torch.empty((1, hidden), dtype=act_dt, device="cuda")
+    bufs = {nm: torch.empty((m, n), dtype=act_dt, device="cuda") for nm, _, n in shapes}
+    bufs["h"] = torch.empty((m, hidden), dtype=act_dt, device="cuda")
     for tag, k in (("h", kin["q"]), ("q", kin["o"]), ("o", kin["gate"]), ("u", kin["down"])):
-        bufs["xq_" + tag] = torch.empty((1, k), dtype=torch.int8, device="cuda")
-        bufs["xs_" + tag] = torch.empty((1,), dtype=torch.float32, device="cuda")
+        bufs["xq_" + tag] = torch.empty((m, k), dtype=torch.int8, device="cuda")
+        bufs["xs_" + tag] = torch.empty((m,), dtype=torch.float32, device="cuda")
+    norms = None
+    if full_layer:
+        norms = []
+        for l in range(layers):
+            norms.append({key: torch.from_numpy(I.norm_weight(kin[src], 50 + 4 * l + j)).cuda()
+                          for j, (key, src) in enumerate((("in", "q"), ("attn_sub", "o"),
+                                                          ("ffn_in", "gate"), ("ffn_sub", "down")))})
     graphs = []
     launches = 0
     for r in range(replicas):
-        step = chain_fn(torch, N, stack[r], h0, bufs)
+        step = chain_fn(torch, N, stack[r], h0, bufs, norms)
         step()
         torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
@@ -162,8 +193,8 @@ def decode_leg(torch, N, I, name, steps, warmup):
     per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
     pct = {q: per[min(steps - 1, int(q / 100 * steps))] for q in (10, 50, 90)}
     gbs = per_stack / (ms * 1e-3) / 1e9
-    log(f"{name}: {ms * 1e3:.1f} us/token, {gbs:.1f} GB/s packed, "
-        f"{ms * 1e3 / launches:.2f} us per launch")
+    log(f"{name} (M={m}{', full layer' if full_layer else ''}): {ms * 1e3:.1f} us/step, "
+        f"{gbs:.1f} GB/s packed, {ms * 1e3 / launches:.2f} us per launch")
     res = dict(ms=ms, gbs=gbs, per_stack=per_stack, replicas=replicas, launches=launches,
                layers=layers, shapes=shapes, act=wl["act"],
                ms_p10=pct[10], ms_median=pct[50], ms_p90=pct[90])
@@ -171,6 +202,13 @@ def decode_leg(torch, N, I, name, steps, warmup):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def leg_summary(d, m):
+    return {"gbs": round(d["gbs"], 1), "frac_of_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(d["ms"], 4), "tokens_per_s": round(m * 1e3 / d["ms"], 1),
+            "packed_bytes_per_step": d["per_stack"], "launches_per_step": d["launches"],
+            "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 3)}
 
 
 def prefill(torch, N, I, layer_shapes, ms, steps):
@@ -303,17 +341,22 @@ def main():
                      "avg_bytes_per_launch": int(avg_bytes),
                      "launch_time": "graph replay time / launches in the timed steps"},
     }
+    if not args.no_extra:
+        df = decode_leg(torch, N, I, args.workload, args.steps, args.warmup, full_layer=True)
+        result["decode_full_layer"] = dict(
+            workload=args.workload + " with RMS norms and squared-ReLU gating fused in",
+            **leg_summary(df, 1))
+        for m in (1, 16):
+            d8 = decode_leg(torch, N, I, "llama8b-ternary", max(5, args.steps // 3), 2, m=m)
+            result[f"decode_8b_m{m}"] = dict(workload="llama8b-ternary (32 layers)",
+                                             **leg_summary(d8, m))
     if not args.no_100b:
         d5 = decode_leg(torch, N, I, "ternary100b-decode-m1-96L", max(5, args.steps // 5), 2)
-        result["decode_100b"] = {
-            "workload": "ternary100b-decode-m1-96L", "gbs": round(d5["gbs"], 1),
-            "frac_of_hbm_peak": round(d5["gbs"] / HBM_PEAK_GBS, 4),
-            "ms_per_token": round(d5["ms"], 4), "tokens_per_s": round(1e3 / d5["ms"], 1),
-            "packed_bytes_per_token": d5["per_stack"], "launches_per_token": d5["launches"],
-            "avg_launch_us": round(d5["ms"] * 1e3 / d5["launches"], 3)}
+        result["decode_100b"] = dict(workload="ternary100b-decode-m1-96L", **leg_summary(d5, 1))
     if not args.no_prefill:
         result["prefill"] = prefill(torch, N, I, wl["layer"], (512, 4096), steps=10)
-        log(f"prefill: {result['prefill']}")
+        result["prefill_8b"] = prefill(torch, N, I, I.LAYER_8B, (2048,), steps=5)
+        log(f"prefill: {result['prefill']} {result['prefill_8b']}")
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 18
         a = torch.ones(n, dtype=torch.float32, device="cuda")
