@@ -56,6 +56,17 @@ N3  normalise-then-quantise: r is a positive per-token factor and absmax
     v * w (fp32 products) with O4 and folds r into the token scale:
     xq = O4(v * w).xq, d = RN32(O4(v * w).d * r).
 
+Denser packing ([OV] introduction and section 2: a ternary weight carries
+log2(3) ~ 1.58 bits of information; [CM] comparison table: 0.4 GB of
+non-embedding memory for the 2B model, i.e. about 1.6 bits per weight):
+T1  five ternary codes per byte as base-3 digits, byte = sum_j c_j * 3**j with
+    c_j = q_j + 1 (3**5 = 243 <= 256, so 1.6 bits per weight).  A row is padded
+    with q = 0 to a multiple of 80 weights and cut into blocks of 80 weights in
+    16 bytes: byte i (0..15) of block b holds the weights k = 80*b + 16*j + i as
+    digit j (j = 0..4).  Row n occupies bytes [n*R, (n+1)*R), R = 16*ceil(K/80).
+    The pages describe no such format; this layout is ours (each digit j of a
+    block's 16 bytes covers 16 consecutive weights).
+
 bf16 inputs are upcast to fp32 exactly (bit pattern shifted left by 16) before
 any step, so every function here takes fp32 arrays.
 
@@ -380,6 +391,93 @@ def prologue_quantize_acts(x: np.ndarray, up=None, norm_weight=None, eps: float 
     w = np.asarray(norm_weight, dtype=np.float32)
     xq, d = quantize_acts((v * w[None, :]).astype(np.float32))
     return xq, (d * rms_factor(v, eps)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# T1: five ternary codes per byte (base 3)
+# ---------------------------------------------------------------------------
+
+T1_BLOCK_WEIGHTS = 80   # weights per block
+T1_BLOCK_BYTES = 16     # bytes per block
+T1_DIGITS = 5           # base-3 digits per byte
+
+
+def t1_row_bytes(k: int) -> int:
+    """Bytes of one packed row of K weights: 16 * ceil(K / 80)."""
+    return T1_BLOCK_BYTES * ((k + T1_BLOCK_WEIGHTS - 1) // T1_BLOCK_WEIGHTS)
+
+
+def pack_t1(q: np.ndarray) -> np.ndarray:
+    """Pack ternary q [N, K] into uint8 [N, 16*ceil(K/80)] per reading T1.
+
+    Byte i of block b of row n = sum_j (q[n, 80b + 16j + i] + 1) * 3**j, with
+    q = 0 for the padding weights k >= K.
+    """
+    q = np.asarray(q, dtype=np.int8)
+    n_rows, k = q.shape
+    blocks = (k + T1_BLOCK_WEIGHTS - 1) // T1_BLOCK_WEIGHTS
+    codes = np.ones((n_rows, blocks * T1_BLOCK_WEIGHTS), dtype=np.int64)  # padding: code 1
+    codes[:, :k] = q.astype(np.int64) + 1
+    codes = codes.reshape(n_rows, blocks, T1_DIGITS, T1_BLOCK_BYTES)   # [n][b][j][i]
+    value = np.zeros((n_rows, blocks, T1_BLOCK_BYTES), dtype=np.int64)
+    for j in range(T1_DIGITS):
+        value += codes[:, :, j, :] * 3 ** j
+    return value.reshape(n_rows, blocks * T1_BLOCK_BYTES).astype(np.uint8)
+
+
+def unpack_t1(packed: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of pack_t1: uint8 [N, 16*ceil(K/80)] -> int8 q [N, K].
+
+    Bytes above 242 and non-zero padding weights are invalid.
+    """
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    n_rows, row_bytes = p.shape
+    if row_bytes != t1_row_bytes(k):
+        raise ValueError("row length does not match K")
+    if np.any(p > 3 ** T1_DIGITS - 1):
+        raise ValueError("packed byte above 242")
+    blocks = row_bytes // T1_BLOCK_BYTES
+    rest = p.reshape(n_rows, blocks, T1_BLOCK_BYTES)
+    codes = np.empty((n_rows, blocks, T1_DIGITS, T1_BLOCK_BYTES), dtype=np.int64)
+    for j in range(T1_DIGITS):
+        codes[:, :, j, :] = rest % 3
+        rest = rest // 3
+    q = (codes - 1).reshape(n_rows, blocks * T1_BLOCK_WEIGHTS)
+    if np.any(q[:, k:] != 0):
+        raise ValueError("padding weights must be zero")
+    return q[:, :k].astype(np.int8)
+
+
+def quantize_weights_t1(w: np.ndarray):
+    """Readings O1, O2 and T1: returns (packed uint8 [N, 16*ceil(K/80)], gamma*).
+
+    If W holds a non-finite value, gamma* is NaN and packed is None.
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    gamma = weight_scale(w)
+    if not np.isfinite(gamma):
+        return None, gamma
+    return pack_t1(ternarize(w, gamma)), gamma
+
+
+def ternary_linear_t1(packed: np.ndarray, gamma: np.float32, xq: np.ndarray,
+                      d: np.ndarray):
+    """ternary_linear on T1-packed weights: returns (acc int32 [M, N], y fp32 [M, N])."""
+    q = unpack_t1(packed, np.asarray(xq).shape[1])
+    acc = integer_matmul(q, xq)
+    return acc, dequantize(acc, gamma, d)
+
+
+def ternary_linear_t1_at(packed: np.ndarray, gamma: np.float32, xq: np.ndarray,
+                         d: np.ndarray, m_idx, n_idx):
+    """Selected outputs of ternary_linear_t1: acc and y at the pairs (m_idx[i], n_idx[i])."""
+    m_idx = np.asarray(m_idx, dtype=np.int64)
+    n_idx = np.asarray(n_idx, dtype=np.int64)
+    q_rows = unpack_t1(np.asarray(packed)[n_idx], np.asarray(xq).shape[1]).astype(np.int64)
+    x_rows = np.asarray(xq)[m_idx].astype(np.int64)
+    acc = (q_rows * x_rows).sum(axis=1).astype(np.int32)
+    scale = (F32(gamma) * np.asarray(d, dtype=np.float32)[m_idx]).astype(np.float32)
+    return acc, acc.astype(np.float32) * scale
 
 
 def quant_linear(packed: np.ndarray, gamma: np.float32, x: np.ndarray):

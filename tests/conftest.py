@@ -17,3 +17,10 @@ def golden():
     import json
     with open(os.path.join(ROOT, "tests", "golden", "worked_examples.json")) as f:
         return json.load(f)
+
+
+@pytest.fixture(scope="session")
+def t1_golden():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "t1_layout.json")) as f:
+        return json.load(f)

@@ -533,3 +533,128 @@ def test_prologue_quantize_invariants():
     xq2, d2 = O.quantize_acts(O.relu2_glu(g, up))
     np.testing.assert_array_equal(xq1, xq2)
     np.testing.assert_array_equal(d1, d2)
+
+
+# ---------------------------------------------------------------------------
+# T1: five ternary codes per byte (base 3)
+# ---------------------------------------------------------------------------
+
+def _t1_case_q(case):
+    q = np.zeros((1, case["K"]), np.int8)
+    for k, v in case["set"]:
+        q[0, k] = v
+    return q
+
+
+def test_t1_golden_layout(t1_golden):
+    """Hand-worked bytes: catches a transposed block, a reversed digit order, a
+    wrong padding code."""
+    for case in t1_golden["cases"]:
+        q = _t1_case_q(case)
+        want = np.full(O.t1_row_bytes(case["K"]), case["bytes"]["all"], np.uint8)
+        for i, v in case["bytes"].items():
+            if i != "all":
+                want[int(i)] = v
+        np.testing.assert_array_equal(O.pack_t1(q)[0], want, err_msg=case["name"])
+        np.testing.assert_array_equal(O.unpack_t1(want[None, :], case["K"]), q)
+
+
+def test_t1_digits_match_base3_strings():
+    """Every byte value 0..242 decodes to the digits of Python's base-3 string
+    (least significant digit = the block's first 16 weights)."""
+    for v in range(243):
+        q = O.unpack_t1(np.full((1, 16), v, np.uint8), 80)[0]
+        digits = [int(c) for c in reversed(np.base_repr(v, 3).rjust(5, "0"))]
+        for j in range(5):
+            np.testing.assert_array_equal(q[16 * j:16 * j + 16], digits[j] - 1)
+
+
+def test_t1_pack_matches_python_int_parse():
+    """Independent packer: each byte parsed with int(s, 3) from the codes picked
+    by explicit index arithmetic, on ragged rows."""
+    rng = np.random.Generator(np.random.PCG64(51))
+    for k in (1, 7, 79, 80, 81, 173):
+        q = rng.integers(-1, 2, (3, k)).astype(np.int8)
+        got = O.pack_t1(q)
+        nb = (k + 79) // 80
+        assert got.shape == (3, 16 * nb)
+        for n in range(3):
+            for b in range(nb):
+                for i in range(16):
+                    codes = []
+                    for j in range(5):
+                        kk = 80 * b + 16 * j + i
+                        codes.append(int(q[n, kk]) + 1 if kk < k else 1)
+                    want = int("".join(str(c) for c in reversed(codes)), 3)
+                    assert int(got[n, 16 * b + i]) == want, (k, n, b, i)
+
+
+def test_t1_bijection_and_roundtrip():
+    """The 3^5 digit tuples map one-to-one onto 0..242; pack/unpack round trips;
+    bytes above 242 and non-zero padding are rejected."""
+    seen = set()
+    for tup in itertools.product((-1, 0, 1), repeat=5):
+        q = np.zeros((1, 80), np.int8)
+        q[0, [0, 16, 32, 48, 64]] = tup
+        seen.add(int(O.pack_t1(q)[0, 0]))
+    assert seen == set(range(243))
+    rng = np.random.Generator(np.random.PCG64(52))
+    for k in (1, 64, 80, 100, 160, 6912 // 8):
+        q = rng.integers(-1, 2, (5, k)).astype(np.int8)
+        np.testing.assert_array_equal(O.unpack_t1(O.pack_t1(q), k), q)
+    b = O.pack_t1(rng.integers(-1, 2, (4, 160)).astype(np.int8))
+    np.testing.assert_array_equal(O.pack_t1(O.unpack_t1(b, 160)), b)
+    with pytest.raises(ValueError):
+        O.unpack_t1(np.full((1, 16), 243, np.uint8), 80)
+    bad = O.pack_t1(np.zeros((1, 70), np.int8))
+    bad[0, 15] += 81                                   # weight k = 79 >= K = 70
+    with pytest.raises(ValueError):
+        O.unpack_t1(bad, 70)
+
+
+def test_t1_linear_equals_two_bit_linear():
+    """The same ternary matrix in both formats gives identical accumulators and
+    outputs (the 2-bit contraction is pinned by brute force above)."""
+    rng = np.random.Generator(np.random.PCG64(53))
+    for k in (64, 160, 6912 // 16):
+        q = rng.integers(-1, 2, (9, k)).astype(np.int8)
+        xq = rng.integers(-127, 128, (3, k)).astype(np.int8)
+        d = rng.uniform(0.001, 0.05, 3).astype(np.float32)
+        gamma = np.float32(0.0173)
+        acc2, y2 = O.ternary_linear(O.pack_codes(q), gamma, xq, d)
+        acc5, y5 = O.ternary_linear_t1(O.pack_t1(q), gamma, xq, d)
+        np.testing.assert_array_equal(acc5, acc2)
+        np.testing.assert_array_equal(y5.view(np.uint32), y2.view(np.uint32))
+        mi, ni = np.array([0, 2, 1]), np.array([8, 0, 4])
+        acc_s, y_s = O.ternary_linear_t1_at(O.pack_t1(q), gamma, xq, d, mi, ni)
+        np.testing.assert_array_equal(acc_s, acc5[mi, ni])
+        np.testing.assert_array_equal(y_s.view(np.uint32), y5[mi, ni].view(np.uint32))
+
+
+def test_t1_quantize_weights_is_ternarise_then_pack():
+    rng = np.random.Generator(np.random.PCG64(54))
+    w = (rng.standard_normal((6, 200)) * 0.02).astype(np.float32)
+    p2, g2 = O.quantize_weights(w)
+    p5, g5 = O.quantize_weights_t1(w)
+    assert g5.view(np.uint32) == g2.view(np.uint32)
+    np.testing.assert_array_equal(O.unpack_t1(p5, 200), O.unpack_codes(p2))
+    wn = w.copy()
+    wn[1, 3] = np.inf
+    p, g = O.quantize_weights_t1(wn)
+    assert p is None and np.isnan(g)
+
+
+def test_t1_size_matches_page_figure(t1_golden):
+    """The 2B-shaped stack: 0.42 GB at five trits per byte, which matches the
+    0.4 GB the comparison table gives for the 2B model (the 2-bit layout's
+    0.52 GB does not)."""
+    s = t1_golden["size_2b_stack"]
+    layer = [(2560, 2560), (2560, 640), (2560, 640), (2560, 2560), (2560, 6912),
+             (2560, 6912), (6912, 2560)]
+    per_layer = sum(n * O.t1_row_bytes(k) for k, n in layer)
+    assert per_layer == s["layer_bytes"]
+    assert 30 * per_layer == s["stack_bytes"]
+    assert 30 * sum(n * k // 4 for k, n in layer) == s["stack_bytes_2bit"]
+    assert round(s["stack_bytes"] / 1e9, 1) == s["page_figure_gb"]
+    assert round(s["stack_bytes_2bit"] / 1e9, 1) != s["page_figure_gb"]
+    assert O.pack_t1(np.zeros((2, 6912), np.int8)).shape == (2, O.t1_row_bytes(6912))
