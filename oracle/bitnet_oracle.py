@@ -59,13 +59,17 @@ N3  normalise-then-quantise: r is a positive per-token factor and absmax
 Denser packing ([OV] introduction and section 2: a ternary weight carries
 log2(3) ~ 1.58 bits of information; [CM] comparison table: 0.4 GB of
 non-embedding memory for the 2B model, i.e. about 1.6 bits per weight):
-T1  five ternary codes per byte as base-3 digits, byte = sum_j c_j * 3**j with
-    c_j = q_j + 1 (3**5 = 243 <= 256, so 1.6 bits per weight).  A row is padded
-    with q = 0 to a multiple of 80 weights and cut into blocks of 80 weights in
-    16 bytes: byte i (0..15) of block b holds the weights k = 80*b + 16*j + i as
-    digit j (j = 0..4).  Row n occupies bytes [n*R, (n+1)*R), R = 16*ceil(K/80).
-    The pages describe no such format; this layout is ours (each digit j of a
-    block's 16 bytes covers 16 consecutive weights).
+T1  five ternary codes per byte (3**5 = 243 <= 256, so 1.6 bits per weight).
+    The codes c_j = q_j + 1 are the base-3 digits of b = sum_j c_j * 3**j, and
+    the byte holds b / 243 = 0.c4 c3 c2 c1 c0 (base 3) as an 8-bit fixed-point
+    fraction rounded up: byte = ceil(256 * b / 243) (so b = floor(243 * byte /
+    256); 13 byte values are never written).  A row is padded with q = 0 to a
+    multiple of 80 weights and cut into blocks of 80 weights in 16 bytes: byte i
+    (0..15) of block b holds the weights k = 80*b + 16*j + i as digit j
+    (j = 0..4).  Row n occupies bytes [n*R, (n+1)*R), R = 16*ceil(K/80).  The
+    pages describe no such format; this layout is ours (each digit j of a
+    block's 16 bytes covers 16 consecutive weights, and a digit falls out of
+    the fixed-point fraction as the integer part of three times it).
 
 bf16 inputs are upcast to fp32 exactly (bit pattern shifted left by 16) before
 any step, so every function here takes fp32 arrays.
@@ -410,8 +414,9 @@ def t1_row_bytes(k: int) -> int:
 def pack_t1(q: np.ndarray) -> np.ndarray:
     """Pack ternary q [N, K] into uint8 [N, 16*ceil(K/80)] per reading T1.
 
-    Byte i of block b of row n = sum_j (q[n, 80b + 16j + i] + 1) * 3**j, with
-    q = 0 for the padding weights k >= K.
+    Byte i of block b of row n = ceil(256 * v / 243) with
+    v = sum_j (q[n, 80b + 16j + i] + 1) * 3**j and q = 0 for the padding
+    weights k >= K.
     """
     q = np.asarray(q, dtype=np.int8)
     n_rows, k = q.shape
@@ -422,22 +427,26 @@ def pack_t1(q: np.ndarray) -> np.ndarray:
     value = np.zeros((n_rows, blocks, T1_BLOCK_BYTES), dtype=np.int64)
     for j in range(T1_DIGITS):
         value += codes[:, :, j, :] * 3 ** j
-    return value.reshape(n_rows, blocks * T1_BLOCK_BYTES).astype(np.uint8)
+    byte = -((-256 * value) // 243)                          # ceil(256 v / 243)
+    return byte.reshape(n_rows, blocks * T1_BLOCK_BYTES).astype(np.uint8)
 
 
 def unpack_t1(packed: np.ndarray, k: int) -> np.ndarray:
     """Inverse of pack_t1: uint8 [N, 16*ceil(K/80)] -> int8 q [N, K].
 
-    Bytes above 242 and non-zero padding weights are invalid.
+    The base-3 value of a byte is v = floor(243 * byte / 256); a byte that is
+    not ceil(256 * v / 243) of its own v, and non-zero padding weights, are
+    invalid.
     """
     p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
     n_rows, row_bytes = p.shape
     if row_bytes != t1_row_bytes(k):
         raise ValueError("row length does not match K")
-    if np.any(p > 3 ** T1_DIGITS - 1):
-        raise ValueError("packed byte above 242")
+    value = (243 * p) // 256
+    if np.any(-((-256 * value) // 243) != p):
+        raise ValueError("byte is not the encoding of a base-3 value")
     blocks = row_bytes // T1_BLOCK_BYTES
-    rest = p.reshape(n_rows, blocks, T1_BLOCK_BYTES)
+    rest = value.reshape(n_rows, blocks, T1_BLOCK_BYTES)
     codes = np.empty((n_rows, blocks, T1_DIGITS, T1_BLOCK_BYTES), dtype=np.int64)
     for j in range(T1_DIGITS):
         codes[:, :, j, :] = rest % 3

@@ -559,19 +559,39 @@ def test_t1_golden_layout(t1_golden):
         np.testing.assert_array_equal(O.unpack_t1(want[None, :], case["K"]), q)
 
 
-def test_t1_digits_match_base3_strings():
-    """Every byte value 0..242 decodes to the digits of Python's base-3 string
-    (least significant digit = the block's first 16 weights)."""
+def _fixed_point_digits(byte):
+    """Base-3 digits of an 8-bit fixed-point fraction, most significant first:
+    each is the integer part of three times the remaining fraction."""
+    f, out = int(byte), []
+    for _ in range(5):
+        t = 3 * f
+        out.append(t >> 8)
+        f = t & 255
+    return out
+
+
+def test_t1_bytes_are_fixed_point_base3_fractions():
+    """For every v in 0..242 (digits from Python's base-3 string, least
+    significant = the block's first 16 weights): the byte is v/243 rounded up
+    to a multiple of 1/256 (checked with Fraction), its fixed-point digits are
+    the digits of v, and the decoder recovers them."""
     for v in range(243):
-        q = O.unpack_t1(np.full((1, 16), v, np.uint8), 80)[0]
         digits = [int(c) for c in reversed(np.base_repr(v, 3).rjust(5, "0"))]
+        q = np.zeros((1, 80), np.int8)
         for j in range(5):
-            np.testing.assert_array_equal(q[16 * j:16 * j + 16], digits[j] - 1)
+            q[0, 16 * j] = digits[j] - 1
+        byte = int(O.pack_t1(q)[0, 0])
+        gap = Fraction(byte, 256) - Fraction(v, 243)
+        assert 0 <= gap < Fraction(1, 256), (v, byte)
+        assert _fixed_point_digits(byte) == digits[::-1], (v, byte)
+        back = O.unpack_t1(np.full((1, 16), byte, np.uint8), 80)[0]
+        for j in range(5):
+            np.testing.assert_array_equal(back[16 * j:16 * j + 16], digits[j] - 1)
 
 
 def test_t1_pack_matches_python_int_parse():
-    """Independent packer: each byte parsed with int(s, 3) from the codes picked
-    by explicit index arithmetic, on ragged rows."""
+    """Independent packer: each byte from int(s, 3) of the codes picked by
+    explicit index arithmetic, rounded up with Fraction, on ragged rows."""
     rng = np.random.Generator(np.random.PCG64(51))
     for k in (1, 7, 79, 80, 81, 173):
         q = rng.integers(-1, 2, (3, k)).astype(np.int8)
@@ -585,31 +605,33 @@ def test_t1_pack_matches_python_int_parse():
                     for j in range(5):
                         kk = 80 * b + 16 * j + i
                         codes.append(int(q[n, kk]) + 1 if kk < k else 1)
-                    want = int("".join(str(c) for c in reversed(codes)), 3)
+                    v = int("".join(str(c) for c in reversed(codes)), 3)
+                    want = math.ceil(Fraction(256 * v, 243))
                     assert int(got[n, 16 * b + i]) == want, (k, n, b, i)
 
 
 def test_t1_bijection_and_roundtrip():
-    """The 3^5 digit tuples map one-to-one onto 0..242; pack/unpack round trips;
-    bytes above 242 and non-zero padding are rejected."""
+    """The 3^5 digit tuples map one-to-one onto 243 bytes; the other 13 bytes,
+    and non-zero padding, are rejected; pack/unpack round trips."""
     seen = set()
     for tup in itertools.product((-1, 0, 1), repeat=5):
         q = np.zeros((1, 80), np.int8)
         q[0, [0, 16, 32, 48, 64]] = tup
         seen.add(int(O.pack_t1(q)[0, 0]))
-    assert seen == set(range(243))
+    assert len(seen) == 243 and max(seen) == 255 and min(seen) == 0
+    for byte in set(range(256)) - seen:
+        with pytest.raises(ValueError):
+            O.unpack_t1(np.full((1, 16), byte, np.uint8), 80)
     rng = np.random.Generator(np.random.PCG64(52))
     for k in (1, 64, 80, 100, 160, 6912 // 8):
         q = rng.integers(-1, 2, (5, k)).astype(np.int8)
         np.testing.assert_array_equal(O.unpack_t1(O.pack_t1(q), k), q)
     b = O.pack_t1(rng.integers(-1, 2, (4, 160)).astype(np.int8))
     np.testing.assert_array_equal(O.pack_t1(O.unpack_t1(b, 160)), b)
+    q80 = np.zeros((1, 80), np.int8)
+    q80[0, 79] = 1                                     # weight k = 79 >= K = 70
     with pytest.raises(ValueError):
-        O.unpack_t1(np.full((1, 16), 243, np.uint8), 80)
-    bad = O.pack_t1(np.zeros((1, 70), np.int8))
-    bad[0, 15] += 81                                   # weight k = 79 >= K = 70
-    with pytest.raises(ValueError):
-        O.unpack_t1(bad, 70)
+        O.unpack_t1(O.pack_t1(q80), 70)
 
 
 def test_t1_linear_equals_two_bit_linear():
