@@ -22,8 +22,9 @@ Also: the same 2B chain as full layers (RMS norms and squared-ReLU gating fused
 into the launches), the 8B-shaped stack (32 layers) at M = 1 and M = 16, the
 100B-class decode stack (96 layers, 23.35 GB packed, fp32 activations), the
 prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096 and on the
-8B shapes at M = 2048, and the CPU oracle timed on a bounded sample of the same
-decode workload.
+8B shapes at M = 2048, the 2B and 100B chains with weights packed five per byte
+(T1 layout, 1.6 bits per weight), and the CPU oracle timed on a bounded sample
+of the same decode workload.
 """
 
 from __future__ import annotations
@@ -78,14 +79,18 @@ def parse():
     p.add_argument("--no-100b", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the full-layer 2B chain and the 8B-shaped chains")
+    p.add_argument("--no-t1", action="store_true",
+                   help="skip the legs with weights packed five per byte")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this size (PMC calibration)")
     return p.parse_args()
 
 
-def build_stack(torch, N, I, layer_shapes, layers, replicas):
-    """Packed weights + scales on the GPU for replicas x layers x matrices."""
+def build_stack(torch, N, I, layer_shapes, layers, replicas, fmt="2bit"):
+    """Packed weights + scales on the GPU for replicas x layers x matrices (2 bits
+    per weight, or five weights per byte for fmt "t1")."""
+    quantize = N.bitnet_quantize_weights_t1 if fmt == "t1" else N.bitnet_quantize_weights
     stack = []
     for r in range(replicas):
         reps = []
@@ -95,7 +100,7 @@ def build_stack(torch, N, I, layer_shapes, layers, replicas):
                 g = torch.Generator(device="cuda").manual_seed(I.weight_seed(l, i) + 1_000_003 * r)
                 w = torch.randn((n, k), generator=g, device="cuda", dtype=torch.float32)
                 w.mul_(I.WEIGHT_SIGMA)
-                mats[nm] = N.bitnet_quantize_weights(w)
+                mats[nm] = quantize(w)
                 del w
             reps.append(mats)
         stack.append(reps)
@@ -103,7 +108,7 @@ def build_stack(torch, N, I, layer_shapes, layers, replicas):
     return stack
 
 
-def chain_fn(torch, N, layers_mats, h0, bufs, norms=None, eps=1e-5):
+def chain_fn(torch, N, layers_mats, h0, bufs, norms=None, eps=1e-5, fmt="2bit"):
     """Enqueue one step (M tokens) through every layer; returns the number of
     launches.  Plain chain: q, k, v from the layer input; o from q (attention is
     out of scope); gate and up from o; down from up.  Full layer (``norms``): an
@@ -112,6 +117,12 @@ def chain_fn(torch, N, layers_mats, h0, bufs, norms=None, eps=1e-5):
     the BitNet b1.58 2B4T architecture names them), all fused into the launches."""
     m = h0.shape[0]
     per_multi = 1 if m <= 4 else 2   # fused act-quant, or act-quant + linear launches
+    if fmt == "t1":
+        def qlm(mats, x, **kw):
+            return N.bitnet_quant_linear_t1(mats, x, **kw)
+    else:
+        def qlm(mats, x, **kw):
+            return N.bitnet_quant_linear_multi(mats, x, **kw)
 
     def step():
         h = h0
@@ -122,19 +133,19 @@ def chain_fn(torch, N, layers_mats, h0, bufs, norms=None, eps=1e-5):
                 if nw is None:
                     return {}
                 return dict(norm_weight=nw[key], eps=eps, up=up)
-            N.bitnet_quant_linear_multi(
+            qlm(
                 [(*mats["q"], bufs["q"]), (*mats["k"], bufs["k"]), (*mats["v"], bufs["v"])], h,
                 x_q=bufs["xq_h"], x_scale=bufs["xs_h"], **pro("in"))
-            N.bitnet_quant_linear_multi([(*mats["o"], bufs["o"])], bufs["q"], x_q=bufs["xq_q"],
+            qlm([(*mats["o"], bufs["o"])], bufs["q"], x_q=bufs["xq_q"],
                                         x_scale=bufs["xs_q"], **pro("attn_sub"))
-            N.bitnet_quant_linear_multi(
+            qlm(
                 [(*mats["gate"], bufs["gate"]), (*mats["up"], bufs["up"])], bufs["o"],
                 x_q=bufs["xq_o"], x_scale=bufs["xs_o"], **pro("ffn_in"))
             if nw is None:
-                N.bitnet_quant_linear_multi([(*mats["down"], bufs["h"])], bufs["up"],
+                qlm([(*mats["down"], bufs["h"])], bufs["up"],
                                             x_q=bufs["xq_u"], x_scale=bufs["xs_u"])
             else:
-                N.bitnet_quant_linear_multi([(*mats["down"], bufs["h"])], bufs["gate"],
+                qlm([(*mats["down"], bufs["h"])], bufs["gate"],
                                             x_q=bufs["xq_u"], x_scale=bufs["xs_u"],
                                             **pro("ffn_sub", up=bufs["up"]))
             h = bufs["h"]
@@ -142,16 +153,17 @@ def chain_fn(torch, N, layers_mats, h0, bufs, norms=None, eps=1e-5):
     return step
 
 
-def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycle=None):
+def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycle=None,
+               fmt="2bit"):
     """M tokens at a time through a whole layer stack, replayed from HIP graphs."""
     wl = I.WORKLOADS[name]
     shapes, layers = wl["layer"], wl["layers"]
-    per_stack = I.packed_bytes(shapes) * layers
+    per_stack = I.packed_bytes(shapes, fmt) * layers
     replicas = max(1, math.ceil((min_cycle or CACHE_CYCLE_BYTES) / per_stack))
     t0 = time.time()
-    stack = build_stack(torch, N, I, shapes, layers, replicas)
-    log(f"{name}: {layers} layers, {per_stack / 1e6:.1f} MB packed per step, {replicas} replicas, "
-        f"weights ternarised on the GPU in {time.time() - t0:.1f} s")
+    stack = build_stack(torch, N, I, shapes, layers, replicas, fmt)
+    log(f"{name} ({fmt}): {layers} layers, {per_stack / 1e6:.1f} MB packed per step, "
+        f"{replicas} replicas, weights ternarised on the GPU in {time.time() - t0:.1f} s")
     act_dt = torch.bfloat16 if wl["act"] == "bf16" else torch.float32
     hidden = shapes[0][1]
     g = torch.Generator(device="cuda").manual_seed(I.ACT_SEED)
@@ -172,7 +184,7 @@ def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycl
     graphs = []
     launches = 0
     for r in range(replicas):
-        step = chain_fn(torch, N, stack[r], h0, bufs, norms)
+        step = chain_fn(torch, N, stack[r], h0, bufs, norms, fmt=fmt)
         step()
         torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
@@ -193,9 +205,10 @@ def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycl
     per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
     pct = {q: per[min(steps - 1, int(q / 100 * steps))] for q in (10, 50, 90)}
     gbs = per_stack / (ms * 1e-3) / 1e9
-    log(f"{name} (M={m}{', full layer' if full_layer else ''}): {ms * 1e3:.1f} us/step, "
+    log(f"{name} ({fmt}, M={m}{', full layer' if full_layer else ''}): {ms * 1e3:.1f} us/step, "
         f"{gbs:.1f} GB/s packed, {ms * 1e3 / launches:.2f} us per launch")
     res = dict(ms=ms, gbs=gbs, per_stack=per_stack, replicas=replicas, launches=launches,
+               weights=sum(n * k for _, k, n in shapes) * layers,
                layers=layers, shapes=shapes, act=wl["act"],
                ms_p10=pct[10], ms_median=pct[50], ms_p90=pct[90])
     del graphs, stack
@@ -206,6 +219,7 @@ def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycl
 
 def leg_summary(d, m):
     return {"gbs": round(d["gbs"], 1), "frac_of_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),
+            "weights_per_s_G": round(d["weights"] / d["ms"] / 1e6, 1),
             "ms_per_step": round(d["ms"], 4), "tokens_per_s": round(m * 1e3 / d["ms"], 1),
             "packed_bytes_per_step": d["per_stack"], "launches_per_step": d["launches"],
             "avg_launch_us": round(d["ms"] * 1e3 / d["launches"], 3)}
@@ -350,9 +364,19 @@ def main():
             d8 = decode_leg(torch, N, I, "llama8b-ternary", max(5, args.steps // 3), 2, m=m)
             result[f"decode_8b_m{m}"] = dict(workload="llama8b-ternary (32 layers)",
                                              **leg_summary(d8, m))
+    if not args.no_t1:
+        dt = decode_leg(torch, N, I, args.workload, args.steps, args.warmup, fmt="t1")
+        result["decode_t1"] = dict(workload=args.workload + ", weights five per byte (T1 layout)",
+                                   **leg_summary(dt, 1))
     if not args.no_100b:
         d5 = decode_leg(torch, N, I, "ternary100b-decode-m1-96L", max(5, args.steps // 5), 2)
         result["decode_100b"] = dict(workload="ternary100b-decode-m1-96L", **leg_summary(d5, 1))
+        if not args.no_t1:
+            d6 = decode_leg(torch, N, I, "ternary100b-decode-m1-96L", max(5, args.steps // 5), 2,
+                            fmt="t1")
+            result["decode_100b_t1"] = dict(
+                workload="ternary100b-decode-m1-96L, weights five per byte (T1 layout)",
+                **leg_summary(d6, 1))
     if not args.no_prefill:
         result["prefill"] = prefill(torch, N, I, wl["layer"], (512, 4096), steps=10)
         result["prefill_8b"] = prefill(torch, N, I, I.LAYER_8B, (2048,), steps=5)

@@ -214,6 +214,67 @@ bitnet_status bitnet_quant_linear_ex(const bitnet_matrix *mats, int count, const
                                      int64_t K, int8_t *x_q, float *x_scale, int y_dtype,
                                      hipStream_t stream);
 
+/*
+ * Five ternary weights per byte ("T1"): a denser layout for the HBM-bound decode
+ * path.  A ternary weight carries log2(3) ~ 1.58 bits (onedollarvps, section 1
+ * and section 2); the 0.4 GB of non-embedding memory the communeify comparison
+ * table gives for the 2B model is about 1.6 bits per weight, which 3^5 = 243 <=
+ * 256 reaches.  The pages define no layout; this one is:
+ *   the codes c_j = q_j + 1 of five weights form v = sum_j c_j * 3^j, stored as
+ *   the byte ceil(256 * v / 243) (the base-3 fraction v/243 in 8-bit fixed
+ *   point, rounded up; 13 byte values are never written);
+ *   a row is padded with q = 0 to a multiple of 80 weights and cut into blocks
+ *   of 80 weights in 16 bytes: byte i of block b holds the weights
+ *   k = 80*b + 16*j + i as digit j (j = 0..4);
+ *   row n occupies bytes [n*R, (n+1)*R), R = 16 * ceil(K / 80).
+ * Results of the T1 calls are bit-identical to the 2-bit calls on the same
+ * ternary weights.
+ */
+
+/* Bytes of a T1 matrix: N * 16 * ceil(K / 80).  0 for negative sizes. */
+size_t bitnet_t1_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * bitnet_quantize_weights with the T1 output layout.
+ *   N >= 1, K >= 1 (any K: rows are padded), N*K < BITNET_MAX_WEIGHTS.
+ *   w_t1     [N][16*ceil(K/80)] uint8 out, 16-byte aligned.
+ *   other arguments, gamma* and the non-finite behaviour as bitnet_quantize_weights.
+ */
+bitnet_status bitnet_quantize_weights_t1(const void *w, int w_dtype, int64_t N, int64_t K,
+                                         uint8_t *w_t1, float *w_scale, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Exact conversion of a 2-bit packed matrix (bitnet_quantize_weights layout,
+ * K >= 4, K % 4 == 0, N >= 0) to T1.  w_t1 [N][16*ceil(K/80)], 16-byte aligned.
+ * Bytes holding the unused 2-bit code 3 give unspecified output bytes.
+ */
+bitnet_status bitnet_repack_t1(const uint8_t *w_packed, int64_t N, int64_t K, uint8_t *w_t1,
+                               hipStream_t stream);
+
+/*
+ * bitnet_ternary_linear_multi on T1 weights: every mats[i].w_packed is a T1
+ * matrix (16-byte aligned).  Needs K >= 16, K % 16 == 0 and a 16-byte aligned
+ * x_q; otherwise BITNET_ERR_SHAPE / BITNET_ERR_ALIGN (there is no generic
+ * kernel for this layout).  Runs the decode kernel; M > 16 runs in groups of
+ * 16 tokens, each streaming the weights again.
+ */
+bitnet_status bitnet_ternary_linear_t1(const bitnet_matrix *mats, int count, const int8_t *x_q,
+                                       const float *x_scale, int64_t M, int64_t K, int y_dtype,
+                                       hipStream_t stream);
+
+/*
+ * bitnet_quant_linear_ex on T1 weights (same layout requirements as
+ * bitnet_ternary_linear_t1).  The quantisation and prologue are fused into the
+ * decode launch when M <= 4 and the activations of all tokens fit one LDS phase
+ * (M * (80 * ceil(K/80) + 16) <= 46 KiB) and x, up and norm_weight are 16-byte
+ * aligned.
+ */
+bitnet_status bitnet_quant_linear_t1(const bitnet_matrix *mats, int count, const void *x,
+                                     int x_dtype, const bitnet_act_prologue *pro, int64_t M,
+                                     int64_t K, int8_t *x_q, float *x_scale, int y_dtype,
+                                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

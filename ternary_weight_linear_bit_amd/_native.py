@@ -57,6 +57,15 @@ SIGNATURES["bitnet_quant_linear_ex"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _
                                              ctypes.POINTER(BitnetActPrologue), _I64, _I64, _P,
                                              _P, _I, _P])
 
+SIGNATURES["bitnet_t1_packed_bytes"] = (_SZ, [_I64, _I64])
+SIGNATURES["bitnet_quantize_weights_t1"] = (_I, [_P, _I, _I64, _I64, _P, _P, _P, _SZ, _P])
+SIGNATURES["bitnet_repack_t1"] = (_I, [_P, _I64, _I64, _P, _P])
+SIGNATURES["bitnet_ternary_linear_t1"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _P, _P, _I64,
+                                               _I64, _I, _P])
+SIGNATURES["bitnet_quant_linear_t1"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _P, _I,
+                                             ctypes.POINTER(BitnetActPrologue), _I64, _I64, _P,
+                                             _P, _I, _P])
+
 _lib = None
 
 
@@ -264,4 +273,90 @@ def bitnet_quant_linear_multi(mats, x, x_q=None, x_scale=None, y_dtype=None, str
         _check("bitnet_quant_linear_ex", lib().bitnet_quant_linear_ex(
             arr, len(mats), _ptr(x), _dtype_code(x.dtype), pro, m, k, _ptr(x_q), _ptr(x_scale),
             dt, _stream(stream)))
+    return ys, x_q, x_scale
+
+
+# ---------------------------------------------------------------------------
+# five ternary weights per byte (T1 layout)
+# ---------------------------------------------------------------------------
+
+def bitnet_t1_packed_bytes(n: int, k: int) -> int:
+    return lib().bitnet_t1_packed_bytes(n, k)
+
+
+def t1_row_bytes(k: int) -> int:
+    """Bytes per row of a T1 matrix (16 * ceil(K / 80))."""
+    return lib().bitnet_t1_packed_bytes(1, k)
+
+
+def bitnet_quantize_weights_t1(w, packed=None, scale=None, workspace=None, stream=None):
+    """w: [N, K] fp32/bf16 -> (T1 packed uint8 [N, 16*ceil(K/80)], gamma* fp32 [1])."""
+    import torch
+    _need_cuda(w)
+    n, k = w.shape
+    dev = w.device
+    if packed is None:
+        packed = torch.empty((n, t1_row_bytes(k)), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_bytes = lib().bitnet_quantize_weights_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _need_cuda(packed, scale, workspace)
+    _check("bitnet_quantize_weights_t1", lib().bitnet_quantize_weights_t1(
+        _ptr(w), _dtype_code(w.dtype), n, k, _ptr(packed), _ptr(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return packed, scale
+
+
+def bitnet_repack_t1(w_packed, out=None, stream=None):
+    """2-bit packed [N, K/4] -> T1 packed [N, 16*ceil(K/80)]."""
+    import torch
+    _need_cuda(w_packed)
+    n, kb = w_packed.shape
+    k = 4 * kb
+    if out is None:
+        out = torch.empty((n, t1_row_bytes(k)), dtype=torch.uint8, device=w_packed.device)
+    _need_cuda(out)
+    _check("bitnet_repack_t1", lib().bitnet_repack_t1(_ptr(w_packed), n, k, _ptr(out),
+                                                      _stream(stream)))
+    return out
+
+
+def _check_t1(mats, k):
+    r = t1_row_bytes(k)
+    for t in mats:
+        if t[0].shape[1] != r:
+            raise ValueError("T1 matrix rows do not match K")
+
+
+def bitnet_ternary_linear_t1(mats, x_q, x_scale, y_dtype=None, stream=None):
+    """Several (w_t1, w_scale[, y[, acc_out]]) sharing x_q -> list of y."""
+    import torch
+    _need_cuda(x_q, x_scale)
+    m, k = x_q.shape
+    _check_t1(mats, k)
+    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x_q.device)
+    _check("bitnet_ternary_linear_t1", lib().bitnet_ternary_linear_t1(
+        arr, len(mats), _ptr(x_q), _ptr(x_scale), m, k, _dtype_code(ys[0].dtype),
+        _stream(stream)))
+    return ys
+
+
+def bitnet_quant_linear_t1(mats, x, x_q=None, x_scale=None, y_dtype=None, stream=None, up=None,
+                           norm_weight=None, eps=1e-5):
+    """bitnet_quant_linear_multi on T1 matrices: returns (list of y, x_q, x_scale)."""
+    import torch
+    _need_cuda(x)
+    m, k = x.shape
+    _check_t1(mats, k)
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need_cuda(x_q, x_scale)
+    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x.device)
+    _check("bitnet_quant_linear_t1", lib().bitnet_quant_linear_t1(
+        arr, len(mats), _ptr(x), _dtype_code(x.dtype), _prologue(x, up, norm_weight, eps), m, k,
+        _ptr(x_q), _ptr(x_scale), _dtype_code(ys[0].dtype), _stream(stream)))
     return ys, x_q, x_scale

@@ -6,6 +6,7 @@
 namespace {
 
 constexpr size_t kWqWorkspaceBytes = 4096;
+constexpr int kFmt2 = 0, kFmtT1 = 1;  // weight layouts of the decode kernel
 constexpr int64_t kInt32Max = 2147483647;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -77,13 +78,13 @@ bitnet_status run_linear(const bitnet_matrix* mats, int count, const int8_t* x_q
                          hipStream_t stream) {
   if (M == 0) return BITNET_OK;
   const bool yb = y_dtype == BITNET_BF16;
-  if (all_fast(mats, count, x_q, K) && bitnet::gemv_fits(M, K)) {
+  if (all_fast(mats, count, x_q, K) && bitnet::gemv_fits(M, K, kFmt2)) {
     for (int j0 = 0; j0 < count; j0 += bitnet::kMaxGroup) {
       const int c = count - j0 < bitnet::kMaxGroup ? count - j0 : bitnet::kMaxGroup;
       bitnet::GemvArgs a = gemv_args(mats + j0, c, M, K, y_dtype);
       a.xq = x_q;
       a.xs = x_scale;
-      const bitnet_status st = from_hip(bitnet::launch_gemv(a, 0, stream));
+      const bitnet_status st = from_hip(bitnet::launch_gemv(a, 0, kFmt2, stream));
       if (st != BITNET_OK) return st;
     }
     return BITNET_OK;
@@ -129,7 +130,7 @@ bitnet_status quant_linear(const bitnet_matrix* mats, int count, const void* x, 
                            const bitnet::ActPrologue& pro, int64_t M, int64_t K, int8_t* x_q,
                            float* x_scale, int y_dtype, hipStream_t stream) {
   if (M == 0) return BITNET_OK;
-  if (all_fast(mats, count, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K) &&
+  if (all_fast(mats, count, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K, kFmt2) &&
       (!pro.up || aligned(pro.up, 16)) && (!pro.w || aligned(pro.w, 16))) {
     const int c = count < bitnet::kMaxGroup ? count : bitnet::kMaxGroup;
     bitnet::GemvArgs a = gemv_args(mats, c, M, K, y_dtype);
@@ -140,13 +141,73 @@ bitnet_status quant_linear(const bitnet_matrix* mats, int count, const void* x, 
     a.xup = pro.up;
     a.gnorm = pro.w;
     a.eps = pro.eps;
-    if (bitnet::launch_gemv(a, x_dtype, stream) != hipSuccess) return BITNET_ERR_HIP;
+    if (bitnet::launch_gemv(a, x_dtype, kFmt2, stream) != hipSuccess) return BITNET_ERR_HIP;
     if (count == c) return BITNET_OK;
     return run_linear(mats + c, count - c, x_q, x_scale, M, K, y_dtype, stream);
   }
   if (bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, pro, stream) != hipSuccess)
     return BITNET_ERR_HIP;
   return run_linear(mats, count, x_q, x_scale, M, K, y_dtype, stream);
+}
+
+// T1 weights (five codes per byte): only the decode kernel reads them, so M > 16
+// runs as groups of 16 tokens.  Every matrix, x_q and K checked by check_t1.
+bitnet_status run_linear_t1(const bitnet_matrix* mats, int count, const int8_t* x_q,
+                            const float* x_scale, int64_t M, int64_t K, int y_dtype,
+                            hipStream_t stream) {
+  const int64_t ye = (int64_t)esize(y_dtype);
+  for (int64_t t0 = 0; t0 < M; t0 += bitnet::kGemvMaxM) {
+    const int64_t mt = M - t0 < bitnet::kGemvMaxM ? M - t0 : bitnet::kGemvMaxM;
+    for (int j0 = 0; j0 < count; j0 += bitnet::kMaxGroup) {
+      const int c = count - j0 < bitnet::kMaxGroup ? count - j0 : bitnet::kMaxGroup;
+      bitnet_matrix sub[bitnet::kMaxGroup];
+      for (int j = 0; j < c; ++j) {
+        sub[j] = mats[j0 + j];
+        sub[j].y = static_cast<char*>(sub[j].y) + t0 * sub[j].N * ye;
+        if (sub[j].acc_out) sub[j].acc_out += t0 * sub[j].N;
+      }
+      bitnet::GemvArgs a = gemv_args(sub, c, mt, K, y_dtype);
+      a.xq = x_q + t0 * K;
+      a.xs = x_scale + t0;
+      if (bitnet::launch_gemv(a, 0, kFmtT1, stream) != hipSuccess) return BITNET_ERR_HIP;
+    }
+  }
+  return BITNET_OK;
+}
+
+// T1 layout requirements on top of check_group: K % 16 == 0 (K >= 16), 16-byte
+// aligned weights and int8 activations.
+bitnet_status check_t1(const bitnet_matrix* mats, int count, const void* x_q, int64_t M,
+                       int64_t K) {
+  if (K < 16 || (K % 16) != 0) return BITNET_ERR_SHAPE;
+  if (M > 0 && !aligned(x_q, 16)) return BITNET_ERR_ALIGN;
+  for (int j = 0; j < count; ++j)
+    if (!aligned(mats[j].w_packed, 16)) return BITNET_ERR_ALIGN;
+  return BITNET_OK;
+}
+
+bitnet_status quant_linear_t1(const bitnet_matrix* mats, int count, const void* x, int x_dtype,
+                              const bitnet::ActPrologue& pro, int64_t M, int64_t K, int8_t* x_q,
+                              float* x_scale, int y_dtype, hipStream_t stream) {
+  if (M == 0) return BITNET_OK;
+  if (aligned(x, 16) && bitnet::gemv_fused_fits(M, K, kFmtT1) &&
+      (!pro.up || aligned(pro.up, 16)) && (!pro.w || aligned(pro.w, 16))) {
+    const int c = count < bitnet::kMaxGroup ? count : bitnet::kMaxGroup;
+    bitnet::GemvArgs a = gemv_args(mats, c, M, K, y_dtype);
+    a.xf = x;
+    a.xq = x_q;
+    a.xq_out = x_q;
+    a.xs_out = x_scale;
+    a.xup = pro.up;
+    a.gnorm = pro.w;
+    a.eps = pro.eps;
+    if (bitnet::launch_gemv(a, x_dtype, kFmtT1, stream) != hipSuccess) return BITNET_ERR_HIP;
+    if (count == c) return BITNET_OK;
+    return run_linear_t1(mats + c, count - c, x_q, x_scale, M, K, y_dtype, stream);
+  }
+  if (bitnet::launch_aq(x, x_dtype == BITNET_BF16, M, K, x_q, x_scale, pro, stream) != hipSuccess)
+    return BITNET_ERR_HIP;
+  return run_linear_t1(mats, count, x_q, x_scale, M, K, y_dtype, stream);
 }
 
 }  // namespace
@@ -188,6 +249,65 @@ bitnet_status bitnet_quantize_weights(const void* w, int w_dtype, int64_t N, int
     return BITNET_ERR_ALIGN;
   return from_hip(bitnet::launch_wq(w, w_dtype == BITNET_BF16, N * K, w_packed, w_scale, workspace,
                                     stream));
+}
+
+size_t bitnet_t1_packed_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0) return 0;
+  return (size_t)N * (size_t)(16 * ((K + 79) / 80));
+}
+
+bitnet_status bitnet_quantize_weights_t1(const void* w, int w_dtype, int64_t N, int64_t K,
+                                         uint8_t* w_t1, float* w_scale, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !w_t1 || !w_scale) return BITNET_ERR_NULL;
+  if (!valid_dtype(w_dtype)) return BITNET_ERR_DTYPE;
+  if (N < 1 || K < 1 || N >= BITNET_MAX_WEIGHTS / K) return BITNET_ERR_SHAPE;
+  if (!workspace || workspace_bytes < kWqWorkspaceBytes) return BITNET_ERR_WORKSPACE;
+  if (!aligned(w, esize(w_dtype)) || !aligned(w_scale, 4) || !aligned(workspace, 8) ||
+      !aligned(w_t1, 16))
+    return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_wq_t1(w, w_dtype == BITNET_BF16, N, K, w_t1, w_scale, workspace,
+                                       stream));
+}
+
+bitnet_status bitnet_repack_t1(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* w_t1,
+                               hipStream_t stream) {
+  if (!w_packed || !w_t1) return BITNET_ERR_NULL;
+  if (N < 0 || K < 4 || (K % 4) != 0 || (N > 0 && N >= BITNET_MAX_WEIGHTS / K))
+    return BITNET_ERR_SHAPE;
+  if (!aligned(w_t1, 16)) return BITNET_ERR_ALIGN;
+  if (N == 0) return BITNET_OK;
+  return from_hip(bitnet::launch_repack_t1(w_packed, N, K, w_t1, stream));
+}
+
+bitnet_status bitnet_ternary_linear_t1(const bitnet_matrix* mats, int count, const int8_t* x_q,
+                                       const float* x_scale, int64_t M, int64_t K, int y_dtype,
+                                       hipStream_t stream) {
+  if (M > 0 && (!x_scale || !x_q)) return BITNET_ERR_NULL;
+  bitnet_status st = check_group(mats, count, M, K, y_dtype);
+  if (st != BITNET_OK) return st;
+  st = check_t1(mats, count, x_q, M, K);
+  if (st != BITNET_OK) return st;
+  if (x_scale && !aligned(x_scale, 4)) return BITNET_ERR_ALIGN;
+  if (M == 0) return BITNET_OK;
+  return run_linear_t1(mats, count, x_q, x_scale, M, K, y_dtype, stream);
+}
+
+bitnet_status bitnet_quant_linear_t1(const bitnet_matrix* mats, int count, const void* x,
+                                     int x_dtype, const bitnet_act_prologue* pro, int64_t M,
+                                     int64_t K, int8_t* x_q, float* x_scale, int y_dtype,
+                                     hipStream_t stream) {
+  if (M > 0 && (!x_scale || !x || !x_q)) return BITNET_ERR_NULL;
+  if (!valid_dtype(x_dtype)) return BITNET_ERR_DTYPE;
+  bitnet_status st = check_group(mats, count, M, K, y_dtype);
+  if (st != BITNET_OK) return st;
+  st = check_t1(mats, count, x_q, M, K);
+  if (st != BITNET_OK) return st;
+  if (!aligned(x, esize(x_dtype)) || (x_scale && !aligned(x_scale, 4))) return BITNET_ERR_ALIGN;
+  st = check_prologue(pro, x_dtype, M, K);
+  if (st != BITNET_OK) return st;
+  return quant_linear_t1(mats, count, x, x_dtype, act_prologue(pro), M, K, x_q, x_scale, y_dtype,
+                         stream);
 }
 
 bitnet_status bitnet_quantize_acts_ex(const void* x, int x_dtype, const bitnet_act_prologue* pro,

@@ -143,6 +143,12 @@ __device__ __forceinline__ void lds_barrier() {
 // hipGetLastError() after its launches.
 hipError_t launch_wq(const void* w, bool w_bf16, int64_t n_weights, uint8_t* w_packed,
                      float* w_scale, void* workspace, hipStream_t s);
+// The same scale with the T1 layout (five codes per byte, 16 * ceil(K / 80) bytes
+// per row), and the exact conversion of a 2-bit packed matrix (K % 4 == 0) to it.
+hipError_t launch_wq_t1(const void* w, bool w_bf16, int64_t N, int64_t K, uint8_t* w_t1,
+                        float* w_scale, void* workspace, hipStream_t s);
+hipError_t launch_repack_t1(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* w_t1,
+                            hipStream_t s);
 // Input prologue of a layer (squared-ReLU gating and RMS norm), already validated.
 struct ActPrologue {
   const void* up;       // gating: up projection, same dtype and shape as x; else nullptr
@@ -193,11 +199,13 @@ struct GemvArgs {
   float eps, unused2;
 };
 
-// Decode kernel: M <= 16, K % 64 == 0; the fused variant (a.xf != nullptr) also
-// needs M <= 4 and the activations of all tokens in one LDS phase.
-bool gemv_fits(int64_t M, int64_t K);
-bool gemv_fused_fits(int64_t M, int64_t K);
-hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s);
+// Decode kernel: M <= 16 and K % 64 == 0 (fmt 0: 2-bit weights) or K % 16 == 0
+// (fmt 1: T1 weights); the fused variant (a.xf != nullptr) also needs M <= 4 and
+// the activations of all tokens in one LDS phase.
+constexpr int kGemvMaxM = 16;
+bool gemv_fits(int64_t M, int64_t K, int fmt);
+bool gemv_fused_fits(int64_t M, int64_t K, int fmt);
+hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                        const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
                        int32_t* acc_out, hipStream_t s);

@@ -43,6 +43,15 @@
 // RMS-normalised, quantised as RN32(v * w) with the factor
 // r = RN32(1/sqrt(RN32(RN32(mean v^2) + eps))) folded into the token scale (the
 // sum of squares in float64 over the token's threads).
+//
+// FMT 1 reads weights packed five per byte (reading T1: the codes' base-3 value
+// v as the fixed-point fraction ceil(256 v / 243); byte i of a 16-byte block
+// holds the weights 16 j + i of the block's 80 as digit j).  Digit j of the
+// block's 16 bytes covers 16 consecutive weights, so a lane's 16 bytes unpack
+// into five natural-order 16-weight operands and the activations are staged
+// untransposed.  A digit is the integer part of three times the fraction: one
+// packed 16-bit multiply-add per two bytes and digit, whose high byte is the
+// signed weight directly (3f - 256 = 256 (c - 1) + next fraction).
 #include "bitnet_internal.h"
 
 namespace bitnet {
@@ -60,18 +69,36 @@ constexpr int64_t kLatencyBytes = 6000000; // launches above this use the bandwi
 constexpr int kWgsPerCu = 2;               // bandwidth regime: workgroups per compute unit
 constexpr int kFlightLoads = 8192;         // target 1 KiB loads in flight over the chip
 
-// K range staged per phase: a multiple of 256 with M * (kx + 16) <= kXBudget and
-// at most 16 activation pieces (token, 4096-k block), i.e. two staging batches.
-int phase_k(int M, int K) {
-  int kx = ((kXBudget / M - 16) / 256) * 256;
+// Weight formats: 2 bits per weight (K % 64 == 0), or five per byte (T1,
+// K % 16 == 0, rows of 16 * ceil(K / 80) bytes).
+constexpr int kFmt2 = 0, kFmtT1 = 1;
+// zero slot: one B operand set read for tokens >= M and chunks past the end
+constexpr int zero_bytes(int fmt) { return fmt ? 96 : 64; }
+// LDS row of one token's staged activations for a phase of kx weights (T1
+// stages whole 80-k blocks)
+int stage_stride(int kx, int fmt) { return fmt ? 80 * ((kx + 79) / 80) + 16 : kx + 16; }
+// (token, 4096-k block) pieces the int8 staging loads for a phase of klen weights
+int stage_pieces(int M, int klen, int fmt) {
+  const int groups = fmt ? 5 * ((klen + 79) / 80) : klen / 16;
+  return M * ((groups + 255) / 256);
+}
+
+// K range staged per phase: a multiple of 256 (T1: of 1280, one 256-byte run of
+// a row) with M * stride <= kXBudget and at most 16 activation pieces, i.e. two
+// staging batches.
+int phase_k(int M, int K, int fmt) {
+  const int unit = fmt ? 1280 : 256;
+  int kx = ((kXBudget / M - 16) / unit) * unit;
   const int cap = 4096 * (16 / M);
-  if (kx > cap) kx = cap;
+  if (kx > cap) kx = (cap / unit) * unit;
+  while (kx > unit && stage_pieces(M, kx, fmt) > 2 * kStageBatch) kx -= unit;
   return kx >= K ? K : kx;
 }
 
-// LDS: X [M][kx + 16] | zero[64] | part[T][16][16] int | dsc[16] | wred[16] | wss[4] double
-int lds_bytes(int tiles, int M, int K) {
-  return M * (phase_k(M, K) + 16) + 64 + tiles * 1024 + 64 + 64 + 32;
+// LDS: X [M][stride] | zero | part[T][16][16] int | dsc[16] | wred[16] | wss[4] double
+int lds_bytes(int tiles, int M, int K, int fmt) {
+  return M * stage_stride(phase_k(M, K, fmt), fmt) + zero_bytes(fmt) + tiles * 1024 + 64 + 64 +
+         32;
 }
 
 // This workgroup's matrix and the launch's scalars.  Everything the kernel needs
@@ -144,11 +171,57 @@ __device__ __forceinline__ v4i unpack_weights_transposed(uint32_t w) {
   return a;
 }
 
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// One lane's 16 bytes of a T1 block -> the five A operands: operand j holds the
+// signed weights 16 j .. 16 j + 15 of the block in order.  Bytes 0, 2 and 1, 3 of
+// each dword go to 16-bit lanes; each step t = 3 f - 256 (mod 2^16) leaves the
+// digit minus one in the high byte (as a signed byte) and the remaining fraction
+// in the low byte; the high bytes of the two lane pairs are gathered in weight
+// order.  The four dwords' chains are interleaved so that no step waits on the
+// one just issued.
+__device__ __forceinline__ void unpack_t1(const uint4 w, v4i out[5]) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  us2 lo[4], hi[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    lo[x] = __builtin_bit_cast(us2, __builtin_amdgcn_perm(0u, wd[x], 0x0c020c00u));  // bytes 0, 2
+    hi[x] = __builtin_bit_cast(us2, __builtin_amdgcn_perm(0u, wd[x], 0x0c030c01u));  // bytes 1, 3
+  }
+  const us2 three = {3, 3}, minus256 = {0xff00, 0xff00};
+#pragma unroll
+  for (int j = 4; j >= 0; --j) {  // most significant digit first
+    uint32_t tl[4], th[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      tl[x] = __builtin_bit_cast(uint32_t, lo[x] * three + minus256);
+      th[x] = __builtin_bit_cast(uint32_t, hi[x] * three + minus256);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      out[j][x] = (int)__builtin_amdgcn_perm(th[x], tl[x], 0x07030501u);
+      // the next fractions (low bytes) by byte select: a mask would let the
+      // compiler take them from a separate lo * 3, one more multiply per step
+      lo[x] = __builtin_bit_cast(us2, __builtin_amdgcn_perm(0u, tl[x], 0x0c020c00u));
+      hi[x] = __builtin_bit_cast(us2, __builtin_amdgcn_perm(0u, th[x], 0x0c020c00u));
+    }
+  }
+}
+
 __device__ __forceinline__ void store_transposed(uint8_t* dst, uint4 v) {
   const uint32_t in[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
   transpose4x4_bytes(in, o);
   *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Stage one 16-byte group of int8 activations in the format's order.
+template <int FMT>
+__device__ __forceinline__ void store_group(uint8_t* dst, uint4 v) {
+  if (FMT == kFmtT1)
+    *reinterpret_cast<uint4*>(dst) = v;
+  else
+    store_transposed(dst, v);
 }
 
 // The 16 activations of one group from its raw 16-byte words (2 words of bf16 or
@@ -179,7 +252,7 @@ __device__ __forceinline__ void raw_to_f32(const uint4* w, float v[16]) {
 // XMODE 0: int8 x_q.  XMODE 1 + f, f = bf16 (1) | gated by a.xup (2) | RMS norm
 // with a.gnorm (4): fp32 / bf16 input quantised in the kernel.  The prologue
 // options are compile-time so that no load sits behind a runtime branch.
-template <int XMODE, int R>
+template <int XMODE, int R, int FMT>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int F = XMODE > 0 ? XMODE - 1 : 0;
@@ -189,6 +262,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   constexpr bool PRO = GLU || NRM;
   constexpr int NV = BF ? 2 : 4;             // fused: 16-byte words per 16-element group
   constexpr uint32_t ES = BF ? 2u : 4u;      // fused: input element size
+  constexpr int ZB = FMT == kFmtT1 ? 96 : 64;  // zero slot bytes (zero_bytes)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
@@ -197,17 +271,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   // this workgroup's matrix (each workgroup's tiles belong to one matrix)
   const Prologue pro = load_prologue(a);
   const int M = pro.M, K = pro.K, T = pro.T;
-  const uint32_t rowb = (uint32_t)K >> 2;  // packed bytes per row
+  const uint32_t rowb = FMT == kFmtT1 ? 16u * (((uint32_t)K + 79u) / 80u)
+                                      : (uint32_t)K >> 2;  // packed bytes per row
   const uint8_t* wmat = pro.wp;
   const int nrows = pro.n;
   const int tl0 = ((int)blockIdx.x - pro.wg0) * T;   // first tile in the matrix
   const int ntiles = min(T, (nrows + 15) / 16 - tl0);
   const int kx = pro.kx;
-  const int stride = kx + 16;
+  const int stride = FMT == kFmtT1 ? 80 * ((kx + 79) / 80) + 16 : kx + 16;  // stage_stride
 
   uint8_t* xs = smem;                                    // [M][stride]
-  uint8_t* zero = smem + M * stride;                     // 64 zero bytes
-  int* part = reinterpret_cast<int*>(zero + 64);         // [T][16 rows][16 tokens]
+  uint8_t* zero = smem + M * stride;                     // ZB zero bytes
+  int* part = reinterpret_cast<int*>(zero + ZB);         // [T][16 rows][16 tokens]
   float* dsc = reinterpret_cast<float*>(part + T * 256);  // [16]
   float* wred = dsc + 16;                                // [16]
   double* wss = reinterpret_cast<double*>(wred + 16);    // [4]
@@ -227,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   // clear the partial tiles and the zero slot; scalars the epilogue needs are
   // loaded now so that their latency hides behind the stream
   for (int i = tid; i < T * 64; i += kThreads) reinterpret_cast<uint4*>(part)[i] = make_uint4(0, 0, 0, 0);
-  if (tid < 16) reinterpret_cast<uint32_t*>(zero)[tid] = 0u;
+  if (tid < ZB / 4) reinterpret_cast<uint32_t*>(zero)[tid] = 0u;
   // (buffer loads: the pointers come out of the asm above as generic pointers,
   // and generic loads would make the compiler's waits for every load conservative)
   const float xs_t = XMODE == 0 ? __uint_as_float(bload4(make_rsrc(pro.xs, 4u * (uint32_t)M),
@@ -245,18 +320,21 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   for (int p = 0; p < pro.phases; ++p) {
     const int k0 = p * kx;
     const int klen = min(kx, K - k0);
-    const int C = klen >> 6;                       // 64-k chunks in this phase
+    // chunks (16 packed bytes of a row: 64 k, T1 80 k) in this phase
+    const int C = FMT == kFmtT1 ? (klen + 79) / 80 : klen >> 6;
     const int S = (C + 3) >> 2;                    // 256-k super-chunks
     const int J = S > wave ? (S - wave + 3) >> 2 : 0;
     const int Q = ntiles * J;                      // loads per lane in this phase
-    const uint32_t kb0 = (uint32_t)k0 >> 2;        // phase start within a packed row
-    const int K16 = klen >> 4;
+    const uint32_t kb0 = FMT == kFmtT1 ? (uint32_t)k0 / 5u   // phase start within a packed row
+                                       : (uint32_t)k0 >> 2;
+    const int K16 = klen >> 4;                     // 16-k groups of activations
+    const int K16s = FMT == kFmtT1 ? 5 * C : K16;  // groups staged (T1: zeros past klen)
 
     // 1. first activation loads of this phase, then the first weight loads.
     // int8 activations come in pieces (token t, 4096-k block j): lane tid loads
     // 16-byte group c = 256 j + tid of the piece (zeros past the phase); the piece
     // counters are uniform, so no per-lane division is needed
-    const int J16 = (K16 + 255) >> 8;              // blocks per token
+    const int J16 = (K16s + 255) >> 8;             // blocks per token
     uint4 xv[kStageBatch];
     const auto xr = make_rsrc(pro.xq, (uint32_t)M * (uint32_t)K);
     int lt = 0, lj = 0;                            // next piece to load
@@ -340,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
           const int c = 256 * sj + tid;
-          store_transposed((st < M && c < K16) ? xs + st * stride + 16 * c : zero, xv[b]);
+          store_group<FMT>((st < M && c < K16s) ? xs + st * stride + 16 * c : zero, xv[b]);
           if (++sj == J16) {
             sj = 0;
             ++st;
@@ -391,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
       };
       // absmax of the token over its G threads (G >= 64: one token per wave); the
       // held groups keep their values for the quantise pass
-      const int nb = (K16 + G - 1) >> lgG;       // groups per thread, uniform
+      const int nb = (K16s + G - 1) >> lgG;      // groups per thread, uniform
       float amax = 0.0f;
       double ss = 0.0;
       float qh[kHold][16];
@@ -435,9 +513,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
       auto put = [&](int c, const float* v) {
         const uint4 q = make_uint4(quant4(v, s_t), quant4(v + 4, s_t), quant4(v + 8, s_t),
                                    quant4(v + 12, s_t));
-        const bool in = tk < M && c < K16;
-        if (in && blockIdx.x == 0) reinterpret_cast<uint4*>(a.xq_out + (size_t)tk * K)[c] = q;
-        store_transposed(in ? xs + tk * stride + 16 * c : zero, q);
+        if (tk < M && c < K16 && blockIdx.x == 0)
+          reinterpret_cast<uint4*>(a.xq_out + (size_t)tk * K)[c] = q;
+        store_group<FMT>(tk < M && c < K16s ? xs + tk * stride + 16 * c : zero, q);
       };
 #pragma unroll
       for (int b = 0; b < kHold; ++b) put(jg + G * b, qh[b]);
@@ -458,23 +536,38 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     for (int q0 = 0; q0 < Q; q0 += R) {
 #pragma unroll
       for (int u = 0; u < R; ++u) {
-        // unpack the whole chunk before refilling its slot, so the refill can land
-        // in the same registers (no loop-carried copy that would wait for the load)
-        v4i a0 = unpack_weights_transposed(ring[u].x);
-        v4i a1 = unpack_weights_transposed(ring[u].y);
-        v4i a2 = unpack_weights_transposed(ring[u].z);
-        v4i a3 = unpack_weights_transposed(ring[u].w);
-        // the empty asm takes the unpacked operands and orders memory reads after
-        // itself, so the scheduler cannot hoist the refill above the unpack
-        asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)::"memory");
-        ring[u] = next_load();
         const int c = 4 * (wave + 4 * jc) + g;
-        const int bb = (bt >= 0 && c < C) ? bt + 64 * c : M * stride;
-        const v4i* bp = reinterpret_cast<const v4i*>(xs + bb);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bp[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bp[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, bp[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, bp[3], acc, 0, 0, 0);
+        if constexpr (FMT == kFmtT1) {
+          v4i t[5];
+          unpack_t1(ring[u], t);
+          v4i a0 = t[0], a1 = t[1], a2 = t[2], a3 = t[3], a4 = t[4];
+          asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4)::"memory");
+          ring[u] = next_load();
+          const int bb = (bt >= 0 && c < C) ? bt + 80 * c : M * stride;
+          const v4i* bp = reinterpret_cast<const v4i*>(xs + bb);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bp[0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bp[1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, bp[2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, bp[3], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a4, bp[4], acc, 0, 0, 0);
+        } else {
+          // unpack the whole chunk before refilling its slot, so the refill can land
+          // in the same registers (no loop-carried copy that would wait for the load)
+          v4i a0 = unpack_weights_transposed(ring[u].x);
+          v4i a1 = unpack_weights_transposed(ring[u].y);
+          v4i a2 = unpack_weights_transposed(ring[u].z);
+          v4i a3 = unpack_weights_transposed(ring[u].w);
+          // the empty asm takes the unpacked operands and orders memory reads after
+          // itself, so the scheduler cannot hoist the refill above the unpack
+          asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)::"memory");
+          ring[u] = next_load();
+          const int bb = (bt >= 0 && c < C) ? bt + 64 * c : M * stride;
+          const v4i* bp = reinterpret_cast<const v4i*>(xs + bb);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bp[0], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bp[1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, bp[2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, bp[3], acc, 0, 0, 0);
+        }
         if (++jc == J) {
           // D layout: the lane holds rows 4g..4g+3 of the tile for token r
           if (tc < ntiles && r < M) {
@@ -514,25 +607,27 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   }
 }
 
-// Kernel for activation mode XMODE and ring depth 4, 8 or 16 (smallest >= R).
-template <int XMODE>
+// Kernel for activation mode XMODE, weight format FMT and ring depth 4, 8 or 16
+// (smallest >= R).
+template <int XMODE, int FMT>
 const void* ring_kernel(int R) {
-  if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4>);
-  if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8>);
-  return reinterpret_cast<const void*>(gemv_kernel<XMODE, 16>);
+  if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT>);
+  if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8, FMT>);
+  return reinterpret_cast<const void*>(gemv_kernel<XMODE, 16, FMT>);
 }
 
+template <int FMT>
 const void* select_kernel(int xmode, int R) {
   switch (xmode) {
-    case 0: return ring_kernel<0>(R);
-    case 1: return ring_kernel<1>(R);
-    case 2: return ring_kernel<2>(R);
-    case 3: return ring_kernel<3>(R);
-    case 4: return ring_kernel<4>(R);
-    case 5: return ring_kernel<5>(R);
-    case 6: return ring_kernel<6>(R);
-    case 7: return ring_kernel<7>(R);
-    default: return ring_kernel<8>(R);
+    case 0: return ring_kernel<0, FMT>(R);
+    case 1: return ring_kernel<1, FMT>(R);
+    case 2: return ring_kernel<2, FMT>(R);
+    case 3: return ring_kernel<3, FMT>(R);
+    case 4: return ring_kernel<4, FMT>(R);
+    case 5: return ring_kernel<5, FMT>(R);
+    case 6: return ring_kernel<6, FMT>(R);
+    case 7: return ring_kernel<7, FMT>(R);
+    default: return ring_kernel<8, FMT>(R);
   }
 }
 
@@ -550,18 +645,19 @@ int device_cus() {
 
 }  // namespace
 
-bool gemv_fits(int64_t M, int64_t K) {
-  return M >= 1 && M <= kMaxM && K >= 64 && (K % 64) == 0;
+bool gemv_fits(int64_t M, int64_t K, int fmt) {
+  return M >= 1 && M <= kMaxM &&
+         (fmt == kFmtT1 ? K >= 16 && (K % 16) == 0 : K >= 64 && (K % 64) == 0);
 }
 
-bool gemv_fused_fits(int64_t M, int64_t K) {
-  return gemv_fits(M, K) && M <= kMaxFusedM && phase_k((int)M, (int)K) == K;
+bool gemv_fused_fits(int64_t M, int64_t K, int fmt) {
+  return gemv_fits(M, K, fmt) && M <= kMaxFusedM && phase_k((int)M, (int)K, fmt) == K;
 }
 
-hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s) {
+hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
   const bool fused = a.xf != nullptr;
-  if (a.count < 1 || a.count > kMaxGroup || !gemv_fits(a.M, a.K) ||
-      (fused && !gemv_fused_fits(a.M, a.K)))
+  if (a.count < 1 || a.count > kMaxGroup || (fmt != kFmt2 && fmt != kFmtT1) ||
+      !gemv_fits(a.M, a.K, fmt) || (fused && !gemv_fused_fits(a.M, a.K, fmt)))
     return hipErrorInvalidValue;
   if ((a.xup != nullptr || a.gnorm != nullptr) && !fused) return hipErrorInvalidValue;
   const int xmode = !fused ? 0
@@ -571,8 +667,10 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s) {
   for (int j = 0; j < a.count; ++j) total_tiles += tiles[j] = (a.n[j] + 15) / 16;
   if (total_tiles == 0) return hipSuccess;
   // loads per lane of one tile in the first phase (the busiest wave)
-  const int kx = phase_k(a.M, a.K);
-  const int per_tile = ((kx / 64 + 3) / 4 + 3) / 4;
+  const int kx = phase_k(a.M, a.K, fmt);
+  const int chunks = fmt == kFmtT1 ? (kx + 79) / 80 : kx / 64;
+  const int per_tile = ((chunks + 3) / 4 + 3) / 4;
+  const int64_t row_bytes = fmt == kFmtT1 ? 16 * ((a.K + 79) / 80) : a.K / 4;
   // Two regimes (measured on the decode shapes): a launch of at most
   // kLatencyBytes of packed weights gives every tile its own workgroup, so all
   // loads issue at once; a larger one is spread as kWgsPerCu workgroups per
@@ -586,7 +684,7 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s) {
     return w;
   };
   int tpw = 1;
-  if ((int64_t)total_tiles * 16 * (a.K / 4) > kLatencyBytes) {
+  if ((int64_t)total_tiles * 16 * row_bytes > kLatencyBytes) {
     for (int k = kWgsPerCu;; ++k) {
       tpw = (total_tiles + cus * k - 1) / (cus * k);
       if (tpw <= kMaxTiles) break;
@@ -596,8 +694,9 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, hipStream_t s) {
   int ring = 4;
   while (ring < 16 && 2 * ring * 4 * wgs <= kFlightLoads) ring *= 2;
   if (ring > tpw * per_tile) ring = tpw * per_tile;
-  const void* kernel = select_kernel(xmode, ring);
-  const size_t lds = (size_t)lds_bytes(tpw, a.M, a.K);
+  const void* kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring)
+                                     : select_kernel<kFmt2>(xmode, ring);
+  const size_t lds = (size_t)lds_bytes(tpw, a.M, a.K, fmt);
   a.tiles_per_wg = tpw;
   a.kx = kx;
   a.phases = (a.K + kx - 1) / kx;

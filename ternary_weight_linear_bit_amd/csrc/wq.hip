@@ -13,6 +13,13 @@
 // exact and order-free).  Pass 2 (one thread) forms the exact sum in a 320-bit
 // integer, divides by N*K and rounds once to fp32.  Pass 3 ternarises and packs.
 //
+// T1 output (five codes per byte, a reading of the same pages' log2(3) ~ 1.58
+// bits per weight): the codes c = q + 1 of the weights 80 b + 16 j + i of a row
+// form the base-3 value v = sum_j c_j 3^j of byte i of block b, stored as the
+// fixed-point fraction ceil(256 v / 243); rows are padded with q = 0 to whole
+// 80-weight blocks of 16 bytes.  wq_pack_t1 writes it from the master weights,
+// repack_t1 from the 2-bit layout.
+//
 // Workspace layout (device, caller-owned, >= kWsBytes):
 //   [0, 2048)    uint64 buckets[256]   (bucket 255 counts Inf/NaN weights)
 //   [2048, 2052) float  threshold      (see wq_finish)
@@ -224,6 +231,116 @@ __global__ __launch_bounds__(kPackThreads) void wq_pack(const void* __restrict__
   }
 }
 
+// Byte of the T1 layout for the codes c[0..4] of digits 0..4.
+__device__ __forceinline__ uint32_t t1_byte(const uint32_t c[5]) {
+  const uint32_t v = c[0] + 3u * c[1] + 9u * c[2] + 27u * c[3] + 81u * c[4];
+  return (256u * v + 242u) / 243u;  // ceil(256 v / 243)
+}
+
+// 16 bytes (one block) from the codes of its five 16-weight digit groups: group j
+// holds the codes of weights 16 j .. 16 j + 15 in bit pairs 2i..2i+1.
+__device__ __forceinline__ uint4 t1_block(const uint32_t grp[5]) {
+  uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t c[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) c[j] = (grp[j] >> (2 * i)) & 3u;
+    o[i >> 2] |= t1_byte(c) << (8 * (i & 3));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Pass 3 for the T1 layout: one thread per 16-byte block (row n, block b).
+// vec: K % 16 == 0 and a 16-byte aligned base, so each digit group is four (fp32)
+// or two (bf16) 16-byte loads, entirely inside or past the row.
+template <bool BF16>
+__global__ __launch_bounds__(kPackThreads) void wq_pack_t1(const void* __restrict__ w, int64_t N,
+                                                           int64_t K, bool vec,
+                                                           const float* __restrict__ thr_p,
+                                                           uint4* __restrict__ out) {
+  const float thr = *thr_p;
+  const int64_t nb = (K + 79) / 80;
+  const int64_t total = N * nb;
+  const int64_t stride = (int64_t)gridDim.x * kPackThreads;
+  for (int64_t t = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; t < total; t += stride) {
+    const int64_t n = t / nb, b = t - n * nb;
+    uint32_t grp[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int64_t k0 = 80 * b + 16 * j;
+      uint32_t word = 0u;
+      if (vec && k0 < K) {
+        uint32_t bits[16];
+        if (BF16) {
+          const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(w) +
+                                                          n * K + k0);
+          const uint4 x0 = p[0], x1 = p[1];
+          const uint32_t d[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            bits[2 * h] = d[h] << 16;
+            bits[2 * h + 1] = d[h] & 0xffff0000u;
+          }
+        } else {
+          const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(w) +
+                                                          n * K + k0);
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint4 x = p[h];
+            bits[4 * h] = x.x;
+            bits[4 * h + 1] = x.y;
+            bits[4 * h + 2] = x.z;
+            bits[4 * h + 3] = x.w;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) word |= code_of<BF16>(bits[i], thr) << (2 * i);
+      } else {
+        for (int i = 0; i < 16; ++i) {
+          const int64_t k = k0 + i;
+          const uint32_t c = k < K ? code_of<BF16>(load_bits<BF16>(w, n * K + k), thr) : 1u;
+          word |= c << (2 * i);
+        }
+      }
+      grp[j] = word;
+    }
+    out[t] = t1_block(grp);
+  }
+}
+
+// 2-bit layout -> T1, one thread per 16-byte block.  vec: K % 16 == 0 and a
+// 4-byte aligned input, so each digit group is one packed dword.
+__global__ __launch_bounds__(kPackThreads) void repack_t1(const uint8_t* __restrict__ in,
+                                                          int64_t N, int64_t K, bool vec,
+                                                          uint4* __restrict__ out) {
+  const int64_t nb = (K + 79) / 80;
+  const int64_t total = N * nb;
+  const int64_t rowb = K / 4;
+  const int64_t stride = (int64_t)gridDim.x * kPackThreads;
+  for (int64_t t = (int64_t)blockIdx.x * kPackThreads + threadIdx.x; t < total; t += stride) {
+    const int64_t n = t / nb, b = t - n * nb;
+    uint32_t grp[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int64_t k0 = 80 * b + 16 * j;
+      uint32_t word = 0x55555555u;  // padding: code 1
+      if (vec && k0 < K) {
+        word = reinterpret_cast<const uint32_t*>(in + n * rowb)[k0 / 16];
+      } else if (k0 < K) {
+        for (int i = 0; i < 16; i += 4) {
+          if (k0 + i < K) {
+            const uint32_t byte = in[n * rowb + (k0 + i) / 4];
+            word = (word & ~(0xffu << (2 * i))) | (byte << (2 * i));
+          }
+        }
+      }
+      grp[j] = word;
+    }
+    out[t] = t1_block(grp);
+  }
+}
+
 int grid_for(int64_t work_items, int threads, int max_blocks) {
   int64_t b = (work_items + threads - 1) / threads;
   if (b < 1) b = 1;
@@ -231,17 +348,16 @@ int grid_for(int64_t work_items, int threads, int max_blocks) {
   return (int)b;
 }
 
-}  // namespace
-
-hipError_t launch_wq(const void* w, bool w_bf16, int64_t n, uint8_t* w_packed, float* w_scale,
-                     void* workspace, hipStream_t s) {
+// Passes 1 and 2: gamma* into w_scale and the ternarisation threshold into the
+// workspace.  Returns the threshold's device address.
+float* launch_scale(const void* w, bool w_bf16, int64_t n, float* w_scale, void* workspace,
+                    hipStream_t s) {
   auto* buckets = reinterpret_cast<unsigned long long*>(workspace);
   float* thr = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + 2048);
   hipLaunchKernelGGL(wq_clear, dim3(1), dim3(256), 0, s, buckets);
   // 16-byte vector loads need a 16-byte aligned base; otherwise every element
-  // takes the scalar loop.  Packed dword stores need a 4-byte aligned output.
+  // takes the scalar loop.
   const bool w_vec = ((uintptr_t)w & 15u) == 0;
-  const bool pack_vec = w_vec && (((uintptr_t)w_packed & 3u) == 0);
   const int64_t per = w_bf16 ? 8 : 4;
   const int hist_blocks = grid_for(n / per + 1, kHistThreads, 2048);
   if (w_bf16)
@@ -252,6 +368,16 @@ hipError_t launch_wq(const void* w, bool w_bf16, int64_t n, uint8_t* w_packed, f
                        buckets);
   hipLaunchKernelGGL(wq_finish, dim3(1), dim3(64), 0, s, buckets, (unsigned long long)n, w_scale,
                      thr);
+  return thr;
+}
+
+}  // namespace
+
+hipError_t launch_wq(const void* w, bool w_bf16, int64_t n, uint8_t* w_packed, float* w_scale,
+                     void* workspace, hipStream_t s) {
+  const float* thr = launch_scale(w, w_bf16, n, w_scale, workspace, s);
+  // Packed dword stores need a 4-byte aligned output.
+  const bool pack_vec = (((uintptr_t)w & 15u) == 0) && (((uintptr_t)w_packed & 3u) == 0);
   const int pack_blocks = grid_for(n / 16 + 1, kPackThreads, 8192);
   if (w_bf16)
     hipLaunchKernelGGL(wq_pack<true>, dim3(pack_blocks), dim3(kPackThreads), 0, s, w, n,
@@ -259,6 +385,30 @@ hipError_t launch_wq(const void* w, bool w_bf16, int64_t n, uint8_t* w_packed, f
   else
     hipLaunchKernelGGL(wq_pack<false>, dim3(pack_blocks), dim3(kPackThreads), 0, s, w, n,
                        pack_vec, thr, w_packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_wq_t1(const void* w, bool w_bf16, int64_t N, int64_t K, uint8_t* w_t1,
+                        float* w_scale, void* workspace, hipStream_t s) {
+  const float* thr = launch_scale(w, w_bf16, N * K, w_scale, workspace, s);
+  const bool vec = (((uintptr_t)w & 15u) == 0) && (K % 16) == 0;
+  const int blocks = grid_for(N * ((K + 79) / 80), kPackThreads, 8192);
+  auto* out = reinterpret_cast<uint4*>(w_t1);
+  if (w_bf16)
+    hipLaunchKernelGGL(wq_pack_t1<true>, dim3(blocks), dim3(kPackThreads), 0, s, w, N, K, vec,
+                       thr, out);
+  else
+    hipLaunchKernelGGL(wq_pack_t1<false>, dim3(blocks), dim3(kPackThreads), 0, s, w, N, K, vec,
+                       thr, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_t1(const uint8_t* w_packed, int64_t N, int64_t K, uint8_t* w_t1,
+                            hipStream_t s) {
+  const bool vec = (((uintptr_t)w_packed & 3u) == 0) && (K % 16) == 0;
+  const int blocks = grid_for(N * ((K + 79) / 80), kPackThreads, 8192);
+  hipLaunchKernelGGL(repack_t1, dim3(blocks), dim3(kPackThreads), 0, s, w_packed, N, K, vec,
+                     reinterpret_cast<uint4*>(w_t1));
   return hipGetLastError();
 }
 

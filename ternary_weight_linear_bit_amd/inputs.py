@@ -68,5 +68,9 @@ WORKLOADS = {
 }
 
 
-def packed_bytes(layer_shapes) -> int:
+def packed_bytes(layer_shapes, fmt: str = "2bit") -> int:
+    """Packed weight bytes of one layer: N*K/4 (2 bits per weight) or
+    N*16*ceil(K/80) (five weights per byte)."""
+    if fmt == "t1":
+        return sum(n * 16 * ((k + 79) // 80) for _, k, n in layer_shapes)
     return sum(n * k // 4 for _, k, n in layer_shapes)

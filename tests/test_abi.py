@@ -124,3 +124,36 @@ def test_prologue_validation(lib):
     assert f(mats, 1, FAKE, 0, ctypes.byref(P(None, 0x10000, float("inf"))), 1, 8, FAKE, FAKE, 0,
              None) == ESHAPE
     assert f(mats, 1, FAKE, 7, ctypes.byref(P(None, 0x10000, 1e-5)), 1, 8, FAKE, FAKE, 0, None) == EDTYPE
+
+
+def test_t1_sizes_and_validation(lib):
+    assert lib.bitnet_t1_packed_bytes(2560, 6912) == 2560 * 16 * 87
+    assert lib.bitnet_t1_packed_bytes(3, 80) == 48
+    assert lib.bitnet_t1_packed_bytes(3, 1) == 48
+    assert lib.bitnet_t1_packed_bytes(-1, 80) == 0
+    q = lib.bitnet_quantize_weights_t1
+    assert q(None, 0, 4, 8, FAKE, FAKE, FAKE, 4096, None) == ENULL
+    assert q(FAKE, 9, 4, 8, FAKE, FAKE, FAKE, 4096, None) == EDTYPE
+    assert q(FAKE, 0, 4, 0, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
+    assert q(FAKE, 0, 4, 8, FAKE, FAKE, FAKE, 16, None) == EWS
+    assert q(FAKE, 0, 4, 8, FAKE_ODD, FAKE, FAKE, 4096, None) == EALIGN
+    r = lib.bitnet_repack_t1
+    assert r(None, 4, 8, FAKE, None) == ENULL
+    assert r(FAKE, 4, 6, FAKE, None) == ESHAPE
+    assert r(FAKE, -1, 8, FAKE, None) == ESHAPE
+    assert r(FAKE, 4, 8, FAKE_ODD, None) == EALIGN
+    assert r(FAKE, 0, 8, FAKE, None) == OK            # N == 0: nothing to do
+    m = (N.BitnetMatrix * 1)(N.BitnetMatrix(0x10000, 0x10000, 8, 0x10000, 0))
+    modd = (N.BitnetMatrix * 1)(N.BitnetMatrix(0x10002, 0x10000, 8, 0x10000, 0))
+    t = lib.bitnet_ternary_linear_t1
+    assert t(m, 1, FAKE, FAKE, 1, 100, 0, None) == ESHAPE    # K % 16 != 0
+    assert t(m, 1, FAKE, FAKE, 1, 0, 0, None) == ESHAPE      # K < 16
+    assert t(modd, 1, FAKE, FAKE, 1, 96, 0, None) == EALIGN  # weights not 16-byte aligned
+    assert t(m, 1, FAKE_ODD, FAKE, 1, 96, 0, None) == EALIGN
+    assert t(m, 1, None, FAKE, 1, 96, 0, None) == ENULL
+    assert t(m, 1, FAKE, FAKE, 0, 96, 0, None) == OK         # M == 0: nothing to do
+    f = lib.bitnet_quant_linear_t1
+    assert f(m, 1, FAKE, 0, None, 1, 100, FAKE, FAKE, 0, None) == ESHAPE
+    assert f(m, 1, FAKE, 7, None, 1, 96, FAKE, FAKE, 0, None) == EDTYPE
+    assert f(modd, 1, FAKE, 0, None, 1, 96, FAKE, FAKE, 0, None) == EALIGN
+    assert f(m, 1, FAKE, 0, None, 0, 96, FAKE, FAKE, 0, None) == OK

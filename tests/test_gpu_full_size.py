@@ -64,3 +64,37 @@ def test_full_size(k, n, ms):
         np.testing.assert_array_equal(f32_bits(y_h[mi, ni]), f32_bits(y_w))
     del packed_d
     torch.cuda.empty_cache()
+
+
+# The T1 layout (five weights per byte) at the decode shapes of the bench's T1 legs,
+# through the fused act-quant call the bench times (2B: bf16 input; 100B: fp32)
+FULL_T1 = [(2560, 2560, "bf16"), (2560, 6912, "bf16"), (6912, 2560, "bf16"),
+           (8192, 8192, "f32"), (8192, 28672, "f32"), (28672, 8192, "f32")]
+
+
+@pytest.mark.parametrize("k,n,dt", FULL_T1, ids=[f"t1-{k}x{n}" for k, n, _ in FULL_T1])
+def test_full_size_t1(k, n, dt):
+    print(f"full-size T1 K={k} N={n}", flush=True)
+    w = I.master_weights(n, k, I.weight_seed(1, (k * 7 + n) % 7))
+    p_d, s_d = N.bitnet_quantize_weights_t1(torch.from_numpy(w).to(DEV))
+    p_o, gamma = O.quantize_weights_t1(w)
+    del w
+    assert f32_bits(host(s_d))[0] == f32_bits(gamma)
+    np.testing.assert_array_equal(host(p_d), p_o)
+    x = I.activations(1, k, I.ACT_SEED + 1)
+    if dt == "bf16":
+        xt = I.to_bf16(x).to(DEV)
+        x = xt.float().cpu().numpy()
+    else:
+        xt = torch.from_numpy(x).to(DEV)
+    acc_d = torch.empty((1, n), dtype=torch.int32, device=DEV)
+    (y_d,), xq_d, xs_d = N.bitnet_quant_linear_t1([(p_d, s_d, None, acc_d)], xt)
+    xq, d = O.quantize_acts(x)
+    np.testing.assert_array_equal(host(xq_d), xq)
+    np.testing.assert_array_equal(f32_bits(host(xs_d)), f32_bits(d))
+    ni = np.arange(n)
+    acc_w, y_w = O.ternary_linear_t1_at(p_o, gamma, xq, d, np.zeros(n, np.int64), ni)
+    np.testing.assert_array_equal(host(acc_d)[0], acc_w)
+    np.testing.assert_array_equal(f32_bits(host(y_d)[0]), f32_bits(y_w))
+    del p_d
+    torch.cuda.empty_cache()
