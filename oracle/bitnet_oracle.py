@@ -56,6 +56,16 @@ N3  normalise-then-quantise: r is a positive per-token factor and absmax
     v * w (fp32 products) with O4 and folds r into the token scale:
     xq = O4(v * w).xq, d = RN32(O4(v * w).d * r).
 
+Lookup-table contraction ([JJ] juejin.cn, "微软 BitNet：让百亿参数大模型在 CPU
+上飞起来", technical principles, item 2 "查表法优化": bitnet.cpp's kernels use
+T-MAC's lookup-table method, turning the matrix product into table lookups;
+[DT] section 3.2 names the lookup-table kernel types TL1 and TL2):
+L1  per token, every pair of activations (x[2g], x[2g+1]) gets a table of 16
+    partial sums T[g][c0 + 4*c1] = (c0 - 1)*x[2g] + (c1 - 1)*x[2g+1] over the
+    2-bit codes c0, c1 in 0..3, so a nibble of the 2-bit layout (two weights)
+    is the index; acc[m, n] = sum_g T[m][g][nibble g of row n].  The method
+    reaches the same integers as O5.
+
 Denser packing ([OV] introduction and section 2: a ternary weight carries
 log2(3) ~ 1.58 bits of information; [CM] comparison table: 0.4 GB of
 non-embedding memory for the 2B model, i.e. about 1.6 bits per weight):
@@ -487,6 +497,41 @@ def ternary_linear_t1_at(packed: np.ndarray, gamma: np.float32, xq: np.ndarray,
     acc = (q_rows * x_rows).sum(axis=1).astype(np.int32)
     scale = (F32(gamma) * np.asarray(d, dtype=np.float32)[m_idx]).astype(np.float32)
     return acc, acc.astype(np.float32) * scale
+
+
+# ---------------------------------------------------------------------------
+# L1: lookup-table contraction
+# ---------------------------------------------------------------------------
+
+def lut_tables(xq: np.ndarray) -> np.ndarray:
+    """L1 tables: int64 [M, K/2, 16], entry c0 + 4*c1 of pair g of token m is
+    (c0 - 1) * xq[m, 2g] + (c1 - 1) * xq[m, 2g + 1].  K must be even."""
+    x = np.asarray(xq, dtype=np.int64)
+    if x.shape[1] % 2:
+        raise ValueError("K must be even")
+    idx = np.arange(16)
+    q0 = (idx & 3) - 1
+    q1 = (idx >> 2) - 1
+    return q0[None, None, :] * x[:, 0::2, None] + q1[None, None, :] * x[:, 1::2, None]
+
+
+def lut_linear(packed: np.ndarray, gamma: np.float32, xq: np.ndarray, d: np.ndarray):
+    """The layer by table lookup (L1): one lookup per nibble (pair of weights) of
+    the 2-bit layout.  Returns (acc int32 [M, N], y fp32 [M, N])."""
+    p = np.asarray(packed, dtype=np.uint8)
+    n_rows, kb = p.shape
+    nib = np.empty((n_rows, 2 * kb), dtype=np.int64)
+    nib[:, 0::2] = p & 15          # weights 4j, 4j+1 -> pair 2j
+    nib[:, 1::2] = p >> 4          # weights 4j+2, 4j+3 -> pair 2j+1
+    tables = lut_tables(xq)
+    acc = np.empty((tables.shape[0], n_rows), dtype=np.int64)
+    pairs = np.arange(2 * kb)
+    for m in range(tables.shape[0]):
+        acc[m] = tables[m][pairs[None, :], nib].sum(axis=1)
+    if acc.size and np.abs(acc).max() >= 2 ** 31:
+        raise OverflowError("accumulator leaves the int32 range")
+    acc = acc.astype(np.int32)
+    return acc, dequantize(acc, gamma, d)
 
 
 def quant_linear(packed: np.ndarray, gamma: np.float32, x: np.ndarray):

@@ -24,3 +24,10 @@ def t1_golden():
     import json
     with open(os.path.join(ROOT, "tests", "golden", "t1_layout.json")) as f:
         return json.load(f)
+
+
+@pytest.fixture(scope="session")
+def lut_golden():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "lut_table.json")) as f:
+        return json.load(f)

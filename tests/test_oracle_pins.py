@@ -680,3 +680,46 @@ def test_t1_size_matches_page_figure(t1_golden):
     assert round(s["stack_bytes"] / 1e9, 1) == s["page_figure_gb"]
     assert round(s["stack_bytes_2bit"] / 1e9, 1) != s["page_figure_gb"]
     assert O.pack_t1(np.zeros((2, 6912), np.int8)).shape == (2, O.t1_row_bytes(6912))
+
+
+# ---------------------------------------------------------------------------
+# L1: lookup-table contraction
+# ---------------------------------------------------------------------------
+
+def test_lut_golden_tables(lut_golden):
+    """Hand-worked table entries (catches swapped code roles, a missing offset)."""
+    for case in lut_golden["cases"]:
+        t = O.lut_tables(np.array([case["x"]], np.int8))[0, 0]
+        for i, v in case["entries"].items():
+            assert int(t[int(i)]) == v, (case["x"], i)
+    ex = lut_golden["row_example"]
+    acc, _ = O.lut_linear(np.array([[ex["packed_byte"]]], np.uint8), np.float32(1.0),
+                          np.array([ex["x"]], np.int8), np.ones(1, np.float32))
+    assert int(acc[0, 0]) == ex["acc"]
+
+
+def test_lut_entries_are_sum_pos_minus_sum_neg():
+    """Every valid nibble of every random pair: the entry is the pages' form
+    (sum under +1 weights minus sum under -1 weights) of the two weights."""
+    rng = np.random.Generator(np.random.PCG64(61))
+    x = rng.integers(-127, 128, (1, 64)).astype(np.int8)
+    t = O.lut_tables(x)[0]
+    for g in range(32):
+        for c0 in range(3):
+            for c1 in range(3):
+                q = np.array([c0 - 1, c1 - 1])
+                assert t[g, c0 + 4 * c1] == O.sum_pos_minus_sum_neg(q, x[0, 2 * g:2 * g + 2])
+
+
+def test_lut_linear_equals_integer_matmul():
+    """The table method reaches the pinned contraction exactly (acc and y)."""
+    rng = np.random.Generator(np.random.PCG64(62))
+    for m, n, k in ((1, 33, 64), (3, 17, 256), (2, 5, 8)):
+        q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+        xq = rng.integers(-127, 128, (m, k)).astype(np.int8)
+        d = rng.uniform(0.001, 0.05, m).astype(np.float32)
+        p = O.pack_codes(q)
+        acc, y = O.lut_linear(p, np.float32(0.021), xq, d)
+        acc_w, y_w = O.ternary_linear(p, np.float32(0.021), xq, d)
+        np.testing.assert_array_equal(acc, acc_w)
+        np.testing.assert_array_equal(y.view(np.uint32), y_w.view(np.uint32))
