@@ -23,8 +23,9 @@ into the launches), the 8B-shaped stack (32 layers) at M = 1 and M = 16, the
 100B-class decode stack (96 layers, 23.35 GB packed, fp32 activations), the
 prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096 and on the
 8B shapes at M = 2048, the 2B and 100B chains with weights packed five per byte
-(T1 layout, 1.6 bits per weight), and the CPU oracle timed on a bounded sample
-of the same decode workload.
+(T1 layout, 1.6 bits per weight), single matrices at M = 1 through the
+matrix-core kernel (2-bit and T1 weights) and the lookup-table path, and the CPU
+oracle timed on a bounded sample of the same decode workload.
 """
 
 from __future__ import annotations
@@ -81,6 +82,8 @@ def parse():
                    help="skip the full-layer 2B chain and the 8B-shaped chains")
     p.add_argument("--no-t1", action="store_true",
                    help="skip the legs with weights packed five per byte")
+    p.add_argument("--no-compare", action="store_true",
+                   help="skip the single-matrix comparison of the decode kernels")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this size (PMC calibration)")
@@ -277,6 +280,59 @@ def prefill(torch, N, I, layer_shapes, ms, steps):
     return res
 
 
+def kernel_compare(torch, N, I, shapes, steps):
+    """Single matrices at M = 1: the matrix-core decode kernel on 2-bit weights,
+    on T1 weights (five per byte), and the lookup-table path (three launches per
+    token), each replayed from a HIP graph over >= 1 GiB of weight copies."""
+    res = {}
+    for k, n in shapes:
+        g = torch.Generator(device="cuda").manual_seed(I.weight_seed(0, 0))
+        w = torch.randn((n, k), generator=g, device="cuda").mul_(I.WEIGHT_SIGMA)
+        p2, sc = N.bitnet_quantize_weights(w)
+        del w
+        x = torch.randn((1, k), generator=torch.Generator(device="cuda").manual_seed(I.ACT_SEED),
+                        device="cuda").to(torch.bfloat16)
+        xq, xs = N.bitnet_quantize_acts(x)
+        y = torch.empty((1, n), device="cuda")
+        ws = torch.empty(N.lib().bitnet_lut_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+        row = {}
+        for path in ("mfma_2bit", "mfma_t1", "lut_2bit"):
+            base = N.bitnet_repack_t1(p2) if path == "mfma_t1" else p2
+            nbytes = base.numel()
+            copies = max(2, math.ceil(CACHE_CYCLE_BYTES / nbytes))
+            mats = [base.clone() for _ in range(copies)]
+
+            def run():
+                for c in range(copies):
+                    if path == "mfma_2bit":
+                        N.bitnet_ternary_linear(mats[c], sc, xq, xs, y=y)
+                    elif path == "mfma_t1":
+                        N.bitnet_ternary_linear_t1([(mats[c], sc, y)], xq, xs)
+                    else:
+                        N.bitnet_ternary_linear_lut(mats[c], sc, xq, xs, y=y, workspace=ws)
+            run()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                run()
+            gr.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (steps * copies)
+            row[path] = {"us": round(us, 2), "packed_gbs": round(nbytes / us / 1e3, 1),
+                         "weights_per_s_G": round(n * k / us / 1e3, 1)}
+            del gr, mats
+            torch.cuda.empty_cache()
+        res[f"{k}->{n}"] = row
+        log(f"compare {k}->{n}: {row}")
+    return res
+
+
 def cpu_baseline(I, layer_shapes, seconds):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     whole 2B-shaped layers at M = 1 (act-quant + layer per matrix)."""
@@ -377,6 +433,10 @@ def main():
             result["decode_100b_t1"] = dict(
                 workload="ternary100b-decode-m1-96L, weights five per byte (T1 layout)",
                 **leg_summary(d6, 1))
+    if not args.no_compare:
+        result["kernel_compare_m1"] = kernel_compare(
+            torch, N, I, ((2560, 2560), (2560, 6912), (6912, 2560), (8192, 28672), (28672, 8192)),
+            steps=4)
     if not args.no_prefill:
         result["prefill"] = prefill(torch, N, I, wl["layer"], (512, 4096), steps=10)
         result["prefill_8b"] = prefill(torch, N, I, I.LAYER_8B, (2048,), steps=5)

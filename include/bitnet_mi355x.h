@@ -275,6 +275,36 @@ bitnet_status bitnet_quant_linear_t1(const bitnet_matrix *mats, int count, const
                                      int64_t K, int8_t *x_q, float *x_scale, int y_dtype,
                                      hipStream_t stream);
 
+/*
+ * The contraction by table lookup (juejin.cn, "Microsoft BitNet", technical
+ * principles, item 2: bitnet.cpp's kernels use T-MAC's lookup-table method;
+ * dashen-tech, section 3.2: the TL1/TL2 kernel types).  Per token, each pair of
+ * int8 activations gets a table of 16 partial sums, entry c0 + 4*c1 =
+ * (c0 - 1)*x[2g] + (c1 - 1)*x[2g+1], and each nibble of the 2-bit layout (two
+ * weights' codes) indexes it.  Same integers and outputs as
+ * bitnet_ternary_linear; a second kernel family for comparison with the
+ * matrix-core decode kernel.
+ */
+
+/* Bytes of workspace bitnet_ternary_linear_lut needs: 16*K (one token's tables)
+ * plus 4*N (accumulators), each rounded up to 256.  0 for negative sizes. */
+size_t bitnet_lut_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * bitnet_ternary_linear by table lookup.
+ *   w_packed [N][K/4] (2-bit layout), 16-byte aligned; K >= 64, K % 64 == 0.
+ *   workspace >= bitnet_lut_workspace_bytes(N, K) bytes of device memory,
+ *            16-byte aligned; clobbered.
+ *   other arguments as bitnet_ternary_linear.
+ * Tokens run one after another, three launches each (tables, lookups,
+ * rescale), so the weights stream once per token.
+ */
+bitnet_status bitnet_ternary_linear_lut(const uint8_t *w_packed, const float *w_scale,
+                                        const int8_t *x_q, const float *x_scale, int64_t M,
+                                        int64_t N, int64_t K, void *y, int y_dtype,
+                                        int32_t *acc_out, void *workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,10 @@ SIGNATURES["bitnet_quant_linear_t1"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _
                                              ctypes.POINTER(BitnetActPrologue), _I64, _I64, _P,
                                              _P, _I, _P])
 
+SIGNATURES["bitnet_lut_workspace_bytes"] = (_SZ, [_I64, _I64])
+SIGNATURES["bitnet_ternary_linear_lut"] = (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P,
+                                                _SZ, _P])
+
 _lib = None
 
 
@@ -360,3 +364,29 @@ def bitnet_quant_linear_t1(mats, x, x_q=None, x_scale=None, y_dtype=None, stream
         arr, len(mats), _ptr(x), _dtype_code(x.dtype), _prologue(x, up, norm_weight, eps), m, k,
         _ptr(x_q), _ptr(x_scale), _dtype_code(ys[0].dtype), _stream(stream)))
     return ys, x_q, x_scale
+
+
+# ---------------------------------------------------------------------------
+# lookup-table contraction
+# ---------------------------------------------------------------------------
+
+def bitnet_ternary_linear_lut(w_packed, w_scale, x_q, x_scale, y=None, y_dtype=None,
+                              acc_out=None, workspace=None, stream=None):
+    """bitnet_ternary_linear by table lookup: packed W [N, K/4] x int8 X [M, K] -> y."""
+    import torch
+    _need_cuda(w_packed, w_scale, x_q, x_scale, acc_out)
+    m, k = x_q.shape
+    n = w_packed.shape[0]
+    if w_packed.shape[1] * 4 != k:
+        raise ValueError("w_packed and x_q disagree on K")
+    if y is None:
+        y = torch.empty((m, n), dtype=y_dtype or torch.float32, device=x_q.device)
+    ws_bytes = lib().bitnet_lut_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x_q.device)
+    _need_cuda(y, workspace)
+    _check("bitnet_ternary_linear_lut", lib().bitnet_ternary_linear_lut(
+        _ptr(w_packed), _ptr(w_scale), _ptr(x_q), _ptr(x_scale), m, n, k, _ptr(y),
+        _dtype_code(y.dtype), _ptr(acc_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y

@@ -310,6 +310,32 @@ bitnet_status bitnet_quant_linear_t1(const bitnet_matrix* mats, int count, const
                          stream);
 }
 
+size_t bitnet_lut_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0) return 0;
+  return bitnet::lut_workspace_bytes(N, K);
+}
+
+bitnet_status bitnet_ternary_linear_lut(const uint8_t* w_packed, const float* w_scale,
+                                        const int8_t* x_q, const float* x_scale, int64_t M,
+                                        int64_t N, int64_t K, void* y, int y_dtype,
+                                        int32_t* acc_out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(y_dtype)) return BITNET_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 64 || (K % 64) != 0 || K > BITNET_MAX_K || M > kInt32Max ||
+      N > kInt32Max || M * N > ((int64_t)1 << 46))
+    return BITNET_ERR_SHAPE;
+  if (M == 0 || N == 0) return BITNET_OK;
+  if (!w_packed || !w_scale || !x_q || !x_scale || !y) return BITNET_ERR_NULL;
+  if (!workspace || workspace_bytes < bitnet::lut_workspace_bytes(N, K))
+    return BITNET_ERR_WORKSPACE;
+  if (!aligned(w_packed, 16) || !aligned(workspace, 16) || !aligned(w_scale, 4) ||
+      !aligned(x_scale, 4) || !aligned(y, esize(y_dtype)) || (acc_out && !aligned(acc_out, 4)))
+    return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_lut(w_packed, w_scale, x_q, x_scale, M, N, K, y,
+                                     y_dtype == BITNET_BF16, acc_out, workspace,
+                                     bitnet::device_cus(), stream));
+}
+
 bitnet_status bitnet_quantize_acts_ex(const void* x, int x_dtype, const bitnet_act_prologue* pro,
                                       int64_t M, int64_t K, int8_t* x_q, float* x_scale,
                                       hipStream_t stream) {

@@ -209,6 +209,14 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                        const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
                        int32_t* acc_out, hipStream_t s);
+// Lookup-table decode: workspace bytes (tables 16 K + accumulators 4 N, each
+// rounded up to 256) and the launches (three per token).  K % 64 == 0, 16-byte
+// aligned packed weights and workspace.
+size_t lut_workspace_bytes(int64_t N, int64_t K);
+hipError_t launch_lut(const uint8_t* wp, const float* w_scale, const int8_t* xq,
+                      const float* x_scale, int64_t M, int64_t N, int64_t K, void* y,
+                      bool y_bf16, int32_t* acc_out, void* workspace, int cus, hipStream_t s);
+int device_cus();
 hipError_t launch_generic_linear(const uint8_t* wp, const float* w_scale, const int8_t* xq,
                                  const float* x_scale, int64_t M, int64_t N, int64_t K,
                                  void* y, bool y_bf16, int32_t* acc_out, hipStream_t s);

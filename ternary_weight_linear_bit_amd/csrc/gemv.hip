@@ -631,6 +631,9 @@ const void* select_kernel(int xmode, int R) {
   }
 }
 
+
+}  // namespace
+
 // Compute units of the current device (1 if the runtime cannot say).
 int device_cus() {
   int dev = 0, cus = 0;
@@ -642,8 +645,6 @@ int device_cus() {
   }
   return cus;
 }
-
-}  // namespace
 
 bool gemv_fits(int64_t M, int64_t K, int fmt) {
   return M >= 1 && M <= kMaxM &&

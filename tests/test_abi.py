@@ -157,3 +157,20 @@ def test_t1_sizes_and_validation(lib):
     assert f(m, 1, FAKE, 7, None, 1, 96, FAKE, FAKE, 0, None) == EDTYPE
     assert f(modd, 1, FAKE, 0, None, 1, 96, FAKE, FAKE, 0, None) == EALIGN
     assert f(m, 1, FAKE, 0, None, 0, 96, FAKE, FAKE, 0, None) == OK
+
+
+def test_lut_validation(lib):
+    assert lib.bitnet_lut_workspace_bytes(2560, 6912) == 16 * 6912 + 2560 * 4
+    assert lib.bitnet_lut_workspace_bytes(3, 64) == 1024 + 256
+    assert lib.bitnet_lut_workspace_bytes(-1, 64) == 0
+    f = lib.bitnet_ternary_linear_lut
+    ws = lib.bitnet_lut_workspace_bytes(8, 64)
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 9, None, FAKE, ws, None) == EDTYPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 96, FAKE, 0, None, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, -1, 8, 64, FAKE, 0, None, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 8, 64, FAKE, 0, None, FAKE, ws, None) == OK
+    assert f(None, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE, ws, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, None, ws, None) == EWS
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE, ws - 1, None) == EWS
+    assert f(FAKE_ODD, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE, ws, None) == EALIGN
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE_ODD, ws, None) == EALIGN
