@@ -10,10 +10,15 @@
 // accumulators.  K advances in steps of 128:
 //  * activations: the workgroup stages the BM x 128 int8 tile into LDS (double
 //    buffered, one barrier per step), byte-transposed within each 16-byte group;
+//    a wave stages step s + 1 in between its matrix instructions of step s, so
+//    its vector work overlaps its own matrix-core work;
 //  * weights: each wave loads its 64 rows x 128 k of packed codes straight from
-//    global memory (16 bytes per lane) and expands them in registers with the same
-//    shift / mask / byte-lookup as the decode kernel, whose k order matches the
-//    transposed activations, so neither operand needs a per-element shuffle;
+//    global memory (16 bytes per lane) and expands them in registers to the codes
+//    c = q + 1 with one shift and mask per 2-bit field, whose k order matches the
+//    transposed activations, so neither operand needs a per-element shuffle; the
+//    matrix cores sum c * x and the epilogue subtracts each token's sum of x
+//    (four dot-4 instructions per staged 16-byte group), which saves the byte
+//    lookup per field that maps c to q;
 //  * loads run kDepth steps ahead of the matrix cores.
 // Lane (r, h) of a 32 x 32 x 32 operand holds row r and 16 k: with the 16 bytes
 // lane h loads per row (k0 + 64h .. k0 + 64h + 63), MFMA j of a step sums over
@@ -42,16 +47,16 @@ __device__ __forceinline__ int lds_group(int t, int kg) {
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, each with its own L2
 constexpr int kDepth = 2;         // steps of global loads in flight
 
-// Packed dword (16 codes) -> signed int8 operand in the 4x4-byte-transposed k
-// order (byte 4i + b = weight of k-offset 4b + i): mask each 2-bit field and map
-// code c to c - 1 with a byte lookup.
-constexpr uint32_t kCodeLut = 0x000100ffu;
-__device__ __forceinline__ v4i expand_weights(uint32_t w) {
+// Packed dword (16 codes) -> the codes c = q + 1 in {0, 1, 2} as an int8 operand
+// in the 4x4-byte-transposed k order (byte 4i + b = code of k-offset 4b + i): one
+// shift and one mask per 2-bit field.  The matrix cores then sum c * x, and the
+// epilogue subtracts the token's sum of x (q = c - 1).
+__device__ __forceinline__ v4i expand_codes(uint32_t w) {
   v4i a;
-  a.x = (int)__builtin_amdgcn_perm(0u, kCodeLut, w & 0x03030303u);
-  a.y = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 2) & 0x03030303u);
-  a.z = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 4) & 0x03030303u);
-  a.w = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 6) & 0x03030303u);
+  a.x = (int)(w & 0x03030303u);
+  a.y = (int)((w >> 2) & 0x03030303u);
+  a.z = (int)((w >> 4) & 0x03030303u);
+  a.w = (int)((w >> 6) & 0x03030303u);
   return a;
 }
 
@@ -63,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   constexpr int TB = BM / 64;               // 32-token blocks per wave
   constexpr int XG = BM * (BK / 16) / kThreads;  // 16-byte activation groups per thread per step
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * kStride];
+  __shared__ int xsum[BM];                  // per token: sum of its int8 activations
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,75 +109,118 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   // no branch around the loads, whose waits would then sit in a skippable block)
   // (the past-the-end bit is ORed in arithmetically: a select on it is turned
   // into a branch, which also drains every load in flight at the loop top)
-  auto gload = [&](uint4 (&xv)[XG], uint4 (&wv)[2], int s) {
-    const int k0 = s * BK;
+  auto xload = [&](uint4 (&xv)[XG], int s) {
     const uint32_t past = (uint32_t)(s >= steps) << 31;
 #pragma unroll
-    for (int i = 0; i < XG; ++i) xv[i] = bload16(xr, xoff(i, k0) | past);
+    for (int i = 0; i < XG; ++i) xv[i] = bload16(xr, xoff(i, s * BK) | past);
+  };
+  auto wload = [&](uint4 (&wv)[2], int s) {
+    const uint32_t past = (uint32_t)(s >= steps) << 31;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) wv[b] = bload16(wrs, woff(b, k0) | past);
+    for (int b = 0; b < 2; ++b) wv[b] = bload16(wrs, woff(b, s * BK) | past);
   };
 
-  uint4 xv_[kDepth][XG];
-  uint4 wv_[kDepth][2];
+  int rsum[XG] = {};   // partial sums of the activations this thread stages (token g / 8)
+  // stage activation group i of a step into an LDS buffer (transposed within the
+  // 16-byte group) and add it to the token sums
+  auto stage = [&](const uint4& v, int i, uint8_t* buf) {
+    const int g = tid + kThreads * i;
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      rsum[i] = __builtin_amdgcn_sdot4((int)in[e], 0x01010101, rsum[i], false);
+    uint32_t o[4];
+    transpose4x4_bytes(in, o);
+    *reinterpret_cast<uint4*>(buf + lds_group(g >> 3, g & 7)) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  auto aread = [&](const uint8_t* buf, int i, int j) -> v4i {
+    return *reinterpret_cast<const v4i*>(buf + lds_group(wt * (BM / 2) + 32 * i + r, 4 * h + j));
+  };
+
   v16i acc[TB][2];
 #pragma unroll
   for (int i = 0; i < TB; ++i)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[i][b] = (v16i){};
 
+  // Step s: the matrix cores work on step s (activations staged in xs[s & 1],
+  // weights in wv) while the same wave stages the activations of step s + 1
+  // (xv) into the other buffer, one 16-byte group per k-slice j, so that its
+  // vector work runs under its own matrix instructions.  Register set d holds
+  // the weights of step s + d and the activations of step s + 1 + d.
   auto body = [&](uint4 (&xv)[XG], uint4 (&wv)[2], int s) {
-    uint8_t* buf = xs[s & 1];
-    // stage this step's activations (transposed within each 16-byte group)
+    const uint8_t* cur = xs[s & 1];
+    uint8_t* nxt = xs[(s + 1) & 1];
+    const uint32_t wd[2][4] = {{wv[0].x, wv[0].y, wv[0].z, wv[0].w},
+                               {wv[1].x, wv[1].y, wv[1].z, wv[1].w}};
+    v4i a[TB];
 #pragma unroll
-    for (int i = 0; i < XG; ++i) {
-      const int g = tid + kThreads * i;
-      const uint32_t in[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-      uint32_t o[4];
-      transpose4x4_bytes(in, o);
-      *reinterpret_cast<uint4*>(buf + lds_group(g >> 3, g & 7)) =
-          make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    // expand this step's weights before their registers are refilled
-    v4i bop[2][4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      bop[b][0] = expand_weights(wv[b].x);
-      bop[b][1] = expand_weights(wv[b].y);
-      bop[b][2] = expand_weights(wv[b].z);
-      bop[b][3] = expand_weights(wv[b].w);
-    }
-    // the empty asm takes the expanded operands, so the expansion cannot sink
-    // below the refill of the registers it reads (which would force copies and a
-    // full wait for every load in flight at each loop trip)
-    asm volatile("" : "+v"(bop[0][0]), "+v"(bop[0][1]), "+v"(bop[0][2]), "+v"(bop[0][3]),
-                 "+v"(bop[1][0]), "+v"(bop[1][1]), "+v"(bop[1][2]), "+v"(bop[1][3])::"memory");
-    lds_barrier();  // staged tile visible; the other buffer is no longer read
-    gload(xv, wv, s + kDepth);
+    for (int i = 0; i < TB; ++i) a[i] = aread(cur, i, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      v4i bop0 = expand_codes(wd[0][j]);
+      v4i bop1 = expand_codes(wd[1][j]);
+      v4i an[TB];
+      if (j < 3) {
+#pragma unroll
+        for (int i = 0; i < TB; ++i) an[i] = aread(cur, i, j + 1);
+      }
+      static_assert(XG == 4, "one staged group per k-slice");
+      stage(xv[j], j, nxt);
+      if (j == 3) {
+        // every use of xv and wv is above this point (the asm takes the last
+        // expansion and the token sums), so the refills below reuse their
+        // registers without copies, which would wait for the loads in flight
+        asm volatile("" : "+v"(bop0), "+v"(bop1), "+v"(rsum[0]), "+v"(rsum[1]), "+v"(rsum[2]),
+                     "+v"(rsum[3])::"memory");
+        xload(xv, s + 1 + kDepth);
+        wload(wv, s + kDepth);
+      }
 #pragma unroll
       for (int i = 0; i < TB; ++i) {
-        const v4i a = *reinterpret_cast<const v4i*>(
-            buf + lds_group(wt * (BM / 2) + 32 * i + r, 4 * h + j));
+        acc[i][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bop0, acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bop1, acc[i][1], 0, 0, 0);
+      }
+      if (j < 3) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[i][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop[b][j], acc[i][b], 0, 0, 0);
+        for (int i = 0; i < TB; ++i) a[i] = an[i];
       }
     }
+    lds_barrier();  // step s + 1 staged; nobody reads xs[s & 1] any more
   };
 
+  // prologue: the activations of step 0, then the register sets in the order
+  // the loop refills them; step 0 is staged before the loop
+  uint4 x0[XG];
+  xload(x0, 0);
+  uint4 xv_[kDepth][XG];
+  uint4 wv_[kDepth][2];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
-    gload(xv_[d], wv_[d], d);
-    asm volatile("" ::: "memory");  // issue the sets in order, as the loop refills them
+    asm volatile("" ::: "memory");
+    xload(xv_[d], d + 1);
+    wload(wv_[d], d);
   }
-  // register set d holds step s + d; steps past the end (when kDepth does not
-  // divide the step count) only stage zeros and add zero products
+#pragma unroll
+  for (int i = 0; i < XG; ++i) stage(x0[i], i, xs[0]);
+  lds_barrier();
+  // steps past the end (when kDepth does not divide the step count) only add
+  // zero products and stage zeros
   for (int s = 0; s < steps; s += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) body(xv_[d], wv_[d], s + d);
   }
+
+  // token sums: the 8 threads of a token are consecutive lanes
+#pragma unroll
+  for (int i = 0; i < XG; ++i) {
+    int v = rsum[i];
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    if ((tid & 7) == 0) xsum[(tid >> 3) + (kThreads / 8) * i] = v;
+  }
+  __syncthreads();
 
   // D layout (32 x 32): lane l holds output row (n) l % 32 and tokens
   // 8 (v / 4) + 4 (l / 32) + v % 4 for its 16 values v
@@ -180,14 +229,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   for (int i = 0; i < TB; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int m = m0 + wt * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+      const int ml = wt * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+      const int m = m0 + ml;
       if (m < M) {
         const float sc = gamma * x_scale[m];
+        const int xm = xsum[ml];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const int n = wrow0 + 32 * b + r;
           if (n < N) {
-            const int a = acc[i][b][v];
+            const int a = acc[i][b][v] - xm;   // sum (c - 1) x
             const float yv = (float)a * sc;
             const size_t o = (size_t)m * N + n;
             if (acc_out) acc_out[o] = a;
