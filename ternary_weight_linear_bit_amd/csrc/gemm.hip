@@ -32,7 +32,11 @@ namespace {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int BN = 128;         // output rows per workgroup
+#ifndef GEMM_NBW
+#define GEMM_NBW 2
+#endif
+constexpr int NBW = GEMM_NBW;   // 32-row weight blocks per wave
+constexpr int BN = 64 * NBW;    // output rows per workgroup (2 waves along the rows)
 constexpr int BK = 128;         // k per step
 constexpr int kThreads = 256;
 constexpr int kStride = BK;       // LDS bytes per staged token row (groups XOR-swizzled)
@@ -67,8 +71,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     void* __restrict__ y, int y_bf16, int32_t* __restrict__ acc_out) {
   constexpr int TB = BM / 64;               // 32-token blocks per wave
   constexpr int XG = BM * (BK / 16) / kThreads;  // 16-byte activation groups per thread per step
+  static_assert(BM <= kThreads, "one token scale per thread");
   __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * kStride];
   __shared__ int xsum[BM];                  // per token: sum of its int8 activations
+  __shared__ float xsc[BM];                 // per token: its scale d
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -87,6 +93,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const uint32_t rowb = (uint32_t)K >> 2;
   const int steps = (K + BK - 1) / BK;   // K % 64 == 0; a last step of 64 k reads zeros past K
 
+  // the epilogue's scalars, loaded first so that their latency hides behind the
+  // main loop: gamma, and the tile's token scales (one per thread, zeros past M)
+  const float gamma = __uint_as_float(
+      __builtin_amdgcn_readfirstlane(bload4(make_uniform_rsrc(w_scale, 4u), 0u)));
+  const float xs_t = __uint_as_float(
+      bload4(make_uniform_rsrc(x_scale + m0, 4u * (uint32_t)min(BM, M - m0)),
+             tid < BM ? 4u * (uint32_t)tid : kOob));
+
   // activations: group g = tid + 256 i of the BM x 128 tile (token g / 8, k-group g % 8);
   // tokens past M read zeros (range-checked buffer)
   const int mrows = min(BM, M - m0);
@@ -97,8 +111,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     return k < K ? (uint32_t)(g >> 3) * (uint32_t)K + (uint32_t)k : kOob;
   };
   // weights: this wave's 64 rows; rows past N read zeros
-  const int wrow0 = n0 + wr * 64;
-  const int wrows = max(0, min(64, N - wrow0));
+  const int wrow0 = n0 + wr * (BN / 2);
+  const int wrows = max(0, min(BN / 2, N - wrow0));
   const auto wrs = make_uniform_rsrc(wp + (size_t)wrow0 * rowb, (uint32_t)wrows * rowb);
   auto woff = [&](int b, int k0) -> uint32_t {
     const int k = k0 + 64 * h;
@@ -114,10 +128,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < XG; ++i) xv[i] = bload16(xr, xoff(i, s * BK) | past);
   };
-  auto wload = [&](uint4 (&wv)[2], int s) {
+  auto wload = [&](uint4 (&wv)[NBW], int s) {
     const uint32_t past = (uint32_t)(s >= steps) << 31;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) wv[b] = bload16(wrs, woff(b, s * BK) | past);
+    for (int b = 0; b < NBW; ++b) wv[b] = bload16(wrs, woff(b, s * BK) | past);
   };
 
   int rsum[XG] = {};   // partial sums of the activations this thread stages (token g / 8)
@@ -137,29 +151,36 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     return *reinterpret_cast<const v4i*>(buf + lds_group(wt * (BM / 2) + 32 * i + r, 4 * h + j));
   };
 
-  v16i acc[TB][2];
+  v16i acc[TB][NBW];
 #pragma unroll
   for (int i = 0; i < TB; ++i)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[i][b] = (v16i){};
+    for (int b = 0; b < NBW; ++b) acc[i][b] = (v16i){};
 
   // Step s: the matrix cores work on step s (activations staged in xs[s & 1],
   // weights in wv) while the same wave stages the activations of step s + 1
   // (xv) into the other buffer, one 16-byte group per k-slice j, so that its
   // vector work runs under its own matrix instructions.  Register set d holds
   // the weights of step s + d and the activations of step s + 1 + d.
-  auto body = [&](uint4 (&xv)[XG], uint4 (&wv)[2], int s) {
+  auto body = [&](uint4 (&xv)[XG], uint4 (&wv)[NBW], int s) {
     const uint8_t* cur = xs[s & 1];
     uint8_t* nxt = xs[(s + 1) & 1];
-    const uint32_t wd[2][4] = {{wv[0].x, wv[0].y, wv[0].z, wv[0].w},
-                               {wv[1].x, wv[1].y, wv[1].z, wv[1].w}};
+    uint32_t wd[NBW][4];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      wd[b][0] = wv[b].x;
+      wd[b][1] = wv[b].y;
+      wd[b][2] = wv[b].z;
+      wd[b][3] = wv[b].w;
+    }
     v4i a[TB];
 #pragma unroll
     for (int i = 0; i < TB; ++i) a[i] = aread(cur, i, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v4i bop0 = expand_codes(wd[0][j]);
-      v4i bop1 = expand_codes(wd[1][j]);
+      v4i bop[NBW];
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) bop[b] = expand_codes(wd[b][j]);
       v4i an[TB];
       if (j < 3) {
 #pragma unroll
@@ -171,16 +192,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         // every use of xv and wv is above this point (the asm takes the last
         // expansion and the token sums), so the refills below reuse their
         // registers without copies, which would wait for the loads in flight
-        asm volatile("" : "+v"(bop0), "+v"(bop1), "+v"(rsum[0]), "+v"(rsum[1]), "+v"(rsum[2]),
-                     "+v"(rsum[3])::"memory");
+        asm volatile("" : "+v"(bop[0]), "+v"(bop[NBW - 1]), "+v"(rsum[0]), "+v"(rsum[1]),
+                     "+v"(rsum[2]), "+v"(rsum[3])::"memory");
         xload(xv, s + 1 + kDepth);
         wload(wv, s + kDepth);
       }
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bop0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bop1, acc[i][1], 0, 0, 0);
-      }
+      for (int i = 0; i < TB; ++i)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+          acc[i][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bop[b], acc[i][b], 0, 0, 0);
       if (j < 3) {
 #pragma unroll
         for (int i = 0; i < TB; ++i) a[i] = an[i];
@@ -194,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   uint4 x0[XG];
   xload(x0, 0);
   uint4 xv_[kDepth][XG];
-  uint4 wv_[kDepth][2];
+  uint4 wv_[kDepth][NBW];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     asm volatile("" ::: "memory");
@@ -203,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   }
 #pragma unroll
   for (int i = 0; i < XG; ++i) stage(x0[i], i, xs[0]);
+  if (tid < BM) xsc[tid] = xs_t;   // loaded before x0, so no extra wait
   lds_barrier();
   // steps past the end (when kDepth does not divide the step count) only add
   // zero products and stage zeros
@@ -224,7 +246,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
   // D layout (32 x 32): lane l holds output row (n) l % 32 and tokens
   // 8 (v / 4) + 4 (l / 32) + v % 4 for its 16 values v
-  const float gamma = *w_scale;
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
 #pragma unroll
@@ -232,10 +253,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
       const int ml = wt * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
       const int m = m0 + ml;
       if (m < M) {
-        const float sc = gamma * x_scale[m];
+        const float sc = gamma * xsc[ml];
         const int xm = xsum[ml];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NBW; ++b) {
           const int n = wrow0 + 32 * b + r;
           if (n < N) {
             const int a = acc[i][b][v] - xm;   // sum (c - 1) x
