@@ -5,9 +5,9 @@
 // compute-bound (hundreds of int8 ops per packed weight byte), so it runs on
 // v_mfma_i32_32x32x32_i8 with the ternary weights expanded to int8 in registers.
 //
-// Workgroup tile: BM tokens x 128 output rows, 4 waves as 2 (tokens) x 2 (rows);
-// a wave owns (BM / 2) tokens x 64 rows = (BM / 64) x 2 blocks of 32 x 32 int32
-// accumulators.  K advances in steps of 128:
+// Workgroup tile: BM tokens x 64 WN output rows, 2 WN waves as 2 (tokens) x WN
+// (rows); a wave owns (BM / 2) tokens x 64 rows = (BM / 64) x 2 blocks of 32 x 32
+// int32 accumulators.  K advances in steps of 128:
 //  * activations: the workgroup stages the BM x 128 int8 tile into LDS (double
 //    buffered, one barrier per step), byte-transposed within each 16-byte group;
 //    a wave stages step s + 1 in between its matrix instructions of step s, so
@@ -36,9 +36,8 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 #define GEMM_NBW 2
 #endif
 constexpr int NBW = GEMM_NBW;   // 32-row weight blocks per wave
-constexpr int BN = 64 * NBW;    // output rows per workgroup (2 waves along the rows)
 constexpr int BK = 128;         // k per step
-constexpr int kThreads = 256;
+
 constexpr int kStride = BK;       // LDS bytes per staged token row (groups XOR-swizzled)
 
 // LDS byte offset of 16-byte group kg of staged token row t (128-byte rows).  The
@@ -64,11 +63,14 @@ __device__ __forceinline__ v4i expand_codes(uint32_t w) {
   return a;
 }
 
-template <int BM>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+// WN waves along the output rows (2 along the tokens): BN = 32 * NBW * WN rows
+template <int BM, int WN>
+__global__ __launch_bounds__(128 * WN) void gemm_kernel(
     const uint8_t* __restrict__ wp, const float* __restrict__ w_scale,
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale, int M, int N, int K,
     void* __restrict__ y, int y_bf16, int32_t* __restrict__ acc_out) {
+  constexpr int kThreads = 128 * WN;
+  constexpr int BN = 32 * NBW * WN;         // output rows per workgroup
   constexpr int TB = BM / 64;               // 32-token blocks per wave
   constexpr int XG = BM * (BK / 16) / kThreads;  // 16-byte activation groups per thread per step
   static_assert(BM <= kThreads, "one token scale per thread");
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = wave >> 1, wr = wave & 1;
+  const int wt = wave / WN, wr = wave % WN;
   const int r = lane & 31, h = lane >> 5;
   // XCD-aware tile order: workgroup b runs on XCD b % 8 (round-robin dispatch);
   // each XCD takes a contiguous run of tiles in token-major order, so the
@@ -111,8 +113,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     return k < K ? (uint32_t)(g >> 3) * (uint32_t)K + (uint32_t)k : kOob;
   };
   // weights: this wave's 64 rows; rows past N read zeros
-  const int wrow0 = n0 + wr * (BN / 2);
-  const int wrows = max(0, min(BN / 2, N - wrow0));
+  const int wrow0 = n0 + wr * (32 * NBW);
+  const int wrows = max(0, min(32 * NBW, N - wrow0));
   const auto wrs = make_uniform_rsrc(wp + (size_t)wrow0 * rowb, (uint32_t)wrows * rowb);
   auto woff = [&](int b, int k0) -> uint32_t {
     const int k = k0 + 64 * h;
@@ -186,14 +188,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int i = 0; i < TB; ++i) an[i] = aread(cur, i, j + 1);
       }
-      static_assert(XG == 4, "one staged group per k-slice");
-      stage(xv[j], j, nxt);
+      static_assert(4 % XG == 0, "staged groups spread over the k-slices");
+      if (j % (4 / XG) == 0) stage(xv[j / (4 / XG)], j / (4 / XG), nxt);
       if (j == 3) {
         // every use of xv and wv is above this point (the asm takes the last
         // expansion and the token sums), so the refills below reuse their
         // registers without copies, which would wait for the loads in flight
-        asm volatile("" : "+v"(bop[0]), "+v"(bop[NBW - 1]), "+v"(rsum[0]), "+v"(rsum[1]),
-                     "+v"(rsum[2]), "+v"(rsum[3])::"memory");
+        asm volatile("" : "+v"(bop[0]), "+v"(bop[NBW - 1]), "+v"(rsum[0]), "+v"(rsum[XG - 1])
+                     ::"memory");
         xload(xv, s + 1 + kDepth);
         wload(wv, s + kDepth);
       }
@@ -307,13 +309,26 @@ hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq
                        const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
                        int32_t* acc_out, hipStream_t s) {
   if (K % 64 != 0) return hipErrorInvalidValue;
-  // 128-token tiles: 256-token ones (2 x 2 waves of 128 x 64) measured slower on
-  // every prefill shape (more registers, fewer waves to hide latency)
-  const int64_t tiles = (int64_t)((N + BN - 1) / BN) * ((M + 127) / 128);
+  // Tiles of 128 tokens x 128 rows (4 waves; three workgroups per compute unit)
+  // or 128 x 256 (8 waves; one per compute unit, half the activation traffic and
+  // staging per product).  Measured on the prefill shapes: the 8-wave tile wins
+  // (by 10-13%) only when its tiles fill one round of the chip almost exactly;
+  // otherwise the finer 4-wave tiles and their extra waves win.  256-token tiles
+  // and 4 x 32-row blocks per wave measured slower everywhere (registers: one
+  // wave per SIMD).
+  const int64_t mt = (M + 127) / 128;
+  const int64_t t4 = (int64_t)((N + 255) / 256) * mt;
+  const int cus = device_cus();
+  const bool wide = t4 <= cus && 10 * t4 >= 9 * (int64_t)cus;
+  const int64_t tiles = wide ? t4 : (int64_t)((N + 127) / 128) * mt;
   if (tiles > (int64_t)1 << 30) return hipErrorInvalidValue;  // grid and tile index limits
   const dim3 grid((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds));
-  hipLaunchKernelGGL(gemm_kernel<128>, grid, dim3(kThreads), 0, s, wp, w_scale, xq, x_scale, M, N,
-                     K, y, y_bf16 ? 1 : 0, acc_out);
+  if (wide)
+    hipLaunchKernelGGL((gemm_kernel<128, 4>), grid, dim3(512), 0, s, wp, w_scale, xq, x_scale, M,
+                       N, K, y, y_bf16 ? 1 : 0, acc_out);
+  else
+    hipLaunchKernelGGL((gemm_kernel<128, 2>), grid, dim3(256), 0, s, wp, w_scale, xq, x_scale, M,
+                       N, K, y, y_bf16 ? 1 : 0, acc_out);
   return hipGetLastError();
 }
 

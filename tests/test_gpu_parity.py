@@ -152,6 +152,9 @@ LINEAR_SHAPES = [
     # prefill kernel: ragged M and N, several 128 x 128 tiles
     (17, 100, 256), (100, 130, 2560), (300, 257, 192), (128, 128, 64), (513, 640, 512),
     (16, 50, 4096),
+    # prefill kernel, 128 x 256 tiles (chosen when they fill one round of the
+    # chip's compute units almost exactly): ragged M and N
+    (2000, 4000, 64), (1920, 3900, 192),
     # decode kernel: several K phases, multi-tile workgroups, M = 16 at large K
     (16, 100, 14336), (1, 40, 28672), (3, 24, 65536), (1, 20, 131072), (2, 9000, 256),
     (1, 70000, 64), (16, 300, 1088),
