@@ -229,7 +229,13 @@ def leg_summary(d, m):
 
 
 def prefill(torch, N, I, layer_shapes, ms, steps):
-    """int8 TOPS of the prefill kernel on one layer's matrices at M tokens."""
+    """int8 TOPS of the prefill kernel on one layer's matrices at M tokens (q, k, v
+    in one launch, o, gate and up in one launch, down), and of its largest matrix
+    alone."""
+    names = [nm for nm, _, _ in layer_shapes]
+    groups = [g for g in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+              if all(nm in names for nm in g)]
+    assert sorted(sum(groups, ())) == sorted(names), "layer with an unknown matrix set"
     mats = {}
     for i, (nm, k, n) in enumerate(layer_shapes):
         g = torch.Generator(device="cuda").manual_seed(I.weight_seed(0, i))
@@ -246,11 +252,17 @@ def prefill(torch, N, I, layer_shapes, ms, steps):
         ys = {nm: torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for nm, _, n in layer_shapes}
         ops = sum(2 * m * n * k for _, k, n in layer_shapes)
 
+        kin = {nm: k for nm, k, _ in layer_shapes}
+
         def run(only=None, reps=1):
             for _ in range(reps):
-                for nm, k, _ in layer_shapes:
-                    if only is None or nm == only:
-                        N.bitnet_ternary_linear(*mats[nm], *xq[k], y=ys[nm])
+                if only is not None:
+                    N.bitnet_ternary_linear(*mats[only], *xq[kin[only]], y=ys[only])
+                    continue
+                # matrices that share an input run in one launch (q, k, v; gate, up)
+                for grp in groups:
+                    N.bitnet_ternary_linear_multi([(*mats[nm], ys[nm]) for nm in grp],
+                                                  *xq[kin[grp[0]]])
 
         def timed(fn):
             fn()

@@ -62,7 +62,8 @@ typedef enum bitnet_status {
 
 typedef enum bitnet_dtype { BITNET_F32 = 0, BITNET_BF16 = 1 } bitnet_dtype;
 
-/* One weight matrix of a grouped call (all pointers device memory). */
+/* One weight matrix of a grouped call (all pointers device memory; they may be
+ * NULL when the call has no tokens or the matrix no rows). */
 typedef struct bitnet_matrix {
   const uint8_t *w_packed; /* [N][K/4] packed codes from bitnet_quantize_weights */
   const float *w_scale;    /* [1] gamma* */

@@ -25,10 +25,12 @@ bitnet_status check_sizes(int64_t M, int64_t K) {
   return BITNET_OK;
 }
 
-// Per-matrix checks shared by the single and grouped calls.
+// Per-matrix checks shared by the single and grouped calls.  A matrix with no
+// outputs (M == 0 or N == 0) is never read or written, so its pointers may be NULL.
 bitnet_status check_matrix(const bitnet_matrix& m, int64_t M, int64_t K, int y_dtype) {
-  if (!m.w_scale || !m.y || (K > 0 && !m.w_packed)) return BITNET_ERR_NULL;
   if (m.N < 0 || m.N > kInt32Max || M * m.N > ((int64_t)1 << 46)) return BITNET_ERR_SHAPE;
+  if (M == 0 || m.N == 0) return BITNET_OK;
+  if (!m.w_scale || !m.y || (K > 0 && !m.w_packed)) return BITNET_ERR_NULL;
   if (!aligned(m.y, esize(y_dtype)) || !aligned(m.w_scale, 4) ||
       (m.acc_out && !aligned(m.acc_out, 4)))
     return BITNET_ERR_ALIGN;
@@ -89,19 +91,36 @@ bitnet_status run_linear(const bitnet_matrix* mats, int count, const int8_t* x_q
     }
     return BITNET_OK;
   }
+  // prefill: matrices in the fast layout go to the matrix-core kernel in groups
+  // of up to four per launch; the others to the generic kernel
+  bitnet::GemmArgs g{};
+  auto flush = [&]() -> bool {
+    if (g.count == 0) return true;
+    g.xq = x_q;
+    g.xs = x_scale;
+    g.M = (int)M;
+    g.K = (int)K;
+    g.y_bf16 = yb ? 1 : 0;
+    const bool ok = bitnet::launch_gemm(g, stream) == hipSuccess;
+    g = bitnet::GemmArgs{};
+    return ok;
+  };
   for (int j = 0; j < count; ++j) {
     const bitnet_matrix& m = mats[j];
     if (m.N == 0) continue;
-    hipError_t e;
-    if (fast_layout(m.w_packed, x_q, K))
-      e = bitnet::launch_gemm(m.w_packed, m.w_scale, x_q, x_scale, (int)M, (int)m.N, (int)K, m.y,
-                              yb, m.acc_out, stream);
-    else
-      e = bitnet::launch_generic_linear(m.w_packed, m.w_scale, x_q, x_scale, M, m.N, K, m.y, yb,
-                                        m.acc_out, stream);
-    if (e != hipSuccess) return BITNET_ERR_HIP;
+    if (fast_layout(m.w_packed, x_q, K)) {
+      g.wp[g.count] = m.w_packed;
+      g.ws[g.count] = m.w_scale;
+      g.y[g.count] = m.y;
+      g.acc[g.count] = m.acc_out;
+      g.n[g.count] = (int)m.N;
+      if (++g.count == bitnet::kMaxGroup && !flush()) return BITNET_ERR_HIP;
+    } else if (bitnet::launch_generic_linear(m.w_packed, m.w_scale, x_q, x_scale, M, m.N, K, m.y,
+                                             yb, m.acc_out, stream) != hipSuccess) {
+      return BITNET_ERR_HIP;
+    }
   }
-  return BITNET_OK;
+  return flush() ? BITNET_OK : BITNET_ERR_HIP;
 }
 
 bitnet::ActPrologue act_prologue(const bitnet_act_prologue* pro) {

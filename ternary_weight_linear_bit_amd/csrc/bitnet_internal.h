@@ -206,9 +206,21 @@ constexpr int kGemvMaxM = 16;
 bool gemv_fits(int64_t M, int64_t K, int fmt);
 bool gemv_fused_fits(int64_t M, int64_t K, int fmt);
 hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s);
-hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
-                       const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
-                       int32_t* acc_out, hipStream_t s);
+// Prefill kernel arguments: up to kMaxGroup weight matrices sharing K and the
+// int8 activations, passed by value.  launch_gemm fills nb0.
+struct GemmArgs {
+  const uint8_t* wp[kMaxGroup];
+  const float* ws[kMaxGroup];
+  void* y[kMaxGroup];
+  int32_t* acc[kMaxGroup];
+  int n[kMaxGroup];
+  int nb0[kMaxGroup + 1];    // first row tile of each matrix; nb0[count] = all row tiles
+  const int8_t* xq;          // int8 activations [M][K]
+  const float* xs;           // their token scales
+  int count, M, K, y_bf16;
+};
+// Prefill kernel: K % 64 == 0, 16-byte aligned packed weights and activations.
+hipError_t launch_gemm(GemmArgs a, hipStream_t s);
 // Lookup-table decode: workspace bytes (tables 16 K + accumulators 4 N, each
 // rounded up to 256) and the launches (three per token).  K % 64 == 0, 16-byte
 // aligned packed weights and workspace.

@@ -5,7 +5,8 @@
 // compute-bound (hundreds of int8 ops per packed weight byte), so it runs on
 // v_mfma_i32_32x32x32_i8 with the ternary weights expanded to int8 in registers.
 //
-// Workgroup tile: BM tokens x 64 WN output rows, 2 WN waves as 2 (tokens) x WN
+// Workgroup tile: BM tokens x 64 WN output rows of one of up to four matrices that
+// share the activations (q, k, v or gate, up), 2 WN waves as 2 (tokens) x WN
 // (rows); a wave owns (BM / 2) tokens x 64 rows = (BM / 64) x 2 blocks of 32 x 32
 // int32 accumulators.  K advances in steps of 128:
 //  * activations: the workgroup stages the BM x 128 int8 tile into LDS (double
@@ -65,10 +66,7 @@ __device__ __forceinline__ v4i expand_codes(uint32_t w) {
 
 // WN waves along the output rows (2 along the tokens): BN = 32 * NBW * WN rows
 template <int BM, int WN>
-__global__ __launch_bounds__(128 * WN) void gemm_kernel(
-    const uint8_t* __restrict__ wp, const float* __restrict__ w_scale,
-    const int8_t* __restrict__ xq, const float* __restrict__ x_scale, int M, int N, int K,
-    void* __restrict__ y, int y_bf16, int32_t* __restrict__ acc_out) {
+__global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
   constexpr int kThreads = 128 * WN;
   constexpr int BN = 32 * NBW * WN;         // output rows per workgroup
   constexpr int TB = BM / 64;               // 32-token blocks per wave
@@ -82,16 +80,33 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave / WN, wr = wave % WN;
   const int r = lane & 31, h = lane >> 5;
-  // XCD-aware tile order: workgroup b runs on XCD b % 8 (round-robin dispatch);
-  // each XCD takes a contiguous run of tiles in token-major order, so the
-  // workgroups that share an activation tile share one XCD's L2
-  const int nb = (N + BN - 1) / BN;
-  const int tiles = nb * ((M + BM - 1) / BM);
+  const int M = args.M, K = args.K;
+  // Tiles are numbered token-tile-major over the row tiles of all the launch's
+  // matrices (which share the activations).  XCD-aware order: workgroup b runs
+  // on XCD b % 8 (round-robin dispatch); each XCD takes a contiguous run of
+  // tiles, so the workgroups that share an activation tile share one XCD's L2.
+  const int nbt = args.nb0[args.count];     // row tiles of all matrices
+  const int tiles = nbt * ((M + BM - 1) / BM);
   const int per_xcd = (tiles + kXcds - 1) / kXcds;
   const int t = ((int)blockIdx.x % kXcds) * per_xcd + (int)blockIdx.x / kXcds;
   if (t >= tiles) return;
-  const int m0 = (t / nb) * BM;
-  const int n0 = (t % nb) * BN;
+  const int mt = t / nbt, rt = t - mt * nbt;
+  // this tile's matrix (entries past count have nb0 = nbt and are never chosen)
+  const int jm = (rt >= args.nb0[1]) + (rt >= args.nb0[2]) + (rt >= args.nb0[3]);
+  static_assert(kMaxGroup == 4, "matrix selection lists four matrices");
+  const uint8_t* wp = args.wp[0];
+  const float* w_scale = args.ws[0];
+  void* y = args.y[0];
+  int32_t* acc_out = args.acc[0];
+  int N = args.n[0], nbase = 0;
+  if (jm >= 1) { wp = args.wp[1]; w_scale = args.ws[1]; y = args.y[1]; acc_out = args.acc[1]; N = args.n[1]; nbase = args.nb0[1]; }
+  if (jm >= 2) { wp = args.wp[2]; w_scale = args.ws[2]; y = args.y[2]; acc_out = args.acc[2]; N = args.n[2]; nbase = args.nb0[2]; }
+  if (jm >= 3) { wp = args.wp[3]; w_scale = args.ws[3]; y = args.y[3]; acc_out = args.acc[3]; N = args.n[3]; nbase = args.nb0[3]; }
+  const int8_t* xq = args.xq;
+  const float* x_scale = args.xs;
+  const int y_bf16 = args.y_bf16;
+  const int m0 = mt * BM;
+  const int n0 = (rt - nbase) * BN;
   const uint32_t rowb = (uint32_t)K >> 2;
   const int steps = (K + BK - 1) / BK;   // K % 64 == 0; a last step of 64 k reads zeros past K
 
@@ -305,30 +320,36 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* wp, const float* w_scale, const int8_t* xq,
-                       const float* x_scale, int M, int N, int K, void* y, bool y_bf16,
-                       int32_t* acc_out, hipStream_t s) {
-  if (K % 64 != 0) return hipErrorInvalidValue;
+hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
+  if (a.K % 64 != 0 || a.count < 1 || a.count > kMaxGroup) return hipErrorInvalidValue;
   // Tiles of 128 tokens x 128 rows (4 waves; three workgroups per compute unit)
   // or 128 x 256 (8 waves; one per compute unit, half the activation traffic and
   // staging per product).  Measured on the prefill shapes: the 8-wave tile wins
-  // (by 10-13%) only when its tiles fill one round of the chip almost exactly;
+  // (by 10-12%) only when its tiles fill one round of the chip almost exactly;
   // otherwise the finer 4-wave tiles and their extra waves win.  256-token tiles
   // and 4 x 32-row blocks per wave measured slower everywhere (registers: one
   // wave per SIMD).
-  const int64_t mt = (M + 127) / 128;
-  const int64_t t4 = (int64_t)((N + 255) / 256) * mt;
+  const int64_t mt = (a.M + 127) / 128;
+  int64_t rows4 = 0;
+  for (int j = 0; j < a.count; ++j) rows4 += (a.n[j] + 255) / 256;
   const int cus = device_cus();
-  const bool wide = t4 <= cus && 10 * t4 >= 9 * (int64_t)cus;
-  const int64_t tiles = wide ? t4 : (int64_t)((N + 127) / 128) * mt;
+  const bool wide = rows4 * mt <= cus && 10 * rows4 * mt >= 9 * (int64_t)cus;
+  const int bn = wide ? 256 : 128;
+  int64_t nbt = 0;
+  for (int j = 0; j < kMaxGroup; ++j) {
+    a.nb0[j] = (int)nbt;
+    if (j < a.count) nbt += (a.n[j] + bn - 1) / bn;
+  }
+  a.nb0[kMaxGroup] = (int)nbt;
+  for (int j = a.count; j <= kMaxGroup; ++j) a.nb0[j] = (int)nbt;
+  const int64_t tiles = nbt * mt;
+  if (tiles == 0) return hipSuccess;
   if (tiles > (int64_t)1 << 30) return hipErrorInvalidValue;  // grid and tile index limits
   const dim3 grid((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds));
   if (wide)
-    hipLaunchKernelGGL((gemm_kernel<128, 4>), grid, dim3(512), 0, s, wp, w_scale, xq, x_scale, M,
-                       N, K, y, y_bf16 ? 1 : 0, acc_out);
+    hipLaunchKernelGGL((gemm_kernel<128, 4>), grid, dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<128, 2>), grid, dim3(256), 0, s, wp, w_scale, xq, x_scale, M,
-                       N, K, y, y_bf16 ? 1 : 0, acc_out);
+    hipLaunchKernelGGL((gemm_kernel<128, 2>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

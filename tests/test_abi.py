@@ -89,6 +89,8 @@ def test_ternary_linear_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 3, 8, FAKE, 0, FAKE_ODD, None) == EALIGN
     assert f(FAKE, FAKE, FAKE, FAKE, 0, 3, 8, FAKE, 0, None, None) == OK   # empty batch
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 0, 8, FAKE, 0, None, None) == OK   # no outputs
+    assert f(None, None, FAKE, FAKE, 2, 0, 8, None, 0, None, None) == OK   # ... nothing to point at
+    assert f(None, None, None, None, 0, 3, 8, None, 0, None, None) == OK
 
 
 def test_quant_linear_validation(lib):

@@ -315,15 +315,20 @@ def test_repeatable_and_stream_ordered():
 
 
 def _group(ns, k, seed):
-    return [O.quantize_weights(I.master_weights(n, k, seed + i)) for i, n in enumerate(ns)]
+    # an empty matrix (N = 0) has no weights to take a scale from: any gamma will do
+    return [O.quantize_weights(I.master_weights(n, k, seed + i)) if n else
+            (np.zeros((0, k // 4), np.uint8), np.float32(1.0)) for i, n in enumerate(ns)]
 
 
 @pytest.mark.parametrize("m,k,ns", [(1, 2560, (2560, 640, 640)), (5, 256, (100, 37, 16, 64, 200)),
                                     (16, 1024, (48, 33)), (40, 512, (100, 130, 17)),
-                                    (1, 64, (30000, 20000, 7))])
+                                    (1, 64, (30000, 20000, 7)),
+                                    (300, 256, (100, 37, 260, 5, 129)), (129, 128, (0, 300, 64)),
+                                    (2000, 64, (1990, 2000))])
 def test_ternary_linear_multi(m, k, ns):
-    """Grouped matrices sharing x_q, including more than 4 (split into launches) and
-    M beyond the decode kernel (one prefill launch per matrix)."""
+    """Grouped matrices sharing x_q, including more than 4 (split into launches),
+    an empty matrix, and M beyond the decode kernel (up to four matrices per
+    prefill launch; 2000 x (1990, 2000) selects the 128 x 256 tiles)."""
     mats = _group(ns, k, 900)
     xq, d = O.quantize_acts(I.activations(m, k, 901))
     accs = [torch.empty((m, n), dtype=torch.int32, device=DEV) for n in ns]
