@@ -35,6 +35,12 @@ FLAGS = [
 ]
 
 
+# Per-source flags: the decode kernel's leading scalar arguments are preloaded
+# into SGPRs at wave launch (gfx950 kernarg preload; the compiler adds the
+# fallback preamble for firmware without it).
+EXTRA = {"gemv.hip": ("-mllvm", "-amdgpu-kernarg-preload-count=10")}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -45,7 +51,8 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[HIPCC, *FLAGS, *EXTRA.get(s, ()), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 4)) as ex:
         for r in ex.map(_run, cmds):
             if verbose and (r.stdout or r.stderr):

@@ -6,7 +6,6 @@
 namespace {
 
 constexpr size_t kWqWorkspaceBytes = 4096;
-constexpr int kFmt2 = 0, kFmtT1 = 1;  // weight layouts of the decode kernel
 constexpr int64_t kInt32Max = 2147483647;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -80,13 +79,13 @@ bitnet_status run_linear(const bitnet_matrix* mats, int count, const int8_t* x_q
                          hipStream_t stream) {
   if (M == 0) return BITNET_OK;
   const bool yb = y_dtype == BITNET_BF16;
-  if (all_fast(mats, count, x_q, K) && bitnet::gemv_fits(M, K, kFmt2)) {
+  if (all_fast(mats, count, x_q, K) && bitnet::gemv_fits(M, K, bitnet::kFmt2)) {
     for (int j0 = 0; j0 < count; j0 += bitnet::kMaxGroup) {
       const int c = count - j0 < bitnet::kMaxGroup ? count - j0 : bitnet::kMaxGroup;
       bitnet::GemvArgs a = gemv_args(mats + j0, c, M, K, y_dtype);
       a.xq = x_q;
       a.xs = x_scale;
-      const bitnet_status st = from_hip(bitnet::launch_gemv(a, 0, kFmt2, stream));
+      const bitnet_status st = from_hip(bitnet::launch_gemv(a, 0, bitnet::kFmt2, stream));
       if (st != BITNET_OK) return st;
     }
     return BITNET_OK;
@@ -149,7 +148,7 @@ bitnet_status quant_linear(const bitnet_matrix* mats, int count, const void* x, 
                            const bitnet::ActPrologue& pro, int64_t M, int64_t K, int8_t* x_q,
                            float* x_scale, int y_dtype, hipStream_t stream) {
   if (M == 0) return BITNET_OK;
-  if (all_fast(mats, count, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K, kFmt2) &&
+  if (all_fast(mats, count, x_q, K) && aligned(x, 16) && bitnet::gemv_fused_fits(M, K, bitnet::kFmt2) &&
       (!pro.up || aligned(pro.up, 16)) && (!pro.w || aligned(pro.w, 16))) {
     const int c = count < bitnet::kMaxGroup ? count : bitnet::kMaxGroup;
     bitnet::GemvArgs a = gemv_args(mats, c, M, K, y_dtype);
@@ -160,7 +159,7 @@ bitnet_status quant_linear(const bitnet_matrix* mats, int count, const void* x, 
     a.xup = pro.up;
     a.gnorm = pro.w;
     a.eps = pro.eps;
-    if (bitnet::launch_gemv(a, x_dtype, kFmt2, stream) != hipSuccess) return BITNET_ERR_HIP;
+    if (bitnet::launch_gemv(a, x_dtype, bitnet::kFmt2, stream) != hipSuccess) return BITNET_ERR_HIP;
     if (count == c) return BITNET_OK;
     return run_linear(mats + c, count - c, x_q, x_scale, M, K, y_dtype, stream);
   }
@@ -188,17 +187,17 @@ bitnet_status run_linear_t1(const bitnet_matrix* mats, int count, const int8_t* 
       bitnet::GemvArgs a = gemv_args(sub, c, mt, K, y_dtype);
       a.xq = x_q + t0 * K;
       a.xs = x_scale + t0;
-      if (bitnet::launch_gemv(a, 0, kFmtT1, stream) != hipSuccess) return BITNET_ERR_HIP;
+      if (bitnet::launch_gemv(a, 0, bitnet::kFmtT1, stream) != hipSuccess) return BITNET_ERR_HIP;
     }
   }
   return BITNET_OK;
 }
 
-// T1 layout requirements on top of check_group: K % 16 == 0 (K >= 16), 16-byte
-// aligned weights and int8 activations.
+// T1 layout requirements on top of check_group: K % 16 == 0 (16 <= K < 2^19),
+// 16-byte aligned weights and int8 activations.
 bitnet_status check_t1(const bitnet_matrix* mats, int count, const void* x_q, int64_t M,
                        int64_t K) {
-  if (K < 16 || (K % 16) != 0) return BITNET_ERR_SHAPE;
+  if (K < 16 || K > bitnet::kGemvMaxK || (K % 16) != 0) return BITNET_ERR_SHAPE;
   if (M > 0 && !aligned(x_q, 16)) return BITNET_ERR_ALIGN;
   for (int j = 0; j < count; ++j)
     if (!aligned(mats[j].w_packed, 16)) return BITNET_ERR_ALIGN;
@@ -209,7 +208,7 @@ bitnet_status quant_linear_t1(const bitnet_matrix* mats, int count, const void* 
                               const bitnet::ActPrologue& pro, int64_t M, int64_t K, int8_t* x_q,
                               float* x_scale, int y_dtype, hipStream_t stream) {
   if (M == 0) return BITNET_OK;
-  if (aligned(x, 16) && bitnet::gemv_fused_fits(M, K, kFmtT1) &&
+  if (aligned(x, 16) && bitnet::gemv_fused_fits(M, K, bitnet::kFmtT1) &&
       (!pro.up || aligned(pro.up, 16)) && (!pro.w || aligned(pro.w, 16))) {
     const int c = count < bitnet::kMaxGroup ? count : bitnet::kMaxGroup;
     bitnet::GemvArgs a = gemv_args(mats, c, M, K, y_dtype);
@@ -220,7 +219,7 @@ bitnet_status quant_linear_t1(const bitnet_matrix* mats, int count, const void* 
     a.xup = pro.up;
     a.gnorm = pro.w;
     a.eps = pro.eps;
-    if (bitnet::launch_gemv(a, x_dtype, kFmtT1, stream) != hipSuccess) return BITNET_ERR_HIP;
+    if (bitnet::launch_gemv(a, x_dtype, bitnet::kFmtT1, stream) != hipSuccess) return BITNET_ERR_HIP;
     if (count == c) return BITNET_OK;
     return run_linear_t1(mats + c, count - c, x_q, x_scale, M, K, y_dtype, stream);
   }

@@ -192,17 +192,20 @@ struct GemvArgs {
   int count, unused0;
   int M, K;                  // pairs of ints are read as one 64-bit value each
   int y_bf16, tiles_per_wg;  // row tiles per workgroup (set by launch_gemv)
-  int kx, phases;            // K range staged per phase and phase count (launch_gemv)
   int mdiv, unused1;         // ceil(65536 / M) (launch_gemv)
   const void* xup;           // fused prologue: up projection (gating) or nullptr
   const float* gnorm;        // fused prologue: RMS norm weight or nullptr
   float eps, unused2;
 };
 
+// Weight formats of the decode kernel: 2 bits per weight (K % 64 == 0), or five
+// per byte (T1, K % 16 == 0, rows of 16 * ceil(K / 80) bytes).
+constexpr int kFmt2 = 0, kFmtT1 = 1;
 // Decode kernel: M <= 16 and K % 64 == 0 (fmt 0: 2-bit weights) or K % 16 == 0
 // (fmt 1: T1 weights); the fused variant (a.xf != nullptr) also needs M <= 4 and
 // the activations of all tokens in one LDS phase.
 constexpr int kGemvMaxM = 16;
+constexpr int64_t kGemvMaxK = (1 << 19) - 1;  // K travels in 19 bits of a kernel argument
 bool gemv_fits(int64_t M, int64_t K, int fmt);
 bool gemv_fused_fits(int64_t M, int64_t K, int fmt);
 hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s);

@@ -69,16 +69,15 @@ constexpr int64_t kLatencyBytes = 6000000; // launches above this use the bandwi
 constexpr int kWgsPerCu = 2;               // bandwidth regime: workgroups per compute unit
 constexpr int kFlightLoads = 8192;         // target 1 KiB loads in flight over the chip
 
-// Weight formats: 2 bits per weight (K % 64 == 0), or five per byte (T1,
-// K % 16 == 0, rows of 16 * ceil(K / 80) bytes).
-constexpr int kFmt2 = 0, kFmtT1 = 1;
 // zero slot: one B operand set read for tokens >= M and chunks past the end
 constexpr int zero_bytes(int fmt) { return fmt ? 96 : 64; }
 // LDS row of one token's staged activations for a phase of kx weights (T1
 // stages whole 80-k blocks)
-int stage_stride(int kx, int fmt) { return fmt ? 80 * ((kx + 79) / 80) + 16 : kx + 16; }
+constexpr int stage_stride(int kx, int fmt) {
+  return fmt ? 80 * ((kx + 79) / 80) + 16 : kx + 16;
+}
 // (token, 4096-k block) pieces the int8 staging loads for a phase of klen weights
-int stage_pieces(int M, int klen, int fmt) {
+constexpr int stage_pieces(int M, int klen, int fmt) {
   const int groups = fmt ? 5 * ((klen + 79) / 80) : klen / 16;
   return M * ((groups + 255) / 256);
 }
@@ -86,7 +85,7 @@ int stage_pieces(int M, int klen, int fmt) {
 // K range staged per phase: a multiple of 256 (T1: of 1280, one 256-byte run of
 // a row) with M * stride <= kXBudget and at most 16 activation pieces, i.e. two
 // staging batches.
-int phase_k(int M, int K, int fmt) {
+constexpr int phase_k(int M, int K, int fmt) {
   const int unit = fmt ? 1280 : 256;
   int kx = ((kXBudget / M - 16) / unit) * unit;
   const int cap = 4096 * (16 / M);
@@ -101,58 +100,64 @@ int lds_bytes(int tiles, int M, int K, int fmt) {
          32;
 }
 
-// This workgroup's matrix and the launch's scalars.  Everything the kernel needs
-// from its arguments is fetched in one round of scalar loads: the empty asm makes
-// the values materialise before the matrix is selected (selecting by index first
-// would fetch the chosen matrix's fields in a second, dependent round, and a
-// field first touched in the epilogue would cost a round trip there).  Pairs of
-// ints travel as one 64-bit value to stay within the asm operand limit.
+// The launch's scalars.  The ones the first loads depend on (activations, the
+// first three matrices' packed weights, row counts and first workgroups, and
+// M | T << 5 | count << 10 | K << 13) are the kernel's leading scalar arguments,
+// which the hardware preloads into SGPRs at wave launch (this file is built with
+// a kernarg preload count of 10): no argument load sits in front of the first
+// global loads.  The rest comes from GemvArgs in one round of scalar loads (the
+// empty asm makes them materialise together rather than as dependent rounds
+// after the matrix is known); its latency hides behind the first loads.  Pairs
+// of ints travel as one 64-bit value to stay within the asm operand limit.
 // Matrices j >= count have wg0[j] = grid size and are never selected.
 struct Prologue {
-  const uint8_t* wp;
   const float* ws;
   void* y;
   int32_t* acc;
-  int n, wg0;
-  const int8_t* xq;
   const float* xs;
-  const void* xf;
-  int M, K, y_bf16, T, kx, phases, mdiv;
+  int y_bf16, mdiv, g3;
 };
 __device__ __forceinline__ uint64_t arg_pair(const int* p) {
   return *reinterpret_cast<const uint64_t*>(p);
 }
-__device__ __forceinline__ Prologue load_prologue(const GemvArgs& a) {
+__device__ __forceinline__ Prologue load_prologue(const GemvArgs& a, int g1, int g2) {
   static_assert(kMaxGroup == 4, "load_prologue lists four matrices");
-  static_assert(offsetof(GemvArgs, n) % 8 == 0 && offsetof(GemvArgs, wg0) % 8 == 0 &&
-                    offsetof(GemvArgs, M) % 8 == 0 && offsetof(GemvArgs, y_bf16) % 8 == 0 &&
-                    offsetof(GemvArgs, kx) % 8 == 0 && offsetof(GemvArgs, mdiv) % 8 == 0,
+  static_assert(offsetof(GemvArgs, wg0) % 8 == 0 && offsetof(GemvArgs, y_bf16) % 8 == 0 &&
+                    offsetof(GemvArgs, mdiv) % 8 == 0,
                 "64-bit aligned int pairs");
-  const uint8_t *wp0 = a.wp[0], *wp1 = a.wp[1], *wp2 = a.wp[2], *wp3 = a.wp[3];
   const float *ws0 = a.ws[0], *ws1 = a.ws[1], *ws2 = a.ws[2], *ws3 = a.ws[3];
   void *y0 = a.y[0], *y1 = a.y[1], *y2 = a.y[2], *y3 = a.y[3];
   int32_t *c0 = a.acc[0], *c1 = a.acc[1], *c2 = a.acc[2], *c3 = a.acc[3];
-  uint64_t n01 = arg_pair(&a.n[0]), n23 = arg_pair(&a.n[2]);
-  uint64_t g01 = arg_pair(&a.wg0[0]), g23 = arg_pair(&a.wg0[2]);
-  uint64_t mk = arg_pair(&a.M), bt = arg_pair(&a.y_bf16), kp = arg_pair(&a.kx);
-  uint64_t md = arg_pair(&a.mdiv);
-  const int8_t* xq = a.xq;
+  uint64_t g23 = arg_pair(&a.wg0[2]), bt = arg_pair(&a.y_bf16), md = arg_pair(&a.mdiv);
   const float* xs = a.xs;
-  const void* xf = a.xf;
   asm volatile(""
-               : "+s"(wp0), "+s"(wp1), "+s"(wp2), "+s"(wp3), "+s"(ws0), "+s"(ws1), "+s"(ws2),
-                 "+s"(ws3), "+s"(y0), "+s"(y1), "+s"(y2), "+s"(y3), "+s"(c0), "+s"(c1),
-                 "+s"(c2), "+s"(c3), "+s"(n01), "+s"(n23), "+s"(g01), "+s"(g23), "+s"(mk),
-                 "+s"(bt), "+s"(kp), "+s"(md), "+s"(xq), "+s"(xs), "+s"(xf));
+               : "+s"(ws0), "+s"(ws1), "+s"(ws2), "+s"(ws3), "+s"(y0), "+s"(y1), "+s"(y2),
+                 "+s"(y3), "+s"(c0), "+s"(c1), "+s"(c2), "+s"(c3), "+s"(g23), "+s"(bt),
+                 "+s"(md), "+s"(xs));
   const int b = (int)blockIdx.x;
-  const int g1 = (int)(g01 >> 32), g2 = (int)g23, g3 = (int)(g23 >> 32);
-  Prologue v{wp0, ws0, y0, c0, (int)n01, 0, xq, xs, xf,
-             (int)mk, (int)(mk >> 32), (int)bt, (int)(bt >> 32), (int)kp, (int)(kp >> 32),
-             (int)md};
-  if (b >= g1) { v.wp = wp1; v.ws = ws1; v.y = y1; v.acc = c1; v.n = (int)(n01 >> 32); v.wg0 = g1; }
-  if (b >= g2) { v.wp = wp2; v.ws = ws2; v.y = y2; v.acc = c2; v.n = (int)n23; v.wg0 = g2; }
-  if (b >= g3) { v.wp = wp3; v.ws = ws3; v.y = y3; v.acc = c3; v.n = (int)(n23 >> 32); v.wg0 = g3; }
+  const int g3 = (int)(g23 >> 32);
+  Prologue v{ws0, y0, c0, xs, (int)bt, (int)md, g3};
+  if (b >= g1) { v.ws = ws1; v.y = y1; v.acc = c1; }
+  if (b >= g2) { v.ws = ws2; v.y = y2; v.acc = c2; }
+  if (b >= g3) { v.ws = ws3; v.y = y3; v.acc = c3; }
   return v;
+}
+
+// phase_k(M, K, FMT) == min(K, kx_cap<FMT>(M)): the M-dependent cap, from a
+// compile-time table (a run-time division by M would cost a long vector sequence
+// in front of the first loads).
+template <int FMT>
+__device__ __forceinline__ int kx_cap(int M) {
+  constexpr int kBig = 1 << 30;
+  switch (M) {
+#define BITNET_KX_CASE(m) case m: return phase_k(m, kBig, FMT);
+    BITNET_KX_CASE(1) BITNET_KX_CASE(2) BITNET_KX_CASE(3) BITNET_KX_CASE(4)
+    BITNET_KX_CASE(5) BITNET_KX_CASE(6) BITNET_KX_CASE(7) BITNET_KX_CASE(8)
+    BITNET_KX_CASE(9) BITNET_KX_CASE(10) BITNET_KX_CASE(11) BITNET_KX_CASE(12)
+    BITNET_KX_CASE(13) BITNET_KX_CASE(14) BITNET_KX_CASE(15)
+#undef BITNET_KX_CASE
+    default: return phase_k(16, kBig, FMT);
+  }
 }
 
 __device__ __forceinline__ int ceil_log2(int m) { return m > 1 ? 32 - __builtin_clz(m - 1) : 0; }
@@ -249,11 +254,31 @@ __device__ __forceinline__ void raw_to_f32(const uint4* w, float v[16]) {
   }
 }
 
+// What a workgroup needs before its first loads comes as leading scalar
+// arguments, which are preloaded into scalar registers at wave launch (the
+// library builds this file with kernarg preload): the activations xin, the
+// first three matrices' weights and rows, the first workgroups g1, g2 of
+// matrices 1 and 2, and mtck = M | T << 5 | count << 10 | K << 13 (T = row tiles
+// per workgroup).  The rest stays in the argument block a, read after the first
+// loads are issued.  Arguments are laid out in order, each at its natural
+// alignment, so the block starts at kArgsAt.
+struct LeadArgs {
+  const void* xin;
+  const uint8_t *wp0, *wp1, *wp2;
+  int n0, n1, n2, g1, g2;
+  uint32_t mtck;
+};
+constexpr int kArgsAt =
+    (sizeof(LeadArgs) + alignof(GemvArgs) - 1) / alignof(GemvArgs) * alignof(GemvArgs);
+
 // XMODE 0: int8 x_q.  XMODE 1 + f, f = bf16 (1) | gated by a.xup (2) | RMS norm
 // with a.gnorm (4): fp32 / bf16 input quantised in the kernel.  The prologue
 // options are compile-time so that no load sits behind a runtime branch.
 template <int XMODE, int R, int FMT>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const uint8_t* wp0,
+                                                        const uint8_t* wp1, const uint8_t* wp2,
+                                                        int n0, int n1, int n2, int g1, int g2,
+                                                        uint32_t mtck, const GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int F = XMODE > 0 ? XMODE - 1 : 0;
   constexpr bool BF = (F & 1) != 0;
@@ -268,16 +293,42 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
   const int r = lane & 15;  // A operand: row of the tile; B operand: token
   const int g = lane >> 4;  // 16-k block of the operand within a 64-k chunk
-  // this workgroup's matrix (each workgroup's tiles belong to one matrix)
-  const Prologue pro = load_prologue(a);
-  const int M = pro.M, K = pro.K, T = pro.T;
+  const int M = (int)(mtck & 31u), T = (int)((mtck >> 5) & 31u), K = (int)(mtck >> 13);
+  // this workgroup's matrix (each workgroup's tiles belong to one matrix); only a
+  // fourth matrix waits for the argument block
+  const int b = (int)blockIdx.x;
+  const uint8_t* wmat = wp0;
+  int nrows = n0, wgm = 0;
+  if (b >= g1) { wmat = wp1; nrows = n1; wgm = g1; }
+  if (b >= g2) { wmat = wp2; nrows = n2; wgm = g2; }
+  if (((mtck >> 10) & 7u) == 4u) {
+    // (loaded and waited for in one asm block: loads the compiler sees, it hoists
+    // to the entry, and every launch would then wait for them before its first
+    // weight loads)
+    int g3, n3;
+    uint64_t w3;
+    asm volatile(
+        "s_load_dword %0, %3, %4\n\t"
+        "s_load_dword %1, %3, %5\n\t"
+        "s_load_dwordx2 %2, %3, %6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=s"(g3), "=s"(n3), "=s"(w3)
+        : "s"(__builtin_amdgcn_kernarg_segment_ptr()),
+          "i"(kArgsAt + offsetof(GemvArgs, wg0) + 12), "i"(kArgsAt + offsetof(GemvArgs, n) + 12),
+          "i"(kArgsAt + offsetof(GemvArgs, wp) + 24));
+    if (b >= g3) {
+      wmat = reinterpret_cast<const uint8_t*>(w3);
+      nrows = n3;
+      wgm = g3;
+    }
+  }
   const uint32_t rowb = FMT == kFmtT1 ? 16u * (((uint32_t)K + 79u) / 80u)
                                       : (uint32_t)K >> 2;  // packed bytes per row
-  const uint8_t* wmat = pro.wp;
-  const int nrows = pro.n;
-  const int tl0 = ((int)blockIdx.x - pro.wg0) * T;   // first tile in the matrix
+  const int tl0 = (b - wgm) * T;                     // first tile in the matrix
   const int ntiles = min(T, (nrows + 15) / 16 - tl0);
-  const int kx = pro.kx;
+  // the fused modes stage all of K in one phase (launch_gemv checks it)
+  const int kx = XMODE > 0 ? K : min(K, kx_cap<FMT>(M));
+  const int phases = XMODE > 0 ? 1 : (K + kx - 1) / kx;
   const int stride = FMT == kFmtT1 ? 80 * ((kx + 79) / 80) + 16 : kx + 16;  // stage_stride
 
   uint8_t* xs = smem;                                    // [M][stride]
@@ -299,16 +350,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     return make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), bytes);
   };
 
-  // clear the partial tiles and the zero slot; scalars the epilogue needs are
-  // loaded now so that their latency hides behind the stream
+  // clear the partial tiles and the zero slot
   for (int i = tid; i < T * 64; i += kThreads) reinterpret_cast<uint4*>(part)[i] = make_uint4(0, 0, 0, 0);
   if (tid < ZB / 4) reinterpret_cast<uint32_t*>(zero)[tid] = 0u;
-  // (buffer loads: the pointers come out of the asm above as generic pointers,
-  // and generic loads would make the compiler's waits for every load conservative)
-  const float xs_t = XMODE == 0 ? __uint_as_float(bload4(make_rsrc(pro.xs, 4u * (uint32_t)M),
-                                                         4u * (uint32_t)min(tid, M - 1)))
-                                : 0.0f;
-  const float gamma = __uint_as_float(bload4(make_rsrc(pro.ws, 4u), 0u));
+  // the rest of the arguments and the epilogue's scalars, fetched once the first
+  // activation and weight loads are in flight (phase 0 below)
+  Prologue pro{};
+  float xs_t = 0.0f, gamma = 0.0f;
 
   // token groups: G consecutive threads per token (G = 256 / 2^ceil(log2 M));
   // threads of tokens >= M idle in the per-token passes
@@ -317,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
   const int tk = tid >> lgG;
   const int jg = tid & (G - 1);
 
-  for (int p = 0; p < pro.phases; ++p) {
+  for (int p = 0; p < phases; ++p) {
     const int k0 = p * kx;
     const int klen = min(kx, K - k0);
     // chunks (16 packed bytes of a row: 64 k, T1 80 k) in this phase
@@ -336,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     // counters are uniform, so no per-lane division is needed
     const int J16 = (K16s + 255) >> 8;             // blocks per token
     uint4 xv[kStageBatch];
-    const auto xr = make_rsrc(pro.xq, (uint32_t)M * (uint32_t)K);
+    const auto xr = make_rsrc(xin, (uint32_t)M * (uint32_t)K);
     int lt = 0, lj = 0;                            // next piece to load
     auto xload = [&]() -> uint4 {
       const int c = 256 * lj + tid;
@@ -350,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
       return v;
     };
     // fused: group c of this thread's token (zeros past the end or for idle threads)
-    const auto fr = make_rsrc(pro.xf, (uint32_t)M * (uint32_t)K * ES);
+    const auto fr = make_rsrc(xin, (uint32_t)M * (uint32_t)K * ES);
     auto foff = [&](int c, int h) -> uint32_t {
       return (tk < M && c < K16) ? ((uint32_t)tk * (uint32_t)K + 16u * (uint32_t)c) * ES + 16u * h
                                  : kOob;
@@ -358,8 +406,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     // prologue operands: the up projection (same layout as the input) and the
     // norm weight (fp32 [K], 64 bytes per group)
     constexpr bool glu = GLU, nrm = NRM;
-    const auto ur = make_rsrc(glu ? a.xup : pro.xf, (uint32_t)M * (uint32_t)K * ES);
-    const auto gr = make_rsrc(nrm ? (const void*)a.gnorm : pro.xf, nrm ? 4u * (uint32_t)K : 0u);
+    const auto ur = make_rsrc(glu ? a.xup : xin, (uint32_t)M * (uint32_t)K * ES);
+    const auto gr = make_rsrc(nrm ? (const void*)a.gnorm : xin, nrm ? 4u * (uint32_t)K : 0u);
     auto goff = [&](int c, int h) -> uint32_t {
       return (tk < M && c < K16) ? 64u * (uint32_t)c + 16u * (uint32_t)h : kOob;
     };
@@ -402,6 +450,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
     for (int u = 0; u < R; ++u) {
       ring[u] = next_load();
       asm volatile("" ::: "memory");  // keep the ring's loads in slot order
+    }
+    if (p == 0) {
+      pro = load_prologue(a, g1, g2);
+      // (buffer loads: the pointers come out of the asm in load_prologue as generic
+      // pointers, and generic loads would make the compiler's waits conservative)
+      if (XMODE == 0)
+        xs_t = __uint_as_float(bload4(make_rsrc(pro.xs, 4u * (uint32_t)M),
+                                      4u * (uint32_t)min(tid, M - 1)));
+      gamma = __uint_as_float(bload4(make_rsrc(pro.ws, 4u), 0u));
     }
 
     // 2. stage the activations, transposed within each 16-byte group
@@ -526,7 +583,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         put(jg + G * b, v);
       }
     }
-    if (XMODE == 0 && p == 0 && tid < M) dsc[tid] = xs_t;
     lds_barrier();
 
     // 3. stream: consumer position (tc, jc); flush a tile's partial when it ends
@@ -543,7 +599,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
           v4i a0 = t[0], a1 = t[1], a2 = t[2], a3 = t[3], a4 = t[4];
           asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(a4)::"memory");
           ring[u] = next_load();
-          const int bb = (bt >= 0 && c < C) ? bt + 80 * c : M * stride;
+          // (a 24-bit product: a 32-bit one is made a 64-bit multiply-add whose
+          // unused high addend can be a register with a load in flight, which the
+          // compiler then waits for)
+          const int bb = (bt >= 0 && c < C) ? bt + (int)__umul24(80u, (uint32_t)c) : M * stride;
           const v4i* bp = reinterpret_cast<const v4i*>(xs + bb);
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bp[0], acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bp[1], acc, 0, 0, 0);
@@ -581,8 +640,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a) {
         }
       }
     }
-    if (p + 1 < pro.phases) lds_barrier();  // the next phase overwrites the staged activations
+    if (p + 1 < phases) lds_barrier();  // the next phase overwrites the staged activations
   }
+  // token scales of the int8 input (loaded after the ring, so written only now,
+  // when the stream has waited for every load)
+  if (XMODE == 0 && tid < M) dsc[tid] = xs_t;
   lds_barrier();
 
   // 4. rescale, store: index = ((tile * M) + token) * 16 + row
@@ -647,7 +709,7 @@ int device_cus() {
 }
 
 bool gemv_fits(int64_t M, int64_t K, int fmt) {
-  return M >= 1 && M <= kMaxM &&
+  return M >= 1 && M <= kMaxM && K <= kGemvMaxK &&
          (fmt == kFmtT1 ? K >= 16 && (K % 16) == 0 : K >= 64 && (K % 64) == 0);
 }
 
@@ -699,15 +761,22 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
                                      : select_kernel<kFmt2>(xmode, ring);
   const size_t lds = (size_t)lds_bytes(tpw, a.M, a.K, fmt);
   a.tiles_per_wg = tpw;
-  a.kx = kx;
-  a.phases = (a.K + kx - 1) / kx;
   a.mdiv = (65536 + a.M - 1) / a.M;  // tt / M == (tt * mdiv) >> 16 for tt < 256, M <= 16
   int w0 = 0;
   for (int j = 0; j < kMaxGroup; ++j) {
     a.wg0[j] = w0;
     if (j < a.count) w0 += (tiles[j] + tpw - 1) / tpw;
   }
-  void* args[] = {&a};
+  // the preloaded leading arguments (LeadArgs)
+  const void* xin = fused ? a.xf : static_cast<const void*>(a.xq);
+  const uint8_t* wp0 = a.wp[0];
+  const uint8_t* wp1 = a.count > 1 ? a.wp[1] : a.wp[0];
+  const uint8_t* wp2 = a.count > 2 ? a.wp[2] : a.wp[0];
+  int n0 = a.n[0], n1 = a.count > 1 ? a.n[1] : 0, n2 = a.count > 2 ? a.n[2] : 0;
+  int g1 = a.wg0[1], g2 = a.wg0[2];
+  uint32_t mtck = (uint32_t)a.M | ((uint32_t)tpw << 5) | ((uint32_t)a.count << 10) |
+                  ((uint32_t)a.K << 13);
+  void* args[] = {&xin, &wp0, &wp1, &wp2, &n0, &n1, &n2, &g1, &g2, &mtck, &a};
   return hipLaunchKernel(kernel, dim3((unsigned)wgs), dim3(kThreads), args, lds, s);
 }
 
