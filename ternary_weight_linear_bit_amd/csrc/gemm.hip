@@ -322,19 +322,33 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 
 hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (a.K % 64 != 0 || a.count < 1 || a.count > kMaxGroup) return hipErrorInvalidValue;
-  // Tiles of 128 tokens x 128 rows (4 waves; three workgroups per compute unit)
-  // or 128 x 256 (8 waves; one per compute unit, half the activation traffic and
-  // staging per product).  Measured on the prefill shapes: the 8-wave tile wins
-  // (by 10-12%) only when its tiles fill one round of the chip almost exactly;
-  // otherwise the finer 4-wave tiles and their extra waves win.  256-token tiles
-  // and 4 x 32-row blocks per wave measured slower everywhere (registers: one
-  // wave per SIMD).
-  const int64_t mt = (a.M + 127) / 128;
-  int64_t rows4 = 0;
-  for (int j = 0; j < a.count; ++j) rows4 += (a.n[j] + 255) / 256;
+  // Three tile shapes:
+  //  * 256 tokens x 256 rows (8 waves of 128 x 64; one workgroup per compute
+  //    unit, two waves per SIMD): a wave's weight expansion serves twice the
+  //    tokens and the staging of the activations twice the rows, about 5 vector
+  //    instructions per matrix instruction instead of 8 (vector and matrix
+  //    instructions of one SIMD largely take turns, so this is the main cost
+  //    besides the products).  Chosen when its tiles fill at least 80% of the
+  //    compute units over the launch's rounds;
+  //  * 128 x 256 (8 waves of 64 x 64; one per compute unit), when its tiles fill
+  //    90-100% of one round;
+  //  * else 128 x 128 (4 waves; three workgroups per compute unit).
+  // Measured on the prefill shapes; 4 x 32-row blocks per wave measured slower
+  // everywhere (registers: one wave per SIMD).
   const int cus = device_cus();
-  const bool wide = rows4 * mt <= cus && 10 * rows4 * mt >= 9 * (int64_t)cus;
-  const int bn = wide ? 256 : 128;
+  auto row_tiles = [&](int bn) {
+    int64_t t = 0;
+    for (int j = 0; j < a.count; ++j) t += (a.n[j] + bn - 1) / bn;
+    return t;
+  };
+  const int64_t big_tiles = ((a.M + 255) / 256) * row_tiles(256);
+  const int64_t big_rounds = (big_tiles + cus - 1) / cus;
+  const bool big = big_tiles > 0 && 5 * big_tiles >= 4 * big_rounds * (int64_t)cus;
+  const int64_t mt = (a.M + 127) / 128;
+  const int64_t rows4 = row_tiles(256);
+  const bool wide = !big && rows4 * mt <= cus && 10 * rows4 * mt >= 9 * (int64_t)cus;
+  const int bm = big ? 256 : 128;
+  const int bn = big || wide ? 256 : 128;
   int64_t nbt = 0;
   for (int j = 0; j < kMaxGroup; ++j) {
     a.nb0[j] = (int)nbt;
@@ -342,11 +356,13 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   }
   a.nb0[kMaxGroup] = (int)nbt;
   for (int j = a.count; j <= kMaxGroup; ++j) a.nb0[j] = (int)nbt;
-  const int64_t tiles = nbt * mt;
+  const int64_t tiles = nbt * ((a.M + bm - 1) / bm);
   if (tiles == 0) return hipSuccess;
   if (tiles > (int64_t)1 << 30) return hipErrorInvalidValue;  // grid and tile index limits
   const dim3 grid((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds));
-  if (wide)
+  if (big)
+    hipLaunchKernelGGL((gemm_kernel<256, 4>), grid, dim3(512), 0, s, a);
+  else if (wide)
     hipLaunchKernelGGL((gemm_kernel<128, 4>), grid, dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((gemm_kernel<128, 2>), grid, dim3(256), 0, s, a);

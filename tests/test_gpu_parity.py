@@ -155,6 +155,9 @@ LINEAR_SHAPES = [
     # prefill kernel, 128 x 256 tiles (chosen when they fill one round of the
     # chip's compute units almost exactly): ragged M and N
     (2000, 4000, 64), (1920, 3900, 192),
+    # prefill kernel, 256 x 256 tiles (chosen when they fill at least 80% of the
+    # compute units over the launch's rounds): ragged M and N, K of one half step
+    (2000, 6600, 64), (1100, 10400, 192),
     # decode kernel: several K phases, multi-tile workgroups, M = 16 at large K
     (16, 100, 14336), (1, 40, 28672), (3, 24, 65536), (1, 20, 131072), (2, 9000, 256),
     (1, 70000, 64), (16, 300, 1088),
@@ -324,11 +327,12 @@ def _group(ns, k, seed):
                                     (16, 1024, (48, 33)), (40, 512, (100, 130, 17)),
                                     (1, 64, (30000, 20000, 7)),
                                     (300, 256, (100, 37, 260, 5, 129)), (129, 128, (0, 300, 64)),
-                                    (2000, 64, (1990, 2000))])
+                                    (2000, 64, (1990, 2000)), (800, 64, (9000, 4100, 300))])
 def test_ternary_linear_multi(m, k, ns):
     """Grouped matrices sharing x_q, including more than 4 (split into launches),
     an empty matrix, and M beyond the decode kernel (up to four matrices per
-    prefill launch; 2000 x (1990, 2000) selects the 128 x 256 tiles)."""
+    prefill launch; 2000 x (1990, 2000) selects the 128 x 256 tiles and
+    800 x (9000, 4100, 300) the 256 x 256 tiles)."""
     mats = _group(ns, k, 900)
     xq, d = O.quantize_acts(I.activations(m, k, 901))
     accs = [torch.empty((m, n), dtype=torch.int32, device=DEV) for n in ns]
