@@ -255,8 +255,8 @@ bitnet_status bitnet_repack_t1(const uint8_t *w_packed, int64_t N, int64_t K, ui
 
 /*
  * bitnet_ternary_linear_multi on T1 weights: every mats[i].w_packed is a T1
- * matrix (16-byte aligned).  Needs 16 <= K < 524288, K % 16 == 0 and a 16-byte
- * aligned x_q; otherwise BITNET_ERR_SHAPE / BITNET_ERR_ALIGN (there is no generic
+ * matrix (16-byte aligned).  Needs K >= 16, K % 16 == 0 and a 16-byte aligned
+ * x_q; otherwise BITNET_ERR_SHAPE / BITNET_ERR_ALIGN (there is no generic
  * kernel for this layout).  Runs the decode kernel; M > 16 runs in groups of
  * 16 tokens, each streaming the weights again.
  */

@@ -193,8 +193,8 @@ bitnet_status run_linear_t1(const bitnet_matrix* mats, int count, const int8_t* 
   return BITNET_OK;
 }
 
-// T1 layout requirements on top of check_group: K % 16 == 0 (16 <= K < 2^19),
-// 16-byte aligned weights and int8 activations.
+// T1 layout requirements on top of check_group: K % 16 == 0, K >= 16, 16-byte
+// aligned weights and int8 activations.
 bitnet_status check_t1(const bitnet_matrix* mats, int count, const void* x_q, int64_t M,
                        int64_t K) {
   if (K < 16 || K > bitnet::kGemvMaxK || (K % 16) != 0) return BITNET_ERR_SHAPE;

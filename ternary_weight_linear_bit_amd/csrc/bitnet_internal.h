@@ -205,7 +205,8 @@ constexpr int kFmt2 = 0, kFmtT1 = 1;
 // (fmt 1: T1 weights); the fused variant (a.xf != nullptr) also needs M <= 4 and
 // the activations of all tokens in one LDS phase.
 constexpr int kGemvMaxM = 16;
-constexpr int64_t kGemvMaxK = (1 << 19) - 1;  // K travels in 19 bits of a kernel argument
+// K travels in 19 bits of a kernel argument (the linear calls accept K <= 2^17)
+constexpr int64_t kGemvMaxK = (1 << 19) - 1;
 bool gemv_fits(int64_t M, int64_t K, int fmt);
 bool gemv_fused_fits(int64_t M, int64_t K, int fmt);
 hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s);

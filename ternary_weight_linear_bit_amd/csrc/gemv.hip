@@ -105,10 +105,11 @@ int lds_bytes(int tiles, int M, int K, int fmt) {
 // M | T << 5 | count << 10 | K << 13) are the kernel's leading scalar arguments,
 // which the hardware preloads into SGPRs at wave launch (this file is built with
 // a kernarg preload count of 10): no argument load sits in front of the first
-// global loads.  The rest comes from GemvArgs in one round of scalar loads (the
-// empty asm makes them materialise together rather than as dependent rounds
-// after the matrix is known); its latency hides behind the first loads.  Pairs
-// of ints travel as one 64-bit value to stay within the asm operand limit.
+// global loads.  The rest comes from GemvArgs in one round of scalar loads,
+// issued once the first weight loads are in flight (the empty asm makes them
+// materialise together rather than as dependent rounds after the matrix is
+// known); their latency hides behind those loads.  Pairs of ints travel as one
+// 64-bit value to stay within the asm operand limit.
 // Matrices j >= count have wg0[j] = grid size and are never selected.
 struct Prologue {
   const float* ws;

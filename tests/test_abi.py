@@ -150,7 +150,7 @@ def test_t1_sizes_and_validation(lib):
     t = lib.bitnet_ternary_linear_t1
     assert t(m, 1, FAKE, FAKE, 1, 100, 0, None) == ESHAPE    # K % 16 != 0
     assert t(m, 1, FAKE, FAKE, 1, 0, 0, None) == ESHAPE      # K < 16
-    assert t(m, 1, FAKE, FAKE, 1, 1 << 19, 0, None) == ESHAPE  # K >= 2^19
+    assert t(m, 1, FAKE, FAKE, 1, 131072 + 16, 0, None) == ESHAPE  # K > BITNET_MAX_K
     assert t(modd, 1, FAKE, FAKE, 1, 96, 0, None) == EALIGN  # weights not 16-byte aligned
     assert t(m, 1, FAKE_ODD, FAKE, 1, 96, 0, None) == EALIGN
     assert t(m, 1, None, FAKE, 1, 96, 0, None) == ENULL
