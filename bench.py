@@ -72,7 +72,7 @@ def recorded_traffic():
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="bitnet2b-decode-m1-30L")
     p.add_argument("--no-cpu-baseline", action="store_true")
