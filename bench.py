@@ -345,15 +345,15 @@ def kernel_compare(torch, N, I, shapes, steps):
     return res
 
 
-def cpu_baseline(I, layer_shapes, seconds):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    whole 2B-shaped layers at M = 1 (act-quant + layer per matrix)."""
+_ORACLE_LAYER = None   # (mats, x0) shared with forked workers
+
+
+def _oracle_layers(seconds):
+    """Whole 2B-shaped layers at M = 1 through the oracle for `seconds`:
+    (packed bytes streamed, layers, elapsed)."""
     from oracle import bitnet_oracle as O
-    mats = {}
-    for i, (nm, k, n) in enumerate(layer_shapes):
-        mats[nm] = O.quantize_weights(I.master_weights(n, k, I.weight_seed(0, i)))
-    x0 = I.activations(1, layer_shapes[0][1])
-    nbytes = 0
+    mats, x0 = _ORACLE_LAYER
+    per_layer = sum(p.nbytes for p, _ in mats.values())
     layers_done = 0
     t0 = time.perf_counter()
     while True:
@@ -365,16 +365,41 @@ def cpu_baseline(I, layer_shapes, seconds):
         O.quant_linear(*mats["gate"], o)
         u = O.quant_linear(*mats["up"], o)[3]
         O.quant_linear(*mats["down"], u)
-        nbytes += sum(p.nbytes for p, _ in mats.values())
         layers_done += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{layers_done} x one 2B-shaped layer (7 matrices, "
-                      f"{sum(p.nbytes for p, _ in mats.values())} packed bytes) at M=1, "
-                      f"act-quant + unpack + int64 contraction + rescale, {el:.1f} s",
-            "host": platform.processor() or platform.machine(), "host_threads": os.cpu_count()}
+            return per_layer * layers_done, layers_done, el
+
+
+def cpu_baseline(I, layer_shapes, seconds, workers):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole 2B-shaped layers at M = 1 (act-quant + layer per matrix), on one core
+    and on `workers` processes at once (each runs its own layers; numpy's integer
+    contraction is single-threaded).  Runs before the GPU is touched, so the
+    worker processes are plain forks."""
+    global _ORACLE_LAYER
+    from oracle import bitnet_oracle as O
+    mats = {}
+    for i, (nm, k, n) in enumerate(layer_shapes):
+        mats[nm] = O.quantize_weights(I.master_weights(n, k, I.weight_seed(0, i)))
+    _ORACLE_LAYER = (mats, I.activations(1, layer_shapes[0][1]))
+    per_layer = sum(p.nbytes for p, _ in mats.values())
+    nbytes, layers_done, el = _oracle_layers(seconds)
+    res = {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{layers_done} x one 2B-shaped layer (7 matrices, {per_layer} packed bytes) "
+                     f"at M=1, act-quant + unpack + int64 contraction + rescale, {el:.1f} s",
+           "host": platform.processor() or platform.machine(), "host_threads": os.cpu_count()}
+    if workers > 1:
+        import multiprocessing
+        with multiprocessing.get_context("fork").Pool(workers) as pool:
+            parts = pool.map(_oracle_layers, [seconds] * workers)
+        total = sum(b for b, _, _ in parts)
+        wall = max(e for _, _, e in parts)
+        res["all_cores"] = {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
+                            "sample": f"{sum(n for _, n, _ in parts)} layers over {workers} processes, "
+                                      f"{wall:.1f} s"}
+    _ORACLE_LAYER = None
+    return res
 
 
 def main():
@@ -390,6 +415,12 @@ def main():
     wl = I.WORKLOADS[args.workload]
     if wl["m"] != (1,) or len(wl["layer"]) != 7:
         raise SystemExit("bench.py times the layer-stack decode workloads")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before the GPU is initialised: the all-cores leg forks worker processes
+        workers = min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(I, wl["layer"], args.cpu_seconds, workers)
+        log(f"cpu baseline: {cpu}")
     torch.cuda.set_device(0)
     N.lib()
     d = decode_leg(torch, N, I, args.workload, args.steps, args.warmup)
@@ -461,9 +492,8 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         result["calib_copy_bytes"] = 2 * a.numel() * 4
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(I, wl["layer"], args.cpu_seconds)
-        log(f"cpu baseline: {result['cpu_baseline']}")
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
