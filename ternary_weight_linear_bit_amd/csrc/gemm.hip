@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 
 hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (a.K % 64 != 0 || a.count < 1 || a.count > kMaxGroup) return hipErrorInvalidValue;
-  // Three tile shapes:
+  // Four tile shapes:
   //  * 256 tokens x 256 rows (8 waves of 128 x 64; one workgroup per compute
   //    unit, two waves per SIMD): a wave's weight expansion serves twice the
   //    tokens and the staging of the activations twice the rows, about 5 vector
@@ -332,7 +332,10 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   //    compute units over the launch's rounds;
   //  * 128 x 256 (8 waves of 64 x 64; one per compute unit), when its tiles fill
   //    90-100% of one round;
-  //  * else 128 x 128 (4 waves; three workgroups per compute unit).
+  //  * else 128 x 128 (4 waves; three workgroups per compute unit), or 64 x 128
+  //    (4 waves of 32 x 64) when 128 x 128 tiles would not cover the compute
+  //    units once: twice the tiles, each half as long, at some cost per product
+  //    (the weight expansion serves half the tokens).
   // Measured on the prefill shapes; 4 x 32-row blocks per wave measured slower
   // everywhere (registers: one wave per SIMD).
   const int cus = device_cus();
@@ -347,7 +350,8 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   const int64_t mt = (a.M + 127) / 128;
   const int64_t rows4 = row_tiles(256);
   const bool wide = !big && rows4 * mt <= cus && 10 * rows4 * mt >= 9 * (int64_t)cus;
-  const int bm = big ? 256 : 128;
+  const bool small = !big && !wide && mt * row_tiles(128) <= cus;
+  const int bm = big ? 256 : small ? 64 : 128;
   const int bn = big || wide ? 256 : 128;
   int64_t nbt = 0;
   for (int j = 0; j < kMaxGroup; ++j) {
@@ -362,6 +366,8 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   const dim3 grid((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds));
   if (big)
     hipLaunchKernelGGL((gemm_kernel<256, 4>), grid, dim3(512), 0, s, a);
+  else if (small)
+    hipLaunchKernelGGL((gemm_kernel<64, 2>), grid, dim3(256), 0, s, a);
   else if (wide)
     hipLaunchKernelGGL((gemm_kernel<128, 4>), grid, dim3(512), 0, s, a);
   else

@@ -149,9 +149,12 @@ LINEAR_SHAPES = [
     # decode kernel: several 16-row tiles, ragged N, K not a multiple of 256
     (1, 16, 64), (1, 37, 256), (1, 640, 2560), (1, 200, 320), (3, 100, 1024), (4, 256, 256),
     (16, 48, 2048), (5, 33, 6912), (2, 17, 28672), (1, 2560, 6912),
-    # prefill kernel: ragged M and N, several 128 x 128 tiles
+    # prefill kernel, 64 x 128 tiles (chosen when 128 x 128 tiles would not cover
+    # the compute units once): ragged M and N
     (17, 100, 256), (100, 130, 2560), (300, 257, 192), (128, 128, 64), (513, 640, 512),
     (16, 50, 4096),
+    # prefill kernel, 128 x 128 tiles: ragged M and N, K of one and a half steps
+    (1000, 5000, 192), (700, 9000, 64),
     # prefill kernel, 128 x 256 tiles (chosen when they fill one round of the
     # chip's compute units almost exactly): ragged M and N
     (2000, 4000, 64), (1920, 3900, 192),
