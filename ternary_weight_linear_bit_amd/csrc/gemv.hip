@@ -305,7 +305,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   if (((mtck >> 10) & 7u) == 4u) {
     // (loaded and waited for in one asm block: loads the compiler sees, it hoists
     // to the entry, and every launch would then wait for them before its first
-    // weight loads)
+    // weight loads; early-clobber outputs, since the block issues several loads
+    // from the one segment pointer)
     int g3, n3;
     uint64_t w3;
     asm volatile(
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
         "s_load_dword %1, %3, %5\n\t"
         "s_load_dwordx2 %2, %3, %6\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=s"(g3), "=s"(n3), "=s"(w3)
+        : "=&s"(g3), "=&s"(n3), "=&s"(w3)
         : "s"(__builtin_amdgcn_kernarg_segment_ptr()),
           "i"(kArgsAt + offsetof(GemvArgs, wg0) + 12), "i"(kArgsAt + offsetof(GemvArgs, n) + 12),
           "i"(kArgsAt + offsetof(GemvArgs, wp) + 24));
