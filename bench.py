@@ -24,8 +24,9 @@ into the launches), the 8B-shaped stack (32 layers) at M = 1 and M = 16, the
 prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096 and on the
 8B shapes at M = 2048, the 2B and 100B chains with weights packed five per byte
 (T1 layout, 1.6 bits per weight), single matrices at M = 1 through the
-matrix-core kernel (2-bit and T1 weights) and the lookup-table path, and the CPU
-oracle timed on a bounded sample of the same decode workload.
+matrix-core kernel (2-bit and T1 weights) and the lookup-table path, the
+standalone weight and activation quantisers against HBM, and the CPU oracle
+timed on a bounded sample of the same decode workload (one core and all cores).
 """
 
 from __future__ import annotations
@@ -82,6 +83,8 @@ def parse():
                    help="skip the full-layer 2B chain and the 8B-shaped chains")
     p.add_argument("--no-t1", action="store_true",
                    help="skip the legs with weights packed five per byte")
+    p.add_argument("--no-quant", action="store_true",
+                   help="skip the standalone quantiser leg")
     p.add_argument("--no-compare", action="store_true",
                    help="skip the single-matrix comparison of the decode kernels")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -345,6 +348,69 @@ def kernel_compare(torch, N, I, shapes, steps):
     return res
 
 
+def quantisers(torch, N, I, steps):
+    """The standalone quantisers against HBM: bitnet_quantize_weights (absmean
+    scale + ternary 2-bit pack; two passes over the master weights, 2 x (2|4) B
+    in + 0.25 B out per weight) and bitnet_quantize_acts (per-token absmax int8;
+    M K (2|4) B in, M K + 4 M B out).  Each shape runs over >= 1 GiB of input
+    copies, replayed from a HIP graph, so inputs stream from HBM."""
+    res = {}
+    for n, k, dt in ((6912, 2560, torch.float32), (6912, 2560, torch.bfloat16),
+                     (28672, 8192, torch.float32)):
+        es = 2 if dt == torch.bfloat16 else 4
+        copies = max(2, math.ceil(CACHE_CYCLE_BYTES / (n * k * es)))
+        g = torch.Generator(device="cuda").manual_seed(I.weight_seed(0, 0))
+        ws = [torch.randn((n, k), generator=g, device="cuda").mul_(I.WEIGHT_SIGMA).to(dt)
+              for _ in range(copies)]
+        packed = torch.empty((n, k // 4), dtype=torch.uint8, device="cuda")
+        scale = torch.empty(1, dtype=torch.float32, device="cuda")
+        work = torch.empty(N.lib().bitnet_quantize_weights_workspace_bytes(n, k),
+                           dtype=torch.uint8, device="cuda")
+        us = _graph_time(torch, lambda: [N.bitnet_quantize_weights(w, packed, scale, work)
+                                         for w in ws], steps) / copies
+        nbytes = n * k * (2 * es) + n * k // 4
+        res[f"weights {n}x{k} {'bf16' if es == 2 else 'f32'}"] = {
+            "us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+            "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del ws, packed, scale, work
+        torch.cuda.empty_cache()
+    for m, k in ((4096, 6912), (4096, 2560), (2048, 14336)):
+        copies = max(2, math.ceil(CACHE_CYCLE_BYTES / (m * k * 2)))
+        g = torch.Generator(device="cuda").manual_seed(I.ACT_SEED)
+        xs = [torch.randn((m, k), generator=g, device="cuda").to(torch.bfloat16) for _ in range(copies)]
+        x_q = torch.empty((m, k), dtype=torch.int8, device="cuda")
+        x_s = torch.empty(m, dtype=torch.float32, device="cuda")
+        us = _graph_time(torch, lambda: [N.bitnet_quantize_acts(x, x_q, x_s) for x in xs],
+                         steps) / copies
+        nbytes = m * k * 2 + m * k + 4 * m
+        res[f"acts {m}x{k} bf16"] = {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1),
+                                     "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del xs, x_q, x_s
+        torch.cuda.empty_cache()
+    log(f"quantisers: {res}")
+    return res
+
+
+def _graph_time(torch, fn, steps):
+    """Mean microseconds of one replay of fn captured in a HIP graph."""
+    fn()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        fn()
+    gr.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del gr
+    return us
+
+
 _ORACLE_LAYER = None   # (mats, x0) shared with forked workers
 
 
@@ -476,6 +542,8 @@ def main():
             result["decode_100b_t1"] = dict(
                 workload="ternary100b-decode-m1-96L, weights five per byte (T1 layout)",
                 **leg_summary(d6, 1))
+    if not args.no_quant:
+        result["quantisers"] = quantisers(torch, N, I, steps=3)
     if not args.no_compare:
         result["kernel_compare_m1"] = kernel_compare(
             torch, N, I, ((2560, 2560), (2560, 6912), (6912, 2560), (8192, 28672), (28672, 8192)),

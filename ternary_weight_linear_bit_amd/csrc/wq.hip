@@ -10,7 +10,7 @@
 // Every finite fp32 |w| is an integer count of 2^-149 units: (2^23 + frac) shifted
 // left by (biased exponent - 1), or frac for sub-normals.  Pass 1 adds the 24-bit
 // significands into 256 uint64 buckets keyed by biased exponent (integer atomics:
-// exact and order-free).  Pass 2 (one thread) forms the exact sum in a 320-bit
+// exact and order-free).  Pass 2 (one wave) forms the exact sum in a 320-bit
 // integer, divides by N*K and rounds once to fp32.  Pass 3 ternarises and packs.
 //
 // T1 output (five codes per byte, a reading of the same pages' log2(3) ~ 1.58
@@ -52,6 +52,37 @@ __device__ __forceinline__ void hist_add(unsigned long long* sb, uint32_t bits) 
   }
 }
 
+// A thread's running sums for a window of kWin consecutive exponents starting at
+// base (set by its first nonzero finite weight, a few octaves below it): the
+// weights of a matrix crowd into a few octaves, so most of them land here and
+// only the rest become LDS atomics (which serialise when a wave's lanes hit the
+// same bucket, as most of them would).
+constexpr int kWin = 8;
+struct HistWindow {
+  unsigned long long acc[kWin];
+  int base;
+};
+
+__device__ __forceinline__ void window_add(HistWindow& h, unsigned long long* sb,
+                                           uint32_t bits) {
+  const uint32_t e = (bits >> 23) & 0xffu;
+  const uint32_t f = bits & 0x7fffffu;
+  if (e == 0xffu) {
+    atomicAdd(&sb[255], 1ull);                      // non-finite flag
+    return;
+  }
+  const uint32_t m = e ? (f | 0x800000u) : f;       // units of 2^(max(e,1)-1-149)
+  if (!m) return;
+  if (h.base < 0) h.base = e > kWin - 3 ? (int)e - (kWin - 3) : 0;
+  const uint32_t d = e - (uint32_t)h.base;
+  if (d < (uint32_t)kWin) {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j) h.acc[j] += d == (uint32_t)j ? m : 0u;
+  } else {
+    atomicAdd(&sb[e], (unsigned long long)m);
+  }
+}
+
 // Pass 1: per-exponent integer sums of the significands of |w|.
 template <bool BF16>
 __global__ __launch_bounds__(kHistThreads) void wq_hist(const void* __restrict__ w,
@@ -65,18 +96,36 @@ __global__ __launch_bounds__(kHistThreads) void wq_hist(const void* __restrict__
   const int64_t nvec = vec ? count / kVec : 0;
   const int64_t stride = (int64_t)gridDim.x * kHistThreads;
   const uint4* wv = reinterpret_cast<const uint4*>(w);
-  for (int64_t v = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; v < nvec; v += stride) {
-    const uint4 p = wv[v];
-    const uint32_t d[4] = {p.x, p.y, p.z, p.w};
+  HistWindow hw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (BF16) {
-        hist_add(sb, d[j] << 16);
-        hist_add(sb, d[j] & 0xffff0000u);
-      } else {
-        hist_add(sb, d[j]);
+  for (int j = 0; j < kWin; ++j) hw.acc[j] = 0ull;
+  hw.base = -1;
+  // four vectors in flight per thread (zeros past the end add nothing)
+  constexpr int kIn = 4;
+  for (int64_t v = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; v < nvec;
+       v += kIn * stride) {
+    uint4 p[kIn];
+#pragma unroll
+    for (int u = 0; u < kIn; ++u)
+      p[u] = v + u * stride < nvec ? wv[v + u * stride] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kIn; ++u) {
+      const uint32_t d[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (BF16) {
+          window_add(hw, sb, d[j] << 16);
+          window_add(hw, sb, d[j] & 0xffff0000u);
+        } else {
+          window_add(hw, sb, d[j]);
+        }
       }
     }
+  }
+  if (hw.base >= 0) {
+#pragma unroll
+    for (int j = 0; j < kWin; ++j)
+      if (hw.acc[j]) atomicAdd(&sb[hw.base + j], hw.acc[j]);
   }
   for (int64_t i = nvec * kVec + (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < count;
        i += stride)
@@ -86,20 +135,42 @@ __global__ __launch_bounds__(kHistThreads) void wq_hist(const void* __restrict__
   if (s) atomicAdd(&gb[threadIdx.x], s);
 }
 
-__device__ __forceinline__ void add_u64(uint64_t L[5], uint64_t x) {
-  uint64_t prev = L[0];
-  L[0] += x;
-  uint64_t carry = L[0] < prev;
+// L += x * 2^sh for a 320-bit L (five 64-bit limbs, least significant first);
+// sh <= 253 and the sum stays below 2^320.
+__device__ __forceinline__ void add_shifted(uint64_t L[5], uint64_t x, int sh) {
+  const int li = sh >> 6, off = sh & 63;
+  uint64_t add[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
 #pragma unroll
-  for (int i = 1; i < 5; ++i) {
-    prev = L[i];
-    L[i] += carry;
-    carry = (L[i] < prev);
+  for (int i = 0; i < 5; ++i) {
+    if (i == li) add[i] = x << off;
+    if (i == li + 1 && off) add[i] = x >> (64 - off);
+  }
+  uint64_t carry = 0ull;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t s = L[i] + add[i];
+    const uint64_t c1 = s < L[i];
+    L[i] = s + carry;
+    carry = c1 | (L[i] < s);
   }
 }
 
-// Pass 2 (one thread): gamma* = max(RN32(S * 2^-149 / count), RN32(1e-5)) and the
-// ternarisation threshold.
+// L += R (320-bit).
+__device__ __forceinline__ void add_limbs(uint64_t L[5], const uint64_t R[5]) {
+  uint64_t carry = 0ull;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t s = L[i] + R[i];
+    const uint64_t c1 = s < L[i];
+    L[i] = s + carry;
+    carry = c1 | (L[i] < s);
+  }
+}
+
+// Pass 2 (one wave): gamma* = max(RN32(S * 2^-149 / count), RN32(1e-5)) and the
+// ternarisation threshold.  Lane l adds buckets 4l .. 4l + 3, each shifted to its
+// place, into a 320-bit partial sum; five rounds of shuffles add the partials
+// (integer sums: the same S in any order); lane 0 rounds.
 //
 // Threshold: q = +1 exactly when RN32(w / gamma*) > 0.5.  The fp32 values next to
 // 0.5 are 0.5 - 2^-25 and 0.5 + 2^-24, and a tie at 0.5 + 2^-25 rounds to 0.5
@@ -108,27 +179,38 @@ __device__ __forceinline__ void add_u64(uint64_t L[5], uint64_t x) {
 // significands), and for fp32 w the test w > T equals w >= thr with thr the
 // smallest fp32 above T.  q = -1 is the mirror image.  This gives the quotient's
 // correctly rounded decision without a per-weight division.
-__global__ void wq_finish(const unsigned long long* __restrict__ b, unsigned long long count,
-                          float* __restrict__ w_scale, float* __restrict__ thr_out) {
-  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+__global__ __launch_bounds__(64) void wq_finish(const unsigned long long* __restrict__ b,
+                                                 unsigned long long count,
+                                                 float* __restrict__ w_scale,
+                                                 float* __restrict__ thr_out) {
+  const int lane = threadIdx.x;
+  if (blockIdx.x != 0 || lane >= 64) return;
   if (b[255] != 0ull) {
-    *w_scale = __uint_as_float(0x7fc00000u);
-    *thr_out = __uint_as_float(0x7fc00000u);
+    if (lane == 0) {
+      *w_scale = __uint_as_float(0x7fc00000u);
+      *thr_out = __uint_as_float(0x7fc00000u);
+    }
     return;
   }
-  // S = sum_{e>=1} b[e] * 2^(e-1) + b[0]  (Horner from the top exponent down)
+  // S = sum_{e>=1} b[e] * 2^(e-1) + b[0]
   uint64_t L[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
-  for (int e = 254; e >= 1; --e) {
-    uint64_t carry = 0ull;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int e = 4 * lane + t;
+    if (e < 255) add_shifted(L, b[e], e > 0 ? e - 1 : 0);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint64_t R[5];
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-      const uint64_t v = L[i];
-      L[i] = (v << 1) | carry;
-      carry = v >> 63;
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)L[i], o, 64);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(L[i] >> 32), o, 64);
+      R[i] = ((uint64_t)hi << 32) | lo;
     }
-    add_u64(L, b[e]);
+    add_limbs(L, R);
   }
-  add_u64(L, b[0]);
+  if (lane != 0) return;
 
   float gamma = 0.0f;
   int top = -1;

@@ -174,8 +174,11 @@ def test_ternary_linear_bit_exact(m, n, k):
     check_linear(packed, gamma, xq, d, m, n, k)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 640, 2560), (300, 257, 192)])
+@pytest.mark.parametrize("m,n,k", [(1, 640, 2560), (300, 257, 192), (1000, 5000, 192),
+                                   (2000, 4000, 64), (2000, 6600, 64)])
 def test_ternary_linear_bf16_output(m, n, k):
+    """bf16 output from the decode kernel and from each prefill tile shape (64 x 128,
+    128 x 128, 128 x 256, 256 x 256)."""
     packed, gamma = O.quantize_weights(I.master_weights(n, k, 300 + n))
     xq, d = O.quantize_acts(I.activations(m, k, 400 + m))
     check_linear(packed, gamma, xq, d, m, n, k, y_dtype=torch.bfloat16)
@@ -350,7 +353,8 @@ def test_ternary_linear_multi(m, k, ns):
 @pytest.mark.parametrize("m,k,ns,dt", [(1, 2560, (2560, 640, 640), "bf16"),
                                        (1, 2560, (6912, 6912), "bf16"),
                                        (3, 512, (100, 37, 16, 64, 200), "f32"),
-                                       (1, 28672, (40, 24), "f32"), (8, 256, (16, 20), "f32")])
+                                       (1, 28672, (40, 24), "f32"), (8, 256, (16, 20), "f32"),
+                                       (600, 256, (300, 100, 700), "bf16")])
 def test_quant_linear_multi(m, k, ns, dt):
     mats = _group(ns, k, 950)
     xt, x_or = acts(m, k, 951, dt)
