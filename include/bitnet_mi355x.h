@@ -84,7 +84,7 @@ const char *bitnet_status_string(int status);
 /* Bytes of the packed weight matrix: N * (K / 4).  0 for invalid sizes. */
 size_t bitnet_packed_bytes(int64_t N, int64_t K);
 
-/* Bytes of device workspace bitnet_quantize_weights needs (a constant 4096). */
+/* Bytes of device workspace bitnet_quantize_weights needs (a constant 16640). */
 size_t bitnet_quantize_weights_workspace_bytes(int64_t N, int64_t K);
 
 /*

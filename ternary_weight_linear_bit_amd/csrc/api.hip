@@ -5,7 +5,6 @@
 
 namespace {
 
-constexpr size_t kWqWorkspaceBytes = 4096;
 constexpr int64_t kInt32Max = 2147483647;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -253,7 +252,7 @@ size_t bitnet_packed_bytes(int64_t N, int64_t K) {
 size_t bitnet_quantize_weights_workspace_bytes(int64_t N, int64_t K) {
   (void)N;
   (void)K;
-  return kWqWorkspaceBytes;
+  return bitnet::kWqWorkspaceBytes;
 }
 
 bitnet_status bitnet_quantize_weights(const void* w, int w_dtype, int64_t N, int64_t K,
@@ -262,7 +261,7 @@ bitnet_status bitnet_quantize_weights(const void* w, int w_dtype, int64_t N, int
   if (!w || !w_packed || !w_scale) return BITNET_ERR_NULL;
   if (!valid_dtype(w_dtype)) return BITNET_ERR_DTYPE;
   if (N < 1 || K < 4 || (K % 4) != 0 || N >= BITNET_MAX_WEIGHTS / K) return BITNET_ERR_SHAPE;
-  if (!workspace || workspace_bytes < kWqWorkspaceBytes) return BITNET_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < bitnet::kWqWorkspaceBytes) return BITNET_ERR_WORKSPACE;
   if (!aligned(w, esize(w_dtype)) || !aligned(w_scale, 4) || !aligned(workspace, 8))
     return BITNET_ERR_ALIGN;
   return from_hip(bitnet::launch_wq(w, w_dtype == BITNET_BF16, N * K, w_packed, w_scale, workspace,
@@ -280,7 +279,7 @@ bitnet_status bitnet_quantize_weights_t1(const void* w, int w_dtype, int64_t N, 
   if (!w || !w_t1 || !w_scale) return BITNET_ERR_NULL;
   if (!valid_dtype(w_dtype)) return BITNET_ERR_DTYPE;
   if (N < 1 || K < 1 || N >= BITNET_MAX_WEIGHTS / K) return BITNET_ERR_SHAPE;
-  if (!workspace || workspace_bytes < kWqWorkspaceBytes) return BITNET_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < bitnet::kWqWorkspaceBytes) return BITNET_ERR_WORKSPACE;
   if (!aligned(w, esize(w_dtype)) || !aligned(w_scale, 4) || !aligned(workspace, 8) ||
       !aligned(w_t1, 16))
     return BITNET_ERR_ALIGN;

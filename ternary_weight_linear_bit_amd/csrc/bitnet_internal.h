@@ -141,6 +141,11 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Host-side launchers (one per kernel family); each returns a hipError_t from
 // hipGetLastError() after its launches.
+// Weight quantisation workspace: kWqCopies copies of the 256 exponent buckets
+// (uint64) and the ternarisation threshold.
+constexpr int kWqCopies = 8;
+constexpr size_t kWqThresholdAt = (size_t)kWqCopies * 256 * 8;
+constexpr size_t kWqWorkspaceBytes = kWqThresholdAt + 256;
 hipError_t launch_wq(const void* w, bool w_bf16, int64_t n_weights, uint8_t* w_packed,
                      float* w_scale, void* workspace, hipStream_t s);
 // The same scale with the T1 layout (five codes per byte, 16 * ceil(K / 80) bytes

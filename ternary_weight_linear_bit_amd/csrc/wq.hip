@@ -10,7 +10,8 @@
 // Every finite fp32 |w| is an integer count of 2^-149 units: (2^23 + frac) shifted
 // left by (biased exponent - 1), or frac for sub-normals.  Pass 1 adds the 24-bit
 // significands into 256 uint64 buckets keyed by biased exponent (integer atomics:
-// exact and order-free).  Pass 2 (one wave) forms the exact sum in a 320-bit
+// exact and order-free; kWqCopies copies of the buckets, by workgroup, spread the
+// global atomics of the hot buckets over more addresses).  Pass 2 (one wave) forms the exact sum in a 320-bit
 // integer, divides by N*K and rounds once to fp32.  Pass 3 ternarises and packs.
 //
 // T1 output (five codes per byte, a reading of the same pages' log2(3) ~ 1.58
@@ -21,8 +22,9 @@
 // repack_t1 from the 2-bit layout.
 //
 // Workspace layout (device, caller-owned, >= kWsBytes):
-//   [0, 2048)    uint64 buckets[256]   (bucket 255 counts Inf/NaN weights)
-//   [2048, 2052) float  threshold      (see wq_finish)
+//   [0, kWqThresholdAt)  uint64 buckets[kWqCopies][256]  (bucket 255 counts
+//                        Inf/NaN weights)
+//   kWqThresholdAt       float threshold  (see wq_finish)
 #include "bitnet_internal.h"
 
 namespace bitnet {
@@ -32,7 +34,7 @@ constexpr int kHistThreads = 256;
 constexpr int kPackThreads = 256;
 
 __global__ __launch_bounds__(256) void wq_clear(unsigned long long* __restrict__ buckets) {
-  buckets[threadIdx.x] = 0ull;
+  for (int i = threadIdx.x; i < kWqCopies * 256; i += 256) buckets[i] = 0ull;
 }
 
 template <bool BF16>
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(kHistThreads) void wq_hist(const void* __restrict__
     hist_add(sb, load_bits<BF16>(w, i));
   __syncthreads();
   const unsigned long long s = sb[threadIdx.x];
-  if (s) atomicAdd(&gb[threadIdx.x], s);
+  if (s) atomicAdd(&gb[256 * (blockIdx.x % kWqCopies) + threadIdx.x], s);
 }
 
 // L += x * 2^sh for a 320-bit L (five 64-bit limbs, least significant first);
@@ -185,7 +187,17 @@ __global__ __launch_bounds__(64) void wq_finish(const unsigned long long* __rest
                                                  float* __restrict__ thr_out) {
   const int lane = threadIdx.x;
   if (blockIdx.x != 0 || lane >= 64) return;
-  if (b[255] != 0ull) {
+  // the copies' sums (each below 2^62: N K < 2^38 significands of < 2^24)
+  unsigned long long bk[4], nonfinite = 0ull;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bk[t] = 0ull;
+#pragma unroll
+    for (int c = 0; c < kWqCopies; ++c) bk[t] += b[256 * c + 4 * lane + t];
+  }
+#pragma unroll
+  for (int c = 0; c < kWqCopies; ++c) nonfinite |= b[256 * c + 255];
+  if (nonfinite != 0ull) {
     if (lane == 0) {
       *w_scale = __uint_as_float(0x7fc00000u);
       *thr_out = __uint_as_float(0x7fc00000u);
@@ -197,7 +209,7 @@ __global__ __launch_bounds__(64) void wq_finish(const unsigned long long* __rest
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int e = 4 * lane + t;
-    if (e < 255) add_shifted(L, b[e], e > 0 ? e - 1 : 0);
+    if (e < 255) add_shifted(L, bk[t], e > 0 ? e - 1 : 0);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -435,7 +447,7 @@ int grid_for(int64_t work_items, int threads, int max_blocks) {
 float* launch_scale(const void* w, bool w_bf16, int64_t n, float* w_scale, void* workspace,
                     hipStream_t s) {
   auto* buckets = reinterpret_cast<unsigned long long*>(workspace);
-  float* thr = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + 2048);
+  float* thr = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kWqThresholdAt);
   hipLaunchKernelGGL(wq_clear, dim3(1), dim3(256), 0, s, buckets);
   // 16-byte vector loads need a 16-byte aligned base; otherwise every element
   // takes the scalar loop.

@@ -48,22 +48,23 @@ def test_status_strings_and_sizes(lib):
     assert lib.bitnet_packed_bytes(2560, 6912) == 2560 * 6912 // 4
     assert lib.bitnet_packed_bytes(3, 6) == 0
     assert lib.bitnet_packed_bytes(-1, 8) == 0
-    assert lib.bitnet_quantize_weights_workspace_bytes(1, 4) >= 2048 + 4
+    assert lib.bitnet_quantize_weights_workspace_bytes(1, 4) == 16640   # 8 x 256 buckets + threshold
 
 
 def test_quantize_weights_validation(lib):
     f = lib.bitnet_quantize_weights
-    assert f(None, 0, 4, 8, FAKE, FAKE, FAKE, 4096, None) == ENULL
-    assert f(FAKE, 0, 4, 8, None, FAKE, FAKE, 4096, None) == ENULL
-    assert f(FAKE, 9, 4, 8, FAKE, FAKE, FAKE, 4096, None) == EDTYPE
-    assert f(FAKE, 0, 0, 8, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
-    assert f(FAKE, 0, 4, 6, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
-    assert f(FAKE, 0, 4, 0, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
-    assert f(FAKE, 0, 1 << 20, 1 << 18, FAKE, FAKE, FAKE, 4096, None) == ESHAPE  # N*K = 2^38
-    assert f(FAKE, 0, 4, 8, FAKE, FAKE, None, 4096, None) == EWS
+    ws = lib.bitnet_quantize_weights_workspace_bytes(4, 8)
+    assert f(None, 0, 4, 8, FAKE, FAKE, FAKE, ws, None) == ENULL
+    assert f(FAKE, 0, 4, 8, None, FAKE, FAKE, ws, None) == ENULL
+    assert f(FAKE, 9, 4, 8, FAKE, FAKE, FAKE, ws, None) == EDTYPE
+    assert f(FAKE, 0, 0, 8, FAKE, FAKE, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, 0, 4, 6, FAKE, FAKE, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, 0, 4, 0, FAKE, FAKE, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, 0, 1 << 20, 1 << 18, FAKE, FAKE, FAKE, ws, None) == ESHAPE  # N*K = 2^38
+    assert f(FAKE, 0, 4, 8, FAKE, FAKE, None, ws, None) == EWS
     assert f(FAKE, 0, 4, 8, FAKE, FAKE, FAKE, 100, None) == EWS
-    assert f(FAKE_ODD, 0, 4, 8, FAKE, FAKE, FAKE, 4096, None) == EALIGN     # fp32 at 2 bytes
-    assert f(FAKE, 0, 4, 8, FAKE, FAKE, FAKE_ODD, 4096, None) == EALIGN
+    assert f(FAKE_ODD, 0, 4, 8, FAKE, FAKE, FAKE, ws, None) == EALIGN     # fp32 at 2 bytes
+    assert f(FAKE, 0, 4, 8, FAKE, FAKE, FAKE_ODD, ws, None) == EALIGN
 
 
 def test_quantize_acts_validation(lib):
@@ -134,11 +135,12 @@ def test_t1_sizes_and_validation(lib):
     assert lib.bitnet_t1_packed_bytes(3, 1) == 48
     assert lib.bitnet_t1_packed_bytes(-1, 80) == 0
     q = lib.bitnet_quantize_weights_t1
-    assert q(None, 0, 4, 8, FAKE, FAKE, FAKE, 4096, None) == ENULL
-    assert q(FAKE, 9, 4, 8, FAKE, FAKE, FAKE, 4096, None) == EDTYPE
-    assert q(FAKE, 0, 4, 0, FAKE, FAKE, FAKE, 4096, None) == ESHAPE
+    ws = lib.bitnet_quantize_weights_workspace_bytes(4, 8)
+    assert q(None, 0, 4, 8, FAKE, FAKE, FAKE, ws, None) == ENULL
+    assert q(FAKE, 9, 4, 8, FAKE, FAKE, FAKE, ws, None) == EDTYPE
+    assert q(FAKE, 0, 4, 0, FAKE, FAKE, FAKE, ws, None) == ESHAPE
     assert q(FAKE, 0, 4, 8, FAKE, FAKE, FAKE, 16, None) == EWS
-    assert q(FAKE, 0, 4, 8, FAKE_ODD, FAKE, FAKE, 4096, None) == EALIGN
+    assert q(FAKE, 0, 4, 8, FAKE_ODD, FAKE, FAKE, ws, None) == EALIGN
     r = lib.bitnet_repack_t1
     assert r(None, 4, 8, FAKE, None) == ENULL
     assert r(FAKE, 4, 6, FAKE, None) == ESHAPE
