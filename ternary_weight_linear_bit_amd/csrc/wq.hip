@@ -54,14 +54,18 @@ __device__ __forceinline__ void hist_add(unsigned long long* sb, uint32_t bits) 
   }
 }
 
-// A thread's running sums for a window of kWin consecutive exponents starting at
-// base (set by its first nonzero finite weight, a few octaves below it): the
+// A thread's running sum for a window of kWin consecutive exponents starting at
+// base >= 1 (set by its first nonzero normal weight, a few octaves below it): the
 // weights of a matrix crowd into a few octaves, so most of them land here and
 // only the rest become LDS atomics (which serialise when a wave's lanes hit the
-// same bucket, as most of them would).
+// same bucket, as most of them would).  acc = sum of m * 2^(e - base), i.e. the
+// window's part of S in units of 2^(base - 1): added to the buckets as
+// (acc mod 2^(kWin-1)) in bucket base and (acc >> (kWin - 1)) in bucket
+// base + kWin - 1, it contributes exactly the same S, and each bucket still
+// receives less than 2^24 per weight.
 constexpr int kWin = 8;
 struct HistWindow {
-  unsigned long long acc[kWin];
+  unsigned long long acc;
   int base;
 };
 
@@ -73,16 +77,17 @@ __device__ __forceinline__ void window_add(HistWindow& h, unsigned long long* sb
     atomicAdd(&sb[255], 1ull);                      // non-finite flag
     return;
   }
-  const uint32_t m = e ? (f | 0x800000u) : f;       // units of 2^(max(e,1)-1-149)
-  if (!m) return;
-  if (h.base < 0) h.base = e > kWin - 3 ? (int)e - (kWin - 3) : 0;
-  const uint32_t d = e - (uint32_t)h.base;
-  if (d < (uint32_t)kWin) {
-#pragma unroll
-    for (int j = 0; j < kWin; ++j) h.acc[j] += d == (uint32_t)j ? m : 0u;
-  } else {
-    atomicAdd(&sb[e], (unsigned long long)m);
+  if (e == 0u) {                                    // sub-normal: units of 2^-149
+    if (f) atomicAdd(&sb[0], (unsigned long long)f);
+    return;
   }
+  const uint32_t m = f | 0x800000u;                 // units of 2^(e-1-149)
+  if (h.base < 0) h.base = min(max((int)e - (kWin - 3), 1), 254 - (kWin - 1));
+  const uint32_t d = e - (uint32_t)h.base;
+  if (d < (uint32_t)kWin)
+    h.acc += (unsigned long long)m << d;
+  else
+    atomicAdd(&sb[e], (unsigned long long)m);
 }
 
 // Pass 1: per-exponent integer sums of the significands of |w|.
@@ -99,8 +104,7 @@ __global__ __launch_bounds__(kHistThreads) void wq_hist(const void* __restrict__
   const int64_t stride = (int64_t)gridDim.x * kHistThreads;
   const uint4* wv = reinterpret_cast<const uint4*>(w);
   HistWindow hw;
-#pragma unroll
-  for (int j = 0; j < kWin; ++j) hw.acc[j] = 0ull;
+  hw.acc = 0ull;
   hw.base = -1;
   // four vectors in flight per thread (zeros past the end add nothing)
   constexpr int kIn = 4;
@@ -124,10 +128,10 @@ __global__ __launch_bounds__(kHistThreads) void wq_hist(const void* __restrict__
       }
     }
   }
-  if (hw.base >= 0) {
-#pragma unroll
-    for (int j = 0; j < kWin; ++j)
-      if (hw.acc[j]) atomicAdd(&sb[hw.base + j], hw.acc[j]);
+  if (hw.acc) {
+    const unsigned long long lo = hw.acc & ((1ull << (kWin - 1)) - 1ull);
+    if (lo) atomicAdd(&sb[hw.base], lo);
+    atomicAdd(&sb[hw.base + kWin - 1], hw.acc >> (kWin - 1));
   }
   for (int64_t i = nvec * kVec + (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < count;
        i += stride)
