@@ -14,8 +14,11 @@
 //
 // One workgroup per token row.  Pass 1 reduces max|v*w| (exact in any order) and
 // sum v^2 (float64; the products are exact) with wave butterflies and a
-// cross-wave step in LDS; pass 2 re-reads the row (now in L1/L2) and writes 16
-// int8 per 16-byte store.
+// cross-wave step in LDS; pass 2 writes 16 int8 per 16-byte store.  Each thread's
+// first H groups of 16 stay in registers between the passes, all loaded before
+// any is used; H (1, 2 or 4) covers the row when it can (K <= 16 H kAqThreads)
+// and no more, since the registers cost occupancy; groups past those are read
+// again in pass 2 (from L1/L2).
 #include "bitnet_internal.h"
 
 namespace bitnet {
@@ -75,7 +78,7 @@ __device__ __forceinline__ float prologue1(const void* row, const void* urow, co
   return v;
 }
 
-template <bool BF16>
+template <bool BF16, int H>
 __global__ __launch_bounds__(kAqThreads) void aq_kernel(const void* __restrict__ x, int64_t K,
                                                        bool vec, int8_t* __restrict__ xq,
                                                        float* __restrict__ xs,
@@ -93,7 +96,21 @@ __global__ __launch_bounds__(kAqThreads) void aq_kernel(const void* __restrict__
 
   float a = 0.0f;
   double ss = 0.0;
-  for (int64_t c = tid; c < n16; c += kAqThreads) {
+  // held groups: an index past the row reads its last group again (valid memory)
+  // and is dropped from the max, the sum and the stores
+  float hold[H][16];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const int64_t c = tid + (int64_t)h * kAqThreads;
+    double s2 = 0.0;
+    if (n16 > 0) prologue16<BF16>(row, urow, pro.w, c < n16 ? c : n16 - 1, hold[h], s2);
+    if (c < n16) {
+      ss += s2;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(hold[h][j]));
+    }
+  }
+  for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
     float v[16];
     prologue16<BF16>(row, urow, pro.w, c, v, ss);
 #pragma unroll
@@ -118,7 +135,19 @@ __global__ __launch_bounds__(kAqThreads) void aq_kernel(const void* __restrict__
 
   const float astar = fmaxf(a, kEps);
   const float s = kQb / astar;   // correctly rounded fp32 division
-  for (int64_t c = tid; c < n16; c += kAqThreads) {
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const int64_t c = tid + (int64_t)h * kAqThreads;
+    if (c < n16) {
+      uint4 o;
+      o.x = quant4(hold[h], s);
+      o.y = quant4(hold[h] + 4, s);
+      o.z = quant4(hold[h] + 8, s);
+      o.w = quant4(hold[h] + 12, s);
+      reinterpret_cast<uint4*>(qrow)[c] = o;
+    }
+  }
+  for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
     float v[16];
     double unused = 0.0;
     prologue16<BF16>(row, urow, pro.w, c, v, unused);
@@ -151,13 +180,14 @@ hipError_t launch_aq(const void* x, bool x_bf16, int64_t M, int64_t K, int8_t* x
   const auto a16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; };
   const bool vec = (K % 16 == 0) && a16(x) && a16(x_q) && a16(pro.up) && a16(pro.w) &&
                    ((K * esz) % 16 == 0);
-  if (x_bf16)
-    hipLaunchKernelGGL(aq_kernel<true>, dim3((unsigned)M), dim3(kAqThreads), 0, s, x, K, vec, x_q,
-                       x_scale, pro);
-  else
-    hipLaunchKernelGGL(aq_kernel<false>, dim3((unsigned)M), dim3(kAqThreads), 0, s, x, K, vec, x_q,
-                       x_scale, pro);
-  return hipGetLastError();
+  const int64_t per_thread = (K / 16 + kAqThreads - 1) / kAqThreads;   // groups per thread
+  const int h = per_thread <= 1 ? 1 : per_thread <= 2 ? 2 : 4;
+  const void* kern = x_bf16 ? (h == 1 ? (const void*)aq_kernel<true, 1>
+                               : h == 2 ? (const void*)aq_kernel<true, 2> : (const void*)aq_kernel<true, 4>)
+                            : (h == 1 ? (const void*)aq_kernel<false, 1>
+                               : h == 2 ? (const void*)aq_kernel<false, 2> : (const void*)aq_kernel<false, 4>);
+  void* args[] = {(void*)&x, (void*)&K, (void*)&vec, (void*)&x_q, (void*)&x_scale, (void*)&pro};
+  return hipLaunchKernel(kern, dim3((unsigned)M), dim3(kAqThreads), args, 0, s);
 }
 
 }  // namespace bitnet
