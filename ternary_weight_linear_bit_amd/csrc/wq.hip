@@ -11,8 +11,9 @@
 // left by (biased exponent - 1), or frac for sub-normals.  Pass 1 adds the 24-bit
 // significands into 256 uint64 buckets keyed by biased exponent (integer atomics:
 // exact and order-free; kWqCopies copies of the buckets, by workgroup, spread the
-// global atomics of the hot buckets over more addresses).  Pass 2 (one wave) forms the exact sum in a 320-bit
-// integer, divides by N*K and rounds once to fp32.  Pass 3 ternarises and packs.
+// global atomics of the hot buckets over more addresses).  Pass 2 (one wave)
+// forms the exact sum in a 320-bit integer, divides by N*K and rounds once to
+// fp32.  Pass 3 ternarises and packs.
 //
 // T1 output (five codes per byte, a reading of the same pages' log2(3) ~ 1.58
 // bits per weight): the codes c = q + 1 of the weights 80 b + 16 j + i of a row
@@ -21,7 +22,7 @@
 // 80-weight blocks of 16 bytes.  wq_pack_t1 writes it from the master weights,
 // repack_t1 from the 2-bit layout.
 //
-// Workspace layout (device, caller-owned, >= kWsBytes):
+// Workspace layout (device, caller-owned, >= kWqWorkspaceBytes):
 //   [0, kWqThresholdAt)  uint64 buckets[kWqCopies][256]  (bucket 255 counts
 //                        Inf/NaN weights)
 //   kWqThresholdAt       float threshold  (see wq_finish)
@@ -61,8 +62,8 @@ __device__ __forceinline__ void hist_add(unsigned long long* sb, uint32_t bits) 
 // same bucket, as most of them would).  acc = sum of m * 2^(e - base), i.e. the
 // window's part of S in units of 2^(base - 1): added to the buckets as
 // (acc mod 2^(kWin-1)) in bucket base and (acc >> (kWin - 1)) in bucket
-// base + kWin - 1, it contributes exactly the same S, and each bucket still
-// receives less than 2^24 per weight.
+// base + kWin - 1, it contributes exactly the same S, and the buckets keep their
+// bound: less than 2^24 per weight, plus less than 2^7 per thread.
 constexpr int kWin = 8;
 struct HistWindow {
   unsigned long long acc;
