@@ -347,6 +347,27 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   const int64_t big_tiles = ((a.M + 255) / 256) * row_tiles(256);
   const int64_t big_rounds = (big_tiles + cus - 1) / cus;
   const bool big = big_tiles > 0 && 5 * big_tiles >= 4 * big_rounds * (int64_t)cus;
+  // A last round of 256 x 256 tiles that fills under 40% of the compute units
+  // idles most of the chip for a whole tile time: the token tiles that fit in the
+  // full rounds run as one launch, and the remaining tokens as a second launch
+  // with its own tile choice (2B gate + up at M = 4096: 213 -> 195 us).
+  if (big && big_rounds > 1 && 5 * (big_tiles - (big_rounds - 1) * cus) < 2 * (int64_t)cus) {
+    const int64_t m1 = (big_rounds - 1) * cus / row_tiles(256) * 256;   // tokens
+    if (m1 > 0 && m1 < a.M) {
+      GemmArgs rest = a;
+      rest.M = (int)(a.M - m1);
+      rest.xq = a.xq + m1 * a.K;
+      rest.xs = a.xs + m1;
+      const size_t es = a.y_bf16 ? 2 : 4;
+      for (int j = 0; j < a.count; ++j) {
+        rest.y[j] = static_cast<char*>(a.y[j]) + (size_t)m1 * a.n[j] * es;
+        if (a.acc[j]) rest.acc[j] = a.acc[j] + (size_t)m1 * a.n[j];
+      }
+      a.M = (int)m1;
+      const hipError_t e = launch_gemm(a, s);
+      return e != hipSuccess ? e : launch_gemm(rest, s);
+    }
+  }
   const int64_t mt = (a.M + 127) / 128;
   const int64_t rows4 = row_tiles(256);
   const bool wide = !big && rows4 * mt <= cus && 10 * rows4 * mt >= 9 * (int64_t)cus;

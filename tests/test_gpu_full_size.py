@@ -14,7 +14,7 @@ from oracle import bitnet_oracle as O
 from ternary_weight_linear_bit_amd import _native as N
 from ternary_weight_linear_bit_amd import inputs as I
 
-from gpu_helpers import DEV, f32_bits, host
+from gpu_helpers import DEV, bf16_bits, f32_bits, host
 
 pytestmark = pytest.mark.gpu
 
@@ -97,4 +97,41 @@ def test_full_size_t1(k, n, dt):
     np.testing.assert_array_equal(host(acc_d)[0], acc_w)
     np.testing.assert_array_equal(f32_bits(host(y_d)[0]), f32_bits(y_w))
     del p_d
+    torch.cuda.empty_cache()
+
+
+def test_full_size_gate_up_grouped():
+    """Gate and up of the 2B layer at M = 4096 in one grouped prefill launch: 864
+    tiles of 256 x 256 leave a last round under 40% full, so the launch splits at
+    token 3584 into 256 x 256 tiles and a second launch for the last 512 tokens.
+    Sampled outputs on both sides of the split (and the tokens at it), plus one
+    full output row of each matrix."""
+    k, n, m = 2560, 6912, 4096
+    print(f"full-size grouped gate+up K={k} N={n} x 2 M={m}", flush=True)
+    mats, mats_d = [], []
+    for j in range(2):
+        w = I.master_weights(n, k, I.weight_seed(0, 4 + j))
+        p_d, s_d = N.bitnet_quantize_weights(torch.from_numpy(w).to(DEV))
+        gamma = O.weight_scale(w)
+        assert f32_bits(host(s_d))[0] == f32_bits(gamma)
+        mats.append((O.pack_codes(O.ternarize(w, gamma)), gamma))
+        mats_d.append((p_d, s_d))
+        del w
+    x = I.activations(m, k, I.ACT_SEED + 7)
+    xq_d, xs_d = N.bitnet_quantize_acts(torch.from_numpy(x).to(DEV))
+    xq, d = O.quantize_acts(x)
+    accs = [torch.empty((m, n), dtype=torch.int32, device=DEV) for _ in range(2)]
+    ys = N.bitnet_ternary_linear_multi([(p, s, None, a) for (p, s), a in zip(mats_d, accs)],
+                                       xq_d, xs_d, y_dtype=torch.bfloat16)
+    rng = np.random.Generator(np.random.PCG64(4096))
+    edge = np.array([0, 255, 3583, 3584, 3585, 3839, 3840, 4095])
+    for (packed_o, gamma), acc_d, y_d in zip(mats, accs, ys):
+        acc_h, y_b = host(acc_d), bf16_bits(y_d)
+        mi = np.concatenate([rng.integers(0, m, 256), np.repeat(edge, 32), np.full(n, 3584)])
+        ni = np.concatenate([rng.integers(0, n, 256), rng.integers(0, n, 32 * len(edge)),
+                             np.arange(n)])
+        acc_w, y_w = O.ternary_linear_at(packed_o, gamma, xq, d, mi, ni)
+        np.testing.assert_array_equal(acc_h[mi, ni], acc_w)
+        np.testing.assert_array_equal(y_b[mi, ni], O.f32_to_bf16_bits(y_w))
+    del mats_d, accs, ys
     torch.cuda.empty_cache()
