@@ -33,10 +33,7 @@ namespace {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-#ifndef GEMM_NBW
-#define GEMM_NBW 2
-#endif
-constexpr int NBW = GEMM_NBW;   // 32-row weight blocks per wave
+constexpr int NBW = 2;          // 32-row weight blocks per wave
 constexpr int BK = 128;         // k per step
 
 constexpr int kStride = BK;       // LDS bytes per staged token row (groups XOR-swizzled)
