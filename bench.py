@@ -391,6 +391,43 @@ def quantisers(torch, N, I, steps):
     return res
 
 
+def mfma_ceiling(torch, N):
+    """The chip's int8 matrix-core rate (bitnet_probe_mfma_i8, two waves per SIMD,
+    ten launches of ~2 ms per operand kind, before the prefill legs): all-zero
+    operands (the issue rate: no data switching), all-ones, and random int8
+    activations against random ternary codes {0, 1, 2} (the prefill kernel's
+    operands).  The rate falls as more operand bits switch: the chip's power
+    management lowers the clock."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters, launches = 2 * cus, 2000, 10
+    res = {"waves_per_simd": 2}
+    for kind in ("zero", "ones", "random_int8_x_ternary"):
+        ops = torch.full((wgs * 256, 16, 16), 1 if kind == "ones" else 0, dtype=torch.uint8,
+                         device="cuda")
+        if kind == "random_int8_x_ternary":
+            g = torch.Generator(device="cuda").manual_seed(11)
+            ops[:, :8] = torch.randint(0, 256, (wgs * 256, 8, 16), generator=g, device="cuda",
+                                       dtype=torch.uint8)
+            ops[:, 8:] = torch.randint(0, 3, (wgs * 256, 8, 16), generator=g, device="cuda",
+                                       dtype=torch.uint8)
+        out = torch.empty((wgs * 256, 64), dtype=torch.uint8, device="cuda")
+        N.bitnet_probe_mfma_i8(ops, wgs, iters, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            N.bitnet_probe_mfma_i8(ops, wgs, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3
+        res[f"{kind}_tops"] = round(launches * wgs * 4 * iters * 32 * 65536 / sec / 1e12, 1)
+        del ops, out
+    res["frac_of_peak"] = {k: round(v / INT8_MFMA_PEAK_TOPS, 4) for k, v in res.items()
+                           if k.endswith("_tops")}
+    log(f"mfma ceiling: {res}")
+    return res
+
+
 def _graph_time(torch, fn, steps):
     """Mean microseconds of one replay of fn captured in a HIP graph."""
     fn()
@@ -549,6 +586,7 @@ def main():
             torch, N, I, ((2560, 2560), (2560, 6912), (6912, 2560), (8192, 28672), (28672, 8192)),
             steps=4)
     if not args.no_prefill:
+        result["mfma_ceiling"] = mfma_ceiling(torch, N)
         result["prefill"] = prefill(torch, N, I, wl["layer"], (512, 4096), steps=10)
         result["prefill_8b"] = prefill(torch, N, I, I.LAYER_8B, (2048,), steps=5)
         log(f"prefill: {result['prefill']} {result['prefill_8b']}")

@@ -69,6 +69,7 @@ SIGNATURES["bitnet_quant_linear_t1"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _
 SIGNATURES["bitnet_lut_workspace_bytes"] = (_SZ, [_I64, _I64])
 SIGNATURES["bitnet_ternary_linear_lut"] = (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P,
                                                 _SZ, _P])
+SIGNATURES["bitnet_probe_mfma_i8"] = (_I, [_P, _I, _I, _P, _P])
 
 _lib = None
 
@@ -390,3 +391,16 @@ def bitnet_ternary_linear_lut(w_packed, w_scale, x_q, x_scale, y=None, y_dtype=N
         _dtype_code(y.dtype), _ptr(acc_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
+
+
+def bitnet_probe_mfma_i8(ops, workgroups, iters, out, stream=None):
+    """Diagnostic: launch the int8 matrix-core rate probe (see the C header).
+    ops: uint8 device tensor of >= workgroups * 65536 bytes; out: >= workgroups *
+    16384 bytes.  The caller times it."""
+    _need_cuda(ops, out)
+    if ops.numel() * ops.element_size() < workgroups * 65536 or \
+            out.numel() * out.element_size() < workgroups * 16384:
+        raise ValueError("probe buffers too small")
+    _check("bitnet_probe_mfma_i8", lib().bitnet_probe_mfma_i8(
+        _ptr(ops), int(workgroups), int(iters), _ptr(out), _stream(stream)))
+

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitnet_mi355x.so")
-SOURCES = ("api.hip", "wq.hip", "aq.hip", "gemv.hip", "gemm.hip", "lut.hip")
+SOURCES = ("api.hip", "wq.hip", "aq.hip", "gemv.hip", "gemm.hip", "lut.hip", "probe.hip")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -420,4 +420,12 @@ bitnet_status bitnet_quant_linear(const uint8_t* w_packed, const float* w_scale,
   return bitnet_quant_linear_multi(&m, 1, x, x_dtype, M, K, x_q, x_scale, y_dtype, stream);
 }
 
+bitnet_status bitnet_probe_mfma_i8(const void* ops, int workgroups, int iters, void* out,
+                                   hipStream_t stream) {
+  if (!ops || !out) return BITNET_ERR_NULL;
+  if (workgroups < 1 || iters < 1) return BITNET_ERR_SHAPE;
+  if (!aligned(ops, 16) || !aligned(out, 16)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_mfma_probe(ops, workgroups, iters, out, stream));
+}
+
 }  // extern "C"

@@ -179,3 +179,13 @@ def test_lut_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE, ws - 1, None) == EWS
     assert f(FAKE_ODD, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE, ws, None) == EALIGN
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE_ODD, ws, None) == EALIGN
+
+
+def test_probe_validation(lib):
+    f = lib.bitnet_probe_mfma_i8
+    assert f(None, 1, 1, FAKE, None) == ENULL
+    assert f(FAKE, 1, 1, None, None) == ENULL
+    assert f(FAKE, 0, 1, FAKE, None) == ESHAPE
+    assert f(FAKE, 1, 0, FAKE, None) == ESHAPE
+    assert f(FAKE_ODD, 1, 1, FAKE, None) == EALIGN
+
