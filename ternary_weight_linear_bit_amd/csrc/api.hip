@@ -229,6 +229,14 @@ bitnet_status quant_linear_t1(const bitnet_matrix* mats, int count, const void* 
 
 }  // namespace
 
+namespace bitnet {
+// Matrix-core rate probe (diagnostic, probe.hip): workgroups x 256 threads, each
+// thread's 16 x 16-byte operand sets at ops[thread * 16 ...], one 64-byte result
+// per thread.
+hipError_t launch_mfma_probe(const void* ops, int workgroups, int iters, void* out,
+                             hipStream_t s);
+}  // namespace bitnet
+
 extern "C" {
 
 const char* bitnet_status_string(int status) {

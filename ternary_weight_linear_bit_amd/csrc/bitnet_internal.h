@@ -141,10 +141,6 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Host-side launchers (one per kernel family); each returns a hipError_t from
 // hipGetLastError() after its launches.
-// Matrix-core rate probe (diagnostic): workgroups x 256 threads, each thread's
-// 16 x 16-byte operand sets at ops[thread * 16 ...], one 64-byte result per thread.
-hipError_t launch_mfma_probe(const void* ops, int workgroups, int iters, void* out,
-                             hipStream_t s);
 // Weight quantisation workspace: kWqCopies copies of the 256 exponent buckets
 // (uint64) and the ternarisation threshold.
 constexpr int kWqCopies = 8;
