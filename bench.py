@@ -508,7 +508,7 @@ def cpu_baseline(I, layer_shapes, seconds, workers):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path "
+        print("bench.py runs on one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -29,8 +29,8 @@ Sources (web pages, cited by title and section)
       (GeekNews summary), Hacker News comments: the stored 2-bit field can hold
       the four values -1, 0, 1, 2.
 
-Readings taken where the pages are silent (each is also listed in the design doc)
-----------------------------------------------------------------------------
+Readings taken where the pages are silent
+-----------------------------------------
 O1  weight scale: one per-tensor scale; the mean |W| is taken exactly and
     rounded once to fp32 (RN32, ties to even); gamma* = max(gamma, RN32(1e-5)).
 O2  ternarise: t = RN32(W / gamma*) (correctly rounded fp32 division), then
