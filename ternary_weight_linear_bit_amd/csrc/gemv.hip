@@ -61,8 +61,11 @@ constexpr int kThreads = 256;              // 4 waves
 constexpr int kMaxTiles = 16;              // row tiles per workgroup
 constexpr int kMaxM = 16;
 constexpr int kMaxFusedM = 4;
-constexpr int kXBudget = 46 * 1024;        // LDS bytes of staged activations per phase
-                                           // (with 16 tiles of partials: < 64 KiB in all)
+constexpr int kXBudget = 16 * (4096 + 16); // LDS bytes of staged activations per phase:
+                                           // K = 4096 in one phase at M = 16 (gfx950's
+                                           // 160 KiB of LDS still holds two workgroups
+                                           // of up to 14 tiles)
+constexpr int kFusedXBudget = 46 * 1024;   // fused quantisation: M * K staged at most
 constexpr int kStageBatch = 8;             // 16-byte activation loads per thread per batch
 constexpr int kHold = 2;                   // fused: groups per thread held in registers
 constexpr int64_t kLatencyBytes = 6000000; // launches above this use the bandwidth regime
@@ -83,11 +86,11 @@ constexpr int stage_pieces(int M, int klen, int fmt) {
 }
 
 // K range staged per phase: a multiple of 256 (T1: of 1280, one 256-byte run of
-// a row) with M * stride <= kXBudget and at most 16 activation pieces, i.e. two
+// a row) with M * stride <= budget and at most 16 activation pieces, i.e. two
 // staging batches.
-constexpr int phase_k(int M, int K, int fmt) {
+constexpr int phase_k(int M, int K, int fmt, int budget = kXBudget) {
   const int unit = fmt ? 1280 : 256;
-  int kx = ((kXBudget / M - 16) / unit) * unit;
+  int kx = ((budget / M - 16) / unit) * unit;
   const int cap = 4096 * (16 / M);
   if (kx > cap) kx = (cap / unit) * unit;
   while (kx > unit && stage_pieces(M, kx, fmt) > 2 * kStageBatch) kx -= unit;
@@ -716,7 +719,8 @@ bool gemv_fits(int64_t M, int64_t K, int fmt) {
 }
 
 bool gemv_fused_fits(int64_t M, int64_t K, int fmt) {
-  return gemv_fits(M, K, fmt) && M <= kMaxFusedM && phase_k((int)M, (int)K, fmt) == K;
+  return gemv_fits(M, K, fmt) && M <= kMaxFusedM &&
+         phase_k((int)M, (int)K, fmt, kFusedXBudget) == K;
 }
 
 hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
