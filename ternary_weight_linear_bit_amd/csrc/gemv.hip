@@ -370,6 +370,41 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   const int tk = tid >> lgG;
   const int jg = tid & (G - 1);
 
+  // Producer of the weight ring: phase pp, tile tp, step jp of this wave's
+  // super-chunks (past the last tile or chunk the offset is out of range and the
+  // load reads zeros; a wave without super-chunks never advances past its first
+  // tile).  With several phases it runs on into the next one: a phase's last
+  // round of refills issues the next phase's first R loads, whose latency then
+  // overlaps the barrier and the staging of the next activations.
+  int pp = -1, tp = 0, jp = 0, Cp = 0, Jp = 0;
+  uint32_t kb0p = 0;
+  auto rs = tile_rsrc(0);
+  auto producer_phase = [&](int ph) {
+    const int k0p = ph * kx, klenp = min(kx, K - k0p);
+    Cp = FMT == kFmtT1 ? (klenp + 79) / 80 : klenp >> 6;
+    const int Sp = (Cp + 3) >> 2;
+    Jp = Sp > wave ? (Sp - wave + 3) >> 2 : 0;
+    kb0p = FMT == kFmtT1 ? (uint32_t)k0p / 5u : (uint32_t)k0p >> 2;
+    pp = ph;
+    tp = 0;
+    jp = 0;
+    rs = tile_rsrc(0);
+  };
+  auto next_load = [&]() -> uint4 {
+    const int c = 4 * (wave + 4 * jp) + g;
+    const uint4 v = bload16(rs, (tp < ntiles && c < Cp)
+                                    ? (uint32_t)r * rowb + kb0p + 16u * (uint32_t)c
+                                    : kOob);
+    if (++jp == Jp) {
+      jp = 0;
+      ++tp;
+      rs = tile_rsrc(tp);
+    }
+    return v;
+  };
+  uint4 ring[R];
+  bool carried = false;  // the ring already holds this phase's first loads
+
   for (int p = 0; p < phases; ++p) {
     const int k0 = p * kx;
     const int klen = min(kx, K - k0);
@@ -378,8 +413,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     const int S = (C + 3) >> 2;                    // 256-k super-chunks
     const int J = S > wave ? (S - wave + 3) >> 2 : 0;
     const int Q = ntiles * J;                      // loads per lane in this phase
-    const uint32_t kb0 = FMT == kFmtT1 ? (uint32_t)k0 / 5u   // phase start within a packed row
-                                       : (uint32_t)k0 >> 2;
     const int K16 = klen >> 4;                     // 16-k groups of activations
     const int K16s = FMT == kFmtT1 ? 5 * C : K16;  // groups staged (T1: zeros past klen)
 
@@ -433,29 +466,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
         }
       }
     }
-    // producer position of the ring: tile tp, step jp of this wave's super-chunks
-    // (past the last tile or chunk the offset is out of range and the load reads
-    // zeros; a wave without super-chunks never advances past its first tile)
-    int tp = 0, jp = 0;
-    auto rs = tile_rsrc(0);
-    auto next_load = [&]() -> uint4 {
-      const int c = 4 * (wave + 4 * jp) + g;
-      const uint4 v = bload16(rs, (tp < ntiles && c < C)
-                                      ? (uint32_t)r * rowb + kb0 + 16u * (uint32_t)c
-                                      : kOob);
-      if (++jp == J) {
-        jp = 0;
-        ++tp;
-        rs = tile_rsrc(tp);
-      }
-      return v;
-    };
-    uint4 ring[R];
+    if (!carried) {
+      if (pp != p) producer_phase(p);
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-      ring[u] = next_load();
-      asm volatile("" ::: "memory");  // keep the ring's loads in slot order
+      for (int u = 0; u < R; ++u) {
+        ring[u] = next_load();
+        asm volatile("" ::: "memory");  // keep the ring's loads in slot order
+      }
     }
+    carried = false;
     if (p == 0) {
       pro = load_prologue(a, g1, g2);
       // (buffer loads: the pointers come out of the asm in load_prologue as generic
@@ -595,6 +614,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     int tc = 0, jc = 0;
     v4i acc = {0, 0, 0, 0};
     for (int q0 = 0; q0 < Q; q0 += R) {
+      if (XMODE == 0 && q0 + R >= Q && p + 1 < phases) {
+        // last round: its refills are the next phase's first loads
+        producer_phase(p + 1);
+        carried = true;
+      }
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int c = 4 * (wave + 4 * jc) + g;
