@@ -20,7 +20,7 @@
 //    matrix cores sum c * x and the epilogue subtracts each token's sum of x
 //    (four dot-4 instructions per staged 16-byte group), which saves the byte
 //    lookup per field that maps c to q;
-//  * loads run kDepth steps ahead of the matrix cores.
+//  * loads run D steps ahead of the matrix cores (kDepth = 2; 4 on 64 x 128 tiles).
 // Lane (r, h) of a 32 x 32 x 32 operand holds row r and 16 k: with the 16 bytes
 // lane h loads per row (k0 + 64h .. k0 + 64h + 63), MFMA j of a step sums over
 // k0 + 64h + 16j + (0..15) for h = 0, 1; the A operand reads the matching LDS
@@ -46,7 +46,7 @@ __device__ __forceinline__ int lds_group(int t, int kg) {
   return t * kStride + 16 * (kg ^ (t & 7));
 }
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, each with its own L2
-constexpr int kDepth = 2;         // steps of global loads in flight
+constexpr int kDepth = 2;         // steps of global loads in flight (default)
 
 // Packed dword (16 codes) -> the codes c = q + 1 in {0, 1, 2} as an int8 operand
 // in the 4x4-byte-transposed k order (byte 4i + b = code of k-offset 4b + i): one
@@ -62,7 +62,7 @@ __device__ __forceinline__ v4i expand_codes(uint32_t w) {
 }
 
 // WN waves along the output rows (2 along the tokens): BN = 32 * NBW * WN rows
-template <int BM, int WN>
+template <int BM, int WN, int D = kDepth>
 __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
   constexpr int kThreads = 128 * WN;
   constexpr int BN = 32 * NBW * WN;         // output rows per workgroup
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
         // registers without copies, which would wait for the loads in flight
         asm volatile("" : "+v"(bop[0]), "+v"(bop[NBW - 1]), "+v"(rsum[0]), "+v"(rsum[XG - 1])
                      ::"memory");
-        xload(xv, s + 1 + kDepth);
-        wload(wv, s + kDepth);
+        xload(xv, s + 1 + D);
+        wload(wv, s + D);
       }
 #pragma unroll
       for (int i = 0; i < TB; ++i)
@@ -228,10 +228,10 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
   // the loop refills them; step 0 is staged before the loop
   uint4 x0[XG];
   xload(x0, 0);
-  uint4 xv_[kDepth][XG];
-  uint4 wv_[kDepth][NBW];
+  uint4 xv_[D][XG];
+  uint4 wv_[D][NBW];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
+  for (int d = 0; d < D; ++d) {
     asm volatile("" ::: "memory");
     xload(xv_[d], d + 1);
     wload(wv_[d], d);
@@ -240,11 +240,11 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
   for (int i = 0; i < XG; ++i) stage(x0[i], i, xs[0]);
   if (tid < BM) xsc[tid] = xs_t;   // loaded before x0, so no extra wait
   lds_barrier();
-  // steps past the end (when kDepth does not divide the step count) only add
+  // steps past the end (when D does not divide the step count) only add
   // zero products and stage zeros
-  for (int s = 0; s < steps; s += kDepth) {
+  for (int s = 0; s < steps; s += D) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) body(xv_[d], wv_[d], s + d);
+    for (int d = 0; d < D; ++d) body(xv_[d], wv_[d], s + d);
   }
 
   // token sums: the 8 threads of a token are consecutive lanes
@@ -332,7 +332,10 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   //  * else 128 x 128 (4 waves; three workgroups per compute unit), or 64 x 128
   //    (4 waves of 32 x 64) when 128 x 128 tiles would not cover the compute
   //    units once: twice the tiles, each half as long, at some cost per product
-  //    (the weight expansion serves half the tokens).
+  //    (the weight expansion serves half the tokens).  These short steps leave
+  //    the loads' latency exposed, so the 64 x 128 kernel loads four steps ahead
+  //    (2B layer at M = 512: 108 -> 100 us; three, five or more steps ahead, or
+  //    deeper loads on the other shapes, measured no better).
   // Measured on the prefill shapes; 4 x 32-row blocks per wave measured slower
   // everywhere (registers: one wave per SIMD).
   const int cus = device_cus();
@@ -385,7 +388,7 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (big)
     hipLaunchKernelGGL((gemm_kernel<256, 4>), grid, dim3(512), 0, s, a);
   else if (small)
-    hipLaunchKernelGGL((gemm_kernel<64, 2>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<64, 2, 4>), grid, dim3(256), 0, s, a);
   else if (wide)
     hipLaunchKernelGGL((gemm_kernel<128, 4>), grid, dim3(512), 0, s, a);
   else
