@@ -164,6 +164,10 @@ LINEAR_SHAPES = [
     # decode kernel: several K phases, multi-tile workgroups, M = 16 at large K
     (16, 100, 14336), (1, 40, 28672), (3, 24, 65536), (1, 20, 131072), (2, 9000, 256),
     (1, 70000, 64), (16, 300, 1088),
+    # decode kernel, bandwidth regime with two tiles per workgroup and two K phases
+    # at M = 16, the second phase one 256-k super-chunk long (three of the four
+    # waves have no loads in it): the weight ring runs on across tiles and phases
+    (16, 9000, 4352),
 ]
 
 
