@@ -328,7 +328,8 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   //    besides the products).  Chosen when its tiles fill at least 80% of the
   //    compute units over the launch's rounds;
   //  * 128 x 256 (8 waves of 64 x 64; one per compute unit), when its tiles fill
-  //    90-100% of one round;
+  //    80-100% of one round (from 90%: 2B gate+up at M = 512 went to these tiles,
+  //    the layer 100.7 -> 98.7 us);
   //  * else 128 x 128 (4 waves; three workgroups per compute unit), or 64 x 128
   //    (4 waves of 32 x 64) when 128 x 128 tiles would not cover the compute
   //    units once: twice the tiles, each half as long, at some cost per product
@@ -370,7 +371,7 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   }
   const int64_t mt = (a.M + 127) / 128;
   const int64_t rows4 = row_tiles(256);
-  const bool wide = !big && rows4 * mt <= cus && 10 * rows4 * mt >= 9 * (int64_t)cus;
+  const bool wide = !big && rows4 * mt <= cus && 10 * rows4 * mt >= 8 * (int64_t)cus;
   const bool small = !big && !wide && mt * row_tiles(128) <= cus;
   const int bm = big ? 256 : small ? 64 : 128;
   const int bn = big || wide ? 256 : 128;

@@ -154,10 +154,10 @@ LINEAR_SHAPES = [
     (17, 100, 256), (100, 130, 2560), (300, 257, 192), (128, 128, 64), (513, 640, 512),
     (16, 50, 4096),
     # prefill kernel, 128 x 128 tiles: ragged M and N, K of one and a half steps
-    (1000, 5000, 192), (700, 9000, 64),
-    # prefill kernel, 128 x 256 tiles (chosen when they fill one round of the
-    # chip's compute units almost exactly): ragged M and N
-    (2000, 4000, 64), (1920, 3900, 192),
+    (1000, 5000, 192), (900, 6000, 64),
+    # prefill kernel, 128 x 256 tiles (chosen when they fill 80-100% of one round
+    # of the chip's compute units): ragged M and N
+    (2000, 4000, 64), (1920, 3900, 192), (700, 9000, 64),
     # prefill kernel, 256 x 256 tiles (chosen when they fill at least 80% of the
     # compute units over the launch's rounds): ragged M and N, K of one half step
     (2000, 6600, 64), (1100, 10400, 192),
