@@ -32,12 +32,6 @@ __device__ __forceinline__ float load_act(const void* x, int64_t i) {
   return reinterpret_cast<const float*>(x)[i];
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // 16 consecutive prologue values (the quantised ones, q) of group c; adds v^2
 // to ss when the norm is on.
 template <bool BF16>

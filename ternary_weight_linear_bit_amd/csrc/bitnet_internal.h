@@ -26,11 +26,47 @@ __device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
 }
 
 // Wave64 reductions (butterfly over all 64 lanes).
+// Wave-wide reductions on DPP: quad permutes and the two row mirrors make every
+// lane of a 16-lane row hold the row's result; row broadcasts 15 and 31 (rows
+// 1 and 3, then rows 2 and 3) carry it into lane 63, which is read back as a
+// wave-uniform scalar.  A few vector instructions, where a shuffle tree costs
+// six round trips through the LDS crossbar.  Every lane must be active; lanes
+// a broadcast does not reach keep the identity (zero) as their operand.
+#define BITNET_DPP(old, v, ctrl, rows) __builtin_amdgcn_update_dpp((old), (v), (ctrl), (rows), 0xF, false)
+// max over the wave of non-negative values
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  int b = __float_as_int(v);
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(BITNET_DPP(0, b, 0xB1, 0xF))));   // lane ^ 1
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(BITNET_DPP(0, b, 0x4E, 0xF))));   // lane ^ 2
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(BITNET_DPP(0, b, 0x141, 0xF))));  // half-row mirror
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(BITNET_DPP(0, b, 0x140, 0xF))));  // row mirror
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(BITNET_DPP(0, b, 0x142, 0xA))));  // row bcast 15
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(BITNET_DPP(0, b, 0x143, 0xC))));  // row bcast 31
+  return __int_as_float(__builtin_amdgcn_readlane(b, 63));
 }
+// sum over the wave (fp64, both halves moved by DPP)
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  auto step = [](double x, double y) { return x + y; };
+#define BITNET_DPP_F64(ctrl, rows)                                                        \
+  {                                                                                       \
+    const uint64_t u = (uint64_t)__double_as_longlong(v);                                 \
+    const uint32_t lo = (uint32_t)BITNET_DPP(0, (int)(uint32_t)u, ctrl, rows);            \
+    const uint32_t hi = (uint32_t)BITNET_DPP(0, (int)(uint32_t)(u >> 32), ctrl, rows);    \
+    v = step(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));            \
+  }
+  BITNET_DPP_F64(0xB1, 0xF)
+  BITNET_DPP_F64(0x4E, 0xF)
+  BITNET_DPP_F64(0x141, 0xF)
+  BITNET_DPP_F64(0x140, 0xF)
+  BITNET_DPP_F64(0x142, 0xA)
+  BITNET_DPP_F64(0x143, 0xC)
+#undef BITNET_DPP_F64
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+#undef BITNET_DPP
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -569,8 +569,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
       amax = wave_max(amax);
       if (lane == 0) wred[wave] = amax;
       if (PRO) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        ss = wave_sum_f64(ss);
         if (lane == 0) wss[wave] = ss;
       }
       lds_barrier();
