@@ -70,7 +70,7 @@ constexpr int kStageBatch = 8;             // 16-byte activation loads per threa
 constexpr int kHold = 2;                   // fused: groups per thread held in registers
 constexpr int64_t kLatencyBytes = 6000000; // launches above this use the bandwidth regime
 constexpr int kWgsPerCu = 2;               // bandwidth regime: workgroups per compute unit
-constexpr int kFlightLoads = 8192;         // target 1 KiB loads in flight over the chip
+constexpr int kFlightLoads = 4096;         // target 1 KiB loads in flight over the chip
 
 // zero slot: one B operand set read for tokens >= M and chunks past the end
 constexpr int zero_bytes(int fmt) { return fmt ? 96 : 64; }
@@ -767,8 +767,9 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
   // kLatencyBytes of packed weights gives every tile its own workgroup, so all
   // loads issue at once; a larger one is spread as kWgsPerCu workgroups per
   // compute unit with equal tile counts.  The ring depth targets kFlightLoads
-  // 1 KiB loads in flight over the whole chip: deeper rings measured slower
-  // (more requests queue without more throughput).
+  // 1 KiB loads in flight over the whole chip (in effect: R = 4 from 129
+  // workgroups up): deeper rings measured slower (more requests queue without
+  // more throughput).
   const int cus = device_cus();
   auto count_wgs = [&](int t) {
     int w = 0;
