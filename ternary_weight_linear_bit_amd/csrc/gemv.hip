@@ -697,10 +697,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   }
 }
 
-// Kernel for activation mode XMODE, weight format FMT and ring depth 4, 8 or 16
-// (smallest >= R).
+// Kernel for activation mode XMODE, weight format FMT and ring depth 2, 4, 8 or
+// 16 (smallest >= R).
 template <int XMODE, int FMT>
 const void* ring_kernel(int R) {
+  if (R <= 2) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT>);
   if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT>);
   if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8, FMT>);
   return reinterpret_cast<const void*>(gemv_kernel<XMODE, 16, FMT>);
@@ -786,6 +787,11 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
   const int wgs = count_wgs(tpw);
   int ring = 4;
   while (ring < 16 && 2 * ring * 4 * wgs <= kFlightLoads) ring *= 2;
+  // several tiles per workgroup but short rows (at most 6 loads per wave in all,
+  // over more than 256 workgroups): two loads ahead measured faster than four
+  // (2B gate+up, 2560 -> 13824: the chain 5.49 -> 5.34 us per launch); longer
+  // streams lose with it (100B-class stack 16.3 -> 18.0 us)
+  if (wgs > 256 && tpw >= 2 && tpw * per_tile <= 6) ring = 2;
   if (ring > tpw * per_tile) ring = tpw * per_tile;
   const void* kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring)
                                      : select_kernel<kFmt2>(xmode, ring);
