@@ -391,13 +391,18 @@ def quantisers(torch, N, I, steps):
     return res
 
 
-def mfma_ceiling(torch, N):
-    """The chip's int8 matrix-core rate (bitnet_probe_mfma_i8, two waves per SIMD,
-    ten launches of ~2 ms per operand kind, before the prefill legs): all-zero
-    operands (the issue rate: no data switching), all-ones, and random int8
-    activations against random ternary codes {0, 1, 2} (the prefill kernel's
-    operands).  The rate falls as more operand bits switch: the chip's power
-    management lowers the clock."""
+def mfma_ceiling(torch):
+    """The chip's int8 matrix-core rate (a bench-only probe library, two waves per
+    SIMD, ten launches of ~2 ms per operand kind, before the prefill legs):
+    all-zero operands (the issue rate: no data switching), all-ones, and random
+    int8 activations against random ternary codes {0, 1, 2} (the prefill kernel's
+    operands).  Context only: the roofline peak stays the published 5.0 POPS."""
+    import ctypes
+    path = os.path.join(ROOT, "ternary_weight_linear_bit_amd", "libbitnet_bench_probe.so")
+    probe = ctypes.CDLL(path).bitnet_bench_probe_mfma_i8
+    probe.restype = ctypes.c_int
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs, iters, launches = 2 * cus, 2000, 10
     res = {"waves_per_simd": 2}
@@ -411,12 +416,16 @@ def mfma_ceiling(torch, N):
             ops[:, 8:] = torch.randint(0, 3, (wgs * 256, 8, 16), generator=g, device="cuda",
                                        dtype=torch.uint8)
         out = torch.empty((wgs * 256, 64), dtype=torch.uint8, device="cuda")
-        N.bitnet_probe_mfma_i8(ops, wgs, iters, out)
+
+        def run():
+            if probe(ops.data_ptr(), wgs, iters, out.data_ptr(), stream) != 0:
+                raise RuntimeError("matrix-core probe launch failed")
+        run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(launches):
-            N.bitnet_probe_mfma_i8(ops, wgs, iters, out)
+            run()
         e1.record()
         torch.cuda.synchronize()
         sec = e0.elapsed_time(e1) * 1e-3
@@ -586,7 +595,7 @@ def main():
             torch, N, I, ((2560, 2560), (2560, 6912), (6912, 2560), (8192, 28672), (28672, 8192)),
             steps=4)
     if not args.no_prefill:
-        result["mfma_ceiling"] = mfma_ceiling(torch, N)
+        result["mfma_ceiling"] = mfma_ceiling(torch)
         result["prefill"] = prefill(torch, N, I, wl["layer"], (512, 4096), steps=10)
         result["prefill_8b"] = prefill(torch, N, I, I.LAYER_8B, (2048,), steps=5)
         log(f"prefill: {result['prefill']} {result['prefill_8b']}")

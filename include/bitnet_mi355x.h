@@ -306,20 +306,6 @@ bitnet_status bitnet_ternary_linear_lut(const uint8_t *w_packed, const float *w_
                                         int32_t *acc_out, void *workspace,
                                         size_t workspace_bytes, hipStream_t stream);
 
-/*
- * Diagnostic, not part of the method: the chip's int8 matrix-core rate, the
- * ceiling the prefill kernel is read against.  Launches `workgroups` x 256
- * threads; each wave runs `iters` x 32 v_mfma_i32_32x32x32_i8 (65536 int8 ops
- * each) on operands it reads once from `ops` (workgroups * 256 * 256 bytes,
- * 16-byte aligned: per thread 8 A then 8 B operand vectors of 16 bytes) and
- * writes 64 bytes per thread to `out`.  The caller times it (stream events):
- * rate = workgroups * 4 * iters * 32 * 65536 / time.  Constant operands give
- * the issue rate; random ones the rate under real data switching.
- *   workgroups >= 1, iters >= 1; otherwise BITNET_ERR_SHAPE.
- */
-bitnet_status bitnet_probe_mfma_i8(const void *ops, int workgroups, int iters, void *out,
-                                   hipStream_t stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -69,7 +69,6 @@ SIGNATURES["bitnet_quant_linear_t1"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _
 SIGNATURES["bitnet_lut_workspace_bytes"] = (_SZ, [_I64, _I64])
 SIGNATURES["bitnet_ternary_linear_lut"] = (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P,
                                                 _SZ, _P])
-SIGNATURES["bitnet_probe_mfma_i8"] = (_I, [_P, _I, _I, _P, _P])
 
 _lib = None
 
@@ -126,6 +125,47 @@ def _need_cuda(*ts):
             raise ValueError("tensors must be contiguous CUDA tensors")
 
 
+def _expect(t, shape, dtypes, name):
+    """Raise ValueError unless tensor t (if given) has this shape and one of these
+    dtypes: the kernels write through raw pointers, so a wrong-sized or
+    wrong-typed output would be written out of bounds."""
+    import torch
+    if t is None:
+        return
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes:
+        raise ValueError(f"{name}: expected shape {tuple(shape)} and dtype "
+                         f"{' or '.join(str(d) for d in dtypes)}, got {tuple(t.shape)} {t.dtype}")
+    _need_cuda(t)
+
+
+def _floats():
+    import torch
+    return (torch.float32, torch.bfloat16)
+
+
+def _check_act_operands(x, x_q, x_scale, up=None, norm_weight=None):
+    """x [M, K] fp32/bf16 (2-D), x_q int8 [M, K], x_scale fp32 [M], the prologue's
+    up (like x) and norm weight (fp32 [K])."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    _expect(x, (m, k), _floats(), "x")
+    _expect(x_q, (m, k), torch.int8, "x_q")
+    _expect(x_scale, (m,), torch.float32, "x_scale")
+    _expect(up, (m, k), x.dtype, "up")
+    _expect(norm_weight, (k,), torch.float32, "norm_weight")
+
+
+def _check_scale(w_scale):
+    import torch
+    if w_scale is not None and (w_scale.numel() < 1 or w_scale.dtype != torch.float32):
+        raise ValueError("w_scale must hold at least one float32")
+    _need_cuda(w_scale)
+
+
 def bitnet_packed_bytes(n: int, k: int) -> int:
     return lib().bitnet_packed_bytes(n, k)
 
@@ -143,7 +183,10 @@ def bitnet_quantize_weights(w, packed=None, scale=None, workspace=None, stream=N
     ws_bytes = lib().bitnet_quantize_weights_workspace_bytes(n, k)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    _need_cuda(packed, scale, workspace)
+    _expect(w, (n, k), _floats(), "w")
+    _expect(packed, (n, k // 4), torch.uint8, "packed")
+    _check_scale(scale)
+    _need_cuda(workspace)
     _check("bitnet_quantize_weights", lib().bitnet_quantize_weights(
         _ptr(w), _dtype_code(w.dtype), n, k, _ptr(packed), _ptr(scale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -174,7 +217,7 @@ def bitnet_quantize_acts(x, x_q=None, x_scale=None, stream=None, up=None, norm_w
         x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
     if x_scale is None:
         x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
-    _need_cuda(x_q, x_scale)
+    _check_act_operands(x, x_q, x_scale, up, norm_weight)
     pro = _prologue(x, up, norm_weight, eps)
     if pro is None:
         _check("bitnet_quantize_acts", lib().bitnet_quantize_acts(
@@ -197,7 +240,12 @@ def bitnet_ternary_linear(w_packed, w_scale, x_q, x_scale, y=None, y_dtype=None,
         raise ValueError("w_packed and x_q disagree on K")
     if y is None:
         y = torch.empty((m, n), dtype=y_dtype or torch.float32, device=x_q.device)
-    _need_cuda(y)
+    _expect(w_packed, (n, k // 4), torch.uint8, "w_packed")
+    _check_scale(w_scale)
+    _expect(x_q, (m, k), torch.int8, "x_q")
+    _expect(x_scale, (m,), torch.float32, "x_scale")
+    _expect(y, (m, n), _floats(), "y")
+    _expect(acc_out, (m, n), torch.int32, "acc_out")
     _check("bitnet_ternary_linear", lib().bitnet_ternary_linear(
         _ptr(w_packed), _ptr(w_scale), _ptr(x_q), _ptr(x_scale), m, n, k, _ptr(y),
         _dtype_code(y.dtype), _ptr(acc_out), _stream(stream)))
@@ -219,25 +267,38 @@ def bitnet_quant_linear(w_packed, w_scale, x, x_q=None, x_scale=None, y=None, y_
         x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
     if y is None:
         y = torch.empty((m, n), dtype=y_dtype or torch.float32, device=x.device)
-    _need_cuda(x_q, x_scale, y)
+    _check_act_operands(x, x_q, x_scale)
+    _expect(w_packed, (n, k // 4), torch.uint8, "w_packed")
+    _check_scale(w_scale)
+    _expect(y, (m, n), _floats(), "y")
+    _expect(acc_out, (m, n), torch.int32, "acc_out")
     _check("bitnet_quant_linear", lib().bitnet_quant_linear(
         _ptr(w_packed), _ptr(w_scale), _ptr(x), _dtype_code(x.dtype), m, n, k, _ptr(x_q),
         _ptr(x_scale), _ptr(y), _dtype_code(y.dtype), _ptr(acc_out), _stream(stream)))
     return y, x_q, x_scale
 
 
-def _matrices(mats, m, dtype, device):
-    """[(w_packed, w_scale[, y[, acc_out]])] -> ctypes array and the y tensors."""
+def _matrices(mats, m, k, dtype, device, row_bytes=None):
+    """[(w_packed, w_scale[, y[, acc_out]])] -> ctypes array and the y tensors.
+    Every y must be [M, N] of one shared dtype (fp32 or bf16), every acc_out
+    int32 [M, N], every w_packed uint8 [N, row_bytes] (K/4 for the 2-bit layout)."""
     import torch
+    if not mats:
+        raise ValueError("at least one matrix")
+    rb = k // 4 if row_bytes is None else row_bytes
     arr = (BitnetMatrix * len(mats))()
     ys = []
     for i, t in enumerate(mats):
         w_packed, w_scale = t[0], t[1]
+        n = w_packed.shape[0]
         y = t[2] if len(t) > 2 and t[2] is not None else torch.empty(
-            (m, w_packed.shape[0]), dtype=dtype, device=device)
+            (m, n), dtype=dtype if not ys else ys[0].dtype, device=device)
         acc = t[3] if len(t) > 3 else None
-        _need_cuda(w_packed, w_scale, y, acc)
-        arr[i] = BitnetMatrix(w_packed.data_ptr(), w_scale.data_ptr(), w_packed.shape[0],
+        _expect(w_packed, (n, rb), torch.uint8, f"w_packed[{i}]")
+        _check_scale(w_scale)
+        _expect(y, (m, n), ys[0].dtype if ys else _floats(), f"y[{i}]")
+        _expect(acc, (m, n), torch.int32, f"acc_out[{i}]")
+        arr[i] = BitnetMatrix(w_packed.data_ptr(), w_scale.data_ptr(), n,
                               y.data_ptr(), 0 if acc is None else acc.data_ptr())
         ys.append(y)
     return arr, ys
@@ -248,7 +309,9 @@ def bitnet_ternary_linear_multi(mats, x_q, x_scale, y_dtype=None, stream=None):
     import torch
     _need_cuda(x_q, x_scale)
     m, k = x_q.shape
-    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x_q.device)
+    _expect(x_q, (m, k), torch.int8, "x_q")
+    _expect(x_scale, (m,), torch.float32, "x_scale")
+    arr, ys = _matrices(mats, m, k, y_dtype or torch.float32, x_q.device)
     dt = _dtype_code(ys[0].dtype)
     _check("bitnet_ternary_linear_multi", lib().bitnet_ternary_linear_multi(
         arr, len(mats), _ptr(x_q), _ptr(x_scale), m, k, dt, _stream(stream)))
@@ -266,8 +329,8 @@ def bitnet_quant_linear_multi(mats, x, x_q=None, x_scale=None, y_dtype=None, str
         x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
     if x_scale is None:
         x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
-    _need_cuda(x_q, x_scale)
-    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x.device)
+    _check_act_operands(x, x_q, x_scale, up, norm_weight)
+    arr, ys = _matrices(mats, m, k, y_dtype or torch.float32, x.device)
     dt = _dtype_code(ys[0].dtype)
     pro = _prologue(x, up, norm_weight, eps)
     if pro is None:
@@ -307,7 +370,10 @@ def bitnet_quantize_weights_t1(w, packed=None, scale=None, workspace=None, strea
     ws_bytes = lib().bitnet_quantize_weights_workspace_bytes(n, k)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    _need_cuda(packed, scale, workspace)
+    _expect(w, (n, k), _floats(), "w")
+    _expect(packed, (n, t1_row_bytes(k)), torch.uint8, "packed")
+    _check_scale(scale)
+    _need_cuda(workspace)
     _check("bitnet_quantize_weights_t1", lib().bitnet_quantize_weights_t1(
         _ptr(w), _dtype_code(w.dtype), n, k, _ptr(packed), _ptr(scale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -322,17 +388,11 @@ def bitnet_repack_t1(w_packed, out=None, stream=None):
     k = 4 * kb
     if out is None:
         out = torch.empty((n, t1_row_bytes(k)), dtype=torch.uint8, device=w_packed.device)
-    _need_cuda(out)
+    _expect(w_packed, (n, kb), torch.uint8, "w_packed")
+    _expect(out, (n, t1_row_bytes(k)), torch.uint8, "out")
     _check("bitnet_repack_t1", lib().bitnet_repack_t1(_ptr(w_packed), n, k, _ptr(out),
                                                       _stream(stream)))
     return out
-
-
-def _check_t1(mats, k):
-    r = t1_row_bytes(k)
-    for t in mats:
-        if t[0].shape[1] != r:
-            raise ValueError("T1 matrix rows do not match K")
 
 
 def bitnet_ternary_linear_t1(mats, x_q, x_scale, y_dtype=None, stream=None):
@@ -340,8 +400,9 @@ def bitnet_ternary_linear_t1(mats, x_q, x_scale, y_dtype=None, stream=None):
     import torch
     _need_cuda(x_q, x_scale)
     m, k = x_q.shape
-    _check_t1(mats, k)
-    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x_q.device)
+    _expect(x_q, (m, k), torch.int8, "x_q")
+    _expect(x_scale, (m,), torch.float32, "x_scale")
+    arr, ys = _matrices(mats, m, k, y_dtype or torch.float32, x_q.device, t1_row_bytes(k))
     _check("bitnet_ternary_linear_t1", lib().bitnet_ternary_linear_t1(
         arr, len(mats), _ptr(x_q), _ptr(x_scale), m, k, _dtype_code(ys[0].dtype),
         _stream(stream)))
@@ -354,13 +415,12 @@ def bitnet_quant_linear_t1(mats, x, x_q=None, x_scale=None, y_dtype=None, stream
     import torch
     _need_cuda(x)
     m, k = x.shape
-    _check_t1(mats, k)
     if x_q is None:
         x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
     if x_scale is None:
         x_scale = torch.empty(m, dtype=torch.float32, device=x.device)
-    _need_cuda(x_q, x_scale)
-    arr, ys = _matrices(mats, m, y_dtype or torch.float32, x.device)
+    _check_act_operands(x, x_q, x_scale, up, norm_weight)
+    arr, ys = _matrices(mats, m, k, y_dtype or torch.float32, x.device, t1_row_bytes(k))
     _check("bitnet_quant_linear_t1", lib().bitnet_quant_linear_t1(
         arr, len(mats), _ptr(x), _dtype_code(x.dtype), _prologue(x, up, norm_weight, eps), m, k,
         _ptr(x_q), _ptr(x_scale), _dtype_code(ys[0].dtype), _stream(stream)))
@@ -385,22 +445,16 @@ def bitnet_ternary_linear_lut(w_packed, w_scale, x_q, x_scale, y=None, y_dtype=N
     ws_bytes = lib().bitnet_lut_workspace_bytes(n, k)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x_q.device)
-    _need_cuda(y, workspace)
+    _expect(w_packed, (n, k // 4), torch.uint8, "w_packed")
+    _check_scale(w_scale)
+    _expect(x_q, (m, k), torch.int8, "x_q")
+    _expect(x_scale, (m,), torch.float32, "x_scale")
+    _expect(y, (m, n), _floats(), "y")
+    _expect(acc_out, (m, n), torch.int32, "acc_out")
+    _need_cuda(workspace)
     _check("bitnet_ternary_linear_lut", lib().bitnet_ternary_linear_lut(
         _ptr(w_packed), _ptr(w_scale), _ptr(x_q), _ptr(x_scale), m, n, k, _ptr(y),
         _dtype_code(y.dtype), _ptr(acc_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
-
-
-def bitnet_probe_mfma_i8(ops, workgroups, iters, out, stream=None):
-    """Diagnostic: launch the int8 matrix-core rate probe (see the C header).
-    ops: uint8 device tensor of >= workgroups * 65536 bytes; out: >= workgroups *
-    16384 bytes.  The caller times it."""
-    _need_cuda(ops, out)
-    if ops.numel() * ops.element_size() < workgroups * 65536 or \
-            out.numel() * out.element_size() < workgroups * 16384:
-        raise ValueError("probe buffers too small")
-    _check("bitnet_probe_mfma_i8", lib().bitnet_probe_mfma_i8(
-        _ptr(ops), int(workgroups), int(iters), _ptr(out), _stream(stream)))
 

@@ -1,5 +1,7 @@
-// Diagnostic: the int8 matrix-core rate of this chip, as the ceiling against
-// which the prefill kernel is read (not part of the method).
+// Bench-only diagnostic, built into its own library (libbitnet_bench_probe.so)
+// and loaded only by bench.py: the int8 matrix-core rate of this chip, the
+// ceiling against which the prefill kernel is read.  Not part of the method and
+// not part of the public ABI.
 //
 // Each wave runs v_mfma_i32_32x32x32_i8 on four accumulator chains with its
 // operands cycling through eight register sets.  The operands come from memory
@@ -7,11 +9,12 @@
 // ternary codes {0, 1, 2} (the prefill kernel's operands) show the rate the chip
 // sustains while switching real data (its power management lowers the clock).
 // No memory traffic inside the loop.
-#include "bitnet_internal.h"
+#include <hip/hip_runtime.h>
+#include <stdint.h>
 
-namespace bitnet {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 __global__ __launch_bounds__(256) void mfma_probe(const v4i* __restrict__ ops, int iters,
@@ -39,11 +42,18 @@ __global__ __launch_bounds__(256) void mfma_probe(const v4i* __restrict__ ops, i
 
 }  // namespace
 
-hipError_t launch_mfma_probe(const void* ops, int workgroups, int iters, void* out,
-                             hipStream_t s) {
+// Launches `workgroups` x 256 threads; each wave runs `iters` x 32
+// v_mfma_i32_32x32x32_i8 (65536 int8 ops each) on operands read once from `ops`
+// (workgroups * 65536 bytes, 16-byte aligned: per thread 8 A then 8 B operand
+// vectors of 16 bytes) and writes 64 bytes per thread to `out`.  Returns 0, 2
+// for bad sizes, 4 for misalignment, 6 for a failed launch.  The caller times
+// it: rate = workgroups * 4 * iters * 32 * 65536 / time.
+extern "C" int bitnet_bench_probe_mfma_i8(const void* ops, int workgroups, int iters, void* out,
+                                          hipStream_t s) {
+  if (!ops || !out) return 1;
+  if (workgroups < 1 || iters < 1) return 2;
+  if (((uintptr_t)ops & 15) || ((uintptr_t)out & 15)) return 4;
   hipLaunchKernelGGL(mfma_probe, dim3((unsigned)workgroups), dim3(256), 0, s,
                      static_cast<const v4i*>(ops), iters, static_cast<v16i*>(out));
-  return hipGetLastError();
+  return hipGetLastError() == hipSuccess ? 0 : 6;
 }
-
-}  // namespace bitnet

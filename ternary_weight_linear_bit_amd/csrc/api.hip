@@ -229,14 +229,6 @@ bitnet_status quant_linear_t1(const bitnet_matrix* mats, int count, const void* 
 
 }  // namespace
 
-namespace bitnet {
-// Matrix-core rate probe (diagnostic, probe.hip): workgroups x 256 threads, each
-// thread's 16 x 16-byte operand sets at ops[thread * 16 ...], one 64-byte result
-// per thread.
-hipError_t launch_mfma_probe(const void* ops, int workgroups, int iters, void* out,
-                             hipStream_t s);
-}  // namespace bitnet
-
 extern "C" {
 
 const char* bitnet_status_string(int status) {
@@ -426,14 +418,6 @@ bitnet_status bitnet_quant_linear(const uint8_t* w_packed, const float* w_scale,
                                   hipStream_t stream) {
   const bitnet_matrix m{w_packed, w_scale, N, y, acc_out};
   return bitnet_quant_linear_multi(&m, 1, x, x_dtype, M, K, x_q, x_scale, y_dtype, stream);
-}
-
-bitnet_status bitnet_probe_mfma_i8(const void* ops, int workgroups, int iters, void* out,
-                                   hipStream_t stream) {
-  if (!ops || !out) return BITNET_ERR_NULL;
-  if (workgroups < 1 || iters < 1) return BITNET_ERR_SHAPE;
-  if (!aligned(ops, 16) || !aligned(out, 16)) return BITNET_ERR_ALIGN;
-  return from_hip(bitnet::launch_mfma_probe(ops, workgroups, iters, out, stream));
 }
 
 }  // extern "C"

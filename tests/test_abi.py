@@ -181,11 +181,111 @@ def test_lut_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, 0, None, FAKE_ODD, ws, None) == EALIGN
 
 
-def test_probe_validation(lib):
-    f = lib.bitnet_probe_mfma_i8
-    assert f(None, 1, 1, FAKE, None) == ENULL
-    assert f(FAKE, 1, 1, None, None) == ENULL
-    assert f(FAKE, 0, 1, FAKE, None) == ESHAPE
-    assert f(FAKE, 1, 0, FAKE, None) == ESHAPE
-    assert f(FAKE_ODD, 1, 1, FAKE, None) == EALIGN
+# ---------------------------------------------------------------------------
+# the Python binding validates every caller-supplied output before the C call
+# ---------------------------------------------------------------------------
 
+class _NoCall:
+    """Stands in for the library: any call means validation let a bad tensor through."""
+    def __getattr__(self, name):
+        if name == "bitnet_t1_packed_bytes":
+            return lambda n, k: n * 16 * ((k + 79) // 80)
+        if name.endswith("_workspace_bytes"):
+            return lambda n, k: 1 << 20
+        def call(*a):
+            raise AssertionError(f"{name} reached the C library with a bad tensor")
+        return call
+
+
+@pytest.fixture
+def cpu_binding(monkeypatch):
+    monkeypatch.setattr(N, "_need_cuda", lambda *ts: None)
+    monkeypatch.setattr(N, "lib", lambda: _NoCall())
+    return N
+
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("case", [
+    "y_dtype_mixed", "y_short", "acc_dtype", "acc_short", "xq_short", "xscale_short",
+    "packed_short"])
+def test_binding_rejects_bad_outputs_multi(cpu_binding, case):
+    import torch
+    m, k, n0, n1 = 2, 64, 32, 16
+    x = _t((m, k), torch.float32)
+    w0, w1 = _t((n0, k // 4), torch.uint8), _t((n1, k // 4), torch.uint8)
+    s = _t((1,), torch.float32)
+    y0, y1 = _t((m, n0), torch.float32), _t((m, n1), torch.float32)
+    acc1 = _t((m, n1), torch.int32)
+    x_q, x_scale = _t((m, k), torch.int8), _t((m,), torch.float32)
+    if case == "y_dtype_mixed":
+        y1 = _t((m, n1), torch.bfloat16)
+    elif case == "y_short":
+        y1 = _t((m, n1 - 1), torch.float32)
+    elif case == "acc_dtype":
+        acc1 = _t((m, n1), torch.float32)
+    elif case == "acc_short":
+        acc1 = _t((m - 1, n1), torch.int32)
+    elif case == "xq_short":
+        x_q = _t((m, k - 4), torch.int8)
+    elif case == "xscale_short":
+        x_scale = _t((m - 1,), torch.float32)
+    elif case == "packed_short":
+        w1 = _t((n1, k // 4 - 1), torch.uint8)
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_quant_linear_multi([(w0, s, y0), (w1, s, y1, acc1)], x, x_q=x_q,
+                                              x_scale=x_scale)
+
+
+def test_binding_rejects_bad_outputs_single(cpu_binding):
+    import torch
+    m, k, n = 3, 64, 8
+    w, s = _t((n, k // 4), torch.uint8), _t((1,), torch.float32)
+    xq, xs = _t((m, k), torch.int8), _t((m,), torch.float32)
+    bad = [dict(y=_t((m, n + 1), torch.float32)), dict(y=_t((m, n), torch.float16)),
+           dict(acc_out=_t((m, n), torch.int64)), dict(acc_out=_t((m, n - 1), torch.int32))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            cpu_binding.bitnet_ternary_linear(w, s, xq, xs, **kw)
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_ternary_linear(w, s, xq, _t((m + 1,), torch.float32))
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_ternary_linear(w, _t((1,), torch.float64), xq, xs)
+    x = _t((m, k), torch.float32)
+    for kw in (dict(x_q=_t((m, k), torch.uint8)), dict(x_scale=_t((m,), torch.bfloat16)),
+               dict(y=_t((n, m), torch.float32))):
+        with pytest.raises(ValueError):
+            cpu_binding.bitnet_quant_linear(w, s, x, **kw)
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_quantize_acts(x, x_q=_t((m, k - 1), torch.int8))
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_quantize_acts(x, norm_weight=_t((k + 1,), torch.float32))
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_quantize_weights(_t((n, k), torch.float32),
+                                            packed=_t((n, k // 4 - 1), torch.uint8))
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_quantize_weights(_t((n, k), torch.float32),
+                                            scale=_t((0,), torch.float32))
+
+
+def test_binding_rejects_bad_outputs_t1_lut(cpu_binding):
+    import torch
+    m, k, n = 2, 160, 8
+    rb = 16 * ((k + 79) // 80)
+    s = _t((1,), torch.float32)
+    xq, xs = _t((m, k), torch.int8), _t((m,), torch.float32)
+    with pytest.raises(ValueError):   # a 2-bit matrix handed to the T1 call
+        cpu_binding.bitnet_ternary_linear_t1([(_t((n, k // 4), torch.uint8), s)], xq, xs)
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_ternary_linear_t1([(_t((n, rb), torch.uint8), s,
+                                               _t((m, n), torch.int32))], xq, xs)
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_repack_t1(_t((n, k // 4), torch.uint8), out=_t((n, rb - 16), torch.uint8))
+    k = 128
+    with pytest.raises(ValueError):
+        cpu_binding.bitnet_ternary_linear_lut(_t((n, k // 4), torch.uint8), s,
+                                              _t((m, k), torch.int8), _t((m,), torch.float32),
+                                              y=_t((m, n), torch.int32), workspace=_t((1,), torch.uint8))

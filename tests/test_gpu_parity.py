@@ -15,6 +15,7 @@ from oracle import bitnet_oracle as O
 from ternary_weight_linear_bit_amd import _native as N
 from ternary_weight_linear_bit_amd import inputs as I
 
+from golden_util import f32_from_hex, golden_arrays, hex_bits
 from gpu_helpers import DEV, acts, bf16_bits, dev, f32_bits, host, weights
 
 pytestmark = pytest.mark.gpu
@@ -94,19 +95,39 @@ def test_quantize_weights_unaligned_buffers():
 
 
 def test_golden_examples_on_gpu(golden):
+    """The hand-worked examples through every kernel family: as given (decode kernel
+    at K % 64 == 0, else the generic one), with the token tiled to 20 rows (the
+    prefill kernel at K % 64 == 0), and through the fused act-quant + linear call."""
     for ex in golden["examples"]:
-        w = np.array(ex["W"], np.float32)
-        x = np.array(ex["X"], np.float32)
+        w, x, _, want_xq = golden_arrays(ex)
+        want_gamma = (f32_from_hex(ex["gamma_bits"]) if "gamma_bits" in ex
+                      else np.float32(ex["gamma"]))
         packed, scale = N.bitnet_quantize_weights(dev(w))
         np.testing.assert_array_equal(host(packed), np.array(ex["packed"], np.uint8))
-        xq, xs = N.bitnet_quantize_acts(dev(x))
-        np.testing.assert_array_equal(host(xq), np.array(ex["xq"], np.int8))
-        np.testing.assert_array_equal(f32_bits(host(xs)), [int(h, 16) for h in ex["d_bits"]])
+        assert f32_bits(host(scale))[0] == f32_bits(want_gamma), ex["name"]
+        want_acc = np.array(ex["acc"], np.int32)
+        want_y = hex_bits(ex["y_bits"])
+        want_b = hex_bits(ex["y_bf16_bits"], np.uint16)
+        want_d = np.array([int(h, 16) for h in ex["d_bits"]], np.uint32)
+        for rep in (1, 20):
+            xt = np.tile(x, (rep, 1))
+            xq, xs = N.bitnet_quantize_acts(dev(xt))
+            np.testing.assert_array_equal(host(xq), np.tile(want_xq, (rep, 1)))
+            np.testing.assert_array_equal(f32_bits(host(xs)), np.tile(want_d, rep))
+            acc = torch.empty((xt.shape[0], w.shape[0]), dtype=torch.int32, device=DEV)
+            y = N.bitnet_ternary_linear(packed, scale, xq, xs, acc_out=acc)
+            np.testing.assert_array_equal(host(acc), np.tile(want_acc, (rep, 1)), ex["name"])
+            np.testing.assert_array_equal(f32_bits(host(y)), np.tile(want_y, (rep, 1)), ex["name"])
+            yb = N.bitnet_ternary_linear(packed, scale, xq, xs, y_dtype=torch.bfloat16)
+            np.testing.assert_array_equal(bf16_bits(yb), np.tile(want_b, (rep, 1)), ex["name"])
+        xq, xs = (torch.empty(x.shape, dtype=torch.int8, device=DEV),
+                  torch.empty(x.shape[0], dtype=torch.float32, device=DEV))
         acc = torch.empty((x.shape[0], w.shape[0]), dtype=torch.int32, device=DEV)
-        y = N.bitnet_ternary_linear(packed, scale, xq, xs, acc_out=acc)
-        np.testing.assert_array_equal(host(acc), np.array(ex["acc"], np.int32))
-        np.testing.assert_array_equal(f32_bits(host(y)),
-                                      np.array([[int(h, 16) for h in r] for r in ex["y_bits"]]))
+        y, _, _ = N.bitnet_quant_linear(packed, scale, dev(x), x_q=xq, x_scale=xs, acc_out=acc)
+        np.testing.assert_array_equal(host(xq), want_xq)
+        np.testing.assert_array_equal(f32_bits(host(xs)), want_d)
+        np.testing.assert_array_equal(host(acc), want_acc, ex["name"])
+        np.testing.assert_array_equal(f32_bits(host(y)), want_y, ex["name"])
 
 
 # ---------------------------------------------------------------------------

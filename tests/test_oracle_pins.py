@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import bitnet_oracle as O
+from golden_util import golden_arrays
 
 F32 = np.float32
 
@@ -28,17 +29,24 @@ def frac_of(v):
 # ---------------------------------------------------------------------------
 
 def test_golden_worked_examples(golden):
-    """Full layer on hand-derived examples: catches any wrong step end to end."""
+    """Full layer on hand-derived examples: catches any wrong step end to end.
+
+    The example with gamma and d both away from 1 fixes three readings that
+    plainer examples leave open: the weight is divided by gamma (one correctly
+    rounded division, not a product with a rounded reciprocal: one weight's
+    quotient lands within 2^-25 of 0.5), the token scale is RN32(a*/127) (not
+    the reciprocal of s, nor a* times RN32(1/127)), and the rescale multiplies
+    acc by RN32(gamma * d) (the two other orders of the two products give
+    different fp32 outputs)."""
     for ex in golden["examples"]:
-        w = np.array(ex["W"], dtype=np.float32)
-        x = np.array(ex["X"], dtype=np.float32)
+        w, x, want_q, want_xq = golden_arrays(ex)
         packed, gamma = O.quantize_weights(w)
         want_gamma = f32_from_hex(ex["gamma_bits"]) if "gamma_bits" in ex else F32(ex["gamma"])
         assert gamma.view(np.uint32) == want_gamma.view(np.uint32), ex["name"]
-        np.testing.assert_array_equal(O.ternarize(w, gamma), np.array(ex["q"], dtype=np.int8))
+        np.testing.assert_array_equal(O.ternarize(w, gamma), want_q)
         np.testing.assert_array_equal(packed, np.array(ex["packed"], dtype=np.uint8))
         xq, d = O.quantize_acts(x)
-        np.testing.assert_array_equal(xq, np.array(ex["xq"], dtype=np.int8))
+        np.testing.assert_array_equal(xq, want_xq)
         np.testing.assert_array_equal(d.view(np.uint32),
                                       np.array([int(h, 16) for h in ex["d_bits"]], dtype=np.uint32))
         acc, y = O.ternary_linear(packed, gamma, xq, d)
