@@ -105,6 +105,24 @@ bitnet_status bitnet_quantize_weights(const void *w, int w_dtype, int64_t N, int
                                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * bitnet_quantize_weights for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the library's own workspace in
+ * place of the caller's.  That workspace is a device array of 16640 bytes
+ * (bitnet_quantize_weights_workspace_bytes()) in the library's code object: each
+ * device holds one copy from the first call on it until the process ends.  The
+ * call allocates and frees nothing.  Arguments and limits as for
+ * bitnet_quantize_weights (N*K < BITNET_MAX_WEIGHTS; the workspace size does not
+ * depend on N or K).  Every call on one device shares its array and clears it
+ * first (with a kernel): calls that overlap on one device (two streams, or two
+ * host threads) race and must be serialised by the caller.  First call on a
+ * device: BITNET_ERR_HIP if the array's address cannot be looked up.
+ */
+bitnet_status bitnet_quantize_weights_noalloc(const void *w, int w_dtype, int64_t N, int64_t K,
+                                              uint8_t *w_packed, float *w_scale,
+                                              hipStream_t stream);
+
+/*
  * Per-token absmax int8 activation quantisation (communeify, quantisation
  * details: 8-bit activations; the scheme is the per-token reading above).
  *   x        [M][K] fp32 or bf16 (x_dtype), finite values, element-aligned.

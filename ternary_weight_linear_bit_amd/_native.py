@@ -26,6 +26,7 @@ SIGNATURES = {
     "bitnet_packed_bytes": (_SZ, [_I64, _I64]),
     "bitnet_quantize_weights_workspace_bytes": (_SZ, [_I64, _I64]),
     "bitnet_quantize_weights": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _SZ, _P]),
+    "bitnet_quantize_weights_noalloc": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bitnet_quantize_acts": (_I, [_P, _I, _I64, _I64, _P, _P, _P]),
     "bitnet_ternary_linear": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P]),
     "bitnet_quant_linear": (_I, [_P, _P, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P]),
@@ -190,6 +191,20 @@ def bitnet_quantize_weights(w, packed=None, scale=None, workspace=None, stream=N
     _check("bitnet_quantize_weights", lib().bitnet_quantize_weights(
         _ptr(w), _dtype_code(w.dtype), n, k, _ptr(packed), _ptr(scale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return packed, scale
+
+
+def bitnet_quantize_weights_noalloc(w, packed, scale, stream=None):
+    """bitnet_quantize_weights with the library's own per-device workspace: the
+    caller supplies packed uint8 [N, K/4] and scale fp32 [1]; nothing is allocated."""
+    import torch
+    _need_cuda(w)
+    n, k = w.shape
+    _expect(w, (n, k), _floats(), "w")
+    _expect(packed, (n, k // 4), torch.uint8, "packed")
+    _check_scale(scale)
+    _check("bitnet_quantize_weights_noalloc", lib().bitnet_quantize_weights_noalloc(
+        _ptr(w), _dtype_code(w.dtype), n, k, _ptr(packed), _ptr(scale), _stream(stream)))
     return packed, scale
 
 

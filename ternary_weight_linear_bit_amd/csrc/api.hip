@@ -268,6 +268,17 @@ bitnet_status bitnet_quantize_weights(const void* w, int w_dtype, int64_t N, int
                                     stream));
 }
 
+bitnet_status bitnet_quantize_weights_noalloc(const void* w, int w_dtype, int64_t N, int64_t K,
+                                              uint8_t* w_packed, float* w_scale,
+                                              hipStream_t stream) {
+  if (!w || !w_packed || !w_scale) return BITNET_ERR_NULL;
+  if (!valid_dtype(w_dtype)) return BITNET_ERR_DTYPE;
+  if (N < 1 || K < 4 || (K % 4) != 0 || N >= BITNET_MAX_WEIGHTS / K) return BITNET_ERR_SHAPE;
+  if (!aligned(w, esize(w_dtype)) || !aligned(w_scale, 4)) return BITNET_ERR_ALIGN;
+  return from_hip(bitnet::launch_wq_noalloc(w, w_dtype == BITNET_BF16, N * K, w_packed, w_scale,
+                                            stream));
+}
+
 size_t bitnet_t1_packed_bytes(int64_t N, int64_t K) {
   if (N < 0 || K < 0) return 0;
   return (size_t)N * (size_t)(16 * ((K + 79) / 80));

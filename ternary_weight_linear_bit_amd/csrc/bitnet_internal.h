@@ -184,6 +184,10 @@ constexpr size_t kWqThresholdAt = (size_t)kWqCopies * 256 * 8;
 constexpr size_t kWqWorkspaceBytes = kWqThresholdAt + 256;
 hipError_t launch_wq(const void* w, bool w_bf16, int64_t n_weights, uint8_t* w_packed,
                      float* w_scale, void* workspace, hipStream_t s);
+// The same with the library's own per-device workspace (a file-scope device array
+// of kWqWorkspaceBytes): allocates nothing.
+hipError_t launch_wq_noalloc(const void* w, bool w_bf16, int64_t n_weights, uint8_t* w_packed,
+                             float* w_scale, hipStream_t s);
 // The same scale with the T1 layout (five codes per byte, 16 * ceil(K / 80) bytes
 // per row), and the exact conversion of a 2-bit packed matrix (K % 4 == 0) to it.
 hipError_t launch_wq_t1(const void* w, bool w_bf16, int64_t N, int64_t K, uint8_t* w_t1,

@@ -28,7 +28,17 @@
 //   kWqThresholdAt       float threshold  (see wq_finish)
 #include "bitnet_internal.h"
 
+#include <mutex>
+
 namespace bitnet {
+
+// Workspace of the allocation-free entry point (bitnet_quantize_weights_noalloc):
+// one weight-quantisation workspace per device, created with the code object and
+// held until the process ends.  Host code never passes this name to a kernel (on
+// the host it is only a stand-in for the symbol): it uses the per-device address
+// from hipGetSymbolAddress, taken once per device by wq_scratch.
+static __device__ __align__(256) unsigned char scratch[kWqWorkspaceBytes];
+
 namespace {
 
 constexpr int kHistThreads = 256;
@@ -485,6 +495,35 @@ hipError_t launch_wq(const void* w, bool w_bf16, int64_t n, uint8_t* w_packed, f
     hipLaunchKernelGGL(wq_pack<false>, dim3(pack_blocks), dim3(kPackThreads), 0, s, w, n,
                        pack_vec, thr, w_packed);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept: each device holds its own copy.
+hipError_t wq_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_wq_noalloc(const void* w, bool w_bf16, int64_t n, uint8_t* w_packed,
+                             float* w_scale, hipStream_t s) {
+  void* ws = nullptr;
+  const hipError_t e = wq_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_wq(w, w_bf16, n, w_packed, w_scale, ws, s);
 }
 
 hipError_t launch_wq_t1(const void* w, bool w_bf16, int64_t N, int64_t K, uint8_t* w_t1,
