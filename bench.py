@@ -88,6 +88,8 @@ def parse():
     p.add_argument("--no-compare", action="store_true",
                    help="skip the single-matrix comparison of the decode kernels")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--chain-sweep", action="store_true",
+                   help="only time the decode chain at ring depths 4, 8, 16 (C5 and C2)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this size (PMC calibration)")
     return p.parse_args()
@@ -218,6 +220,74 @@ def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycl
                layers=layers, shapes=shapes, act=wl["act"],
                ms_p10=pct[10], ms_median=pct[50], ms_p90=pct[90])
     del graphs, stack
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def chain_leg(torch, N, I, name, steps, warmup, m=1, min_cycle=None, ring=None):
+    """The same stack through the decode chain: one cooperative launch per token
+    runs every layer's four fused act-quant + linear stages with grid barriers
+    between them (bitnet_chain_plan / bitnet_chain_run)."""
+    wl = I.WORKLOADS[name]
+    shapes, layers = wl["layer"], wl["layers"]
+    per_stack = I.packed_bytes(shapes) * layers
+    replicas = max(1, math.ceil((min_cycle or CACHE_CYCLE_BYTES) / per_stack))
+    t0 = time.time()
+    stack = build_stack(torch, N, I, shapes, layers, replicas)
+    log(f"{name} (chain): {layers} layers, {per_stack / 1e6:.1f} MB packed per step, "
+        f"{replicas} replicas, weights ternarised on the GPU in {time.time() - t0:.1f} s")
+    act_dt = torch.bfloat16 if wl["act"] == "bf16" else torch.float32
+    hidden = shapes[0][1]
+    g = torch.Generator(device="cuda").manual_seed(I.ACT_SEED)
+    h0 = torch.randn((m, hidden), generator=g, device="cuda").to(act_dt)
+    kin = {nm: k for nm, k, _ in shapes}
+    bufs = {nm: torch.empty((m, n), dtype=act_dt, device="cuda") for nm, _, n in shapes}
+    for tag, k in (("h", kin["q"]), ("q", kin["o"]), ("o", kin["gate"]), ("u", kin["down"])):
+        bufs["xq_" + tag] = torch.empty((m, k), dtype=torch.int8, device="cuda")
+        bufs["xs_" + tag] = torch.empty((m,), dtype=torch.float32, device="cuda")
+    chains = []
+    for r in range(replicas):
+        st = []
+        h = h0
+        for mats in stack[r]:
+            st.append(dict(x=h, x_q=bufs["xq_h"], x_scale=bufs["xs_h"],
+                           mats=[(*mats["q"], bufs["q"]), (*mats["k"], bufs["k"]),
+                                 (*mats["v"], bufs["v"])]))
+            st.append(dict(x=bufs["q"], x_q=bufs["xq_q"], x_scale=bufs["xs_q"],
+                           mats=[(*mats["o"], bufs["o"])]))
+            st.append(dict(x=bufs["o"], x_q=bufs["xq_o"], x_scale=bufs["xs_o"],
+                           mats=[(*mats["gate"], bufs["gate"]), (*mats["up"], bufs["up"])]))
+            st.append(dict(x=bufs["up"], x_q=bufs["xq_u"], x_scale=bufs["xs_u"],
+                           mats=[(*mats["down"], bufs["down"])]))
+            h = bufs["down"]
+        c = N.bitnet_chain_plan(st, m)
+        if ring:
+            c.handle.ring = ring
+        chains.append(c)
+    for i in range(max(warmup, replicas)):
+        N.bitnet_chain_run(chains[i % replicas])
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        N.bitnet_chain_run(chains[i % replicas])
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    err = max(N.bitnet_chain_error(c) for c in chains)
+    if err:
+        raise RuntimeError(f"decode chain abandoned a barrier (error word {err})")
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    pct = {q: per[min(steps - 1, int(q / 100 * steps))] for q in (10, 50, 90)}
+    gbs = per_stack / (ms * 1e-3) / 1e9
+    log(f"{name} (chain, M={m}, ring {chains[0].handle.ring}, grid {chains[0].handle.grid}): "
+        f"{ms * 1e3:.1f} us/step, {gbs:.1f} GB/s packed")
+    res = dict(ms=ms, gbs=gbs, per_stack=per_stack, replicas=replicas, launches=1,
+               weights=sum(n * k for _, k, n in shapes) * layers, layers=layers, shapes=shapes,
+               act=wl["act"], ms_p10=pct[10], ms_median=pct[50], ms_p90=pct[90],
+               ring=chains[0].handle.ring, grid=chains[0].handle.grid)
+    del chains, stack
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
@@ -535,6 +605,11 @@ def main():
         log(f"cpu baseline: {cpu}")
     torch.cuda.set_device(0)
     N.lib()
+    if args.chain_sweep:
+        for wname in ("ternary100b-decode-m1-96L", "bitnet2b-decode-m1-30L"):
+            for ring in (4, 8, 16):
+                chain_leg(torch, N, I, wname, args.steps, args.warmup, ring=ring)
+        return
     d = decode_leg(torch, N, I, args.workload, args.steps, args.warmup)
     avg_launch = d["ms"] * 1e-3 / d["launches"]
     avg_bytes = d["per_stack"] / d["launches"]

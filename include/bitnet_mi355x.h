@@ -324,6 +324,64 @@ bitnet_status bitnet_ternary_linear_lut(const uint8_t *w_packed, const float *w_
                                         int32_t *acc_out, void *workspace,
                                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Decode chain: a sequence of fused act-quant + ternary linear stages (each one
+ * bitnet_quant_linear_multi: quantise the stage input per token, then apply up
+ * to four matrices that share it) run in ONE launch per token, with a grid-wide
+ * barrier between stages, so a stage may read any earlier stage's outputs (the
+ * layer stack of a decoder: q, k, v from the layer input, o from q, gate and up
+ * from o, down from up, the next layer from down).  Results are those of the
+ * bitnet_quant_linear_multi calls made one after another, bit for bit (same
+ * arithmetic: onedollarvps section 2, dashen-tech sections 2.3 and 3.1,
+ * communeify quantisation details).
+ *
+ * Plan once, run per token:
+ *   bitnet_chain_plan checks every stage, assigns row tiles to workgroups and
+ *   copies the stage table into `plan` (device memory of
+ *   bitnet_chain_plan_bytes(n_stages) bytes, 256-byte aligned, caller-owned,
+ *   untouched by anything else while the chain is in use).  It synchronises
+ *   (blocking copy), so it is a set-up call: not under graph capture.
+ *   bitnet_chain_run enqueues one cooperative launch on `stream`; the pointers
+ *   in the stages must stay valid.  Runs on one device must not overlap (they
+ *   share the plan's barrier counters).
+ * Stage requirements: M in 1..4 (decode), K % 64 == 0, 64 <= K, M * (K + 16) <=
+ * 65536; x, x_q, every w_packed 16-byte aligned; y and acc_out as for
+ * bitnet_quant_linear_multi; N >= 1 per matrix; 1..4 matrices per stage.
+ * Otherwise BITNET_ERR_SHAPE / BITNET_ERR_NULL / BITNET_ERR_ALIGN /
+ * BITNET_ERR_DTYPE, and nothing is copied.
+ * Every wait inside the launch is bounded: if a barrier does not complete (it
+ * cannot while the chain's workgroups are all resident, which the cooperative
+ * launch guarantees), the launch stops waiting and sets a sticky error word,
+ * readable with bitnet_chain_error (1 = abandoned, outputs unspecified; reset
+ * by planning again).
+ */
+typedef struct bitnet_chain_stage {
+  const void *x;               /* stage input [M][K] */
+  int x_dtype;                 /* BITNET_F32 or BITNET_BF16 */
+  int y_dtype;                 /* dtype of every output y of the stage */
+  int64_t K;
+  const bitnet_matrix *mats;   /* 1..4 matrices sharing x (read at plan time) */
+  int count;
+  int8_t *x_q;                 /* out [M][K]: the quantised input */
+  float *x_scale;              /* out [M]: its token scales */
+} bitnet_chain_stage;
+
+typedef struct bitnet_chain {
+  void *plan;                  /* the device memory given to bitnet_chain_plan */
+  int n_stages, M;
+  int grid;                    /* workgroups of the launch (all co-resident) */
+  int kmax, tmax;              /* largest K and row tiles per workgroup of any stage */
+  int ring;                    /* weight loads in flight per lane: 4 (default), 8 or 16 */
+} bitnet_chain;
+
+size_t bitnet_chain_plan_bytes(int n_stages);
+bitnet_status bitnet_chain_plan(const bitnet_chain_stage *stages, int n_stages, int64_t M,
+                                void *plan, size_t plan_bytes, bitnet_chain *chain);
+bitnet_status bitnet_chain_run(const bitnet_chain *chain, hipStream_t stream);
+/* Reads the plan's error word into *error (0 = every run so far completed its
+ * barriers).  Synchronises with the device. */
+bitnet_status bitnet_chain_error(const bitnet_chain *chain, int *error);
+
 #ifdef __cplusplus
 }
 #endif

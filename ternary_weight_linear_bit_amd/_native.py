@@ -473,3 +473,83 @@ def bitnet_ternary_linear_lut(w_packed, w_scale, x_q, x_scale, y=None, y_dtype=N
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
 
+
+
+# ---------------------------------------------------------------------------
+# decode chain: every stage of a token in one launch
+# ---------------------------------------------------------------------------
+
+class BitnetChainStage(ctypes.Structure):
+    """struct bitnet_chain_stage of the public header."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int), ("y_dtype", ctypes.c_int),
+                ("K", ctypes.c_int64), ("mats", ctypes.POINTER(BitnetMatrix)),
+                ("count", ctypes.c_int), ("x_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p)]
+
+
+class BitnetChain(ctypes.Structure):
+    """struct bitnet_chain of the public header."""
+    _fields_ = [("plan", ctypes.c_void_p), ("n_stages", ctypes.c_int), ("M", ctypes.c_int),
+                ("grid", ctypes.c_int), ("kmax", ctypes.c_int), ("tmax", ctypes.c_int),
+                ("ring", ctypes.c_int)]
+
+
+SIGNATURES["bitnet_chain_plan_bytes"] = (_SZ, [_I])
+SIGNATURES["bitnet_chain_plan"] = (_I, [ctypes.POINTER(BitnetChainStage), _I, _I64, _P, _SZ,
+                                        ctypes.POINTER(BitnetChain)])
+SIGNATURES["bitnet_chain_run"] = (_I, [ctypes.POINTER(BitnetChain), _P])
+SIGNATURES["bitnet_chain_error"] = (_I, [ctypes.POINTER(BitnetChain), ctypes.POINTER(_I)])
+
+
+class Chain:
+    """A planned decode chain: the device plan, the bitnet_chain handle and the
+    tensors it points to (kept alive here)."""
+
+    def __init__(self, plan, handle, keep):
+        self.plan = plan
+        self.handle = handle
+        self._keep = keep
+
+
+def bitnet_chain_plan(stages, m):
+    """stages: list of dicts with x [M, K] (fp32/bf16), mats [(w_packed, w_scale, y[,
+    acc_out])], x_q int8 [M, K], x_scale fp32 [M].  Every y must already exist (a
+    later stage's x is usually an earlier stage's y).  Returns a Chain."""
+    import torch
+    n = len(stages)
+    arr = (BitnetChainStage * n)()
+    keep = []
+    device = None
+    for i, st in enumerate(stages):
+        x, x_q, x_scale = st["x"], st["x_q"], st["x_scale"]
+        _need_cuda(x)
+        if x.dim() != 2 or x.shape[0] != m:
+            raise ValueError(f"stage {i}: x must be [M, K] with M = {m}")
+        k = x.shape[1]
+        _check_act_operands(x, x_q, x_scale)
+        mats = st["mats"]
+        if any(len(t) < 3 or t[2] is None for t in mats):
+            raise ValueError(f"stage {i}: every matrix needs its output y")
+        marr, ys = _matrices(mats, m, k, mats[0][2].dtype, x.device)
+        arr[i] = BitnetChainStage(x.data_ptr(), _dtype_code(x.dtype), _dtype_code(ys[0].dtype), k,
+                                  marr, len(mats), x_q.data_ptr(), x_scale.data_ptr())
+        keep += [x, x_q, x_scale, marr, ys, mats]
+        device = x.device
+    nbytes = lib().bitnet_chain_plan_bytes(n)
+    plan = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    handle = BitnetChain()
+    _check("bitnet_chain_plan", lib().bitnet_chain_plan(arr, n, m, _ptr(plan), nbytes,
+                                                        ctypes.byref(handle)))
+    return Chain(plan, handle, keep)
+
+
+def bitnet_chain_run(chain, stream=None):
+    """Enqueue one launch of the whole chain (one token)."""
+    _check("bitnet_chain_run", lib().bitnet_chain_run(ctypes.byref(chain.handle), _stream(stream)))
+
+
+def bitnet_chain_error(chain) -> int:
+    """The plan's sticky error word (0 = every run completed its barriers); syncs."""
+    e = ctypes.c_int(0)
+    _check("bitnet_chain_error", lib().bitnet_chain_error(ctypes.byref(chain.handle),
+                                                          ctypes.byref(e)))
+    return e.value

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitnet_mi355x.so")
-SOURCES = ("api.hip", "wq.hip", "aq.hip", "gemv.hip", "gemm.hip", "lut.hip")
+SOURCES = ("api.hip", "wq.hip", "aq.hip", "gemv.hip", "gemm.hip", "lut.hip", "chain.hip")
 # bench-only diagnostic (int8 matrix-core rate), its own library: not part of the ABI
 PROBE_SRC = os.path.join(PKG, "bench_probe", "mfma_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libbitnet_bench_probe.so")

@@ -3,6 +3,10 @@
 #include "bitnet_mi355x.h"
 #include "bitnet_internal.h"
 
+#include <string.h>
+
+#include <vector>
+
 namespace {
 
 constexpr int64_t kInt32Max = 2147483647;
@@ -429,6 +433,104 @@ bitnet_status bitnet_quant_linear(const uint8_t* w_packed, const float* w_scale,
                                   hipStream_t stream) {
   const bitnet_matrix m{w_packed, w_scale, N, y, acc_out};
   return bitnet_quant_linear_multi(&m, 1, x, x_dtype, M, K, x_q, x_scale, y_dtype, stream);
+}
+
+size_t bitnet_chain_plan_bytes(int n_stages) {
+  if (n_stages < 1) return 0;
+  return bitnet::chain_plan_bytes(n_stages);
+}
+
+bitnet_status bitnet_chain_plan(const bitnet_chain_stage* stages, int n_stages, int64_t M,
+                                void* plan, size_t plan_bytes, bitnet_chain* chain) {
+  if (!stages || !plan || !chain) return BITNET_ERR_NULL;
+  if (n_stages < 1 || M < 1 || M > bitnet::kChainMaxM) return BITNET_ERR_SHAPE;
+  if (plan_bytes < bitnet_chain_plan_bytes(n_stages)) return BITNET_ERR_WORKSPACE;
+  if (!aligned(plan, 256)) return BITNET_ERR_ALIGN;
+  int kmax = 64;
+  for (int s = 0; s < n_stages; ++s) {
+    const bitnet_chain_stage& st = stages[s];
+    if (!st.x || !st.x_q || !st.x_scale || !st.mats) return BITNET_ERR_NULL;
+    if (!valid_dtype(st.x_dtype) || !valid_dtype(st.y_dtype)) return BITNET_ERR_DTYPE;
+    if (st.count < 1 || st.count > bitnet::kMaxGroup || st.K < 64 || (st.K % 64) != 0 ||
+        M * (st.K + 16) > 65536)
+      return BITNET_ERR_SHAPE;
+    if (!aligned(st.x, 16) || !aligned(st.x_q, 16) || !aligned(st.x_scale, 4))
+      return BITNET_ERR_ALIGN;
+    for (int j = 0; j < st.count; ++j) {
+      const bitnet_matrix& m = st.mats[j];
+      if (m.N < 1 || M * m.N >= ((int64_t)1 << 30)) return BITNET_ERR_SHAPE;
+      if (!m.w_packed || !m.w_scale || !m.y) return BITNET_ERR_NULL;
+      if (!aligned(m.w_packed, 16) || !aligned(m.w_scale, 4) || !aligned(m.y, esize(st.y_dtype)) ||
+          (m.acc_out && !aligned(m.acc_out, 4)))
+        return BITNET_ERR_ALIGN;
+    }
+    if (st.K > kmax) kmax = (int)st.K;
+  }
+  const int ring = 4;
+  const int grid = bitnet::chain_grid((int)M, kmax, bitnet::kChainMaxTiles, ring);
+  if (grid < 1) return BITNET_ERR_HIP;
+  // host image of the plan: zeroed counters, then the stage table
+  std::vector<char> host(bitnet_chain_plan_bytes(n_stages), 0);
+  auto* table = reinterpret_cast<bitnet::ChainStage*>(host.data() + bitnet::kChainHeaderBytes);
+  int tmax = 1;
+  for (int s = 0; s < n_stages; ++s) {
+    const bitnet_chain_stage& st = stages[s];
+    bitnet::ChainStage d;
+    memset(&d, 0, sizeof(d));
+    d.x = st.x;
+    d.xq_out = st.x_q;
+    d.xs_out = st.x_scale;
+    int total = 0;
+    for (int j = 0; j < bitnet::kMaxGroup; ++j) {
+      d.tc0[j] = total;
+      if (j < st.count) {
+        d.wp[j] = st.mats[j].w_packed;
+        d.ws[j] = st.mats[j].w_scale;
+        d.y[j] = st.mats[j].y;
+        d.acc[j] = st.mats[j].acc_out;
+        d.n[j] = (int)st.mats[j].N;
+        total += (int)((st.mats[j].N + 15) / 16);
+      }
+    }
+    d.tc0[bitnet::kMaxGroup] = total;
+    // the tile list is spread evenly: at most ceil(total / grid) tiles per workgroup
+    const int T = (total + grid - 1) / grid;
+    if (T > bitnet::kChainMaxTiles) return BITNET_ERR_SHAPE;
+    if (T > tmax) tmax = T;
+    d.K = (int)st.K;
+    d.count = st.count;
+    d.flags = (st.x_dtype == BITNET_BF16 ? 1 : 0) | (st.y_dtype == BITNET_BF16 ? 2 : 0);
+    table[s] = d;
+  }
+  if (hipMemcpy(plan, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return BITNET_ERR_HIP;
+  chain->plan = plan;
+  chain->n_stages = n_stages;
+  chain->M = (int)M;
+  chain->grid = grid;
+  chain->kmax = kmax;
+  chain->tmax = tmax;
+  chain->ring = ring;
+  return BITNET_OK;
+}
+
+bitnet_status bitnet_chain_run(const bitnet_chain* chain, hipStream_t stream) {
+  if (!chain || !chain->plan) return BITNET_ERR_NULL;
+  if (chain->n_stages < 1 || chain->M < 1 || chain->M > bitnet::kChainMaxM || chain->grid < 1 ||
+      chain->kmax < 64 || chain->tmax < 1 || chain->tmax > bitnet::kChainMaxTiles ||
+      (chain->ring != 4 && chain->ring != 8 && chain->ring != 16))
+    return BITNET_ERR_SHAPE;
+  return from_hip(bitnet::launch_chain(chain->plan, chain->n_stages, chain->M, chain->grid,
+                                       chain->kmax, chain->tmax, chain->ring, stream));
+}
+
+bitnet_status bitnet_chain_error(const bitnet_chain* chain, int* error) {
+  if (!chain || !chain->plan || !error) return BITNET_ERR_NULL;
+  unsigned word = 0;
+  const char* at = static_cast<const char*>(chain->plan) + bitnet::kChainErrorAt;
+  if (hipMemcpy(&word, at, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return BITNET_ERR_HIP;
+  *error = (int)word;
+  return BITNET_OK;
 }
 
 }  // extern "C"

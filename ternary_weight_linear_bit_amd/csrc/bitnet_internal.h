@@ -87,6 +87,28 @@ __device__ __forceinline__ void transpose4x4_bytes(const uint32_t in[4], uint32_
   out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
+// One packed dword (codes of k-offsets 0..15, byte b holding 4b..4b+3) -> the
+// 16-byte operand whose byte 4i + b is the weight q = c - 1 of k-offset 4b + i.
+// Each field is isolated with a mask and mapped through a byte lookup (v_perm:
+// selector byte c picks byte c of kCodeLut: 0 -> -1, 1 -> 0, 2 -> +1).
+constexpr uint32_t kCodeLut = 0x000100ffu;
+__device__ __forceinline__ v4i unpack_weights_transposed(uint32_t w) {
+  v4i a;
+  a.x = (int)__builtin_amdgcn_perm(0u, kCodeLut, w & 0x03030303u);
+  a.y = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 2) & 0x03030303u);
+  a.z = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 4) & 0x03030303u);
+  a.w = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 6) & 0x03030303u);
+  return a;
+}
+
+// Stage one 16-byte group of int8 activations in the unpacked weights' k order.
+__device__ __forceinline__ void store_transposed(uint8_t* dst, uint4 v) {
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+  transpose4x4_bytes(in, o);
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Quantise four activations with the token's factor s = RN32(127 / a*):
 // clip(rne(RN32(x * s)), -128, 127), packed little-endian into one dword.
 __device__ __forceinline__ uint32_t quant4(const float* v, float s) {
@@ -125,6 +147,31 @@ __device__ __forceinline__ void load16_act(const void* x, int64_t i16, float v[1
       v[4 * h + 1] = a.y;
       v[4 * h + 2] = a.z;
       v[4 * h + 3] = a.w;
+    }
+  }
+}
+
+// The 16 activations of one group from its raw 16-byte words (2 words of bf16 or
+// 4 of fp32); bf16 -> fp32 is exact.
+template <bool BF>
+__device__ __forceinline__ void raw_to_f32(const uint4* w, float v[16]) {
+  if (BF) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t d[4] = {w[h].x, w[h].y, w[h].z, w[h].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * h + 2 * j] = __uint_as_float(d[j] << 16);
+        v[8 * h + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[4 * h] = __uint_as_float(w[h].x);
+      v[4 * h + 1] = __uint_as_float(w[h].y);
+      v[4 * h + 2] = __uint_as_float(w[h].z);
+      v[4 * h + 3] = __uint_as_float(w[h].w);
     }
   }
 }
@@ -255,6 +302,38 @@ constexpr int64_t kGemvMaxK = (1 << 19) - 1;
 bool gemv_fits(int64_t M, int64_t K, int fmt);
 bool gemv_fused_fits(int64_t M, int64_t K, int fmt);
 hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s);
+// Decode chain (one cooperative launch per token, chain.hip): the device-side
+// descriptor of one stage, i.e. one fused act-quant + linear over up to
+// kMaxGroup matrices that share the stage input.  Filled by bitnet_chain_plan.
+struct ChainStage {
+  const void* x;             // stage input [M][K], fp32 or bf16 (flags bit 0)
+  int8_t* xq_out;            // the quantised input [M][K] and its token scales [M],
+  float* xs_out;             //   written by workgroup 0
+  const uint8_t* wp[kMaxGroup];
+  const float* ws[kMaxGroup];
+  void* y[kMaxGroup];        // outputs [M][N], fp32 or bf16 (flags bit 1)
+  int32_t* acc[kMaxGroup];   // optional int32 accumulators [M][N]
+  int n[kMaxGroup];
+  int tc0[kMaxGroup + 1];    // first 16-row tile of each matrix in the stage's tile list;
+                             //   tc0[count..] = all tiles (spread evenly over the grid)
+  int K, count, flags;
+};
+constexpr int kChainMaxM = 4;
+constexpr int kChainMaxTiles = 16;       // row tiles per workgroup and stage
+constexpr int kChainThreads = 512;     // 4 streaming + 4 staging waves
+constexpr size_t kChainHeaderBytes = 4096;  // barrier counters and the error word
+constexpr int kChainGroups = 8;             // barrier groups (counter lines 0-7)
+constexpr size_t kChainErrorAt = 256 * (kChainGroups + 2);  // byte offset of the error word
+// LDS bytes of the chain kernel for M tokens, inputs up to kmax and up to tmax
+// tiles per workgroup.
+size_t chain_lds_bytes(int M, int kmax, int tmax);
+// Bytes of a plan: header (counters), stage table.
+size_t chain_plan_bytes(int n_stages);
+// One token through every stage; grid = workgroups (all co-resident).
+hipError_t launch_chain(const void* plan, int n_stages, int M, int grid, int kmax, int tmax,
+                        int ring, hipStream_t s);
+int chain_grid(int M, int kmax, int tmax, int ring);
+
 // Prefill kernel arguments: up to kMaxGroup weight matrices sharing K and the
 // int8 activations, passed by value.  launch_gemm fills nb0.
 struct GemmArgs {

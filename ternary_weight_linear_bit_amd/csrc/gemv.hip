@@ -166,20 +166,6 @@ __device__ __forceinline__ int kx_cap(int M) {
 
 __device__ __forceinline__ int ceil_log2(int m) { return m > 1 ? 32 - __builtin_clz(m - 1) : 0; }
 
-// One packed dword (codes of k-offsets 0..15, byte b holding 4b..4b+3) -> the
-// 16-byte operand whose byte 4i + b is the weight q = c - 1 of k-offset 4b + i.
-// Each field is isolated with a mask and mapped through a byte lookup (v_perm:
-// selector byte c picks byte c of kCodeLut: 0 -> -1, 1 -> 0, 2 -> +1).
-constexpr uint32_t kCodeLut = 0x000100ffu;
-__device__ __forceinline__ v4i unpack_weights_transposed(uint32_t w) {
-  v4i a;
-  a.x = (int)__builtin_amdgcn_perm(0u, kCodeLut, w & 0x03030303u);
-  a.y = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 2) & 0x03030303u);
-  a.z = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 4) & 0x03030303u);
-  a.w = (int)__builtin_amdgcn_perm(0u, kCodeLut, (w >> 6) & 0x03030303u);
-  return a;
-}
-
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 // One lane's 16 bytes of a T1 block -> the five A operands: operand j holds the
@@ -217,13 +203,6 @@ __device__ __forceinline__ void unpack_t1(const uint4 w, v4i out[5]) {
   }
 }
 
-__device__ __forceinline__ void store_transposed(uint8_t* dst, uint4 v) {
-  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
-  transpose4x4_bytes(in, o);
-  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-}
-
 // Stage one 16-byte group of int8 activations in the format's order.
 template <int FMT>
 __device__ __forceinline__ void store_group(uint8_t* dst, uint4 v) {
@@ -231,31 +210,6 @@ __device__ __forceinline__ void store_group(uint8_t* dst, uint4 v) {
     *reinterpret_cast<uint4*>(dst) = v;
   else
     store_transposed(dst, v);
-}
-
-// The 16 activations of one group from its raw 16-byte words (2 words of bf16 or
-// 4 of fp32); bf16 -> fp32 is exact.
-template <bool BF>
-__device__ __forceinline__ void raw_to_f32(const uint4* w, float v[16]) {
-  if (BF) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t d[4] = {w[h].x, w[h].y, w[h].z, w[h].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * h + 2 * j] = __uint_as_float(d[j] << 16);
-        v[8 * h + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      v[4 * h] = __uint_as_float(w[h].x);
-      v[4 * h + 1] = __uint_as_float(w[h].y);
-      v[4 * h + 2] = __uint_as_float(w[h].z);
-      v[4 * h + 3] = __uint_as_float(w[h].w);
-    }
-  }
 }
 
 // What a workgroup needs before its first loads comes as leading scalar

@@ -289,3 +289,46 @@ def test_binding_rejects_bad_outputs_t1_lut(cpu_binding):
         cpu_binding.bitnet_ternary_linear_lut(_t((n, k // 4), torch.uint8), s,
                                               _t((m, k), torch.int8), _t((m,), torch.float32),
                                               y=_t((m, n), torch.int32), workspace=_t((1,), torch.uint8))
+
+
+def test_chain_plan_validation(lib):
+    """bitnet_chain_plan rejects bad stages before any HIP call (FAKE pointers are
+    never dereferenced)."""
+    plan_bytes = lib.bitnet_chain_plan_bytes(2)
+    assert plan_bytes > 4096 and lib.bitnet_chain_plan_bytes(0) == 0
+    mats = (N.BitnetMatrix * 1)(N.BitnetMatrix(0x10000, 0x10000, 64, 0x10000, None))
+
+    def stage(**kw):
+        f = dict(x=0x10000, x_dtype=0, y_dtype=0, K=256, mats=mats, count=1, x_q=0x10000,
+                 x_scale=0x10000)
+        f.update(kw)
+        return N.BitnetChainStage(f["x"], f["x_dtype"], f["y_dtype"], f["K"], f["mats"],
+                                  f["count"], f["x_q"], f["x_scale"])
+
+    def plan(st, m=1, nbytes=plan_bytes, ptr=0x10000):
+        arr = (N.BitnetChainStage * len(st))(*st)
+        h = N.BitnetChain()
+        return lib.bitnet_chain_plan(arr, len(st), m, ctypes.c_void_p(ptr), nbytes, ctypes.byref(h))
+
+    assert lib.bitnet_chain_plan(None, 1, 1, FAKE, plan_bytes, None) == ENULL
+    assert plan([stage()], m=0) == ESHAPE
+    assert plan([stage()], m=5) == ESHAPE
+    assert plan([stage(), stage()], nbytes=plan_bytes - 1) == EWS
+    assert plan([stage()], ptr=0x10010) == EALIGN
+    assert plan([stage(K=100)]) == ESHAPE
+    assert plan([stage(K=65536)]) == ESHAPE
+    assert plan([stage(count=0)]) == ESHAPE
+    assert plan([stage(count=5)]) == ESHAPE
+    assert plan([stage(x_dtype=7)]) == EDTYPE
+    assert plan([stage(x=0x10008)]) == EALIGN
+    assert plan([stage(x_q=0x10004)]) == EALIGN
+    assert plan([stage(x=None)]) == ENULL
+    bad = (N.BitnetMatrix * 1)(N.BitnetMatrix(0x10008, 0x10000, 64, 0x10000, None))
+    assert plan([stage(mats=bad)]) == EALIGN
+    zero_n = (N.BitnetMatrix * 1)(N.BitnetMatrix(0x10000, 0x10000, 0, 0x10000, None))
+    assert plan([stage(mats=zero_n)]) == ESHAPE
+    h = N.BitnetChain()
+    assert lib.bitnet_chain_run(ctypes.byref(h), None) == ENULL
+    h.plan = 0x10000
+    h.n_stages, h.M, h.grid, h.kmax, h.tmax, h.ring = 1, 1, 1, 256, 1, 5
+    assert lib.bitnet_chain_run(ctypes.byref(h), None) == ESHAPE
