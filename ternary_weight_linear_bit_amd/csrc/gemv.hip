@@ -35,8 +35,9 @@
 // XMODE 1-8 fuse the per-token absmax activation quantisation (fp32 / bf16 input,
 // M <= kMaxFusedM, one phase): the workgroup quantises the activations with the
 // same arithmetic as the standalone kernel while staging them (one read of the
-// input; the first kHold groups of each thread stay in registers between the
-// absmax and the quantise pass), and workgroup 0 also writes x_q and x_scale.
+// input: each thread's first groups of 16, eight without a prologue and two with
+// one, stay in registers between the absmax and the quantise pass), and
+// workgroup 0 also writes x_q and x_scale.
 // XMODE 3-8 add the layer's input prologue (communeify.com page on BitNet b1.58
 // 2B4T, architecture item: squared-ReLU activation, subln norm, no biases): the
 // input may be the gate projection, gated as RN32(RN32(relu(x)^2) * up), and / or
@@ -67,7 +68,11 @@ constexpr int kXBudget = 16 * (4096 + 16); // LDS bytes of staged activations pe
                                            // of up to 14 tiles)
 constexpr int kFusedXBudget = 46 * 1024;   // fused quantisation: M * K staged at most
 constexpr int kStageBatch = 8;             // 16-byte activation loads per thread per batch
-constexpr int kHold = 2;                   // fused: groups per thread held in registers
+constexpr int kHold = 2;                   // fused with a prologue: groups per thread held in
+                                           // registers between the absmax and quantise passes
+constexpr int kHoldPlain = 8;              // fused, no prologue: K <= 32768 at M = 1 stays in
+                                           // registers (a long input is then read once, with
+                                           // all its loads in flight together)
 constexpr int64_t kLatencyBytes = 6000000; // launches above this use the bandwidth regime
 constexpr int kWgsPerCu = 2;               // bandwidth regime: workgroups per compute unit
 constexpr int kFlightLoads = 4096;         // target 1 KiB loads in flight over the chip
@@ -165,6 +170,7 @@ __device__ __forceinline__ int kx_cap(int M) {
 }
 
 __device__ __forceinline__ int ceil_log2(int m) { return m > 1 ? 32 - __builtin_clz(m - 1) : 0; }
+int ceil_log2_host(int m) { return m > 1 ? 32 - __builtin_clz((unsigned)(m - 1)) : 0; }
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
@@ -231,8 +237,11 @@ constexpr int kArgsAt =
 
 // XMODE 0: int8 x_q.  XMODE 1 + f, f = bf16 (1) | gated by a.xup (2) | RMS norm
 // with a.gnorm (4): fp32 / bf16 input quantised in the kernel.  The prologue
-// options are compile-time so that no load sits behind a runtime branch.
-template <int XMODE, int R, int FMT>
+// options are compile-time so that no load sits behind a runtime branch.  H:
+// groups of 16 inputs per thread held in registers by the fused modes (without a
+// prologue, kHoldPlain for inputs longer than kHold groups per thread, so that
+// they are read once; else kHold).
+template <int XMODE, int R, int FMT, int H = kHold>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const uint8_t* wp0,
                                                         const uint8_t* wp1, const uint8_t* wp2,
                                                         int n0, int n1, int n2, int g1, int g2,
@@ -244,6 +253,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   constexpr bool NRM = XMODE > 0 && (F & 4) != 0;
   constexpr bool PRO = GLU || NRM;
   constexpr int NV = BF ? 2 : 4;             // fused: 16-byte words per 16-element group
+  constexpr int HOLD = PRO ? kHold : H;       // fused: groups held per thread
   constexpr uint32_t ES = BF ? 2u : 4u;      // fused: input element size
   constexpr int ZB = FMT == kFmtT1 ? 96 : 64;  // zero slot bytes (zero_bytes)
   const int tid = threadIdx.x;
@@ -403,13 +413,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     auto goff = [&](int c, int h) -> uint32_t {
       return (tk < M && c < K16) ? 64u * (uint32_t)c + 16u * (uint32_t)h : kOob;
     };
-    uint4 hold[kHold][NV], holdu[kHold][NV], holdg[kHold][4];
+    uint4 hold[HOLD][NV], holdu[HOLD][NV], holdg[HOLD][4];
     if constexpr (XMODE == 0) {
 #pragma unroll
       for (int b = 0; b < kStageBatch; ++b) xv[b] = xload();
     } else {
 #pragma unroll
-      for (int b = 0; b < kHold; ++b) {
+      for (int b = 0; b < HOLD; ++b) {
 #pragma unroll
         for (int h = 0; h < NV; ++h) hold[b][h] = bload16(fr, foff(jg + G * b, h));
         if (PRO) {
@@ -507,14 +517,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
       const int nb = (K16s + G - 1) >> lgG;      // groups per thread, uniform
       float amax = 0.0f;
       double ss = 0.0;
-      float qh[kHold][16];
+      float qh[HOLD][16];
 #pragma unroll
-      for (int b = 0; b < kHold; ++b) {
+      for (int b = 0; b < HOLD; ++b) {
         values(hold[b], holdu[b], holdg[b], qh[b], ss);
 #pragma unroll
         for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(qh[b][j]));
       }
-      for (int b = kHold; b < nb; ++b) {
+      for (int b = HOLD; b < nb; ++b) {
         float v[16];
         reload(jg + G * b, v, ss);
 #pragma unroll
@@ -552,8 +562,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
         store_group<FMT>(tk < M && c < K16s ? xs + tk * stride + 16 * c : zero, q);
       };
 #pragma unroll
-      for (int b = 0; b < kHold; ++b) put(jg + G * b, qh[b]);
-      for (int b = kHold; b < nb; ++b) {
+      for (int b = 0; b < HOLD; ++b) put(jg + G * b, qh[b]);
+      for (int b = HOLD; b < nb; ++b) {
         float v[16];
         double unused = 0.0;
         reload(jg + G * b, v, unused);
@@ -653,26 +663,26 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
 
 // Kernel for activation mode XMODE, weight format FMT and ring depth 2, 4, 8 or
 // 16 (smallest >= R).
-template <int XMODE, int FMT>
+template <int XMODE, int FMT, int H>
 const void* ring_kernel(int R) {
-  if (R <= 2) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT>);
-  if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT>);
-  if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8, FMT>);
-  return reinterpret_cast<const void*>(gemv_kernel<XMODE, 16, FMT>);
+  if (R <= 2) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H>);
+  if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H>);
+  if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8, FMT, H>);
+  return reinterpret_cast<const void*>(gemv_kernel<XMODE, 16, FMT, H>);
 }
 
 template <int FMT>
-const void* select_kernel(int xmode, int R) {
+const void* select_kernel(int xmode, int R, bool long_input) {
   switch (xmode) {
-    case 0: return ring_kernel<0, FMT>(R);
-    case 1: return ring_kernel<1, FMT>(R);
-    case 2: return ring_kernel<2, FMT>(R);
-    case 3: return ring_kernel<3, FMT>(R);
-    case 4: return ring_kernel<4, FMT>(R);
-    case 5: return ring_kernel<5, FMT>(R);
-    case 6: return ring_kernel<6, FMT>(R);
-    case 7: return ring_kernel<7, FMT>(R);
-    default: return ring_kernel<8, FMT>(R);
+    case 0: return ring_kernel<0, FMT, kHold>(R);
+    case 1: return long_input ? ring_kernel<1, FMT, kHoldPlain>(R) : ring_kernel<1, FMT, kHold>(R);
+    case 2: return long_input ? ring_kernel<2, FMT, kHoldPlain>(R) : ring_kernel<2, FMT, kHold>(R);
+    case 3: return ring_kernel<3, FMT, kHold>(R);
+    case 4: return ring_kernel<4, FMT, kHold>(R);
+    case 5: return ring_kernel<5, FMT, kHold>(R);
+    case 6: return ring_kernel<6, FMT, kHold>(R);
+    case 7: return ring_kernel<7, FMT, kHold>(R);
+    default: return ring_kernel<8, FMT, kHold>(R);
   }
 }
 
@@ -747,8 +757,13 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
   // streams lose with it (100B-class stack 16.3 -> 18.0 us)
   if (wgs > 256 && tpw >= 2 && tpw * per_tile <= 6) ring = 2;
   if (ring > tpw * per_tile) ring = tpw * per_tile;
-  const void* kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring)
-                                     : select_kernel<kFmt2>(xmode, ring);
+  // fused input groups of 16 per thread: held in registers when they are more
+  // than kHold (and at most kHoldPlain)
+  const int staged = fmt == kFmtT1 ? 5 * ((a.K + 79) / 80) : a.K / 16;
+  const int per_thread = (staged + (256 >> ceil_log2_host(a.M)) - 1) / (256 >> ceil_log2_host(a.M));
+  const bool long_input = fused && per_thread > kHold;
+  const void* kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, long_input)
+                                     : select_kernel<kFmt2>(xmode, ring, long_input);
   const size_t lds = (size_t)lds_bytes(tpw, a.M, a.K, fmt);
   a.tiles_per_wg = tpw;
   a.mdiv = (65536 + a.M - 1) / a.M;  // tt / M == (tt * mdiv) >> 16 for tt < 256, M <= 16
