@@ -1,32 +1,30 @@
 #!/usr/bin/env python3
 """Throughput of the ternary linear layer path on one MI355X.
 
-Default workload (`bitnet2b-decode-m1-30L`): BitNet-2B-shaped decode, one token
-(M = 1) streamed through 30 layers of {q, k, v: 2560->2560/640/640, o:
-2560->2560, gate, up: 2560->6912, down: 6912->2560}, bf16 activations between
-layers, the per-token int8 activation quantisation fused into the layers.
-Chain per layer: q, k, v from the layer input (one launch); o from q; gate and up
-from o (one launch); down from up; down is the next layer's input: 4 launches
-per layer.  One step = one token through the whole stack, replayed from a HIP
-graph.  Weights are synthetic N(0, 0.02^2), seeded, ternarised on the GPU by
-the library; the stack is replicated so that more than 1 GiB of weights is cycled
-between reuses (4x the 256 MB Infinity Cache) and weights stream from HBM.
+Default workload (`ternary100b-decode-m1-96L`): the ~100B-class ternary decode
+stack, one token (M = 1) streamed through 96 layers of {q, k, v, o: 8192->8192,
+gate, up: 8192->28672, down: 28672->8192} with fp32 activations between layers
+and the per-token int8 activation quantisation fused into every layer (23.35 GB
+of packed weights per token, resident in HBM).  Chain per layer: q, k, v from
+the layer input (one launch); o from q (attention is out of scope); gate and up
+from o (one launch); down from up; down is the next layer's input: 4 launches per
+layer, 384 per token, replayed from a HIP graph.  Weights are synthetic
+N(0, 0.02^2), seeded, ternarised on the GPU by the library.
 
-Printed: one JSON line.  value = packed weight bytes per step / step time.
-roofline = the decode kernel (the only kernel in the step): achieved = mean
-packed bytes per launch / mean launch time, where the mean launch time is the
-graph replay time over the timed steps divided by the number of launches (so it
-includes the gap between dependent launches); traffic = HBM bytes per launch from
-the PMC summary in profiles/, when it was taken on the current kernel sources.
-Also: the same 2B chain as full layers (RMS norms and squared-ReLU gating fused
-into the launches), the 8B-shaped stack (32 layers) at M = 1 and M = 16, the
-100B-class decode stack (96 layers, 23.35 GB packed, fp32 activations), the
-prefill kernel's int8 TOPS on the 2B layer shapes at M = 512 and 4096 and on the
-8B shapes at M = 2048, the 2B and 100B chains with weights packed five per byte
-(T1 layout, 1.6 bits per weight), single matrices at M = 1 through the
-matrix-core kernel (2-bit and T1 weights) and the lookup-table path, the
-standalone weight and activation quantisers against HBM, and the CPU oracle
-timed on a bounded sample of the same decode workload (one core and all cores).
+Printed: one JSON line.  value = packed weight bytes per token / token time.
+roofline = the decode kernel (the only kernel in the step): achieved = packed
+bytes per launch / mean launch time, the graph replay time of the timed steps
+(HIP events on the stream the kernels run on) over the launches; traffic = HBM
+bytes per launch from the PMC summary in profiles/, when it was taken on the
+current kernel sources.  Also: the BitNet-2B-shaped decode stack (30 layers,
+bf16 activations; plain and with RMS norms and squared-ReLU gating fused), the
+8B-shaped stack at M = 1 and 16, the same 2B and 100B stacks through the
+one-launch decode chain and with weights packed five per byte (T1), the prefill
+kernel's int8 TOPS on the 2B shapes at M = 512 and 4096 and on the 8B shapes at
+M = 2048 (with its own roofline block), single matrices at M = 1 through the
+matrix-core kernel, T1 and the lookup-table path, the standalone quantisers
+against HBM, and the CPU oracle timed on bounded samples of the decode and
+prefill workloads (one core and all cores).
 """
 
 from __future__ import annotations
@@ -52,11 +50,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def recorded_traffic():
+def recorded_traffic(profile="gemv_100b_decode_stack.md"):
     """HBM bytes per decode launch from the committed PMC summary, or None when the
     decode kernel's sources differ from the ones the counters were taken on."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gemv_bitnet2b_decode_chain.md")
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     for line in open(path):
@@ -75,12 +73,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="bitnet2b-decode-m1-30L")
+    p.add_argument("--workload", default="ternary100b-decode-m1-96L")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--no-100b", action="store_true")
+    p.add_argument("--no-2b", action="store_true", help="skip the 2B-shaped decode stacks")
     p.add_argument("--no-extra", action="store_true",
-                   help="skip the full-layer 2B chain and the 8B-shaped chains")
+                   help="skip the full-layer 2B stack and the 8B-shaped stacks")
+    p.add_argument("--no-chain", action="store_true",
+                   help="skip the one-launch decode chain legs")
     p.add_argument("--no-t1", action="store_true",
                    help="skip the legs with weights packed five per byte")
     p.add_argument("--no-quant", action="store_true",
@@ -88,8 +88,6 @@ def parse():
     p.add_argument("--no-compare", action="store_true",
                    help="skip the single-matrix comparison of the decode kernels")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--chain-sweep", action="store_true",
-                   help="only time the decode chain at ring depths 4, 8, 16 (C5 and C2)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this size (PMC calibration)")
     return p.parse_args()
@@ -356,12 +354,21 @@ def prefill(torch, N, I, layer_shapes, ms, steps):
         sec = timed(run)
         nm, k, n = max(layer_shapes, key=lambda t: t[1] * t[2])
         ksec = timed(lambda: run(only=nm, reps=10)) / 10
-        res[str(m)] = {"tops": round(ops / sec / 1e12, 2),
-                       "frac_of_int8_peak": round(ops / sec / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+        tops = ops / sec / 1e12
+        res[str(m)] = {"tops": round(tops, 2),
+                       "frac_of_int8_peak": round(tops / INT8_MFMA_PEAK_TOPS, 4),
                        "layer_ms": round(sec * 1e3, 4),
                        "largest_matrix": f"{k}->{n}",
                        "largest_matrix_us": round(ksec * 1e6, 2),
-                       "largest_matrix_tops": round(2 * m * n * k / ksec / 1e12, 2)}
+                       "largest_matrix_tops": round(2 * m * n * k / ksec / 1e12, 2),
+                       "roofline": {"bound": "mfma", "achieved": round(tops, 1),
+                                    "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOPS (int8)",
+                                    "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "traffic": None,
+                                    "kernel": "gemm_kernel (prefill, int8 MFMA)",
+                                    "ops": "2 M N K per launch, zero weights counted (the "
+                                           "sum_pos - sum_neg form needs ~0.69 M N K add/subs)",
+                                    "launches_per_layer": 4,
+                                    "avg_launch_us": round(sec * 1e6 / 4, 2)}}
     return res
 
 
@@ -527,60 +534,122 @@ def _graph_time(torch, fn, steps):
     return us
 
 
-_ORACLE_LAYER = None   # (mats, x0) shared with forked workers
+_ORACLE = None   # the CPU sample's matrices and inputs, shared with forked workers
 
 
-def _oracle_layers(seconds):
-    """Whole 2B-shaped layers at M = 1 through the oracle for `seconds`:
-    (packed bytes streamed, layers, elapsed)."""
+def _random_packed(I, n, k, seed):
+    """Packed ternary codes [N, K/4] with the value distribution of absmean-quantised
+    N(0, sigma) weights: P(0) = 0.31, P(+1) = P(-1) = 0.345 (the CPU sample needs
+    only valid codes of that mix; generating and quantising fp32 masters of the
+    100B-class shapes on the host would take minutes)."""
     from oracle import bitnet_oracle as O
-    mats, x0 = _ORACLE_LAYER
-    per_layer = sum(p.nbytes for p, _ in mats.values())
-    layers_done = 0
+    import numpy as np
+    u = np.random.Generator(np.random.PCG64(seed)).random((n, k), dtype=np.float32)
+    q = (u > np.float32(0.655)).astype(np.int8) - (u < np.float32(0.345)).astype(np.int8)
+    return O.pack_codes(q)
+
+
+def _oracle_decode(seconds):
+    """100B-class layers at M = 1 through the oracle for `seconds`: act-quant +
+    unpack + integer contraction + rescale per matrix, with the stack's data flow
+    (q, k, v from h; o from q; gate, up from o; down from up; h <- down).
+    Returns (packed bytes streamed, matrices, elapsed)."""
+    from oracle import bitnet_oracle as O
+    mats, x0 = _ORACLE["decode"]
+    nbytes = done = 0
     t0 = time.perf_counter()
+    h = x0
+
+    def lin(nm, x):
+        nonlocal nbytes, done
+        p, g = mats[nm]
+        y = O.quant_linear(p, g, x)[3]
+        nbytes += p.nbytes
+        done += 1
+        return y
     while True:
-        h = x0
-        qv = O.quant_linear(*mats["q"], h)[3]
-        O.quant_linear(*mats["k"], h)
-        O.quant_linear(*mats["v"], h)
-        o = O.quant_linear(*mats["o"], qv)[3]
-        O.quant_linear(*mats["gate"], o)
-        u = O.quant_linear(*mats["up"], o)[3]
-        O.quant_linear(*mats["down"], u)
-        layers_done += 1
+        q = lin("qkv", h)
+        lin("qkv", h)
+        lin("qkv", h)
+        o = lin("o", q)
+        lin("gu", o)
+        up = lin("gu", o)
+        h = lin("down", up)
         el = time.perf_counter() - t0
         if el >= seconds:
-            return per_layer * layers_done, layers_done, el
+            return nbytes, done, el
 
 
-def cpu_baseline(I, layer_shapes, seconds, workers):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    whole 2B-shaped layers at M = 1 (act-quant + layer per matrix), on one core
-    and on `workers` processes at once (each runs its own layers; numpy's integer
-    contraction is single-threaded).  Runs before the GPU is touched, so the
-    worker processes are plain forks."""
-    global _ORACLE_LAYER
+def _oracle_prefill(seconds):
+    """The 2B-shaped layer's matrices at M tokens through the oracle's integer
+    contraction (plus act-quant and rescale) for `seconds`: (int8 ops, elapsed)."""
     from oracle import bitnet_oracle as O
-    mats = {}
-    for i, (nm, k, n) in enumerate(layer_shapes):
-        mats[nm] = O.quantize_weights(I.master_weights(n, k, I.weight_seed(0, i)))
-    _ORACLE_LAYER = (mats, I.activations(1, layer_shapes[0][1]))
-    per_layer = sum(p.nbytes for p, _ in mats.values())
-    nbytes, layers_done, el = _oracle_layers(seconds)
+    mats, xs = _ORACLE["prefill"]
+    ops = 0
+    t0 = time.perf_counter()
+    while True:
+        for p, g in mats:
+            x = xs[p.shape[1] * 4]
+            O.quant_linear(p, g, x)
+            ops += 2 * x.shape[0] * p.shape[0] * p.shape[1] * 4
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return ops, el
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(I, seconds, workers, prefill_m=64):
+    """The CPU oracle, as it stands, on bounded samples of the same workloads, on one
+    core and on `workers` processes at once (each runs its own sample; numpy's
+    integer contraction is single-threaded).  Decode: the 100B-class layer's three
+    matrix shapes at M = 1 in the stack's order, scaled to packed-weight GB/s.
+    Prefill: the 2B-shaped layer's matrices at `prefill_m` tokens (a slice of the
+    M = 512 batch), scaled to int8 TOPS (2 M N K).  Runs before the GPU is touched,
+    so the worker processes are plain forks."""
+    global _ORACLE
+    import numpy as np
+    from oracle import bitnet_oracle as O
+    shapes = {nm: (k, n) for nm, k, n in I.LAYER_100B}
+    dec = {"qkv": (_random_packed(I, 8192, 8192, 1), np.float32(0.0159)),
+           "o": (_random_packed(I, 8192, 8192, 2), np.float32(0.0159)),
+           "gu": (_random_packed(I, 28672, 8192, 3), np.float32(0.0159)),
+           "down": (_random_packed(I, 8192, 28672, 4), np.float32(0.0159))}
+    assert shapes["down"] == (28672, 8192) and shapes["gate"] == (8192, 28672)
+    pre = []
+    for i, (nm, k, n) in enumerate(I.LAYER_2B):
+        pre.append(O.quantize_weights(I.master_weights(n, k, I.weight_seed(0, i))))
+    xs = {k: I.activations(prefill_m, k) for k in {k for _, k, _ in I.LAYER_2B}}
+    _ORACLE = {"decode": (dec, I.activations(1, 8192)), "prefill": (pre, xs)}
+    nbytes, mats_done, el = _oracle_decode(seconds)
     res = {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"{layers_done} x one 2B-shaped layer (7 matrices, {per_layer} packed bytes) "
-                     f"at M=1, act-quant + unpack + int64 contraction + rescale, {el:.1f} s",
-           "host": platform.processor() or platform.machine(), "host_threads": os.cpu_count()}
+           "sample": f"{mats_done} matrices of the 100B-class layer (8192->8192, 8192->28672, "
+                     f"28672->8192 in the stack's order) at M=1, act-quant + unpack + int64 "
+                     f"contraction + rescale, {nbytes / 1e6:.0f} MB packed in {el:.1f} s",
+           "host_cpu": _cpu_model(), "host_threads": os.cpu_count()}
+    ops, el2 = _oracle_prefill(seconds)
+    res["prefill"] = {"value": round(ops / el2 / 1e12, 6), "unit": "TOPS", "cores": 1,
+                      "kind": "oracle",
+                      "sample": f"2B-shaped layer matrices at M={prefill_m} tokens, "
+                                f"{ops / 1e9:.1f} G int8 ops in {el2:.1f} s"}
     if workers > 1:
         import multiprocessing
         with multiprocessing.get_context("fork").Pool(workers) as pool:
-            parts = pool.map(_oracle_layers, [seconds] * workers)
+            parts = pool.map(_oracle_decode, [seconds] * workers)
         total = sum(b for b, _, _ in parts)
         wall = max(e for _, _, e in parts)
         res["all_cores"] = {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": workers,
-                            "sample": f"{sum(n for _, n, _ in parts)} layers over {workers} processes, "
-                                      f"{wall:.1f} s"}
-    _ORACLE_LAYER = None
+                            "sample": f"{sum(n for _, n, _ in parts)} matrices over {workers} "
+                                      f"processes, {wall:.1f} s"}
+    _ORACLE = None
     return res
 
 
@@ -601,15 +670,10 @@ def main():
     if not args.no_cpu_baseline:
         # before the GPU is initialised: the all-cores leg forks worker processes
         workers = min(16, os.cpu_count() or 1)
-        cpu = cpu_baseline(I, wl["layer"], args.cpu_seconds, workers)
+        cpu = cpu_baseline(I, args.cpu_seconds, workers)
         log(f"cpu baseline: {cpu}")
     torch.cuda.set_device(0)
     N.lib()
-    if args.chain_sweep:
-        for wname in ("ternary100b-decode-m1-96L", "bitnet2b-decode-m1-30L"):
-            for ring in (4, 8, 16):
-                chain_leg(torch, N, I, wname, args.steps, args.warmup, ring=ring)
-        return
     d = decode_leg(torch, N, I, args.workload, args.steps, args.warmup)
     avg_launch = d["ms"] * 1e-3 / d["launches"]
     avg_bytes = d["per_stack"] / d["launches"]
@@ -633,36 +697,50 @@ def main():
                    "launches_per_step": d["launches"], "graph": "hip"},
         "ms_per_step_p10_median_p90": [round(d["ms_p10"], 5), round(d["ms_median"], 5),
                                        round(d["ms_p90"], 5)],
+        "tokens_per_s": round(1e3 / d["ms"], 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(),
                      "kernel": "gemv_kernel (decode, fused int8 activation quantisation)",
                      "avg_launch_us": round(avg_launch * 1e6, 3),
                      "avg_bytes_per_launch": int(avg_bytes),
-                     "launch_time": "graph replay time / launches in the timed steps"},
+                     "launch_time": "graph replay time / launches in the timed steps (HIP "
+                                    "events on the kernels' stream)"},
     }
+    two_b = "bitnet2b-decode-m1-30L"
+    if not args.no_2b:
+        d2 = decode_leg(torch, N, I, two_b, args.steps, args.warmup)
+        result["decode_2b"] = dict(workload=two_b, **leg_summary(d2, 1),
+                                   traffic_per_launch=recorded_traffic(
+                                       "gemv_bitnet2b_decode_chain.md"))
     if not args.no_extra:
-        df = decode_leg(torch, N, I, args.workload, args.steps, args.warmup, full_layer=True)
-        result["decode_full_layer"] = dict(
-            workload=args.workload + " with RMS norms and squared-ReLU gating fused in",
-            **leg_summary(df, 1))
+        if not args.no_2b:
+            df = decode_leg(torch, N, I, two_b, args.steps, args.warmup, full_layer=True)
+            result["decode_2b_full_layer"] = dict(
+                workload=two_b + " with RMS norms and squared-ReLU gating fused in",
+                **leg_summary(df, 1))
         for m in (1, 16):
             d8 = decode_leg(torch, N, I, "llama8b-ternary", max(5, args.steps // 3), 2, m=m)
             result[f"decode_8b_m{m}"] = dict(workload="llama8b-ternary (32 layers)",
                                              **leg_summary(d8, m))
+    if not args.no_chain:
+        dc = chain_leg(torch, N, I, args.workload, max(5, args.steps // 5), 2)
+        result["decode_chain"] = dict(
+            workload=args.workload + ", one cooperative launch per token (decode chain)",
+            **leg_summary(dc, 1))
+        if not args.no_2b:
+            dc2 = chain_leg(torch, N, I, two_b, args.steps, args.warmup)
+            result["decode_2b_chain"] = dict(
+                workload=two_b + ", one cooperative launch per token (decode chain)",
+                **leg_summary(dc2, 1))
     if not args.no_t1:
-        dt = decode_leg(torch, N, I, args.workload, args.steps, args.warmup, fmt="t1")
+        dt = decode_leg(torch, N, I, args.workload, max(5, args.steps // 5), 2, fmt="t1")
         result["decode_t1"] = dict(workload=args.workload + ", weights five per byte (T1 layout)",
                                    **leg_summary(dt, 1))
-    if not args.no_100b:
-        d5 = decode_leg(torch, N, I, "ternary100b-decode-m1-96L", max(5, args.steps // 5), 2)
-        result["decode_100b"] = dict(workload="ternary100b-decode-m1-96L", **leg_summary(d5, 1))
-        if not args.no_t1:
-            d6 = decode_leg(torch, N, I, "ternary100b-decode-m1-96L", max(5, args.steps // 5), 2,
-                            fmt="t1")
-            result["decode_100b_t1"] = dict(
-                workload="ternary100b-decode-m1-96L, weights five per byte (T1 layout)",
-                **leg_summary(d6, 1))
+        if not args.no_2b:
+            dt2 = decode_leg(torch, N, I, two_b, args.steps, args.warmup, fmt="t1")
+            result["decode_2b_t1"] = dict(workload=two_b + ", weights five per byte (T1 layout)",
+                                          **leg_summary(dt2, 1))
     if not args.no_quant:
         result["quantisers"] = quantisers(torch, N, I, steps=3)
     if not args.no_compare:
@@ -671,7 +749,7 @@ def main():
             steps=4)
     if not args.no_prefill:
         result["mfma_ceiling"] = mfma_ceiling(torch)
-        result["prefill"] = prefill(torch, N, I, wl["layer"], (512, 4096), steps=10)
+        result["prefill"] = prefill(torch, N, I, I.LAYER_2B, (512, 4096), steps=10)
         result["prefill_8b"] = prefill(torch, N, I, I.LAYER_8B, (2048,), steps=5)
         log(f"prefill: {result['prefill']} {result['prefill_8b']}")
     if args.calib_copy_mib:
