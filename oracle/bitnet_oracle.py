@@ -291,8 +291,19 @@ def quantize_acts(x: np.ndarray):
 # ---------------------------------------------------------------------------
 
 def integer_matmul(q: np.ndarray, xq: np.ndarray) -> np.ndarray:
-    """acc[m, n] = sum_k q[n, k] * xq[m, k] in exact integers -> int32 [M, N]."""
-    acc = np.asarray(xq, dtype=np.int64) @ np.asarray(q, dtype=np.int64).T
+    """acc[m, n] = sum_k q[n, k] * xq[m, k] in exact integers -> int32 [M, N].
+
+    The product is taken by the float64 matrix product (a library routine): every
+    term q * xq is an integer of magnitude <= 128 and every partial sum an integer
+    of magnitude <= 128 K, so while 128 K < 2**53 each intermediate is an exactly
+    representable integer and the result is the exact sum in any summation order.
+    Beyond that bound (never reached by the layer's K), numpy's int64 product."""
+    q = np.asarray(q)
+    xq = np.asarray(xq)
+    if 128 * q.shape[1] < 2 ** 53:
+        acc = np.rint(xq.astype(np.float64) @ q.astype(np.float64).T).astype(np.int64)
+    else:
+        acc = xq.astype(np.int64) @ q.astype(np.int64).T
     if acc.size and np.abs(acc).max() >= 2 ** 31:
         raise OverflowError("accumulator leaves the int32 range")
     return acc.astype(np.int32)

@@ -493,6 +493,9 @@ class BitnetChain(ctypes.Structure):
                 ("ring", ctypes.c_int)]
 
 
+SIGNATURES["bitnet_prefill_tile"] = (_I, [_I64, ctypes.POINTER(_I64), _I,
+                                          ctypes.POINTER(_I), ctypes.POINTER(_I),
+                                          ctypes.POINTER(_I64)])
 SIGNATURES["bitnet_chain_plan_bytes"] = (_SZ, [_I])
 SIGNATURES["bitnet_chain_plan"] = (_I, [ctypes.POINTER(BitnetChainStage), _I, _I64, _P, _SZ,
                                         ctypes.POINTER(BitnetChain)])
@@ -553,3 +556,13 @@ def bitnet_chain_error(chain) -> int:
     _check("bitnet_chain_error", lib().bitnet_chain_error(ctypes.byref(chain.handle),
                                                           ctypes.byref(e)))
     return e.value
+
+
+def bitnet_prefill_tile(m, ns):
+    """(tokens per tile, rows per tile, first launch tokens) of the prefill kernel for
+    M tokens over matrices with ns rows (bitnet_prefill_tile)."""
+    arr = (ctypes.c_int64 * len(ns))(*ns)
+    bm, bn, first = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int64(0)
+    _check("bitnet_prefill_tile", lib().bitnet_prefill_tile(m, arr, len(ns), ctypes.byref(bm),
+                                                            ctypes.byref(bn), ctypes.byref(first)))
+    return bm.value, bn.value, first.value

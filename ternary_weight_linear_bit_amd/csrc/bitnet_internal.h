@@ -349,6 +349,15 @@ struct GemmArgs {
 };
 // Prefill kernel: K % 64 == 0, 16-byte aligned packed weights and activations.
 hipError_t launch_gemm(GemmArgs a, hipStream_t s);
+// The prefill launch's tile for M tokens over `count` matrices of n[j] rows on a
+// device with `cus` compute units: bm tokens x bn rows per workgroup; when
+// first_tokens > 0 the first first_tokens tokens run as one launch with this tile
+// and the rest as a second launch planned on its own.
+struct GemmPlan {
+  int bm, bn;
+  int64_t first_tokens;
+};
+GemmPlan gemm_plan(int64_t M, const int* n, int count, int cus);
 // Lookup-table decode: workspace bytes (tables 16 K + accumulators 4 N, each
 // rounded up to 256) and the launches (three per token).  K % 64 == 0, 16-byte
 // aligned packed weights and workspace.

@@ -317,8 +317,7 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 
 }  // namespace
 
-hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
-  if (a.K % 64 != 0 || a.count < 1 || a.count > kMaxGroup) return hipErrorInvalidValue;
+GemmPlan gemm_plan(int64_t M, const int* n, int count, int cus) {
   // Four tile shapes:
   //  * 256 tokens x 256 rows (8 waves of 128 x 64; one workgroup per compute
   //    unit, two waves per SIMD): a wave's weight expansion serves twice the
@@ -339,13 +338,13 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   //    deeper loads on the other shapes, measured no better).
   // Measured on the prefill shapes; 4 x 32-row blocks per wave measured slower
   // everywhere (registers: one wave per SIMD).
-  const int cus = device_cus();
+  GemmPlan p{128, 128, 0};
   auto row_tiles = [&](int bn) {
     int64_t t = 0;
-    for (int j = 0; j < a.count; ++j) t += (a.n[j] + bn - 1) / bn;
+    for (int j = 0; j < count; ++j) t += (n[j] + bn - 1) / bn;
     return t;
   };
-  const int64_t big_tiles = ((a.M + 255) / 256) * row_tiles(256);
+  const int64_t big_tiles = ((M + 255) / 256) * row_tiles(256);
   const int64_t big_rounds = (big_tiles + cus - 1) / cus;
   const bool big = big_tiles > 0 && 5 * big_tiles >= 4 * big_rounds * (int64_t)cus;
   // A last round of 256 x 256 tiles that fills under 40% of the compute units
@@ -354,27 +353,37 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   // with its own tile choice (4096 x 13824 x 2560: 224-227 -> 206-216 us).
   if (big && big_rounds > 1 && 5 * (big_tiles - (big_rounds - 1) * cus) < 2 * (int64_t)cus) {
     const int64_t m1 = (big_rounds - 1) * cus / row_tiles(256) * 256;   // tokens
-    if (m1 > 0 && m1 < a.M) {
-      GemmArgs rest = a;
-      rest.M = (int)(a.M - m1);
-      rest.xq = a.xq + m1 * a.K;
-      rest.xs = a.xs + m1;
-      const size_t es = a.y_bf16 ? 2 : 4;
-      for (int j = 0; j < a.count; ++j) {
-        rest.y[j] = static_cast<char*>(a.y[j]) + (size_t)m1 * a.n[j] * es;
-        if (a.acc[j]) rest.acc[j] = a.acc[j] + (size_t)m1 * a.n[j];
-      }
-      a.M = (int)m1;
-      const hipError_t e = launch_gemm(a, s);
-      return e != hipSuccess ? e : launch_gemm(rest, s);
-    }
+    if (m1 > 0 && m1 < M) p.first_tokens = m1;
   }
-  const int64_t mt = (a.M + 127) / 128;
+  const int64_t mt = (M + 127) / 128;
   const int64_t rows4 = row_tiles(256);
   const bool wide = !big && rows4 * mt <= cus && 10 * rows4 * mt >= 8 * (int64_t)cus;
   const bool small = !big && !wide && mt * row_tiles(128) <= cus;
-  const int bm = big ? 256 : small ? 64 : 128;
-  const int bn = big || wide ? 256 : 128;
+  p.bm = big ? 256 : small ? 64 : 128;
+  p.bn = big || wide ? 256 : 128;
+  return p;
+}
+
+hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
+  if (a.K % 64 != 0 || a.count < 1 || a.count > kMaxGroup) return hipErrorInvalidValue;
+  const GemmPlan pl = gemm_plan(a.M, a.n, a.count, device_cus());
+  if (pl.first_tokens > 0 && pl.first_tokens < a.M) {
+    const int64_t m1 = pl.first_tokens;
+    GemmArgs rest = a;
+    rest.M = (int)(a.M - m1);
+    rest.xq = a.xq + m1 * a.K;
+    rest.xs = a.xs + m1;
+    const size_t es = a.y_bf16 ? 2 : 4;
+    for (int j = 0; j < a.count; ++j) {
+      rest.y[j] = static_cast<char*>(a.y[j]) + (size_t)m1 * a.n[j] * es;
+      if (a.acc[j]) rest.acc[j] = a.acc[j] + (size_t)m1 * a.n[j];
+    }
+    a.M = (int)m1;
+    const hipError_t e = launch_gemm(a, s);
+    return e != hipSuccess ? e : launch_gemm(rest, s);
+  }
+  const int bm = pl.bm, bn = pl.bn;
+  const bool big = bm == 256, small = bm == 64, wide = bm == 128 && bn == 256;
   int64_t nbt = 0;
   for (int j = 0; j < kMaxGroup; ++j) {
     a.nb0[j] = (int)nbt;

@@ -1,0 +1,77 @@
+"""Prefill kernel at long K, every tile shape, every output compared.
+
+For each of the prefill kernel's tile shapes (256 x 256, 128 x 256, 128 x 128,
+64 x 128 tokens x rows) and for the split launch (the tokens that fill whole
+rounds of 256 x 256 tiles, then the rest with their own tile), one shape at
+K >= 2560 (at least 20 steps of 128 k, so the loads issued ahead run in their
+steady state), with the tile the library picks asserted on a 256-CU MI355X, and
+every int32 accumulator and fp32 output compared with the oracle.  The
+dashen-tech.com page "BitNet.cpp 深度解析", section 3.1, defines the contraction
+(sum over +1 weights minus sum over -1 weights).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bitnet_oracle as O
+from ternary_weight_linear_bit_amd import _native as N
+from ternary_weight_linear_bit_amd import inputs as I
+
+from gpu_helpers import DEV, acts, bf16_bits, dev, f32_bits, host
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (M, rows of each matrix, K, tile expected on 256 CUs, first launch tokens)
+    "256x256": (4096, (4096,), 2560, (256, 256), 0),
+    "128x256": (512, (6912, 6912), 2560, (128, 256), 0),
+    "128x128": (1536, (6912,), 2560, (128, 128), 0),
+    "64x128": (512, (2560,), 6912, (64, 128), 0),
+    "split": (4096, (6912, 6912), 2560, (256, 256), 3584),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    N.lib()
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_prefill_long_k_every_output(name):
+    m, ns, k, tile, first = CASES[name]
+    print(f"prefill long-K case {name}: M={m} N={ns} K={k}", flush=True)
+    bm, bn, f = N.bitnet_prefill_tile(m, ns)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert (bm, bn, f) == (*tile, first), (name, bm, bn, f)
+        if first:
+            # the rest of the tokens: a second launch with its own tile
+            assert N.bitnet_prefill_tile(m - first, ns) == (128, 256, 0)
+    xt, x = acts(m, k, 90 + m, "f32")
+    xq_t, xs_t = N.bitnet_quantize_acts(xt)
+    want_q, want_d = O.quantize_acts(x)
+    np.testing.assert_array_equal(host(xq_t), want_q)
+    mats, wants = [], []
+    for j, n in enumerate(ns):
+        w = I.master_weights(n, k, 7000 + 13 * j + m)
+        p, g = N.bitnet_quantize_weights(dev(w))
+        want_p, want_g = O.quantize_weights(w)
+        np.testing.assert_array_equal(host(p), want_p)
+        y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+        acc = torch.empty((m, n), dtype=torch.int32, device=DEV)
+        mats.append((p, g, y, acc))
+        wants.append((want_p, want_g))
+    N.bitnet_ternary_linear_multi(mats, xq_t, xs_t)
+    torch.cuda.synchronize()
+    for j, ((p, g, y, acc), (want_p, want_g)) in enumerate(zip(mats, wants)):
+        want_acc, want_y = O.ternary_linear(want_p, want_g, want_q, want_d)
+        np.testing.assert_array_equal(host(acc), want_acc, f"{name} matrix {j} acc")
+        np.testing.assert_array_equal(f32_bits(host(y)), f32_bits(want_y), f"{name} matrix {j} y")
+    if name == "split":
+        # bf16 outputs through the same two launches
+        p, g = mats[0][0], mats[0][1]
+        yb = N.bitnet_ternary_linear(p, g, xq_t, xs_t, y_dtype=torch.bfloat16)
+        _, want_y = O.ternary_linear(wants[0][0], wants[0][1], want_q, want_d)
+        np.testing.assert_array_equal(bf16_bits(yb), O.f32_to_bf16_bits(want_y))

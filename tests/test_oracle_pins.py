@@ -366,6 +366,25 @@ def test_matmul_equals_sum_pos_minus_sum_neg():
     np.testing.assert_array_equal(O.integer_matmul(-q, xq), -acc)
 
 
+def test_matmul_equals_int64_product_at_the_largest_k():
+    """The contraction against numpy's int64 product (a different library routine
+    and number type) at the largest K the linear calls accept, with the extreme
+    values: all +1 weights against all 127 (or -128) activations reach
+    |acc| = 128 K.  Catches a contraction that rounds once the sums grow."""
+    k = 131072
+    rng = np.random.Generator(np.random.PCG64(21))
+    q = rng.integers(-1, 2, (6, k)).astype(np.int8)
+    q[0] = 1
+    q[1] = -1
+    xq = rng.integers(-128, 128, (3, k)).astype(np.int8)
+    xq[0] = 127
+    xq[1] = -128
+    acc = O.integer_matmul(q, xq)
+    want = xq.astype(np.int64) @ q.astype(np.int64).T
+    np.testing.assert_array_equal(acc.astype(np.int64), want)
+    assert int(acc[0, 0]) == 127 * k and int(acc[1, 0]) == -128 * k and int(acc[1, 1]) == 128 * k
+
+
 def test_identity_weights_reproduce_activations():
     """W = I: gamma = RN32(1/K), every diagonal t ~ K >= 1.5 -> q = I, acc = xq."""
     k = 64
