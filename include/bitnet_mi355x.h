@@ -196,16 +196,17 @@ bitnet_status bitnet_quant_linear_multi(const bitnet_matrix *mats, int count, co
  *                x): x is then the gate projection and the layer input is
  *                v = RN32(RN32(max(x, 0)^2) * up), elementwise.
  *   norm_weight  NULL, or the RMS norm weight w [K] fp32 (device, 4-byte
- *                aligned): the layer input v is normalised, which the layer
- *                computes by quantising RN32(v * w) per token and multiplying
- *                the token scale by r = RN32(1 / sqrt(RN32(RN32(mean v^2) + eps)))
- *                (square root and division in float64; absmax quantisation is
- *                invariant under the positive per-token factor r).  mean v^2 is
- *                accumulated in float64 (exact products): it may differ from the
- *                exactly rounded mean by one fp32 ulp, so x_scale (and y) match
- *                the exact reading to within a few ulp; x_q is unaffected.
+ *                aligned): the layer input v is RMS-normalised and scaled,
+ *                u = RN32(RN32(v * r) * w) elementwise, with
+ *                r = RN32(1 / sqrt(RN32(ms + eps))) (square root and division in
+ *                float64) and ms = the exactly rounded mean of v^2 over the token
+ *                (one rounding of the exact sum / K, whatever the order of the
+ *                launch's sums); u is then quantised per token as above, so
+ *                x_scale is max|u| / 127.  Bit-exact against that definition.
  *                Needs K >= 1.
- *   norm_eps     eps >= 0, finite.
+ *   norm_eps     eps >= 0, finite.  With eps = 0 a token whose ms rounds to 0
+ *                (all zeros, or a mean below 2^-150) has r = +inf and its codes
+ *                and scale are undefined.
  */
 typedef struct bitnet_act_prologue {
   const void *up;
@@ -214,8 +215,8 @@ typedef struct bitnet_act_prologue {
 } bitnet_act_prologue;
 
 /*
- * bitnet_quantize_acts with the input prologue `pro` (NULL: none).  With
- * norm_weight, x_scale[m] includes the factor r.
+ * bitnet_quantize_acts with the input prologue `pro` (NULL: none): the codes
+ * and scales of the prologue's output u.
  */
 bitnet_status bitnet_quantize_acts_ex(const void *x, int x_dtype, const bitnet_act_prologue *pro,
                                       int64_t M, int64_t K, int8_t *x_q, float *x_scale,

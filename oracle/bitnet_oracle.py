@@ -48,13 +48,12 @@ terms anywhere):
 N1  squared-ReLU gating: u = RN32(RN32(max(g, 0) * max(g, 0)) * up), elementwise,
     where g and up are the gate and up projections of the same input.
 N2  sub-layer RMS normalisation (no bias) of the input v of a BitLinear layer:
-    RMSNorm(v)[k] = v[k] * w[k] * r with r = 1 / sqrt(mean_k v[k]^2 + eps).
+    RMSNorm(v)[k] = v[k] * r * w[k] with r = 1 / sqrt(mean_k v[k]^2 + eps).
     ms = RN32(exact sum_k v^2 / K); r = RN32(1 / sqrt(RN32(ms + eps))) with the
     square root and the division taken in float64.
-N3  normalise-then-quantise: r is a positive per-token factor and absmax
-    quantisation is invariant under such factors, so the layer quantises
-    v * w (fp32 products) with O4 and folds r into the token scale:
-    xq = O4(v * w).xq, d = RN32(O4(v * w).d * r).
+N3  normalise, then quantise: u[k] = RN32(RN32(v[k] * r) * w[k]) (the row scaled
+    by r, then by the norm weight, each product rounded to fp32), and u is the
+    layer's input: xq, d = O4(u).
 
 Lookup-table contraction ([JJ] juejin.cn, "微软 BitNet：让百亿参数大模型在 CPU
 上飞起来", technical principles, item 2 "查表法优化": bitnet.cpp's kernels use
@@ -388,34 +387,42 @@ def exact_square_sum_units(v: np.ndarray) -> int:
     return total
 
 
-def rms_factor(v: np.ndarray, eps: float) -> np.ndarray:
-    """N2: per row, r = RN32(1 / sqrt(RN32(RN32(exact sum v^2 / K) + eps)))."""
+def mean_of_squares(v: np.ndarray) -> np.ndarray:
+    """N2: per row, ms = RN32(exact sum v^2 / K) (one rounding of the exact mean)."""
     v = np.ascontiguousarray(v, dtype=np.float32)
     m_rows, k = v.shape
+    return np.array([rn32_ratio(exact_square_sum_units(v[m]), k << 298) for m in range(m_rows)],
+                    dtype=np.float32)
+
+
+def rms_factor(v: np.ndarray, eps: float) -> np.ndarray:
+    """N2: per row, r = RN32(1 / sqrt(RN32(ms + eps))), the root and division in float64."""
     eps32 = F32(eps)
-    out = np.empty(m_rows, dtype=np.float32)
-    for m in range(m_rows):
-        ms = rn32_ratio(exact_square_sum_units(v[m]), k << 298)
-        t = F32(ms + eps32)
-        out[m] = F32(1.0 / math.sqrt(float(t)))
-    return out
+    ms = mean_of_squares(v)
+    return np.array([F32(1.0 / math.sqrt(float(F32(m + eps32)))) for m in ms], dtype=np.float32)
+
+
+def rms_normalise(v: np.ndarray, norm_weight: np.ndarray, eps: float) -> np.ndarray:
+    """N2-N3: u = RN32(RN32(v * r) * w) per row, r = rms_factor(v, eps)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    r = rms_factor(v, eps)
+    n = (v * r[:, None]).astype(np.float32)
+    return (n * np.asarray(norm_weight, dtype=np.float32)[None, :]).astype(np.float32)
 
 
 def prologue_quantize_acts(x: np.ndarray, up=None, norm_weight=None, eps: float = 1e-5):
     """The layer input after its neighbours, quantised (N1-N3, then O4).
 
     x is the layer input, or the gate projection when ``up`` is given (N1);
-    with ``norm_weight`` the input is RMS-normalised first (N2), quantised as
-    v * w and rescaled by r (N3).  Returns (xq int8 [M, K], d fp32 [M]).
+    with ``norm_weight`` the input is RMS-normalised and scaled by the weight
+    (N2, N3) before the per-token quantisation.  Returns (xq int8 [M, K], d fp32 [M]).
     """
     v = np.ascontiguousarray(x, dtype=np.float32)
     if up is not None:
         v = relu2_glu(v, up)
-    if norm_weight is None:
-        return quantize_acts(v)
-    w = np.asarray(norm_weight, dtype=np.float32)
-    xq, d = quantize_acts((v * w[None, :]).astype(np.float32))
-    return xq, (d * rms_factor(v, eps)).astype(np.float32)
+    if norm_weight is not None:
+        v = rms_normalise(v, norm_weight, eps)
+    return quantize_acts(v)
 
 
 # ---------------------------------------------------------------------------

@@ -8,17 +8,18 @@
 // xq = clip(rne(RN32(x*s)), -128, 127), d = RN32(a*/127).
 // Prologue (same page, architecture item: ReLU^2 activation, subln norm, no
 // biases): with gating the input is v = RN32(RN32(relu(x)^2) * up); with a norm
-// weight w the row is quantised as RN32(v * w) and the token scale becomes
-// RN32(d * r), r = RN32(1/sqrt(RN32(RN32(mean v^2) + eps))) -- absmax
-// quantisation is invariant under the positive per-token factor r.
+// weight w the row is normalised first, u = RN32(RN32(v * r) * w) with
+// r = RN32(1/sqrt(RN32(ms + eps))) and ms = RN32(exact mean of v^2), and u is
+// what is quantised (its own absmax and token scale).
 //
-// One workgroup per token row.  Pass 1 reduces max|v*w| (exact in any order) and
-// sum v^2 (float64; the products are exact) with wave butterflies and a
-// cross-wave step in LDS; pass 2 writes 16 int8 per 16-byte store.  Each thread's
-// first H groups of 16 stay in registers between the passes, all loaded before
-// any is used; H (1, 2 or 4) covers the row when it can (K <= 16 H kAqThreads)
-// and no more, since the registers cost occupancy; groups past those are read
-// again in pass 2 (from L1/L2).
+// One workgroup per token row.  Pass 1 reduces max|v| (exact in any order) or,
+// with the norm, the float64 sum of v^2 (each square exact), from which the
+// exactly rounded mean follows (or, near a rounding boundary, from the exact
+// integer sum in LDS); with the norm, pass 2 forms u and reduces max|u|; the last
+// pass writes 16 int8 per 16-byte store.  Each thread's first H groups of 16 stay
+// in registers between the passes, all loaded before any is used; H (1, 2 or 4)
+// covers the row when it can (K <= 16 H kAqThreads) and no more, since the
+// registers cost occupancy; groups past those are read again (from L1/L2).
 #include "bitnet_internal.h"
 
 namespace bitnet {
@@ -32,44 +33,41 @@ __device__ __forceinline__ float load_act(const void* x, int64_t i) {
   return reinterpret_cast<const float*>(x)[i];
 }
 
-// 16 consecutive prologue values (the quantised ones, q) of group c; adds v^2
-// to ss when the norm is on.
+// 16 consecutive prologue inputs v of group c (the input, or the gated value).
 template <bool BF16>
-__device__ __forceinline__ void prologue16(const void* row, const void* urow, const float* w,
-                                           int64_t c, float q[16], double& ss) {
-  load16_act<BF16>(row, c, q);
+__device__ __forceinline__ void prologue16(const void* row, const void* urow, int64_t c,
+                                           float v[16]) {
+  load16_act<BF16>(row, c, v);
   if (urow) {
     float u[16];
     load16_act<BF16>(urow, c, u);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = glu_value(q[j], u[j]);
-  }
-  if (w) {
-    const float4* wp = reinterpret_cast<const float4*>(w) + 4 * c;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float4 g = wp[h];
-      const float gv[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = q[4 * h + j];
-        ss += (double)v * (double)v;
-        q[4 * h + j] = __fmul_rn(v, gv[j]);
-      }
-    }
+    for (int j = 0; j < 16; ++j) v[j] = glu_value(v[j], u[j]);
   }
 }
 
 template <bool BF16>
-__device__ __forceinline__ float prologue1(const void* row, const void* urow, const float* w,
-                                           int64_t i, double& ss) {
+__device__ __forceinline__ float prologue1(const void* row, const void* urow, int64_t i) {
   float v = load_act<BF16>(row, i);
   if (urow) v = glu_value(v, load_act<BF16>(urow, i));
-  if (w) {
-    ss += (double)v * (double)v;
-    v = __fmul_rn(v, w[i]);
-  }
   return v;
+}
+
+// The quantised values of group c with the norm applied: u = RN32(RN32(v r) w).
+__device__ __forceinline__ void normalise16(float v[16], const float* w, int64_t c, float r) {
+  const float4* wp = reinterpret_cast<const float4*>(w) + 4 * c;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float4 g = wp[h];
+    v[4 * h] = norm_value(v[4 * h], r, g.x);
+    v[4 * h + 1] = norm_value(v[4 * h + 1], r, g.y);
+    v[4 * h + 2] = norm_value(v[4 * h + 2], r, g.z);
+    v[4 * h + 3] = norm_value(v[4 * h + 3], r, g.w);
+  }
+}
+
+__device__ __forceinline__ uint4 quant16(const float v[16], float s) {
+  return make_uint4(quant4(v, s), quant4(v + 4, s), quant4(v + 8, s), quant4(v + 12, s));
 }
 
 template <bool BF16, int H>
@@ -79,52 +77,142 @@ __global__ __launch_bounds__(kAqThreads) void aq_kernel(const void* __restrict__
                                                        const ActPrologue pro) {
   __shared__ float wmax[kAqThreads / 64];
   __shared__ double wss[kAqThreads / 64];
+  __shared__ unsigned long long limbs[kSqLimbs];
+  __shared__ uint32_t sqwork[kSqWork];
+  __shared__ float sh_ms;
   const int64_t m = blockIdx.x;
   const size_t esz = BF16 ? 2 : 4;
   const void* row = reinterpret_cast<const uint8_t*>(x) + (size_t)m * K * esz;
   const void* urow = pro.up ? reinterpret_cast<const uint8_t*>(pro.up) + (size_t)m * K * esz
                             : nullptr;
+  const float* w = pro.w;
   int8_t* qrow = xq + m * K;
   const int tid = threadIdx.x;
   const int64_t n16 = vec ? K / 16 : 0;
+  auto reduce_max = [&](float a) -> float {
+    a = wave_max(a);
+    if ((tid & 63) == 0) wmax[tid >> 6] = a;
+    __syncthreads();
+    a = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kAqThreads / 64; ++i) a = fmaxf(a, wmax[i]);
+    __syncthreads();   // wmax is reused
+    return a;
+  };
 
-  float a = 0.0f;
-  double ss = 0.0;
-  // held groups: an index past the row reads its last group again (valid memory)
-  // and is dropped from the max, the sum and the stores
+  // Pass 1: the prologue inputs v (held groups stay in registers).  Held groups
+  // past the row read its last group again (valid memory) and are dropped.
   float hold[H][16];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     const int64_t c = tid + (int64_t)h * kAqThreads;
-    double s2 = 0.0;
-    if (n16 > 0) prologue16<BF16>(row, urow, pro.w, c < n16 ? c : n16 - 1, hold[h], s2);
-    if (c < n16) {
-      ss += s2;
+    if (n16 > 0) prologue16<BF16>(row, urow, c < n16 ? c : n16 - 1, hold[h]);
+  }
+  float a = 0.0f;
+  if (!w) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(hold[h][j]));
+    for (int h = 0; h < H; ++h)
+      if (tid + (int64_t)h * kAqThreads < n16)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(hold[h][j]));
+    for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
+      float v[16];
+      prologue16<BF16>(row, urow, c, v);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
     }
-  }
-  for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
-    float v[16];
-    prologue16<BF16>(row, urow, pro.w, c, v, ss);
+    for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads)
+      a = fmaxf(a, fabsf(prologue1<BF16>(row, urow, i)));
+    a = reduce_max(a);
+  } else {
+    // the mean of v^2: float64 sum, then the exactly rounded mean
+    double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
-  }
-  for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads)
-    a = fmaxf(a, fabsf(prologue1<BF16>(row, urow, pro.w, i, ss)));
-  a = wave_max(a);
-  ss = wave_sum_f64(ss);
-  if ((tid & 63) == 0) {
-    wmax[tid >> 6] = a;
-    wss[tid >> 6] = ss;
-  }
-  __syncthreads();
-  a = wmax[0];
-  ss = wss[0];
+    for (int h = 0; h < H; ++h)
+      if (tid + (int64_t)h * kAqThreads < n16)
 #pragma unroll
-  for (int w = 1; w < kAqThreads / 64; ++w) {
-    a = fmaxf(a, wmax[w]);
-    ss += wss[w];
+        for (int j = 0; j < 16; ++j) ss += (double)hold[h][j] * (double)hold[h][j];
+    for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
+      float v[16];
+      prologue16<BF16>(row, urow, c, v);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ss += (double)v[j] * (double)v[j];
+    }
+    for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads) {
+      const float v = prologue1<BF16>(row, urow, i);
+      ss += (double)v * (double)v;
+    }
+    ss = wave_sum_f64(ss);
+    if ((tid & 63) == 0) wss[tid >> 6] = ss;
+    __syncthreads();
+    ss = wss[0];
+#pragma unroll
+    for (int i = 1; i < kAqThreads / 64; ++i) ss += wss[i];
+    float ms;
+    if (!mean_sq_fast(ss, K, ms)) {
+      // near a rounding boundary: the exact sum of the squares (uniform branch:
+      // every thread holds the same ss)
+      if (tid < kSqLimbs) limbs[tid] = 0ull;
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        if (tid + (int64_t)h * kAqThreads < n16)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sq_limbs_add(limbs, hold[h][j]);
+      for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
+        float v[16];
+        prologue16<BF16>(row, urow, c, v);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sq_limbs_add(limbs, v[j]);
+      }
+      for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads)
+        sq_limbs_add(limbs, prologue1<BF16>(row, urow, i));
+      __syncthreads();
+      if (tid == 0) sh_ms = sq_limbs_mean(limbs, K, sqwork);
+      __syncthreads();
+      ms = sh_ms;
+    }
+    const float r = rms_factor_of_mean(ms, pro.eps);
+    // pass 2: u = RN32(RN32(v r) w) and its absmax
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const int64_t c = tid + (int64_t)h * kAqThreads;
+      if (c < n16) {
+        normalise16(hold[h], w, c, r);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(hold[h][j]));
+      }
+    }
+    for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
+      float v[16];
+      prologue16<BF16>(row, urow, c, v);
+      normalise16(v, w, c, r);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
+    }
+    for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads)
+      a = fmaxf(a, fabsf(norm_value(prologue1<BF16>(row, urow, i), r, w[i])));
+    a = reduce_max(a);
+    // quantise (below) sees u: recompute it for the groups that are read again
+    const float astar = fmaxf(a, kEps);
+    const float s = kQb / astar;   // correctly rounded fp32 division
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const int64_t c = tid + (int64_t)h * kAqThreads;
+      if (c < n16) reinterpret_cast<uint4*>(qrow)[c] = quant16(hold[h], s);
+    }
+    for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
+      float v[16];
+      prologue16<BF16>(row, urow, c, v);
+      normalise16(v, w, c, r);
+      reinterpret_cast<uint4*>(qrow)[c] = quant16(v, s);
+    }
+    for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads) {
+      const float q = rintf(norm_value(prologue1<BF16>(row, urow, i), r, w[i]) * s);
+      qrow[i] = (int8_t)(int32_t)fminf(fmaxf(q, -128.0f), 127.0f);
+    }
+    if (tid == 0) xs[m] = astar / kQb;
+    return;
   }
 
   const float astar = fmaxf(a, kEps);
@@ -132,36 +220,18 @@ __global__ __launch_bounds__(kAqThreads) void aq_kernel(const void* __restrict__
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     const int64_t c = tid + (int64_t)h * kAqThreads;
-    if (c < n16) {
-      uint4 o;
-      o.x = quant4(hold[h], s);
-      o.y = quant4(hold[h] + 4, s);
-      o.z = quant4(hold[h] + 8, s);
-      o.w = quant4(hold[h] + 12, s);
-      reinterpret_cast<uint4*>(qrow)[c] = o;
-    }
+    if (c < n16) reinterpret_cast<uint4*>(qrow)[c] = quant16(hold[h], s);
   }
   for (int64_t c = tid + (int64_t)H * kAqThreads; c < n16; c += kAqThreads) {
     float v[16];
-    double unused = 0.0;
-    prologue16<BF16>(row, urow, pro.w, c, v, unused);
-    uint4 o;
-    o.x = quant4(v, s);
-    o.y = quant4(v + 4, s);
-    o.z = quant4(v + 8, s);
-    o.w = quant4(v + 12, s);
-    reinterpret_cast<uint4*>(qrow)[c] = o;
+    prologue16<BF16>(row, urow, c, v);
+    reinterpret_cast<uint4*>(qrow)[c] = quant16(v, s);
   }
   for (int64_t i = n16 * 16 + tid; i < K; i += kAqThreads) {
-    double unused = 0.0;
-    float q = rintf(prologue1<BF16>(row, urow, pro.w, i, unused) * s);
+    const float q = rintf(prologue1<BF16>(row, urow, i) * s);
     qrow[i] = (int8_t)(int32_t)fminf(fmaxf(q, -128.0f), 127.0f);
   }
-  if (tid == 0) {
-    float d = astar / kQb;
-    if (pro.w) d = __fmul_rn(d, rms_factor(ss, K, pro.eps));
-    xs[m] = d;
-  }
+  if (tid == 0) xs[m] = astar / kQb;
 }
 
 }  // namespace

@@ -256,12 +256,108 @@ __device__ __forceinline__ float glu_value(float x, float up) {
   return __fmul_rn(__fmul_rn(a, a), up);
 }
 
-// RMS norm factor of a row from its float64 sum of squares ss over K values:
-// r = RN32(1 / sqrt(RN32(RN32(ss / K) + eps))), square root and division in float64.
-__device__ __forceinline__ float rms_factor(double ss, int64_t K, float eps) {
-  const float ms = (float)(ss / (double)K);
+// --- RMS norm: the exactly rounded mean of squares ---------------------------
+//
+// ms = RN32(exact sum_k v_k^2 / K) for finite fp32 v (the reading of the norm:
+// one rounding of the exact mean, so that it does not depend on the order in
+// which a launch sums).  Fast path: the float64 sum ss of the squares (each
+// square exact in float64), in any order, is within (K - 1) 2^-53 S of the exact
+// sum S; when both ends of the widened interval [ss/K (1 - g), ss/K (1 + g)],
+// g = (K + 4) 2^-52, round to the same fp32 value, that value is RN32(S / K)
+// (rounding is monotonic).  Otherwise (the mean lies within about K 2^-53 of a
+// rounding boundary: about one token in K^-1 2^28) the exact path below is
+// taken.
+__device__ __forceinline__ bool mean_sq_fast(double ss, int64_t K, float& ms) {
+  const double m = ss / (double)K;
+  const double g = (double)(K + 4) * 0x1p-52;
+  const float lo = (float)(m * (1.0 - g));
+  const float hi = (float)(m * (1.0 + g));
+  ms = lo;
+  return lo == hi;
+}
+
+// Exact path: S = sum v^2 as an integer count of 2^-298 units (v = m 2^(e-150)
+// for a normal v with biased exponent e and 24-bit significand m, m 2^-149 for a
+// sub-normal: v^2 = m^2 2^(P - 298), P = 2 (max(e, 1) - 1) in [0, 506]), kept in
+// kSqLimbs carry-save limbs of 32-bit digits in LDS (limb i weighs 2^(32 i)).
+// Every square adds three chunks of under 2^32 to three limbs, so a limb holds
+// the chunks of up to 2^31 squares without overflow.
+constexpr int kSqLimbs = 20;
+__device__ __forceinline__ void sq_limbs_add(unsigned long long* limbs, float v) {
+  const uint32_t b = __float_as_uint(v) & 0x7fffffffu;
+  if (b == 0u) return;
+  const uint32_t e = b >> 23;
+  const uint64_t m = e ? ((b & 0x7fffffu) | 0x800000u) : (b & 0x7fffffu);
+  const unsigned __int128 t = (unsigned __int128)(m * m) << ((2 * ((e ? e : 1u) - 1u)) & 31u);
+  const int L = (int)((2 * ((e ? e : 1u) - 1u)) >> 5);
+  atomicAdd(&limbs[L], (unsigned long long)(uint32_t)t);
+  atomicAdd(&limbs[L + 1], (unsigned long long)(uint32_t)(t >> 32));
+  atomicAdd(&limbs[L + 2], (unsigned long long)(t >> 64));
+}
+
+// RN32(S 2^-298 / K) from the limbs, by one thread, with kSqWork words of LDS as
+// work space (kept out of private memory: indexed arrays there would give the
+// kernel a scratch segment).  The limbs are normalised to 32-bit digits, shifted
+// up by 64 bits (so the quotient has at least 47 bits) and divided by K from the
+// top digit down; the quotient's leading 24 bits are rounded to nearest even with
+// the next bit and a sticky bit (lower quotient bits or a nonzero remainder).
+constexpr int kSqDigits = kSqLimbs + 2;   // digits of S * 2^64
+constexpr int kSqWork = 2 * kSqDigits;
+__device__ float sq_limbs_mean(const unsigned long long* limbs, int64_t K, uint32_t* work) {
+  uint32_t* d = work;                // S * 2^64, little-endian 32-bit digits
+  uint32_t* q = work + kSqDigits;    // the quotient
+  d[0] = 0u;
+  d[1] = 0u;
+  unsigned long long carry = 0;
+  for (int i = 0; i < kSqLimbs; ++i) {
+    const unsigned long long v = limbs[i] + carry;
+    d[i + 2] = (uint32_t)v;
+    carry = v >> 32;
+  }
+  unsigned long long rem = 0;
+  for (int i = kSqDigits - 1; i >= 0; --i) {
+    const unsigned long long cur = (rem << 32) | d[i];
+    q[i] = (uint32_t)(cur / (unsigned long long)K);
+    rem = cur % (unsigned long long)K;
+  }
+  int top = kSqDigits - 1;
+  while (top >= 0 && q[top] == 0u) --top;
+  if (top < 0) return 0.0f;          // S / K below 2^-362: rounds to +0
+  const int nq = 32 * top + (32 - __builtin_clz(q[top]));   // bits of the quotient
+  auto bit = [&](int i) -> uint32_t { return i < 0 ? 0u : (q[i >> 5] >> (i & 31)) & 1u; };
+  auto any_below = [&](int i) -> bool {   // any quotient bit below bit i
+    if (i <= 0) return false;
+    for (int w = 0; w < (i >> 5); ++w)
+      if (q[w]) return true;
+    return (i & 31) ? (q[i >> 5] & ((1u << (i & 31)) - 1u)) != 0u : false;
+  };
+  // value = q 2^-362 (+ a fraction below its last bit when rem != 0)
+  int e2 = nq - 1 - 362;            // exponent of the leading bit
+  const bool sub = e2 < -126;
+  const int shift = sub ? 362 - 149 : nq - 24;   // sub-normal: fixed spacing 2^-149
+  uint32_t sig = 0;
+  for (int i = 23; i >= 0; --i) sig = (sig << 1) | bit(shift + i);
+  const bool sticky = any_below(shift - 1) || rem != 0;
+  if (bit(shift - 1) && (sticky || (sig & 1u))) ++sig;
+  if (sub) return __uint_as_float(sig);   // sig <= 2^23: sub-normal or the least normal
+  if (sig == (1u << 24)) {
+    sig >>= 1;
+    ++e2;
+  }
+  if (e2 > 127) return __uint_as_float(0x7f800000u);
+  return __uint_as_float(((uint32_t)(e2 + 127) << 23) | (sig & 0x7fffffu));
+}
+
+// RMS norm factor from the exactly rounded mean of squares:
+// r = RN32(1 / sqrt(RN32(ms + eps))), square root and division in float64.
+__device__ __forceinline__ float rms_factor_of_mean(float ms, float eps) {
   const float t = __fadd_rn(ms, eps);
   return (float)(1.0 / sqrt((double)t));
+}
+
+// The value the layer quantises with a norm: RN32(RN32(v * r) * w).
+__device__ __forceinline__ float norm_value(float v, float r, float w) {
+  return __fmul_rn(__fmul_rn(v, r), w);
 }
 
 hipError_t launch_aq(const void* x, bool x_bf16, int64_t M, int64_t K, int8_t* x_q,

@@ -41,9 +41,9 @@
 // XMODE 3-8 add the layer's input prologue (communeify.com page on BitNet b1.58
 // 2B4T, architecture item: squared-ReLU activation, subln norm, no biases): the
 // input may be the gate projection, gated as RN32(RN32(relu(x)^2) * up), and / or
-// RMS-normalised, quantised as RN32(v * w) with the factor
-// r = RN32(1/sqrt(RN32(RN32(mean v^2) + eps))) folded into the token scale (the
-// sum of squares in float64 over the token's threads).
+// RMS-normalised as u = RN32(RN32(v r) w), r = RN32(1/sqrt(RN32(ms + eps))),
+// ms the exactly rounded mean of v^2 (float64 sum of squares over the token's
+// threads; near a rounding boundary an exact integer sum in LDS), and u quantised.
 //
 // FMT 1 reads weights packed five per byte (reading T1: the codes' base-3 value
 // v as the fixed-point fraction ceil(256 v / 243); byte i of a 16-byte block
@@ -477,78 +477,132 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
         store_batch();
       }
     } else {
-      // the values that are quantised, from the raw input (and up projection and
-      // norm weight) of one group; adds the squares of the gated values to ss
-      auto values = [&](const uint4* xw, const uint4* uw, const uint4* gw, float q[16],
-                        double& ss) {
+      // v: the values of one group before the norm (the raw input, or the gated
+      // one with the up projection)
+      auto values = [&](const uint4* xw, const uint4* uw, float q[16]) {
         raw_to_f32<BF>(xw, q);
-        if (PRO) {
-          if (glu) {
-            float u[16];
-            raw_to_f32<BF>(uw, u);
+        if (PRO && glu) {
+          float u[16];
+          raw_to_f32<BF>(uw, u);
 #pragma unroll
-            for (int j = 0; j < 16; ++j) q[j] = glu_value(q[j], u[j]);
-          }
-          if (nrm) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const uint4 g4 = gw[j >> 2];
-              const uint32_t gb = (j & 3) == 0 ? g4.x : (j & 3) == 1 ? g4.y : (j & 3) == 2 ? g4.z : g4.w;
-              ss += (double)q[j] * (double)q[j];
-              q[j] = __fmul_rn(q[j], __uint_as_float(gb));
-            }
-          }
+          for (int j = 0; j < 16; ++j) q[j] = glu_value(q[j], u[j]);
         }
       };
-      auto reload = [&](int c, float q[16], double& ss) {
-        uint4 xw[NV], uw[NV], gw[4];
+      // u = RN32(RN32(v r) w) with the norm weight w of the group
+      auto normalise = [&](const uint4* gw, float r, float q[16]) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint4 g4 = gw[j >> 2];
+          const uint32_t gb = (j & 3) == 0 ? g4.x : (j & 3) == 1 ? g4.y : (j & 3) == 2 ? g4.z : g4.w;
+          q[j] = norm_value(q[j], r, __uint_as_float(gb));
+        }
+      };
+      // group c read again: v, or with the norm (norm set) the normalised u
+      auto reload = [&](int c, float q[16], bool norm, float r) {
+        uint4 xw[NV], uw[NV];
 #pragma unroll
         for (int h = 0; h < NV; ++h) xw[h] = bload16(fr, foff(c, h));
-        if (PRO) {
+        if (PRO && glu) {
 #pragma unroll
-          for (int h = 0; h < NV; ++h) uw[h] = glu ? bload16(ur, foff(c, h)) : xw[h];
-#pragma unroll
-          for (int h = 0; h < 4; ++h) gw[h] = nrm ? bload16(gr, goff(c, h)) : make_uint4(0, 0, 0, 0);
+          for (int h = 0; h < NV; ++h) uw[h] = bload16(ur, foff(c, h));
         }
-        values(xw, uw, gw, q, ss);
-      };
-      // absmax of the token over its G threads (G >= 64: one token per wave); the
-      // held groups keep their values for the quantise pass
-      const int nb = (K16s + G - 1) >> lgG;      // groups per thread, uniform
-      float amax = 0.0f;
-      double ss = 0.0;
-      float qh[HOLD][16];
+        values(xw, uw, q);
+        if (nrm && norm) {
+          uint4 gw[4];
 #pragma unroll
-      for (int b = 0; b < HOLD; ++b) {
-        values(hold[b], holdu[b], holdg[b], qh[b], ss);
+          for (int h = 0; h < 4; ++h) gw[h] = bload16(gr, goff(c, h));
+          normalise(gw, r, q);
+        }
+      };
+      // the held groups keep their values for the quantise pass; G >= 64 (one
+      // token per wave or more)
+      const int nb = (K16s + G - 1) >> lgG;      // groups per thread, uniform
+      const int nw = G >> 6;                     // waves per token
+      float qh[HOLD][16];
+      float r = 1.0f;
+#pragma unroll
+      for (int b = 0; b < HOLD; ++b) values(hold[b], holdu[b], qh[b]);
+      if constexpr (nrm) {
+        // pass 1: the sum of the squares in float64 over the token's threads
+        double ss = 0.0;
+#pragma unroll
+        for (int b = 0; b < HOLD; ++b)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) ss += (double)qh[b][j] * (double)qh[b][j];
+        for (int b = HOLD; b < nb; ++b) {
+          float v[16];
+          reload(jg + G * b, v, false, 1.0f);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) ss += (double)v[j] * (double)v[j];
+        }
+        ss = wave_sum_f64(ss);
+        if (lane == 0) wss[wave] = ss;
+        lds_barrier();
+        // every thread rounds the mean of every token, so the choice of the
+        // exact path is uniform over the workgroup
+        float ms = 0.0f;
+        bool fast = true;
+        for (int t = 0; t < M; ++t) {
+          double st = 0.0;
+          for (int i = 0; i < nw; ++i) st += wss[(t * nw + i) & 3];
+          float mt;
+          fast = mean_sq_fast(st, K, mt) && fast;
+          if (t == tk) ms = mt;
+        }
+        if (!fast) {
+          // a mean near a rounding boundary: the exact sums of the squares of all
+          // tokens in carry-save limbs, in the partial tiles' LDS (cleared again
+          // afterwards; the stream below starts after two more barriers)
+          static_assert(4 * kSqLimbs * 8 + kSqWork * 4 <= 1024, "limbs fit one partial tile");
+          unsigned long long* limbs = reinterpret_cast<unsigned long long*>(part);  // [4][kSqLimbs]
+          uint32_t* sqwork = reinterpret_cast<uint32_t*>(limbs + 4 * kSqLimbs);
+          if (tid < 4 * kSqLimbs) limbs[tid] = 0ull;
+          lds_barrier();
+          if (tk < M) {
+#pragma unroll
+            for (int b = 0; b < HOLD; ++b)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) sq_limbs_add(limbs + tk * kSqLimbs, qh[b][j]);
+            for (int b = HOLD; b < nb; ++b) {
+              float v[16];
+              reload(jg + G * b, v, false, 1.0f);
+#pragma unroll
+              for (int j = 0; j < 16; ++j) sq_limbs_add(limbs + tk * kSqLimbs, v[j]);
+            }
+          }
+          lds_barrier();
+          if (tid == 0)
+            for (int t = 0; t < M; ++t) dsc[t] = sq_limbs_mean(limbs + t * kSqLimbs, K, sqwork);
+          lds_barrier();
+          if (tk < M) ms = dsc[tk];
+          for (int i = tid; i < T * 64; i += kThreads)
+            reinterpret_cast<uint4*>(part)[i] = make_uint4(0, 0, 0, 0);
+        }
+        r = rms_factor_of_mean(ms, a.eps);
+#pragma unroll
+        for (int b = 0; b < HOLD; ++b) normalise(holdg[b], r, qh[b]);
+      }
+      // absmax of the token (pass 2 with the norm)
+      float amax = 0.0f;
+#pragma unroll
+      for (int b = 0; b < HOLD; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(qh[b][j]));
-      }
       for (int b = HOLD; b < nb; ++b) {
         float v[16];
-        reload(jg + G * b, v, ss);
+        reload(jg + G * b, v, true, r);
 #pragma unroll
         for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
       }
       amax = wave_max(amax);
       if (lane == 0) wred[wave] = amax;
-      if (PRO) {
-        ss = wave_sum_f64(ss);
-        if (lane == 0) wss[wave] = ss;
-      }
       lds_barrier();
-      const int nw = G >> 6;                     // waves per token
       float tmax = 0.0f;
-      double tss = 0.0;
-      for (int i = 0; i < nw; ++i) {
-        tmax = fmaxf(tmax, wred[(tk * nw + i) & 3]);
-        if (PRO) tss += wss[(tk * nw + i) & 3];
-      }
+      for (int i = 0; i < nw; ++i) tmax = fmaxf(tmax, wred[(tk * nw + i) & 3]);
       const float astar = fmaxf(tmax, kEps);
       const float s_t = kQb / astar;
       if (jg == 0 && tk < M) {
-        float d = astar / kQb;
-        if (nrm) d = __fmul_rn(d, rms_factor(tss, K, a.eps));
+        const float d = astar / kQb;
         dsc[tk] = d;
         if (blockIdx.x == 0) a.xs_out[tk] = d;
       }
@@ -565,8 +619,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
       for (int b = 0; b < HOLD; ++b) put(jg + G * b, qh[b]);
       for (int b = HOLD; b < nb; ++b) {
         float v[16];
-        double unused = 0.0;
-        reload(jg + G * b, v, unused);
+        reload(jg + G * b, v, true, r);
         put(jg + G * b, v);
       }
     }

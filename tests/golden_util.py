@@ -25,3 +25,15 @@ def golden_arrays(ex):
 def hex_bits(rows, dtype=np.uint32):
     """Nested lists of hex strings -> an array of bit patterns."""
     return np.array([[int(h, 16) for h in r] for r in rows], dtype=dtype)
+
+
+def norm_example_arrays(ex):
+    """(v [1, K], w [K]) of a hand-worked norm example."""
+    k = ex["K"]
+    v = np.zeros((1, k), np.float32)
+    for i, val in ex["v_entries"]:
+        v[0, i] = val
+    w = np.full(k, ex["w_default"], np.float32)
+    for i, val in ex["w_entries"]:
+        w[i] = val
+    return v, w

@@ -1,10 +1,12 @@
 """The layer's input prologue (squared-ReLU gating, RMS norm) on the HIP path vs
 the oracle (readings N1-N3), through the C ABI.
 
-Bar: the int8 activations and the int32 accumulators are bit-exact.  The token
-scale with a norm carries the factor r, whose mean of squares the GPU sums in
-float64 (the oracle exactly): it is compared to 4e-7 relative (two fp32 ulps),
-and so are the fp32 outputs that use it; without a norm everything is bit-exact.
+Bar: bit-exact everywhere (int8 codes, token scales, int32 accumulators and
+the outputs).  With a norm the mean of squares is the exactly rounded one on
+both sides; the rows built below put it on a rounding midpoint, just above one,
+and at the extremes of the exponent range, so that the GPU's exact path (taken
+when its float64 sum cannot decide the rounding) is exercised and decides the
+codes.
 """
 
 import numpy as np
@@ -16,10 +18,10 @@ from ternary_weight_linear_bit_amd import _native as N
 from ternary_weight_linear_bit_amd import inputs as I
 
 from gpu_helpers import DEV, acts, dev, f32_bits, host
+from golden_util import norm_example_arrays
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-5
-SCALE_RTOL = 4e-7
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -36,11 +38,8 @@ def _inputs(m, k, seed, dt, glu, norm):
     return xt, x, ut, u, (dev(w) if norm else None), w
 
 
-def _check_scale(got, want, norm):
-    if norm:
-        assert np.all(np.abs(got / want - 1.0) <= SCALE_RTOL), (got, want)
-    else:
-        np.testing.assert_array_equal(f32_bits(got), f32_bits(want))
+def _check_scale(got, want, norm=True):
+    np.testing.assert_array_equal(f32_bits(got), f32_bits(want))
 
 
 @pytest.mark.parametrize("m,k,dt,glu,norm", [
@@ -78,11 +77,7 @@ def test_quant_linear_prologue(m, k, ns, dt, glu, norm):
     for (p, g), y, acc in zip(mats, ys, accs):
         acc_w, y_w = O.ternary_linear(p, g, want_q, want_d)
         np.testing.assert_array_equal(host(acc), acc_w)
-        got = host(y)
-        if norm:
-            np.testing.assert_allclose(got, y_w, rtol=2 * SCALE_RTOL, atol=0)
-        else:
-            np.testing.assert_array_equal(f32_bits(got), f32_bits(y_w))
+        np.testing.assert_array_equal(f32_bits(host(y)), f32_bits(y_w))
 
 
 def test_full_layer_chain():
@@ -90,7 +85,7 @@ def test_full_layer_chain():
     norm in front of q/k/v and of gate/up, the sub-layer norm in front of o, and
     squared-ReLU gating plus the sub-layer norm in front of down (o consumes q:
     attention is out of scope).  Activations stay fp32 between layers, so every
-    step is compared: int8 codes exactly, scales and outputs to 2 ulps."""
+    step is compared bit for bit."""
     k_model = 2560
     layers = []
     for l in range(2):
@@ -127,5 +122,104 @@ def test_full_layer_chain():
             _check_scale(host(xs_g), want_d, True)
             for nm in names:
                 _, y_w = O.ternary_linear(*mats[nm], want_q, want_d)
-                np.testing.assert_allclose(host(outs[nm]), y_w, rtol=2 * SCALE_RTOL, atol=0)
+                np.testing.assert_array_equal(f32_bits(host(outs[nm])), f32_bits(y_w))
         ref = host(hd)
+
+
+# --- rows whose mean of squares the float64 sum cannot round -----------------
+#
+# v0 = 1 + t 2^-12 (t odd, t < 2^11) and v2 = 1/4 in a row of K = 2^j inputs,
+# the rest 0: v0^2 + v2^2 = 1 + 2^-4 + t 2^-11 + t^2 2^-24 needs one bit more
+# than fp32 holds in [1, 2), so the exact mean lies on a rounding midpoint (ties
+# to even).  (v2 keeps the largest normalised value away from sqrt(K), which it
+# would equal, whatever the rounding of r, for a single non-zero input.)  Adding
+# v1 = 2^-40 puts the exact mean 2^-80 / K above the midpoint, which a float64
+# sum loses.  Scaled by 2^60 the mean stays a midpoint near 2^114; scaled by
+# 2^-66 it is sub-normal (below 2^-132 / K).
+
+def _row(k, pos, t, kind):
+    v = np.zeros(k, np.float32)
+    v[pos] = np.float32(1 + t * 2.0 ** -12)
+    v[(pos + 2) % k] = np.float32(0.25)
+    if kind == "above":
+        v[(pos + 1) % k] = np.float32(2.0 ** -40)
+    elif kind == "big":
+        v *= np.float32(2.0 ** 60)
+    elif kind == "tiny":
+        v *= np.float32(2.0 ** -66)
+    return v
+
+
+def _sensitive_t(k, pos):
+    """An odd t whose midpoint row and just-above row get different token scales
+    from the oracle (eps = 0): the exact rounding of the mean decides the output."""
+    for t in range(1, 2048, 2):
+        rows = np.stack([_row(k, pos, t, "mid"), _row(k, pos, t, "above")])
+        _, d = O.prologue_quantize_acts(rows, norm_weight=np.ones(k, np.float32), eps=0.0)
+        if d[0] != d[1]:
+            return t
+    raise AssertionError("no sensitive t")
+
+
+def _exact_path_inputs(m, k, pos, kinds, seed):
+    t = _sensitive_t(k, pos)
+    rows = [_row(k, pos, t, kinds[i % len(kinds)]) for i in range(m)]
+    v = np.stack(rows).astype(np.float32)
+    w = np.ones(k, np.float32)
+    w[pos] = np.float32(1.25)   # the norm weight scales the surviving value
+    return v, w
+
+
+@pytest.mark.parametrize("m,k,pos,kinds,glu", [
+    (4, 64, 5, ("mid", "above", "big", "tiny"), False),
+    (4, 64, 63, ("above", "mid", "tiny", "big"), True),
+    (1, 32768, 30001, ("mid",), False),
+    (1, 32768, 30001, ("above",), True),
+    (1, 32768, 7, ("tiny",), False),
+    (2, 8192, 8000, ("above", "big"), False),
+    (3, 4096, 1000, ("big", "above", "mid"), True),
+    (6, 64, 0, ("mid", "above", "big", "tiny"), False),
+    (5, 32768, 30001, ("above", "mid", "tiny"), False)])
+def test_norm_exact_mean_path(m, k, pos, kinds, glu):
+    """Codes, scales and outputs bit-exact on rows whose mean of squares needs the
+    exact path: through the standalone quantisation, and fused into the decode
+    kernel (M <= 4) or the separate quantisation in front of the decode (M > 4).
+    With gating the gate is 1 and the up projection carries the row, so the gated
+    input is the row itself."""
+    v, w = _exact_path_inputs(m, k, pos, kinds, 700 + m + k)
+    x, u = (np.ones_like(v), v) if glu else (v, None)
+    want_q, want_d = O.prologue_quantize_acts(x, up=u, norm_weight=w, eps=0.0)
+    xt, ut, wt = dev(x), (dev(u) if glu else None), dev(w)
+    xq, xs = N.bitnet_quantize_acts(xt, up=ut, norm_weight=wt, eps=0.0)
+    np.testing.assert_array_equal(host(xq), want_q)
+    _check_scale(host(xs), want_d)
+    p, g = O.quantize_weights(I.master_weights(48, k, 710 + m))
+    acc = torch.empty((m, 48), dtype=torch.int32, device=DEV)
+    (y,), xq2, xs2 = N.bitnet_quant_linear_multi([(dev(p), dev(np.array([g], np.float32)), None, acc)],
+                                                 xt, up=ut, norm_weight=wt, eps=0.0)
+    np.testing.assert_array_equal(host(xq2), want_q)
+    _check_scale(host(xs2), want_d)
+    acc_w, y_w = O.ternary_linear(p, g, want_q, want_d)
+    np.testing.assert_array_equal(host(acc), acc_w)
+    np.testing.assert_array_equal(f32_bits(host(y)), f32_bits(y_w))
+
+
+def test_norm_golden_example_on_gpu(golden):
+    """The hand-worked normalise-then-quantise example: codes and token scale equal
+    the values worked out by hand, on the standalone and the fused path."""
+    for ex in golden["norm_examples"]:
+        v, w = norm_example_arrays(ex)
+        want = np.zeros((1, ex["K"]), np.int8)
+        for i, q in ex["xq_entries"]:
+            want[0, i] = q
+        xt, wt = dev(v), dev(w)
+        xq, xs = N.bitnet_quantize_acts(xt, norm_weight=wt, eps=ex["eps"])
+        np.testing.assert_array_equal(host(xq), want)
+        assert f32_bits(host(xs))[0] == int(ex["d_bits"], 16)
+        p, g = O.quantize_weights(I.master_weights(32, ex["K"], 720))
+        acc = torch.empty((1, 32), dtype=torch.int32, device=DEV)
+        _, xq2, xs2 = N.bitnet_quant_linear_multi([(dev(p), dev(np.array([g], np.float32)), None, acc)],
+                                                  xt, norm_weight=wt, eps=ex["eps"])
+        np.testing.assert_array_equal(host(xq2), want)
+        assert f32_bits(host(xs2))[0] == int(ex["d_bits"], 16)
+        np.testing.assert_array_equal(host(acc), O.ternary_linear(p, g, want, host(xs2))[0])

@@ -44,6 +44,21 @@ def _ternarize_reciprocal(w, gamma):
     return np.clip(np.rint(t), -1.0, 1.0).astype(np.int8)
 
 
+def _prologue_fused_order(x, up=None, norm_weight=None, eps=1e-5):
+    v = np.asarray(x, np.float32)
+    if up is not None:
+        v = O.relu2_glu(v, up)
+    if norm_weight is None:
+        return O.quantize_acts(v)
+    xq, d = O.quantize_acts((v * np.asarray(norm_weight, np.float32)[None, :]).astype(np.float32))
+    return xq, (d * O.rms_factor(v, eps)).astype(np.float32)
+
+
+def _rms_normalise_one_rounding(v, w, eps):
+    r = O.rms_factor(v, eps).astype(np.float64)
+    return (np.asarray(v, np.float64) * r[:, None] * np.asarray(w, np.float64)[None, :]).astype(np.float32)
+
+
 ORIG_ACTS = O.quantize_acts
 
 MUTATIONS = {
@@ -53,6 +68,20 @@ MUTATIONS = {
     "rescale RN32(RN32(acc d) gamma)": ("dequantize", _dequant_acc_d_first),
     "ternarise with a rounded reciprocal": ("ternarize", _ternarize_reciprocal),
 }
+
+
+NORM_MUTATIONS = {
+    "norm: quantise v w and fold r into the scale": ("prologue_quantize_acts", _prologue_fused_order),
+    "norm: v r w rounded once": ("rms_normalise", _rms_normalise_one_rounding),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NORM_MUTATIONS))
+def test_norm_golden_example_rejects_mutation(name, golden, monkeypatch):
+    attr, fn = NORM_MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    with pytest.raises(AssertionError):
+        P.test_norm_golden_example(golden)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))

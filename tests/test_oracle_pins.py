@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import bitnet_oracle as O
-from golden_util import golden_arrays
+from golden_util import golden_arrays, norm_example_arrays
 
 F32 = np.float32
 
@@ -519,20 +519,77 @@ def test_rms_factor_power_of_two_scaling_and_float64():
     assert np.all(np.abs(r / ref - 1.0) < 3e-7)
 
 
-def test_prologue_quantize_matches_normalise_then_quantise():
-    """N3 against the textbook order (normalise in float64, then O4 in float64):
-    the int8 codes agree except where a product lands within rounding of a
-    half-integer, the token scale to float rounding."""
-    rng = np.random.default_rng(14)
-    x = rng.standard_normal((8, 2560)).astype(np.float32)
-    w = (1.0 + 0.1 * rng.standard_normal(2560)).astype(np.float32)
-    xq, d = O.prologue_quantize_acts(x, norm_weight=w, eps=1e-5)
-    x64 = x.astype(np.float64)
-    y = x64 / np.sqrt((x64 ** 2).mean(axis=1, keepdims=True) + 1e-5) * w.astype(np.float64)
-    a = np.abs(y).max(axis=1)
-    q64 = np.clip(np.rint(y * (127.0 / a)[:, None]), -128, 127)
-    assert np.mean(xq == q64) > 0.999
-    assert np.all(np.abs(d / (a / 127.0) - 1.0) < 1e-6)
+def test_norm_golden_example(golden):
+    """Hand-worked normalise-then-quantise example (tests/golden/worked_examples.json,
+    norm_examples): the exact mean of squares, r, the normalised and scaled values,
+    and the codes and token scale.  Catches the fused order (quantising v * w and
+    folding r into the token scale: another code and scale here), a rounding of
+    v * w * r in one step, and a mean of squares summed in fp32."""
+    for ex in golden["norm_examples"]:
+        v, w = norm_example_arrays(ex)
+        r = O.rms_factor(v, ex["eps"])
+        assert r.view(np.uint32)[0] == int(ex["r_bits"], 16)
+        u = O.rms_normalise(v, w, ex["eps"])
+        np.testing.assert_array_equal(u[0, :4].view(np.uint32), [int(h, 16) for h in ex["u_bits"]])
+        assert not np.any(u[0, 4:])
+        xq, d = O.prologue_quantize_acts(v, norm_weight=w, eps=ex["eps"])
+        want = np.zeros(ex["K"], np.int8)
+        for i, q in ex["xq_entries"]:
+            want[i] = q
+        np.testing.assert_array_equal(xq[0], want)
+        assert d.view(np.uint32)[0] == int(ex["d_bits"], 16)
+        assert int(xq[0, 0]) != ex["fused_order_xq0"]
+
+
+def test_norm_mean_of_squares_at_a_rounding_midpoint():
+    """A row whose exact mean of squares lies exactly halfway between two fp32
+    values: v0 = 1 + 2^-12, the other 63 inputs 0, so the mean is
+    (1 + 2^-11 + 2^-24) / 64 = 2^-6 + 2^-17 + 2^-30, halfway between
+    2^-6 + 2^-17 and the next fp32 (spacing 2^-29); ties go to the even
+    significand 2^23 + 2^12, i.e. 2^-6 + 2^-17 (0x3c801000).  Catches a mean
+    rounded half away from zero or rounded twice."""
+    v = np.zeros((1, 64), np.float32)
+    v[0, 0] = np.float32(1 + 2.0 ** -12)
+    assert O.mean_of_squares(v).view(np.uint32)[0] == 0x3C801000
+    # scaled by 2^60 the mean is 2^120 times as large: the same significand
+    big = (v * np.float32(2.0 ** 60)).astype(np.float32)
+    assert O.mean_of_squares(big).view(np.uint32)[0] == 0x3C801000 + (120 << 23)
+    # scaled by 2^-70 the mean 2^-146 + 2^-157 + 2^-170 is sub-normal: 2^-149
+    # spacing, 8 + 2^-8 + 2^-21 units, rounds to 8 units (bits 0x00000008)
+    tiny = (v * np.float32(2.0 ** -70)).astype(np.float32)
+    assert O.mean_of_squares(tiny).view(np.uint32)[0] == 8
+
+
+def test_norm_mean_of_squares_just_above_a_midpoint():
+    """The midpoint row above plus v1 = 2^-40: the exact mean exceeds the midpoint
+    by 2^-86 and rounds up to 0x3c801001, while a float64 sum of the squares loses
+    v1^2 = 2^-80 (below half an ulp of 1) and lands on the midpoint itself, which
+    rounds to even (0x3c801000).  Catches a sum of squares that is not exact and a
+    dropped sticky bit."""
+    v = np.zeros((1, 64), np.float32)
+    v[0, 0] = np.float32(1 + 2.0 ** -12)
+    v[0, 1] = np.float32(2.0 ** -40)
+    assert O.mean_of_squares(v).view(np.uint32)[0] == 0x3C801001
+    ss = np.float64(v[0, 0]) ** 2 + np.float64(v[0, 1]) ** 2
+    assert np.float32(ss / 64).view(np.uint32) == 0x3C801000
+
+
+def test_norm_closed_forms():
+    """A constant row c = 2^j (eps = 0): ms = 4^j, r = 2^-j exactly, every
+    normalised value is +-1 and u is the norm weight itself, so the codes and
+    scale are O4 of w, whatever j.  A zero row: u = 0, codes 0, the floor scale."""
+    rng = np.random.default_rng(16)
+    w = (1.0 + 0.3 * rng.standard_normal(256)).astype(np.float32)
+    want_q, want_d = O.quantize_acts(w[None, :])
+    for j in (-9, 0, 5):
+        for sign in (1.0, -1.0):
+            v = np.full((1, 256), sign * 2.0 ** j, np.float32)
+            xq, d = O.prologue_quantize_acts(v, norm_weight=w, eps=0.0)
+            np.testing.assert_array_equal(xq, (want_q * np.int8(sign)).astype(np.int8))
+            np.testing.assert_array_equal(d, want_d)
+    xq0, d0 = O.prologue_quantize_acts(np.zeros((2, 256), np.float32), norm_weight=w, eps=1e-5)
+    assert not np.any(xq0)
+    assert np.all(d0 == np.float32(O.EPS / O.QB))
 
 
 def test_prologue_quantize_invariants():
@@ -548,13 +605,12 @@ def test_prologue_quantize_invariants():
                                            norm_weight=w, eps=0.0)
         np.testing.assert_array_equal(xq2, xq)
         np.testing.assert_array_equal(d2, d)
-    # a gate that is negative everywhere zeroes the row: codes 0, and the scale
-    # is the zero-row act-quant scale times 1/sqrt(eps)
+    # a gate that is negative everywhere zeroes the row: codes 0 and the floor
+    # scale (the normalised row is 0)
     gz = -np.abs(g)
     xq0, d0 = O.prologue_quantize_acts(gz, up=up, norm_weight=w, eps=1e-5)
     assert not np.any(xq0)
-    base = np.float32(O.EPS / O.QB)
-    assert np.all(d0 == np.float32(base * np.float32(1.0 / math.sqrt(float(np.float32(1e-5))))))
+    assert np.all(d0 == np.float32(O.EPS / O.QB))
     # without a norm the prologue is plain O4 of the gated input
     xq1, d1 = O.prologue_quantize_acts(g, up=up)
     xq2, d2 = O.quantize_acts(O.relu2_glu(g, up))
