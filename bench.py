@@ -514,6 +514,92 @@ def mfma_ceiling(torch):
     return res
 
 
+def _probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "ternary_weight_linear_bit_amd", "libbitnet_bench_probe.so"))
+    lib.bitnet_bench_probe_read.restype = ctypes.c_int
+    lib.bitnet_bench_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+    lib.bitnet_bench_probe_empty.restype = ctypes.c_int
+    lib.bitnet_bench_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+def hbm_read_ceiling(torch, gib=4, launches=5):
+    """HBM read rate of this chip (bench-only probe library), the context for the
+    decode kernel's roofline: a 4 GiB buffer (larger than the 256 MB Infinity
+    Cache) read once per launch, streamed with 16-byte loads (1 KiB per wave
+    load) at 1, 2 and 8 workgroups per CU, and in the decode kernel's pattern
+    (16 rows x 64 bytes per wave load over 8192-weight rows) at 2 and 3 per CU.
+    The roofline peak stays the published 8 TB/s."""
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = gib << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    res = {"bytes_per_launch": nbytes}
+    for name, pattern, rowb, per_cu in (("stream_16B_loads", 0, 0, (1, 2, 8)),
+                                        ("decode_pattern_rows_2048B", 1, 2048, (2, 3))):
+        res[name] = {}
+        for k in per_cu:
+            wgs = k * cus
+            out = torch.empty(wgs * 4096, dtype=torch.uint8, device="cuda")
+
+            def run():
+                if lib.bitnet_bench_probe_read(buf.data_ptr(), nbytes, pattern, rowb, wgs,
+                                               out.data_ptr(), stream) != 0:
+                    raise RuntimeError("read probe launch failed")
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(launches):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name][f"gbs_{wgs}_workgroups"] = round(
+                launches * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+            del out
+    best = max(v for name in ("stream_16B_loads", "decode_pattern_rows_2048B")
+               for v in res[name].values())
+    res["best_gbs"] = best
+    res["best_frac_of_hbm_peak"] = round(best / HBM_PEAK_GBS, 4)
+    del buf
+    log(f"hbm read ceiling: {res}")
+    return res
+
+
+def launch_gap(torch, launches=400):
+    """Cost of a dependent launch: an empty kernel replayed from a HIP graph
+    (one workgroup, and two workgroups per CU like the decode kernel)."""
+    lib = _probe_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {}
+    for wgs in (1, 2 * cus):
+        def run():
+            for _ in range(launches):
+                if lib.bitnet_bench_probe_empty(wgs, torch.cuda.current_stream().cuda_stream) != 0:
+                    raise RuntimeError("empty probe launch failed")
+        run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"us_per_empty_launch_{wgs}_workgroups"] = round(e0.elapsed_time(e1) * 1e3 / (5 * launches), 3)
+        del g
+    log(f"launch gap: {res}")
+    return res
+
+
 def _graph_time(torch, fn, steps):
     """Mean microseconds of one replay of fn captured in a HIP graph."""
     fn()
@@ -744,6 +830,8 @@ def main():
     if not args.no_quant:
         result["quantisers"] = quantisers(torch, N, I, steps=3)
     if not args.no_compare:
+        result["hbm_read_ceiling"] = hbm_read_ceiling(torch)
+        result["launch_gap"] = launch_gap(torch)
         result["kernel_compare_m1"] = kernel_compare(
             torch, N, I, ((2560, 2560), (2560, 6912), (6912, 2560), (8192, 28672), (28672, 8192)),
             steps=4)

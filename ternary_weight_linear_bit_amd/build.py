@@ -20,8 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitnet_mi355x.so")
 SOURCES = ("api.hip", "wq.hip", "aq.hip", "gemv.hip", "gemm.hip", "lut.hip", "chain.hip")
-# bench-only diagnostic (int8 matrix-core rate), its own library: not part of the ABI
-PROBE_SRC = os.path.join(PKG, "bench_probe", "mfma_probe.hip")
+# bench-only diagnostics (int8 matrix-core rate, HBM read rates, launch cost), their
+# own library: not part of the ABI
+PROBE_SRCS = [os.path.join(PKG, "bench_probe", f) for f in ("mfma_probe.hip", "hbm_probe.hip")]
 PROBE_LIB = os.path.join(PKG, "libbitnet_bench_probe.so")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -64,7 +65,7 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp"
-    _run([HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp])
+    _run([HIPCC, *FLAGS, "-shared", *PROBE_SRCS, "-o", tmp])
     os.replace(tmp, PROBE_LIB)
     return LIB
 
