@@ -473,12 +473,15 @@ def mfma_ceiling(torch):
     SIMD, ten launches of ~2 ms per operand kind, before the prefill legs):
     all-zero operands (the issue rate: no data switching), all-ones, and random
     int8 activations against random ternary codes {0, 1, 2} (the prefill kernel's
-    operands).  Context only: the roofline peak stays the published 5.0 POPS."""
+    operands); with the shader clock the probe's waves saw under that load and
+    the rate per clock and SIMD (2048 int8 ops is the matrix core's full rate).
+    Context only: the roofline peak stays the published 5.0 POPS."""
     import ctypes
     path = os.path.join(ROOT, "ternary_weight_linear_bit_amd", "libbitnet_bench_probe.so")
     probe = ctypes.CDLL(path).bitnet_bench_probe_mfma_i8
     probe.restype = ctypes.c_int
-    probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs, iters, launches = 2 * cus, 2000, 10
@@ -493,9 +496,10 @@ def mfma_ceiling(torch):
             ops[:, 8:] = torch.randint(0, 3, (wgs * 256, 8, 16), generator=g, device="cuda",
                                        dtype=torch.uint8)
         out = torch.empty((wgs * 256, 64), dtype=torch.uint8, device="cuda")
+        clk = torch.zeros((wgs * 4, 2), dtype=torch.int64, device="cuda")
 
         def run():
-            if probe(ops.data_ptr(), wgs, iters, out.data_ptr(), stream) != 0:
+            if probe(ops.data_ptr(), wgs, iters, out.data_ptr(), clk.data_ptr(), stream) != 0:
                 raise RuntimeError("matrix-core probe launch failed")
         run()
         torch.cuda.synchronize()
@@ -506,8 +510,14 @@ def mfma_ceiling(torch):
         e1.record()
         torch.cuda.synchronize()
         sec = e0.elapsed_time(e1) * 1e-3
-        res[f"{kind}_tops"] = round(launches * wgs * 4 * iters * 32 * 65536 / sec / 1e12, 1)
-        del ops, out
+        tops = launches * wgs * 4 * iters * 32 * 65536 / sec / 1e12
+        c = clk.double()
+        ghz = float((c[:, 0] / c[:, 1]).median()) * 0.1
+        simds = 4 * cus
+        res[f"{kind}_tops"] = round(tops, 1)
+        res[f"{kind}_clock_ghz"] = round(ghz, 3)
+        res[f"{kind}_ops_per_clock_per_simd"] = round(tops * 1e12 / (ghz * 1e9) / simds, 1)
+        del ops, out, clk
     res["frac_of_peak"] = {k: round(v / INT8_MFMA_PEAK_TOPS, 4) for k, v in res.items()
                            if k.endswith("_tops")}
     log(f"mfma ceiling: {res}")

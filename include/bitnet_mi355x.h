@@ -20,7 +20,8 @@
  *  per token m: astar = max(max_k |x[m,k]|, RN32(1e-5)), s = RN32(127 / astar),
  *           xq = clip(round_half_even(RN32(x*s)), -128, 127), d[m] = RN32(astar / 127);
  *  acc[m,n] = sum_k q[n,k] * xq[m,k] (exact int32);
- *  y[m,n]   = RN32(float(acc) * RN32(gamma* * d[m])); bf16 y = round-to-nearest-even.
+ *  y[m,n]   = RN32(float(acc) * RN32(gamma* * d[m])); bf16 y = round-to-nearest-even
+ *             (a NaN y, possible only from non-finite inputs, has an unspecified payload).
  * Every integer result (packed bytes, gamma*, xq, d, acc) is bit-identical to the
  * CPU oracle, and so is y under the rescale order above.
  *

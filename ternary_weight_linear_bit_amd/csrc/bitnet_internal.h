@@ -25,6 +25,17 @@ __device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> bf16 (round to nearest, ties to even) in one gfx950 conversion
+// (v_cvt_pk_bf16_f32): lo in bits 0-15, hi in bits 16-31.  Bit-identical to
+// float_to_bf16_rne for every non-NaN input (all 2^32 fp32 bit patterns compared
+// on gfx950); a NaN keeps payload bits instead of becoming sign | 0x7fc0.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Wave64 reductions (butterfly over all 64 lanes).
 // Wave-wide reductions on DPP: quad permutes and the two row mirrors make every
 // lane of a 16-lane row hold the row's result; row broadcasts 15 and 31 (rows

@@ -61,6 +61,89 @@ __device__ __forceinline__ v4i expand_codes(uint32_t w) {
   return a;
 }
 
+// Epilogue through LDS: a wave's BM/2 tokens x 64 rows of y, rescaled
+// (y = RN32(float(acc - sum x) * RN32(gamma * d))) and rounded to the output type
+// (E bytes), pass by pass through the wave's own slice of the activation buffers
+// (free once the main loop's last barrier is passed), so that the stores go out
+// as 16 bytes per lane, 128 bytes per output row and wave (one store per value
+// would write 2 or 4 bytes per lane).  Units of 16 tokens x 64 rows: per unit a
+// lane writes its 8 values x NBW rows, then 16-byte reads give each lane 16
+// consecutive bytes of one token's row.  Rows of the slice are RB bytes, the two
+// halves swapped for tokens with bit 2 set (the two half-waves write tokens 4
+// apart, which then land in different banks).
+template <int E, int BM, int WN>
+__device__ __forceinline__ void store_tile_impl(void* y, const v16i (&acc)[BM / 64][NBW],
+                                                const int* xsum, const float* xsc, float gamma,
+                                                uint8_t* lds, int m0, int wrow0, int M, int N) {
+  constexpr int TB = BM / 64;
+  constexpr int RB = 64 * E;                       // bytes per token row of the slice
+  constexpr int U = 16 * RB;                       // bytes per unit of 16 tokens
+  constexpr int R = 2 * BM * kStride / (2 * WN);   // LDS bytes per wave
+  constexpr int UPP = R / U;                       // units per pass
+  constexpr int UNITS = 2 * TB;
+  static_assert(UPP >= 1 && UNITS % UPP == 0 && (UPP * U) % 1024 == 0, "epilogue passes");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wt = wave / WN;
+  const int r = lane & 31, h = lane >> 5;
+  uint8_t* base = lds + wave * R;
+#pragma unroll
+  for (int p = 0; p < UNITS / UPP; ++p) {
+#pragma unroll
+    for (int uu = 0; uu < UPP; ++uu) {
+      const int u = p * UPP + uu, i = u >> 1, hq = u & 1;
+#pragma unroll
+      for (int vv = 0; vv < 8; ++vv) {
+        const int v = 8 * hq + vv;
+        const int tl = 8 * (vv >> 2) + 4 * h + (vv & 3);      // token within the unit
+        const int ml = wt * (BM / 2) + 32 * i + 16 * hq + tl;
+        const float sc = gamma * xsc[ml];
+        const int xm = xsum[ml];
+        float yv[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) yv[b] = (float)(acc[i][b][v] - xm) * sc;
+        static_assert(NBW == 2, "bf16 values are converted in pairs");
+        const uint32_t pk = E == 2 ? bf16x2_rne(yv[0], yv[1]) : 0u;
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+          const int off = uu * U + tl * RB + (((32 * b + r) * E) ^ (((tl >> 2) & 1) * (RB / 2)));
+          if constexpr (E == 2)
+            *reinterpret_cast<uint16_t*>(base + off) = (uint16_t)(pk >> (16 * b));
+          else
+            *reinterpret_cast<float*>(base + off) = yv[b];
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < UPP * U / 1024; ++q) {
+      const int byte = q * 1024 + 16 * lane;
+      const int uu = byte / U, rem = byte % U;
+      const int tl = rem / RB, c16 = rem % RB;
+      const uint4 val = *reinterpret_cast<const uint4*>(
+          base + uu * U + tl * RB + (c16 ^ (((tl >> 2) & 1) * (RB / 2))));
+      const int u = p * UPP + uu, i = u >> 1, hq = u & 1;
+      const int m = m0 + wt * (BM / 2) + 32 * i + 16 * hq + tl;
+      const int n = wrow0 + c16 / E;
+      if (m < M) {
+        char* dst = static_cast<char*>(y) + ((size_t)m * N + n) * E;
+        if (n + 16 / E <= N) {
+          *reinterpret_cast<uint4*>(dst) = val;
+        } else {
+          const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+          for (int e = 0; e < 16 / E; ++e)
+            if (n + e < N) {
+              if constexpr (E == 2)
+                reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+              else
+                reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+            }
+        }
+      }
+    }
+  }
+}
+
 // WN waves along the output rows (2 along the tokens): BN = 32 * NBW * WN rows
 template <int BM, int WN, int D = kDepth>
 __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
@@ -260,6 +343,31 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
 
   // D layout (32 x 32): lane l holds output row (n) l % 32 and tokens
   // 8 (v / 4) + 4 (l / 32) + v % 4 for its 16 values v
+  if (acc_out) {
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ml = wt * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int m = m0 + ml;
+        if (m < M) {
+#pragma unroll
+          for (int b = 0; b < NBW; ++b) {
+            const int n = wrow0 + 32 * b + r;
+            if (n < N) acc_out[(size_t)m * N + n] = acc[i][b][v] - xsum[ml];   // sum (c - 1) x
+          }
+        }
+      }
+  }
+  const int es = y_bf16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ((N * es) & 15) == 0) {
+    if (y_bf16)
+      store_tile_impl<2, BM, WN>(y, acc, xsum, xsc, gamma, &xs[0][0], m0, wrow0, M, N);
+    else
+      store_tile_impl<4, BM, WN>(y, acc, xsum, xsc, gamma, &xs[0][0], m0, wrow0, M, N);
+    return;
+  }
+  // y not 16-byte aligned or rows not a whole number of 16 bytes: one store per value
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
 #pragma unroll
@@ -269,18 +377,19 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
       if (m < M) {
         const float sc = gamma * xsc[ml];
         const int xm = xsum[ml];
+        float yv[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) yv[b] = (float)(acc[i][b][v] - xm) * sc;
+        const uint32_t pk = bf16x2_rne(yv[0], yv[1]);
 #pragma unroll
         for (int b = 0; b < NBW; ++b) {
           const int n = wrow0 + 32 * b + r;
           if (n < N) {
-            const int a = acc[i][b][v] - xm;   // sum (c - 1) x
-            const float yv = (float)a * sc;
             const size_t o = (size_t)m * N + n;
-            if (acc_out) acc_out[o] = a;
             if (y_bf16)
-              reinterpret_cast<uint16_t*>(y)[o] = float_to_bf16_rne(yv);
+              reinterpret_cast<uint16_t*>(y)[o] = (uint16_t)(pk >> (16 * b));
             else
-              reinterpret_cast<float*>(y)[o] = yv;
+              reinterpret_cast<float*>(y)[o] = yv[b];
           }
         }
       }
