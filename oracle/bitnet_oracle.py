@@ -80,6 +80,17 @@ T1  five ternary codes per byte (3**5 = 243 <= 256, so 1.6 bits per weight).
     block's 16 bytes covers 16 consecutive weights, and a digit falls out of
     the fixed-point fraction as the integer part of three times it).
 
+Prefill weight layout (the same 2-bit codes as O3, rearranged once for the
+matrix-core kernel; the pages describe only CPU layouts, [DT] section 2.3):
+P1  rows are padded with q = 0 to a multiple of 32 and K to a multiple of 128.
+    The matrix is cut into blocks of 32 rows x 128 k, 1024 bytes each, stored
+    block-row-major: block (rb, s) at byte (rb * S + s) * 1024, S = K_pad / 128.
+    In a block, 16-byte chunk L = r + 32 h (r = 0..31, h = 0, 1) holds row
+    32 rb + r at k = 128 s + 64 h + 0..63; its dword j holds the 16 weights
+    k = 128 s + 64 h + 16 j + t (t = 0..15), the code c = q + 1 of weight t at
+    bits 8 (t mod 4) + 2 (t div 4) (byte t mod 4, bit pair t div 4: O3's byte
+    and bit-pair roles swapped within each dword).
+
 bf16 inputs are upcast to fp32 exactly (bit pattern shifted left by 16) before
 any step, so every function here takes fp32 arrays.
 
@@ -515,6 +526,70 @@ def ternary_linear_t1_at(packed: np.ndarray, gamma: np.float32, xq: np.ndarray,
     acc = (q_rows * x_rows).sum(axis=1).astype(np.int32)
     scale = (F32(gamma) * np.asarray(d, dtype=np.float32)[m_idx]).astype(np.float32)
     return acc, acc.astype(np.float32) * scale
+
+
+# ---------------------------------------------------------------------------
+# P1: prefill weight layout (32-row x 128-k blocks, bit pairs transposed per dword)
+# ---------------------------------------------------------------------------
+
+P1_ROWS = 32            # rows per block
+P1_K = 128              # weights per block row
+P1_BLOCK_BYTES = 1024   # bytes per block
+
+
+def prefill_layout_bytes(n: int, k: int) -> int:
+    """Bytes of an N x K matrix in the P1 layout: ceil(N/32) * ceil(K/128) * 1024."""
+    return (-(-n // P1_ROWS)) * (-(-k // P1_K)) * P1_BLOCK_BYTES
+
+
+def pack_prefill(q: np.ndarray) -> np.ndarray:
+    """Ternary q [N, K] -> uint8 [prefill_layout_bytes(N, K)] per reading P1."""
+    q = np.asarray(q, dtype=np.int8)
+    n_rows, k = q.shape
+    nb, sb = -(-n_rows // P1_ROWS), -(-k // P1_K)
+    codes = np.ones((nb * P1_ROWS, sb * P1_K), dtype=np.uint32)     # padding: q = 0
+    codes[:n_rows, :k] = (q.astype(np.int16) + 1).astype(np.uint32)
+    # [rb][r][s][h][j][t]: block rb, row r, step s, half h, dword j, weight t
+    c = codes.reshape(nb, P1_ROWS, sb, 2, 4, 16)
+    words = np.zeros((nb, P1_ROWS, sb, 2, 4), dtype=np.uint32)
+    for t in range(16):
+        words |= c[..., t] << np.uint32(8 * (t % 4) + 2 * (t // 4))
+    # chunk L = r + 32 h of block (rb, s): order [rb][s][h][r][j]
+    out = words.transpose(0, 2, 3, 1, 4).reshape(-1)
+    return out.astype("<u4").view(np.uint8)
+
+
+def unpack_prefill(packed: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Inverse of pack_prefill: uint8 [prefill_layout_bytes(N, K)] -> q [N, K].
+    Code 3 and non-zero padding weights are invalid."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    if p.size != prefill_layout_bytes(n, k):
+        raise ValueError("size does not match N and K")
+    nb, sb = -(-n // P1_ROWS), -(-k // P1_K)
+    words = p.view("<u4").astype(np.uint32).reshape(nb, sb, 2, P1_ROWS, 4)
+    words = words.transpose(0, 3, 1, 2, 4)                      # [rb][r][s][h][j]
+    codes = np.empty(words.shape + (16,), dtype=np.uint32)
+    for t in range(16):
+        codes[..., t] = (words >> np.uint32(8 * (t % 4) + 2 * (t // 4))) & np.uint32(3)
+    if np.any(codes == 3):
+        raise ValueError("packed weights hold the unused code 3")
+    q = (codes.astype(np.int16) - 1).reshape(nb * P1_ROWS, sb * P1_K)
+    if np.any(q[n:, :]) or np.any(q[:, k:]):
+        raise ValueError("padding weights must be zero")
+    return q[:n, :k].astype(np.int8)
+
+
+def repack_prefill(packed: np.ndarray, k: int) -> np.ndarray:
+    """O3 layout [N, K/4] -> P1 layout (the same codes)."""
+    return pack_prefill(unpack_codes(packed)[:, :k])
+
+
+def ternary_linear_prefill(packed_p1: np.ndarray, n: int, gamma: np.float32, xq: np.ndarray,
+                           d: np.ndarray):
+    """ternary_linear on P1-laid-out weights: returns (acc int32 [M, N], y fp32 [M, N])."""
+    q = unpack_prefill(packed_p1, n, np.asarray(xq).shape[1])
+    acc = integer_matmul(q, xq)
+    return acc, dequantize(acc, gamma, d)
 
 
 # ---------------------------------------------------------------------------

@@ -31,3 +31,10 @@ def lut_golden():
     import json
     with open(os.path.join(ROOT, "tests", "golden", "lut_table.json")) as f:
         return json.load(f)
+
+
+@pytest.fixture(scope="session")
+def prefill_golden():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "prefill_layout.json")) as f:
+        return json.load(f)

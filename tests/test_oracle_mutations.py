@@ -223,6 +223,19 @@ def _lut_tables_swapped_roles(xq):
     return q0[None, None, :] * x[:, 0::2, None] + q1[None, None, :] * x[:, 1::2, None]
 
 
+def _pack_prefill_o3_pairs(q):
+    q = np.asarray(q, np.int8)
+    n, k = q.shape
+    nb, sb = -(-n // 32), -(-k // 128)
+    codes = np.ones((nb * 32, sb * 128), np.uint32)
+    codes[:n, :k] = (q.astype(np.int16) + 1).astype(np.uint32)
+    c = codes.reshape(nb, 32, sb, 2, 4, 16)
+    words = np.zeros((nb, 32, sb, 2, 4), np.uint32)
+    for t in range(16):
+        words |= c[..., t] << np.uint32(2 * t)          # O3's order inside the dword
+    return words.transpose(0, 2, 3, 1, 4).reshape(-1).astype("<u4").view(np.uint8)
+
+
 ORIG_ABS_SUM = O.exact_abs_sum_units
 ORIG_RN32 = O.rn32_ratio
 ORIG_MATMUL = O.integer_matmul
@@ -258,6 +271,8 @@ SLIPS = {
     "gating rounded once": ("relu2_glu", _glu_one_rounding, [P.test_relu2_glu_hand_worked_rounding]),
     "five-per-byte digits in reverse order": ("pack_t1", _pack_t1_digits_reversed,
                                               [lambda g, t1=None: P.test_t1_golden_layout(t1)]),
+    "prefill layout with O3's bit-pair order": (
+        "pack_prefill", _pack_prefill_o3_pairs, [lambda g, pf=None: P.test_prefill_golden_layout(pf)]),
     "lookup-table index with the code roles swapped": (
         "lut_tables", _lut_tables_swapped_roles, [lambda g, lut=None: P.test_lut_golden_tables(lut)]),
 }
@@ -270,13 +285,15 @@ def _call(pin, fixtures):
         return pin(None, fixtures["t1"])
     if params[1:2] == ["lut"]:
         return pin(None, fixtures["lut"])
+    if params[1:2] == ["pf"]:
+        return pin(None, fixtures["pf"])
     return pin(fixtures["golden"]) if len(params) == 1 else pin()
 
 
 @pytest.mark.parametrize("name", sorted(SLIPS))
-def test_pins_reject_slip(name, golden, t1_golden, lut_golden, monkeypatch):
+def test_pins_reject_slip(name, golden, t1_golden, lut_golden, prefill_golden, monkeypatch):
     attr, fn, pins = SLIPS[name]
-    fixtures = {"golden": golden, "t1": t1_golden, "lut": lut_golden}
+    fixtures = {"golden": golden, "t1": t1_golden, "lut": lut_golden, "pf": prefill_golden}
     for pin in pins:
         _call(pin, fixtures)          # the pin holds for the oracle as it stands
     monkeypatch.setattr(O, attr, fn)

@@ -806,3 +806,58 @@ def test_lut_linear_equals_integer_matmul():
         acc_w, y_w = O.ternary_linear(p, np.float32(0.021), xq, d)
         np.testing.assert_array_equal(acc, acc_w)
         np.testing.assert_array_equal(y.view(np.uint32), y_w.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# P1: prefill weight layout
+# ---------------------------------------------------------------------------
+
+def _prefill_case(case):
+    n, k = case["N"], case["K"]
+    q = np.zeros((n, k), np.int8)
+    if "codes_row0" in case:
+        q[0, :] = np.array(case["codes_row0"], np.int16) - 1
+    for r, c, v in case.get("set", []):
+        q[r, c] = v
+    want = np.full(case["size"], case["other"], np.uint8)
+    for off, v in case["bytes"].items():
+        want[int(off)] = v
+    return q, want
+
+
+def test_prefill_golden_layout(prefill_golden):
+    """Hand-worked bytes (tests/golden/prefill_layout.json): catches the bit pairs
+    in O3's order, a wrong block order, a swapped chunk index (r + 32 h) and a
+    wrong padding code."""
+    for case in prefill_golden["cases"]:
+        q, want = _prefill_case(case)
+        assert O.prefill_layout_bytes(case["N"], case["K"]) == case["size"]
+        np.testing.assert_array_equal(O.pack_prefill(q), want, err_msg=case["name"])
+        np.testing.assert_array_equal(O.unpack_prefill(want, case["N"], case["K"]), q)
+
+
+def test_prefill_layout_roundtrip_and_contraction():
+    """Random ternary matrices (ragged N and K, K = 64 mod 128): the layout is a
+    bijection onto valid codes, the O3 repack agrees with packing q directly, and
+    the contraction on P1 weights equals the one on O3 weights (same integers)."""
+    rng = np.random.default_rng(71)
+    for n, k in ((1, 64), (33, 192), (64, 256), (70, 2560), (5, 6912)):
+        q = rng.integers(-1, 2, (n, k)).astype(np.int8)
+        p1 = O.pack_prefill(q)
+        assert p1.size == O.prefill_layout_bytes(n, k)
+        np.testing.assert_array_equal(O.unpack_prefill(p1, n, k), q)
+        np.testing.assert_array_equal(O.repack_prefill(O.pack_codes(q), k), p1)
+        xq = rng.integers(-128, 128, (3, k)).astype(np.int8)
+        d = rng.random(3).astype(np.float32)
+        acc_a, y_a = O.ternary_linear_prefill(p1, n, F32(0.5), xq, d)
+        acc_b, y_b = O.ternary_linear(O.pack_codes(q), F32(0.5), xq, d)
+        np.testing.assert_array_equal(acc_a, acc_b)
+        np.testing.assert_array_equal(y_a, y_b)
+    # a byte holding code 3, and a non-zero padding weight, are rejected
+    p1 = O.pack_prefill(np.zeros((1, 64), np.int8))
+    bad = p1.copy(); bad[0] = 0xFF
+    with pytest.raises(ValueError):
+        O.unpack_prefill(bad, 1, 64)
+    bad = p1.copy(); bad[100] = 0x56          # row 6, inside the padding rows
+    with pytest.raises(ValueError):
+        O.unpack_prefill(bad, 1, 64)
