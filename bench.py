@@ -302,16 +302,18 @@ def leg_summary(d, m):
 def prefill(torch, N, I, layer_shapes, ms, steps):
     """int8 TOPS of the prefill kernel on one layer's matrices at M tokens (q, k, v
     in one launch, o, gate and up in one launch, down), and of its largest matrix
-    alone."""
+    alone: with the weights in the prefill layout (repacked once from the 2-bit
+    rows, outside the timed region), the headline, and in the 2-bit row layout."""
     names = [nm for nm, _, _ in layer_shapes]
     groups = [g for g in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
               if all(nm in names for nm in g)]
     assert sorted(sum(groups, ())) == sorted(names), "layer with an unknown matrix set"
-    mats = {}
+    mats, pre = {}, {}
     for i, (nm, k, n) in enumerate(layer_shapes):
         g = torch.Generator(device="cuda").manual_seed(I.weight_seed(0, i))
         w = torch.randn((n, k), generator=g, device="cuda").mul_(I.WEIGHT_SIGMA)
         mats[nm] = N.bitnet_quantize_weights(w)
+        pre[nm] = (N.bitnet_repack_prefill(mats[nm][0]), mats[nm][1], n)
     res = {}
     for m in ms:
         xq = {}
@@ -325,15 +327,16 @@ def prefill(torch, N, I, layer_shapes, ms, steps):
 
         kin = {nm: k for nm, k, _ in layer_shapes}
 
-        def run(only=None, reps=1):
+        def run(only=None, reps=1, layout="prefill"):
             for _ in range(reps):
-                if only is not None:
-                    N.bitnet_ternary_linear(*mats[only], *xq[kin[only]], y=ys[only])
-                    continue
                 # matrices that share an input run in one launch (q, k, v; gate, up)
-                for grp in groups:
-                    N.bitnet_ternary_linear_multi([(*mats[nm], ys[nm]) for nm in grp],
-                                                  *xq[kin[grp[0]]])
+                for grp in ((only,),) if only is not None else groups:
+                    if layout == "prefill":
+                        N.bitnet_ternary_linear_prefill([(*pre[nm], ys[nm]) for nm in grp],
+                                                        *xq[kin[grp[0]]])
+                    else:
+                        N.bitnet_ternary_linear_multi([(*mats[nm], ys[nm]) for nm in grp],
+                                                      *xq[kin[grp[0]]])
 
         def timed(fn):
             fn()
@@ -352,19 +355,23 @@ def prefill(torch, N, I, layer_shapes, ms, steps):
             return e0.elapsed_time(e1) * 1e-3 / steps
 
         sec = timed(run)
+        sec_rows = timed(lambda: run(layout="rows"))
         nm, k, n = max(layer_shapes, key=lambda t: t[1] * t[2])
         ksec = timed(lambda: run(only=nm, reps=10)) / 10
         tops = ops / sec / 1e12
         res[str(m)] = {"tops": round(tops, 2),
                        "frac_of_int8_peak": round(tops / INT8_MFMA_PEAK_TOPS, 4),
                        "layer_ms": round(sec * 1e3, 4),
+                       "weights": "prefill layout (repacked once from the 2-bit rows)",
+                       "row_layout_tops": round(ops / sec_rows / 1e12, 2),
+                       "row_layout_layer_ms": round(sec_rows * 1e3, 4),
                        "largest_matrix": f"{k}->{n}",
                        "largest_matrix_us": round(ksec * 1e6, 2),
                        "largest_matrix_tops": round(2 * m * n * k / ksec / 1e12, 2),
                        "roofline": {"bound": "mfma", "achieved": round(tops, 1),
                                     "peak": INT8_MFMA_PEAK_TOPS, "unit": "TOPS (int8)",
                                     "frac": round(tops / INT8_MFMA_PEAK_TOPS, 4), "traffic": None,
-                                    "kernel": "gemm_kernel (prefill, int8 MFMA)",
+                                    "kernel": "gemm_kernel (prefill, int8 MFMA, prefill layout)",
                                     "ops": "2 M N K per launch, zero weights counted (the "
                                            "sum_pos - sum_neg form needs ~0.69 M N K add/subs)",
                                     "launches_per_layer": 4,

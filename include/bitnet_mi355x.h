@@ -285,6 +285,43 @@ bitnet_status bitnet_ternary_linear_t1(const bitnet_matrix *mats, int count, con
                                        hipStream_t stream);
 
 /*
+ * Prefill weight layout: the same 2-bit codes, rearranged once for the prefill
+ * kernel (matrix cores) so that each of its 16-byte loads reads 1 KiB of
+ * contiguous memory per wave and the codes expand to int8 in natural k order
+ * without byte shuffles (dashen-tech.com, "BitNet.cpp 深度解析", section 2.3,
+ * describes the 2-bit storage; this arrangement is the library's own).  Rows
+ * are padded with q = 0 to a multiple of 32 and K to a multiple of 128; blocks
+ * of 32 rows x 128 k (1024 bytes) are stored block-row-major, block (rb, s) at
+ * byte (rb * ceil(K/128) + s) * 1024; 16-byte chunk L = r + 32 h of a block
+ * holds row 32 rb + r at k = 128 s + 64 h + 0..63, and its dword j the weights
+ * k = 128 s + 64 h + 16 j + t (t = 0..15), the code q + 1 of weight t at bits
+ * 8 (t mod 4) + 2 (t div 4).
+ * bitnet_prefill_layout_bytes: ceil(N/32) * ceil(K/128) * 1024 (0 for N < 0 or
+ * K < 0).
+ */
+size_t bitnet_prefill_layout_bytes(int64_t N, int64_t K);
+
+/*
+ * Exact conversion of a 2-bit packed matrix (bitnet_quantize_weights layout) to
+ * the prefill layout.  K >= 64, K % 64 == 0, N >= 0, N*K < BITNET_MAX_WEIGHTS;
+ * w_packed and w_prefill (bitnet_prefill_layout_bytes(N, K) bytes, caller-owned)
+ * 16-byte aligned.  Bytes holding the unused code 3 give unspecified output.
+ */
+bitnet_status bitnet_repack_prefill(const uint8_t *w_packed, int64_t N, int64_t K,
+                                    uint8_t *w_prefill, hipStream_t stream);
+
+/*
+ * bitnet_ternary_linear_multi on weights in the prefill layout (every
+ * mats[i].w_packed, 16-byte aligned): the prefill kernel for any M >= 1, up to
+ * four matrices per launch, the same results bit for bit.  Needs K >= 64,
+ * K % 64 == 0 and a 16-byte aligned x_q; otherwise BITNET_ERR_SHAPE /
+ * BITNET_ERR_ALIGN (there is no generic kernel for this layout).
+ */
+bitnet_status bitnet_ternary_linear_prefill(const bitnet_matrix *mats, int count,
+                                            const int8_t *x_q, const float *x_scale, int64_t M,
+                                            int64_t K, int y_dtype, hipStream_t stream);
+
+/*
  * bitnet_quant_linear_ex on T1 weights (same layout requirements as
  * bitnet_ternary_linear_t1).  The quantisation and prologue are fused into the
  * decode launch when M <= 4 and the activations of all tokens fit one LDS phase

@@ -67,6 +67,11 @@ SIGNATURES["bitnet_quant_linear_t1"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _
                                              ctypes.POINTER(BitnetActPrologue), _I64, _I64, _P,
                                              _P, _I, _P])
 
+SIGNATURES["bitnet_prefill_layout_bytes"] = (_SZ, [_I64, _I64])
+SIGNATURES["bitnet_repack_prefill"] = (_I, [_P, _I64, _I64, _P, _P])
+SIGNATURES["bitnet_ternary_linear_prefill"] = (_I, [ctypes.POINTER(BitnetMatrix), _I, _P, _P,
+                                                    _I64, _I64, _I, _P])
+
 SIGNATURES["bitnet_lut_workspace_bytes"] = (_SZ, [_I64, _I64])
 SIGNATURES["bitnet_ternary_linear_lut"] = (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _P,
                                                 _SZ, _P])
@@ -440,6 +445,59 @@ def bitnet_quant_linear_t1(mats, x, x_q=None, x_scale=None, y_dtype=None, stream
         arr, len(mats), _ptr(x), _dtype_code(x.dtype), _prologue(x, up, norm_weight, eps), m, k,
         _ptr(x_q), _ptr(x_scale), _dtype_code(ys[0].dtype), _stream(stream)))
     return ys, x_q, x_scale
+
+
+def prefill_layout_shape(n: int, k: int):
+    """Shape of an N x K matrix in the prefill layout as a uint8 tensor: one row
+    per 32 weight rows, ceil(K/128) * 1024 bytes each."""
+    return ((n + 31) // 32, ((k + 127) // 128) * 1024)
+
+
+def bitnet_repack_prefill(w_packed, out=None, stream=None):
+    """2-bit packed [N, K/4] -> the prefill layout, uint8 prefill_layout_shape(N, K)."""
+    import torch
+    _need_cuda(w_packed)
+    n, kb = w_packed.shape
+    k = 4 * kb
+    shape = prefill_layout_shape(n, k)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=w_packed.device)
+    _expect(w_packed, (n, kb), torch.uint8, "w_packed")
+    _expect(out, shape, torch.uint8, "out")
+    _check("bitnet_repack_prefill", lib().bitnet_repack_prefill(_ptr(w_packed), n, k, _ptr(out),
+                                                                _stream(stream)))
+    return out
+
+
+def bitnet_ternary_linear_prefill(mats, x_q, x_scale, y_dtype=None, stream=None):
+    """Several (w_prefill, w_scale, N[, y[, acc_out]]) sharing x_q -> list of y; each
+    w_prefill in the prefill layout (prefill_layout_shape(N, K))."""
+    import torch
+    _need_cuda(x_q, x_scale)
+    m, k = x_q.shape
+    _expect(x_q, (m, k), torch.int8, "x_q")
+    _expect(x_scale, (m,), torch.float32, "x_scale")
+    if not mats:
+        raise ValueError("at least one matrix")
+    arr = (BitnetMatrix * len(mats))()
+    ys = []
+    for i, t in enumerate(mats):
+        w, w_scale, n = t[0], t[1], int(t[2])
+        y = t[3] if len(t) > 3 and t[3] is not None else torch.empty(
+            (m, n), dtype=(y_dtype or torch.float32) if not ys else ys[0].dtype,
+            device=x_q.device)
+        acc = t[4] if len(t) > 4 else None
+        _expect(w, prefill_layout_shape(n, k), torch.uint8, f"w_prefill[{i}]")
+        _check_scale(w_scale)
+        _expect(y, (m, n), ys[0].dtype if ys else _floats(), f"y[{i}]")
+        _expect(acc, (m, n), torch.int32, f"acc_out[{i}]")
+        arr[i] = BitnetMatrix(w.data_ptr(), w_scale.data_ptr(), n, y.data_ptr(),
+                              0 if acc is None else acc.data_ptr())
+        ys.append(y)
+    _check("bitnet_ternary_linear_prefill", lib().bitnet_ternary_linear_prefill(
+        arr, len(mats), _ptr(x_q), _ptr(x_scale), m, k, _dtype_code(ys[0].dtype),
+        _stream(stream)))
+    return ys
 
 
 # ---------------------------------------------------------------------------

@@ -397,6 +397,66 @@ bitnet_status bitnet_ternary_linear_multi(const bitnet_matrix* mats, int count,
   return run_linear(mats, count, x_q, x_scale, M, K, y_dtype, stream);
 }
 
+size_t bitnet_prefill_layout_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0) return 0;
+  return (size_t)bitnet::prefill_layout_bytes(N, K);
+}
+
+bitnet_status bitnet_repack_prefill(const uint8_t* w_packed, int64_t N, int64_t K,
+                                    uint8_t* w_prefill, hipStream_t stream) {
+  if (!w_packed || !w_prefill) return BITNET_ERR_NULL;
+  if (N < 0 || K < 64 || (K % 64) != 0 || K > BITNET_MAX_K ||
+      (N > 0 && N >= BITNET_MAX_WEIGHTS / K))
+    return BITNET_ERR_SHAPE;
+  if (!aligned(w_packed, 16) || !aligned(w_prefill, 16)) return BITNET_ERR_ALIGN;
+  if (N == 0) return BITNET_OK;
+  return from_hip(bitnet::launch_repack_prefill(w_packed, N, K, w_prefill, stream));
+}
+
+bitnet_status bitnet_ternary_linear_prefill(const bitnet_matrix* mats, int count,
+                                            const int8_t* x_q, const float* x_scale, int64_t M,
+                                            int64_t K, int y_dtype, hipStream_t stream) {
+  if (M > 0 && (!x_scale || !x_q)) return BITNET_ERR_NULL;
+  const bitnet_status st = check_group(mats, count, M, K, y_dtype);
+  if (st != BITNET_OK) return st;
+  if (K < 64 || (K % 64) != 0) return BITNET_ERR_SHAPE;
+  if (x_scale && !aligned(x_scale, 4)) return BITNET_ERR_ALIGN;
+  if (M > 0 && !aligned(x_q, 16)) return BITNET_ERR_ALIGN;
+  for (int j = 0; j < count; ++j)
+    if (M > 0 && mats[j].N > 0 && !aligned(mats[j].w_packed, 16)) return BITNET_ERR_ALIGN;
+  if (M == 0) return BITNET_OK;
+  bitnet::GemmArgs g{};
+  for (int j = 0; j < count; ++j) {
+    const bitnet_matrix& m = mats[j];
+    if (m.N == 0) continue;
+    g.wp[g.count] = m.w_packed;
+    g.ws[g.count] = m.w_scale;
+    g.y[g.count] = m.y;
+    g.acc[g.count] = m.acc_out;
+    g.n[g.count] = (int)m.N;
+    if (++g.count == bitnet::kMaxGroup || j == count - 1) {
+      g.xq = x_q;
+      g.xs = x_scale;
+      g.M = (int)M;
+      g.K = (int)K;
+      g.y_bf16 = y_dtype == BITNET_BF16 ? 1 : 0;
+      g.layout = 1;
+      if (bitnet::launch_gemm(g, stream) != hipSuccess) return BITNET_ERR_HIP;
+      g = bitnet::GemmArgs{};
+    }
+  }
+  if (g.count > 0) {      // the last matrices had N == 0 after a partial group
+    g.xq = x_q;
+    g.xs = x_scale;
+    g.M = (int)M;
+    g.K = (int)K;
+    g.y_bf16 = y_dtype == BITNET_BF16 ? 1 : 0;
+    g.layout = 1;
+    if (bitnet::launch_gemm(g, stream) != hipSuccess) return BITNET_ERR_HIP;
+  }
+  return BITNET_OK;
+}
+
 bitnet_status bitnet_ternary_linear(const uint8_t* w_packed, const float* w_scale,
                                     const int8_t* x_q, const float* x_scale, int64_t M,
                                     int64_t N, int64_t K, void* y, int y_dtype, int32_t* acc_out,

@@ -453,9 +453,15 @@ struct GemmArgs {
   const int8_t* xq;          // int8 activations [M][K]
   const float* xs;           // their token scales
   int count, M, K, y_bf16;
+  int layout;                // weights: 0 = rows of K/4 bytes, 1 = prefill layout
 };
 // Prefill kernel: K % 64 == 0, 16-byte aligned packed weights and activations.
 hipError_t launch_gemm(GemmArgs a, hipStream_t s);
+// Prefill layout: its size, and the conversion from rows of K/4 bytes (K % 64
+// == 0, 16-byte aligned input and output).
+int64_t prefill_layout_bytes(int64_t N, int64_t K);
+hipError_t launch_repack_prefill(const uint8_t* w, int64_t N, int64_t K, uint8_t* out,
+                                 hipStream_t s);
 // The prefill launch's tile for M tokens over `count` matrices of n[j] rows on a
 // device with `cus` compute units: bm tokens x bn rows per workgroup; when
 // first_tokens > 0 the first first_tokens tokens run as one launch with this tile

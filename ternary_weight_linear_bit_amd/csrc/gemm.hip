@@ -145,8 +145,11 @@ __device__ __forceinline__ void store_tile_impl(void* y, const v16i (&acc)[BM / 
 }
 
 // WN waves along the output rows (2 along the tokens): BN = 32 * NBW * WN rows
-template <int BM, int WN, int D = kDepth>
-__global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
+// (prefill layout: at least two waves per SIMD, 256 registers at most,
+// accumulators included)
+template <int BM, int WN, int D, int LAYOUT>
+__global__ __launch_bounds__(128 * WN, LAYOUT == 1 ? 2 : 1) void gemm_kernel(
+    const GemmArgs args) {
   constexpr int kThreads = 128 * WN;
   constexpr int BN = 32 * NBW * WN;         // output rows per workgroup
   constexpr int TB = BM / 64;               // 32-token blocks per wave
@@ -207,13 +210,25 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
     const int k = k0 + 16 * (g & 7);
     return k < K ? (uint32_t)(g >> 3) * (uint32_t)K + (uint32_t)k : kOob;
   };
-  // weights: this wave's 64 rows; rows past N read zeros
+  // weights: this wave's 64 rows; rows past N read zeros.  LAYOUT 0: rows of
+  // K/4 bytes, a lane reads 16 bytes of its row (32 rows x 32 bytes per load).
+  // LAYOUT 1 (prefill layout): 1024-byte blocks of 32 rows x 128 k, block
+  // (row block, step) at (row block * steps + step) * 1024, in the lanes' order,
+  // so a load reads 1 KiB contiguous (the padding rows and k read as code 1,
+  // which meets zero activations or outputs that are not stored)
   const int wrow0 = n0 + wr * (32 * NBW);
   const int wrows = max(0, min(32 * NBW, N - wrow0));
-  const auto wrs = make_uniform_rsrc(wp + (size_t)wrow0 * rowb, (uint32_t)wrows * rowb);
+  const uint32_t wblk = LAYOUT == 1 ? (uint32_t)steps * 1024u : 0u;   // bytes per row block
+  const auto wrs = LAYOUT == 1
+      ? make_uniform_rsrc(wp + (size_t)(wrow0 >> 5) * wblk, (uint32_t)((wrows + 31) >> 5) * wblk)
+      : make_uniform_rsrc(wp + (size_t)wrow0 * rowb, (uint32_t)wrows * rowb);
   auto woff = [&](int b, int k0) -> uint32_t {
-    const int k = k0 + 64 * h;
-    return k < K ? (uint32_t)(32 * b + r) * rowb + ((uint32_t)k >> 2) : kOob;
+    if constexpr (LAYOUT == 1) {
+      return (uint32_t)b * wblk + (uint32_t)(k0 >> 7) * 1024u + 16u * (uint32_t)lane;
+    } else {
+      const int k = k0 + 64 * h;
+      return k < K ? (uint32_t)(32 * b + r) * rowb + ((uint32_t)k >> 2) : kOob;
+    }
   };
 
   // (past the last step the offsets leave the buffers and the loads read zeros:
@@ -241,7 +256,15 @@ __global__ __launch_bounds__(128 * WN) void gemm_kernel(const GemmArgs args) {
     for (int e = 0; e < 4; ++e)
       rsum[i] = __builtin_amdgcn_sdot4((int)in[e], 0x01010101, rsum[i], false);
     uint32_t o[4];
-    transpose4x4_bytes(in, o);
+    if constexpr (LAYOUT == 1) {
+      // the prefill layout's expanded weights are in natural k order
+      o[0] = in[0];
+      o[1] = in[1];
+      o[2] = in[2];
+      o[3] = in[3];
+    } else {
+      transpose4x4_bytes(in, o);
+    }
     *reinterpret_cast<uint4*>(buf + lds_group(g >> 3, g & 7)) = make_uint4(o[0], o[1], o[2], o[3]);
   };
   auto aread = [&](const uint8_t* buf, int i, int j) -> v4i {
@@ -504,14 +527,72 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (tiles > (int64_t)1 << 30) return hipErrorInvalidValue;  // grid and tile index limits
   const dim3 grid((unsigned)(((tiles + kXcds - 1) / kXcds) * kXcds));
-  if (big)
-    hipLaunchKernelGGL((gemm_kernel<256, 4>), grid, dim3(512), 0, s, a);
-  else if (small)
-    hipLaunchKernelGGL((gemm_kernel<64, 2, 4>), grid, dim3(256), 0, s, a);
-  else if (wide)
-    hipLaunchKernelGGL((gemm_kernel<128, 4>), grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<128, 2>), grid, dim3(256), 0, s, a);
+  if (a.layout == 1) {
+    if (big)
+      hipLaunchKernelGGL((gemm_kernel<256, 4, kDepth, 1>), grid, dim3(512), 0, s, a);
+    else if (small)
+      hipLaunchKernelGGL((gemm_kernel<64, 2, 4, 1>), grid, dim3(256), 0, s, a);
+    else if (wide)
+      hipLaunchKernelGGL((gemm_kernel<128, 4, kDepth, 1>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<128, 2, kDepth, 1>), grid, dim3(256), 0, s, a);
+  } else {
+    if (big)
+      hipLaunchKernelGGL((gemm_kernel<256, 4, kDepth, 0>), grid, dim3(512), 0, s, a);
+    else if (small)
+      hipLaunchKernelGGL((gemm_kernel<64, 2, 4, 0>), grid, dim3(256), 0, s, a);
+    else if (wide)
+      hipLaunchKernelGGL((gemm_kernel<128, 4, kDepth, 0>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<128, 2, kDepth, 0>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// O3 rows (K/4 bytes, K % 64 == 0) -> the prefill layout: one thread per 16-byte
+// chunk of the output (row 32 rb + r, k = 128 s + 64 h + 0..63), each dword's bit
+// pairs transposed from (byte, pair) to (pair, byte); padding rows and k get
+// code 1 (0x55 bytes).
+__global__ __launch_bounds__(256) void repack_prefill_kernel(const uint8_t* __restrict__ w,
+                                                            int64_t N, int64_t K, int64_t S,
+                                                            int64_t chunks,
+                                                            uint8_t* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const int64_t blk = c >> 6;
+  const int L = (int)(c & 63);
+  const int64_t rb = blk / S, st = blk - rb * S;
+  const int64_t n = 32 * rb + (L & 31);
+  const int64_t k0 = 128 * st + 64 * (L >> 5);
+  uint4 v = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+  if (n < N && k0 < K) {
+    const uint4 in = *reinterpret_cast<const uint4*>(w + n * (K >> 2) + (k0 >> 2));
+    const uint32_t iw[4] = {in.x, in.y, in.z, in.w};
+    uint32_t ow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t)    // weight t: byte t / 4, pair t % 4 -> byte t % 4, pair t / 4
+        o |= ((iw[j] >> (8 * (t >> 2) + 2 * (t & 3))) & 3u) << (8 * (t & 3) + 2 * (t >> 2));
+      ow[j] = o;
+    }
+    v = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+  reinterpret_cast<uint4*>(out)[c] = v;
+}
+
+int64_t prefill_layout_bytes(int64_t N, int64_t K) {
+  return ((N + 31) / 32) * ((K + 127) / 128) * 1024;
+}
+
+hipError_t launch_repack_prefill(const uint8_t* w, int64_t N, int64_t K, uint8_t* out,
+                                 hipStream_t s) {
+  const int64_t S = (K + 127) / 128;
+  const int64_t chunks = prefill_layout_bytes(N, K) / 16;
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(repack_prefill_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                     s, w, N, K, S, chunks, out);
   return hipGetLastError();
 }
 
