@@ -152,6 +152,87 @@ __device__ __forceinline__ Prologue load_prologue(const GemvArgs& a, int g1, int
   return v;
 }
 
+// Balanced runs: the epilogue's scalars for the two matrices of a workgroup's
+// run, A = jA and B = jA + 1 (B = A when A is the last slot; launch_gemv fills
+// the slots past count with matrix 0's pointers, so B's are always readable).
+struct RunPrologue {
+  const float *wsA, *wsB;
+  void *yA, *yB;
+  int32_t *accA, *accB;
+  const float* xs;
+  int y_bf16, mdiv;
+};
+__device__ __forceinline__ RunPrologue load_run_prologue(const GemvArgs& a, int jA) {
+  const int jB = jA + (jA < kMaxGroup - 1 ? 1 : 0);
+  const float *wsA = a.ws[jA], *wsB = a.ws[jB];
+  void *yA = a.y[jA], *yB = a.y[jB];
+  int32_t *accA = a.acc[jA], *accB = a.acc[jB];
+  uint64_t bt = arg_pair(&a.y_bf16), md = arg_pair(&a.mdiv);
+  const float* xs = a.xs;
+  asm volatile("" : "+s"(wsA), "+s"(wsB), "+s"(yA), "+s"(yB), "+s"(accA), "+s"(accB), "+s"(bt),
+                    "+s"(md), "+s"(xs));
+  return RunPrologue{wsA, wsB, yA, yB, accA, accB, xs, (int)bt, (int)md};
+}
+
+// The matrices of a workgroup's run of tiles (it covers at most two): A, the
+// matrix of tile t, and B, the next one; first tiles c1 <= c2 <= c3 of matrices
+// 1..3.  Chosen in scalar registers in one block (as compare-and-choose code the
+// compiler turned the chain into a table in scratch memory, or repeated a
+// compare per choice).
+struct RunWindow {
+  uint64_t wqA, wqB;   // packed weights
+  int nA, nB;          // rows
+  int cA, cB;          // first tiles (cB = 2^30: no matrix after A)
+  int jA;              // slot of A
+};
+__device__ __forceinline__ RunWindow run_window(int t, int c1, int c2, int c3, uint64_t w0,
+                                                uint64_t w1, uint64_t w2, uint64_t w3, int n0,
+                                                int n1, int n2, int n3) {
+  RunWindow v{w0, w1, n0, n1, 0, c1, 0};
+  asm("s_cmp_ge_i32 %7, %8\n\t"
+      "s_cselect_b64 %0, %11, %0\n\t"
+      "s_cselect_b64 %1, %12, %1\n\t"
+      "s_cselect_b32 %2, %14, %2\n\t"
+      "s_cselect_b32 %3, %15, %3\n\t"
+      "s_cselect_b32 %4, %8, %4\n\t"
+      "s_cselect_b32 %5, %9, %5\n\t"
+      "s_cselect_b32 %6, 1, %6\n\t"
+      "s_cmp_ge_i32 %7, %9\n\t"
+      "s_cselect_b64 %0, %12, %0\n\t"
+      "s_cselect_b64 %1, %13, %1\n\t"
+      "s_cselect_b32 %2, %15, %2\n\t"
+      "s_cselect_b32 %3, %16, %3\n\t"
+      "s_cselect_b32 %4, %9, %4\n\t"
+      "s_cselect_b32 %5, %10, %5\n\t"
+      "s_cselect_b32 %6, 2, %6\n\t"
+      "s_cmp_ge_i32 %7, %10\n\t"
+      "s_cselect_b64 %0, %13, %0\n\t"
+      "s_cselect_b32 %2, %16, %2\n\t"
+      "s_cselect_b32 %4, %10, %4\n\t"
+      "s_cselect_b32 %5, 0x40000000, %5\n\t"
+      "s_cselect_b32 %6, 3, %6"
+      : "+s"(v.wqA), "+s"(v.wqB), "+s"(v.nA), "+s"(v.nB), "+s"(v.cA), "+s"(v.cB), "+s"(v.jA)
+      : "s"(t), "s"(c1), "s"(c2), "s"(c3), "s"(w1), "s"(w2), "s"(w3), "s"(n1), "s"(n2), "s"(n3)
+      : "scc");
+  return v;
+}
+// Weights, rows and first tile of the matrix of tile gt: B's if gt >= cB, else A's.
+struct TileMatrix {
+  uint64_t wq;
+  int n, c;
+};
+__device__ __forceinline__ TileMatrix tile_matrix(int gt, const RunWindow& w) {
+  TileMatrix m{w.wqA, w.nA, w.cA};
+  asm("s_cmp_ge_i32 %3, %4\n\t"
+      "s_cselect_b64 %0, %5, %0\n\t"
+      "s_cselect_b32 %1, %6, %1\n\t"
+      "s_cselect_b32 %2, %4, %2"
+      : "+s"(m.wq), "+s"(m.n), "+s"(m.c)
+      : "s"(gt), "s"(w.cB), "s"(w.wqB), "s"(w.nB)
+      : "scc");
+  return m;
+}
+
 // phase_k(M, K, FMT) == min(K, kx_cap<FMT>(M)): the M-dependent cap, from a
 // compile-time table (a run-time division by M would cost a long vector sequence
 // in front of the first loads).
@@ -221,15 +302,16 @@ __device__ __forceinline__ void store_group(uint8_t* dst, uint4 v) {
 // What a workgroup needs before its first loads comes as leading scalar
 // arguments, which are preloaded into scalar registers at wave launch (the
 // library builds this file with kernarg preload): the activations xin, the
-// first three matrices' weights and rows, the first workgroups g1, g2 of
-// matrices 1 and 2, and mtck = M | T << 5 | count << 10 | K << 13 (T = row tiles
-// per workgroup).  The rest stays in the argument block a, read after the first
-// loads are issued.  Arguments are laid out in order, each at its natural
-// alignment, so the block starts at kArgsAt.
+// first three matrices' weights and rows, the split of the tiles over the
+// workgroups (s1, s2: per-matrix runs, the first workgroups of matrices 1 and 2;
+// balanced runs, qt and rt), and mtck = M | T << 5 | count << 10 | K << 13 (T =
+// the most row tiles of a workgroup).  The rest stays in the argument block a,
+// read after the first loads are issued.  Arguments are laid out in order, each
+// at its natural alignment, so the block starts at kArgsAt.
 struct LeadArgs {
   const void* xin;
   const uint8_t *wp0, *wp1, *wp2;
-  int n0, n1, n2, g1, g2;
+  int n0, n1, n2, s1, s2;
   uint32_t mtck;
 };
 constexpr int kArgsAt =
@@ -241,10 +323,17 @@ constexpr int kArgsAt =
 // groups of 16 inputs per thread held in registers by the fused modes (without a
 // prologue, kHoldPlain for inputs longer than kHold groups per thread, so that
 // they are read once; else kHold).
-template <int XMODE, int R, int FMT, int H = kHold>
+// BAL false: per-matrix runs, each workgroup's tiles belong to one matrix (T
+// tiles, the last run of a matrix shorter).  BAL true: balanced runs, the tiles of
+// all the launch's matrices form one list, matrix after matrix, and workgroup b
+// takes qt + 1 consecutive tiles if b < rt, else qt (a run may cross into the
+// next matrix); used where rounding each matrix's split up would leave more
+// workgroups than the compute units hold at once (the balanced code's extra
+// scalar work measured 0.1-0.2 us per launch, so it is not the default).
+template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const uint8_t* wp0,
                                                         const uint8_t* wp1, const uint8_t* wp2,
-                                                        int n0, int n1, int n2, int g1, int g2,
+                                                        int n0, int n1, int n2, int s1, int s2,
                                                         uint32_t mtck, const GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int F = XMODE > 0 ? XMODE - 1 : 0;
@@ -262,39 +351,70 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   const int r = lane & 15;  // A operand: row of the tile; B operand: token
   const int g = lane >> 4;  // 16-k block of the operand within a 64-k chunk
   const int M = (int)(mtck & 31u), T = (int)((mtck >> 5) & 31u), K = (int)(mtck >> 13);
-  // this workgroup's matrix (each workgroup's tiles belong to one matrix); only a
-  // fourth matrix waits for the argument block
   const int b = (int)blockIdx.x;
+  // per-matrix runs: this workgroup's matrix and its first tile in it
   const uint8_t* wmat = wp0;
-  int nrows = n0, wgm = 0;
-  if (b >= g1) { wmat = wp1; nrows = n1; wgm = g1; }
-  if (b >= g2) { wmat = wp2; nrows = n2; wgm = g2; }
-  if (((mtck >> 10) & 7u) == 4u) {
-    // (loaded and waited for in one asm block: loads the compiler sees, it hoists
-    // to the entry, and every launch would then wait for them before its first
-    // weight loads; early-clobber outputs, since the block issues several loads
-    // from the one segment pointer)
-    int g3, n3;
-    uint64_t w3;
-    asm volatile(
-        "s_load_dword %0, %3, %4\n\t"
-        "s_load_dword %1, %3, %5\n\t"
-        "s_load_dwordx2 %2, %3, %6\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&s"(g3), "=&s"(n3), "=&s"(w3)
-        : "s"(__builtin_amdgcn_kernarg_segment_ptr()),
-          "i"(kArgsAt + offsetof(GemvArgs, wg0) + 12), "i"(kArgsAt + offsetof(GemvArgs, n) + 12),
-          "i"(kArgsAt + offsetof(GemvArgs, wp) + 24));
-    if (b >= g3) {
-      wmat = reinterpret_cast<const uint8_t*>(w3);
-      nrows = n3;
-      wgm = g3;
+  int nrows = n0, tl0 = 0;
+  // balanced runs: the run's first tile in the list and its two-matrix window
+  int t_start = 0;
+  RunWindow win{};
+  int ntiles;
+  if constexpr (!BAL) {
+    // only a fourth matrix waits for the argument block
+    const int g1 = s1, g2 = s2;
+    int wgm = 0;
+    if (b >= g1) { wmat = wp1; nrows = n1; wgm = g1; }
+    if (b >= g2) { wmat = wp2; nrows = n2; wgm = g2; }
+    if (((mtck >> 10) & 7u) == 4u) {
+      // (loaded and waited for in one asm block: loads the compiler sees, it
+      // hoists to the entry, and every launch would then wait for them before its
+      // first weight loads; early-clobber outputs, since the block issues several
+      // loads from the one segment pointer)
+      int g3, n3;
+      uint64_t w3;
+      asm volatile(
+          "s_load_dword %0, %3, %4\n\t"
+          "s_load_dword %1, %3, %5\n\t"
+          "s_load_dwordx2 %2, %3, %6\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&s"(g3), "=&s"(n3), "=&s"(w3)
+          : "s"(__builtin_amdgcn_kernarg_segment_ptr()),
+            "i"(kArgsAt + offsetof(GemvArgs, wg0) + 12),
+            "i"(kArgsAt + offsetof(GemvArgs, n) + 12), "i"(kArgsAt + offsetof(GemvArgs, wp) + 24));
+      if (b >= g3) {
+        wmat = reinterpret_cast<const uint8_t*>(w3);
+        nrows = n3;
+        wgm = g3;
+      }
     }
+    tl0 = (b - wgm) * T;
+    ntiles = min(T, (nrows + 15) / 16 - tl0);
+  } else {
+    const int qt = s1, rt = s2;
+    t_start = b * qt + min(b, rt);
+    ntiles = qt + (b < rt ? 1 : 0);
+    // first tile of matrices 1, 2, 3 (matrices past count have no rows)
+    const int c1 = (n0 + 15) >> 4, c2 = c1 + ((n1 + 15) >> 4), c3 = c2 + ((n2 + 15) >> 4);
+    const uint8_t* wp3 = wp0;
+    int n3 = 0;
+    if (t_start + ntiles > c3) {   // only with a fourth matrix (c3 is else the tile count)
+      uint64_t w3;
+      asm volatile(
+          "s_load_dword %0, %2, %3\n\t"
+          "s_load_dwordx2 %1, %2, %4\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&s"(n3), "=&s"(w3)
+          : "s"(__builtin_amdgcn_kernarg_segment_ptr()),
+            "i"(kArgsAt + offsetof(GemvArgs, n) + 12), "i"(kArgsAt + offsetof(GemvArgs, wp) + 24));
+      wp3 = reinterpret_cast<const uint8_t*>(w3);
+    }
+    // the run covers at most two matrices (launch_gemv makes every matrix at
+    // least a run long)
+    win = run_window(t_start, c1, c2, c3, (uint64_t)wp0, (uint64_t)wp1, (uint64_t)wp2,
+                     (uint64_t)wp3, n0, n1, n2, n3);
   }
   const uint32_t rowb = FMT == kFmtT1 ? 16u * (((uint32_t)K + 79u) / 80u)
                                       : (uint32_t)K >> 2;  // packed bytes per row
-  const int tl0 = (b - wgm) * T;                     // first tile in the matrix
-  const int ntiles = min(T, (nrows + 15) / 16 - tl0);
   // the fused modes stage all of K in one phase (launch_gemv checks it)
   const int kx = XMODE > 0 ? K : min(K, kx_cap<FMT>(M));
   const int phases = XMODE > 0 ? 1 : (K + kx - 1) / kx;
@@ -310,9 +430,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   // Buffer descriptor of local tile tl (wave-uniform; readfirstlane keeps it in
   // scalar registers so the loads need no per-lane legalisation loop).
   auto tile_rsrc = [&](int tl) {
-    const int row0 = (tl0 + tl) * 16;
-    const int rows = max(0, min(16, nrows - row0));
-    const uint64_t base = (uint64_t)(wmat + (size_t)row0 * rowb);
+    int rows;
+    uint64_t base;
+    if constexpr (BAL) {
+      const int gt = __builtin_amdgcn_readfirstlane(t_start + tl);
+      const TileMatrix m = tile_matrix(gt, win);
+      const int row0 = (gt - m.c) * 16;
+      rows = max(0, min(16, m.n - row0));
+      base = m.wq + (uint64_t)row0 * rowb;
+    } else {
+      const int row0 = (tl0 + tl) * 16;
+      rows = max(0, min(16, nrows - row0));
+      base = (uint64_t)(wmat + (size_t)row0 * rowb);
+    }
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
     const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)rows * rowb);
@@ -324,8 +454,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   if (tid < ZB / 4) reinterpret_cast<uint32_t*>(zero)[tid] = 0u;
   // the rest of the arguments and the epilogue's scalars, fetched once the first
   // activation and weight loads are in flight (phase 0 below)
-  Prologue pro{};
+  Prologue pro{};       // per-matrix runs
+  RunPrologue rpro{};   // balanced runs
   float xs_t = 0.0f, gamma = 0.0f;
+  float gamB = 0.0f;    // balanced runs: gamma* of matrix B (gamma: of A)
 
   // token groups: G consecutive threads per token (G = 256 / 2^ceil(log2 M));
   // threads of tokens >= M idle in the per-token passes
@@ -440,13 +572,22 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     }
     carried = false;
     if (p == 0) {
-      pro = load_prologue(a, g1, g2);
       // (buffer loads: the pointers come out of the asm in load_prologue as generic
       // pointers, and generic loads would make the compiler's waits conservative)
+      const float* xsp;
+      if constexpr (BAL) {
+        rpro = load_run_prologue(a, win.jA);
+        xsp = rpro.xs;
+        gamma = __uint_as_float(bload4(make_rsrc(rpro.wsA, 4u), 0u));
+        gamB = __uint_as_float(bload4(make_rsrc(rpro.wsB, 4u), 0u));
+      } else {
+        pro = load_prologue(a, s1, s2);
+        xsp = pro.xs;
+        gamma = __uint_as_float(bload4(make_rsrc(pro.ws, 4u), 0u));
+      }
       if (XMODE == 0)
-        xs_t = __uint_as_float(bload4(make_rsrc(pro.xs, 4u * (uint32_t)M),
+        xs_t = __uint_as_float(bload4(make_rsrc(xsp, 4u * (uint32_t)M),
                                       4u * (uint32_t)min(tid, M - 1)));
-      gamma = __uint_as_float(bload4(make_rsrc(pro.ws, 4u), 0u));
     }
 
     // 2. stage the activations, transposed within each 16-byte group
@@ -693,31 +834,71 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   lds_barrier();
 
   // 4. rescale, store: index = ((tile * M) + token) * 16 + row
-  int32_t* accp = pro.acc;
-  void* yp = pro.y;
-  for (int i = tid; i < ntiles * M * 16; i += kThreads) {
-    const int row = i & 15;
-    const int tt = i >> 4;
-    const int tl = (int)(((uint32_t)tt * (uint32_t)pro.mdiv) >> 16);  // tt / M
-    const int t = tt - tl * M;
-    const int n = (tl0 + tl) * 16 + row;
-    if (n < nrows) {
-      const int accv = part[tl * 256 + row * 16 + t];
-      const float yv = (float)accv * (gamma * dsc[t]);
-      const size_t o = (size_t)t * nrows + n;
-      if (accp) as_global(accp)[o] = accv;
-      if (pro.y_bf16)
-        as_global(reinterpret_cast<uint16_t*>(yp))[o] = float_to_bf16_rne(yv);
-      else
-        as_global(reinterpret_cast<float*>(yp))[o] = yv;
+  if constexpr (!BAL) {
+    int32_t* accp = pro.acc;
+    void* yp = pro.y;
+    for (int i = tid; i < ntiles * M * 16; i += kThreads) {
+      const int row = i & 15;
+      const int tt = i >> 4;
+      const int tl = (int)(((uint32_t)tt * (uint32_t)pro.mdiv) >> 16);  // tt / M
+      const int t = tt - tl * M;
+      const int n = (tl0 + tl) * 16 + row;
+      if (n < nrows) {
+        const int accv = part[tl * 256 + row * 16 + t];
+        const float yv = (float)accv * (gamma * dsc[t]);
+        const size_t o = (size_t)t * nrows + n;
+        if (accp) as_global(accp)[o] = accv;
+        if (pro.y_bf16)
+          as_global(reinterpret_cast<uint16_t*>(yp))[o] = float_to_bf16_rne(yv);
+        else
+          as_global(reinterpret_cast<float*>(yp))[o] = yv;
+      }
+    }
+  } else {
+    // matrix A's part of the run, then B's (tile tl of the run = list tile
+    // t_start + tl; within its matrix, tile t_start + tl - c)
+    const int t_end = t_start + ntiles;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int c = h2 == 0 ? win.cA : win.cB;
+      const int lo = h2 == 0 ? t_start : max(t_start, win.cB);
+      const int hi = h2 == 0 ? min(t_end, win.cB) : t_end;
+      if (lo >= hi) continue;
+      const int nr = h2 == 0 ? win.nA : win.nB;
+      void* yp = h2 == 0 ? rpro.yA : rpro.yB;
+      int32_t* accp = h2 == 0 ? rpro.accA : rpro.accB;
+      const float gm = h2 == 0 ? gamma : gamB;
+      for (int i = tid; i < (hi - lo) * M * 16; i += kThreads) {
+        const int row = i & 15;
+        const int tt = i >> 4;
+        const int tq = (int)(((uint32_t)tt * (uint32_t)rpro.mdiv) >> 16);  // tt / M
+        const int t = tt - tq * M;
+        const int tl = lo - t_start + tq;
+        const int n = (lo - c + tq) * 16 + row;
+        if (n < nr) {
+          const int accv = part[tl * 256 + row * 16 + t];
+          const float yv = (float)accv * (gm * dsc[t]);
+          const size_t o = (size_t)t * nr + n;
+          if (accp) as_global(accp)[o] = accv;
+          if (rpro.y_bf16)
+            as_global(reinterpret_cast<uint16_t*>(yp))[o] = float_to_bf16_rne(yv);
+          else
+            as_global(reinterpret_cast<float*>(yp))[o] = yv;
+        }
+      }
     }
   }
 }
 
 // Kernel for activation mode XMODE, weight format FMT and ring depth 2, 4, 8 or
 // 16 (smallest >= R).
+// (balanced runs come only with more than 256 workgroups, where the ring is at
+// most 4 deep: built for depths 2 and 4)
 template <int XMODE, int FMT, int H>
-const void* ring_kernel(int R) {
+const void* ring_kernel(int R, bool bal) {
+  if (bal)
+    return R <= 2 ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H, true>)
+                  : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, true>);
   if (R <= 2) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H>);
   if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H>);
   if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8, FMT, H>);
@@ -725,17 +906,19 @@ const void* ring_kernel(int R) {
 }
 
 template <int FMT>
-const void* select_kernel(int xmode, int R, bool long_input) {
+const void* select_kernel(int xmode, int R, bool long_input, bool bal) {
   switch (xmode) {
-    case 0: return ring_kernel<0, FMT, kHold>(R);
-    case 1: return long_input ? ring_kernel<1, FMT, kHoldPlain>(R) : ring_kernel<1, FMT, kHold>(R);
-    case 2: return long_input ? ring_kernel<2, FMT, kHoldPlain>(R) : ring_kernel<2, FMT, kHold>(R);
-    case 3: return ring_kernel<3, FMT, kHold>(R);
-    case 4: return ring_kernel<4, FMT, kHold>(R);
-    case 5: return ring_kernel<5, FMT, kHold>(R);
-    case 6: return ring_kernel<6, FMT, kHold>(R);
-    case 7: return ring_kernel<7, FMT, kHold>(R);
-    default: return ring_kernel<8, FMT, kHold>(R);
+    case 0: return ring_kernel<0, FMT, kHold>(R, bal);
+    case 1:
+      return long_input ? ring_kernel<1, FMT, kHoldPlain>(R, bal) : ring_kernel<1, FMT, kHold>(R, bal);
+    case 2:
+      return long_input ? ring_kernel<2, FMT, kHoldPlain>(R, bal) : ring_kernel<2, FMT, kHold>(R, bal);
+    case 3: return ring_kernel<3, FMT, kHold>(R, bal);
+    case 4: return ring_kernel<4, FMT, kHold>(R, bal);
+    case 5: return ring_kernel<5, FMT, kHold>(R, bal);
+    case 6: return ring_kernel<6, FMT, kHold>(R, bal);
+    case 7: return ring_kernel<7, FMT, kHold>(R, bal);
+    default: return ring_kernel<8, FMT, kHold>(R, bal);
   }
 }
 
@@ -794,30 +977,56 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     for (int j = 0; j < a.count; ++j) w += (tiles[j] + t - 1) / t;
     return w;
   };
-  int tpw = 1;
-  if ((int64_t)total_tiles * 16 * row_bytes > kLatencyBytes) {
-    for (int k = kWgsPerCu;; ++k) {
-      tpw = (total_tiles + cus * k - 1) / (cus * k);
-      if (tpw <= kMaxTiles) break;
-    }
-  }
-  const int wgs = count_wgs(tpw);
-  int ring = 4;
-  while (ring < 16 && 2 * ring * 4 * wgs <= kFlightLoads) ring *= 2;
-  // several tiles per workgroup but short rows (at most 6 loads per wave in all,
-  // over more than 256 workgroups): two loads ahead measured faster than four
-  // (2B gate+up, 2560 -> 13824: the chain 5.49 -> 5.34 us per launch); longer
-  // streams lose with it (100B-class stack 16.3 -> 18.0 us)
-  if (wgs > 256 && tpw >= 2 && tpw * per_tile <= 6) ring = 2;
-  if (ring > tpw * per_tile) ring = tpw * per_tile;
   // fused input groups of 16 per thread: held in registers when they are more
   // than kHold (and at most kHoldPlain)
   const int staged = fmt == kFmtT1 ? 5 * ((a.K + 79) / 80) : a.K / 16;
   const int per_thread = (staged + (256 >> ceil_log2_host(a.M)) - 1) / (256 >> ceil_log2_host(a.M));
   const bool long_input = fused && per_thread > kHold;
-  const void* kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, long_input)
-                                     : select_kernel<kFmt2>(xmode, ring, long_input);
-  const size_t lds = (size_t)lds_bytes(tpw, a.M, a.K, fmt);
+  struct Plan {
+    int tpw, wgs;
+    bool bal;
+    const void* kernel;
+    size_t lds;
+  };
+  auto plan = [&](int t, bool bal) {
+    Plan p{t, bal ? (total_tiles + t - 1) / t : count_wgs(t), bal, nullptr, 0};
+    int ring = 4;
+    while (ring < 16 && 2 * ring * 4 * p.wgs <= kFlightLoads) ring *= 2;
+    // several tiles per workgroup but short rows (at most 6 loads per wave in
+    // all, over more than 256 workgroups): two loads ahead measured faster than
+    // four (2B gate+up, 2560 -> 13824: the chain 5.49 -> 5.34 us per launch);
+    // longer streams lose with it (100B-class stack 16.3 -> 18.0 us)
+    if (p.wgs > 256 && t >= 2 && t * per_tile <= 6) ring = 2;
+    if (ring > t * per_tile) ring = t * per_tile;
+    p.kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, long_input, bal)
+                             : select_kernel<kFmt2>(xmode, ring, long_input, bal);
+    p.lds = (size_t)lds_bytes(t, a.M, a.K, fmt);
+    return p;
+  };
+  Plan pl = plan(1, false);
+  if ((int64_t)total_tiles * 16 * row_bytes > kLatencyBytes) {
+    int k = kWgsPerCu;
+    for (;; ++k)
+      if ((total_tiles + cus * k - 1) / (cus * k) <= kMaxTiles) break;
+    const int t = (total_tiles + cus * k - 1) / (cus * k);
+    pl = plan(t, false);
+    // Each matrix's tiles split on their own round up, and can leave more
+    // workgroups than the k per compute unit (three 8192-row matrices in runs of
+    // 3 tiles: 513 workgroups; one compute unit then runs a third after the
+    // others).  Then balanced runs over the list of all the tiles, if every
+    // matrix is at least a run long (a run then covers at most two matrices).
+    // Measured, 100B-class stack (q+k+v = three 8192-row matrices): 6.01 ms per
+    // token with 513 workgroups, 5.99 with 768 runs of 2, 5.93 with balanced runs
+    // for every launch.
+    if (pl.wgs > cus * k && a.count > 1 && (total_tiles + t - 1) / t <= cus * k) {
+      bool runs_fit = true;
+      for (int j = 0; j < a.count; ++j) runs_fit = runs_fit && tiles[j] >= t;
+      if (runs_fit) pl = plan(t, true);
+    }
+  }
+  const int tpw = pl.tpw, wgs = pl.wgs;
+  const void* kernel = pl.kernel;
+  const size_t lds = pl.lds;
   a.tiles_per_wg = tpw;
   a.mdiv = (65536 + a.M - 1) / a.M;  // tt / M == (tt * mdiv) >> 16 for tt < 256, M <= 16
   int w0 = 0;
@@ -831,10 +1040,17 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
   const uint8_t* wp1 = a.count > 1 ? a.wp[1] : a.wp[0];
   const uint8_t* wp2 = a.count > 2 ? a.wp[2] : a.wp[0];
   int n0 = a.n[0], n1 = a.count > 1 ? a.n[1] : 0, n2 = a.count > 2 ? a.n[2] : 0;
-  int g1 = a.wg0[1], g2 = a.wg0[2];
+  for (int j = a.count; j < kMaxGroup; ++j) {   // balanced runs load slot count, never use it
+    a.ws[j] = a.ws[0];
+    a.y[j] = a.y[0];
+    a.acc[j] = a.acc[0];
+  }
+  // per-matrix runs: the first workgroups of matrices 1 and 2; balanced: qt, rt
+  int s1 = pl.bal ? total_tiles / wgs : a.wg0[1];
+  int s2 = pl.bal ? total_tiles % wgs : a.wg0[2];
   uint32_t mtck = (uint32_t)a.M | ((uint32_t)tpw << 5) | ((uint32_t)a.count << 10) |
                   ((uint32_t)a.K << 13);
-  void* args[] = {&xin, &wp0, &wp1, &wp2, &n0, &n1, &n2, &g1, &g2, &mtck, &a};
+  void* args[] = {&xin, &wp0, &wp1, &wp2, &n0, &n1, &n2, &s1, &s2, &mtck, &a};
   return hipLaunchKernel(kernel, dim3((unsigned)wgs), dim3(kThreads), args, lds, s);
 }
 
