@@ -304,7 +304,7 @@ __device__ __forceinline__ void store_group(uint8_t* dst, uint4 v) {
 // library builds this file with kernarg preload): the activations xin, the
 // first three matrices' weights and rows, the split of the tiles over the
 // workgroups (s1, s2: per-matrix runs, the first workgroups of matrices 1 and 2;
-// balanced runs, qt and rt), and mtck = M | T << 5 | count << 10 | K << 13 (T =
+// list runs, L1 | L2 << 8 and h), and mtck = M | T << 5 | count << 10 | K << 13 (T =
 // the most row tiles of a workgroup).  The rest stays in the argument block a,
 // read after the first loads are issued.  Arguments are laid out in order, each
 // at its natural alignment, so the block starts at kArgsAt.
@@ -324,12 +324,11 @@ constexpr int kArgsAt =
 // prologue, kHoldPlain for inputs longer than kHold groups per thread, so that
 // they are read once; else kHold).
 // BAL false: per-matrix runs, each workgroup's tiles belong to one matrix (T
-// tiles, the last run of a matrix shorter).  BAL true: balanced runs, the tiles of
+// tiles, the last run of a matrix shorter).  BAL true: list runs, the tiles of
 // all the launch's matrices form one list, matrix after matrix, and workgroup b
-// takes qt + 1 consecutive tiles if b < rt, else qt (a run may cross into the
-// next matrix); used where rounding each matrix's split up would leave more
-// workgroups than the compute units hold at once (the balanced code's extra
-// scalar work measured 0.1-0.2 us per launch, so it is not the default).
+// takes L1 consecutive tiles if b < h, else L2 (a run may cross into the next
+// matrix); launch_gemv picks the lengths (this code's extra scalar work measured
+// 0.1-0.2 us per launch, so it is not the default).
 template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const uint8_t* wp0,
                                                         const uint8_t* wp1, const uint8_t* wp2,
@@ -390,9 +389,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     tl0 = (b - wgm) * T;
     ntiles = min(T, (nrows + 15) / 16 - tl0);
   } else {
-    const int qt = s1, rt = s2;
-    t_start = b * qt + min(b, rt);
-    ntiles = qt + (b < rt ? 1 : 0);
+    const int L1 = s1 & 255, L2 = s1 >> 8, h = s2;
+    t_start = b < h ? b * L1 : h * L1 + (b - h) * L2;
+    ntiles = b < h ? L1 : L2;
     // first tile of matrices 1, 2, 3 (matrices past count have no rows)
     const int c1 = (n0 + 15) >> 4, c2 = c1 + ((n1 + 15) >> 4), c3 = c2 + ((n2 + 15) >> 4);
     const uint8_t* wp3 = wp0;
@@ -987,9 +986,10 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     bool bal;
     const void* kernel;
     size_t lds;
+    int l1, l2, h;   // list runs: L1 tiles for workgroups b < h, else L2
   };
-  auto plan = [&](int t, bool bal) {
-    Plan p{t, bal ? (total_tiles + t - 1) / t : count_wgs(t), bal, nullptr, 0};
+  auto plan = [&](int t, bool bal, int wgs = 0) {
+    Plan p{t, wgs ? wgs : bal ? (total_tiles + t - 1) / t : count_wgs(t), bal, nullptr, 0, 0, 0, 0};
     int ring = 4;
     while (ring < 16 && 2 * ring * 4 * p.wgs <= kFlightLoads) ring *= 2;
     // several tiles per workgroup but short rows (at most 6 loads per wave in
@@ -1010,18 +1010,39 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
       if ((total_tiles + cus * k - 1) / (cus * k) <= kMaxTiles) break;
     const int t = (total_tiles + cus * k - 1) / (cus * k);
     pl = plan(t, false);
-    // Each matrix's tiles split on their own round up, and can leave more
-    // workgroups than the k per compute unit (three 8192-row matrices in runs of
-    // 3 tiles: 513 workgroups; one compute unit then runs a third after the
-    // others).  Then balanced runs over the list of all the tiles, if every
-    // matrix is at least a run long (a run then covers at most two matrices).
-    // Measured, 100B-class stack (q+k+v = three 8192-row matrices): 6.01 ms per
-    // token with 513 workgroups, 5.99 with 768 runs of 2, 5.93 with balanced runs
-    // for every launch.
-    if (pl.wgs > cus * k && a.count > 1 && (total_tiles + t - 1) / t <= cus * k) {
-      bool runs_fit = true;
-      for (int j = 0; j < a.count; ++j) runs_fit = runs_fit && tiles[j] >= t;
-      if (runs_fit) pl = plan(t, true);
+    // List runs (the tiles of all the matrices as one list, a run may cross into
+    // the next matrix; every matrix at least a run long, so that a run covers at
+    // most two) in two cases, measured on the 100B-class stack:
+    //  * with the two workgroups per compute unit, the one dispatched first (b <
+    //    cus) streams faster (its waves are the older ones), and the other then
+    //    runs alone: when the tiles come to S = total / cus per compute unit,
+    //    S >= 5, the first takes L1 = S / 2 + 1 (rounded down) and the second the
+    //    rest (q+k+v, three 8192-row matrices: 4 + 2 tiles, 12.5 -> 12.2 us;
+    //    gate+up, two 28672-row matrices: 8 + 6, 24.0 -> 23.3 us, where 9 + 5
+    //    and the equal split were slower; the 8B-class gate+up, two 14336-row
+    //    matrices, 4 + 3 in 512 workgroups instead of 448 runs of 4: 8B-class
+    //    stack 0.921 -> 0.897 ms per token);
+    //  * else, where each matrix's split rounded up needs more workgroups than
+    //    the compute units hold two at a time (three 8192-row matrices in runs of
+    //    3: 513), runs of qt + 1 for the first rt workgroups and qt for the rest
+    //    (6.01 -> 5.91 ms per 100B-class token).
+    auto runs_fit = [&](int len) {
+      for (int j = 0; j < a.count; ++j)
+        if (tiles[j] < len) return false;
+      return true;
+    };
+    const int S = total_tiles % cus == 0 ? total_tiles / cus : 0;
+    if (k == kWgsPerCu && S >= 5 && S / 2 + 1 <= kMaxTiles && runs_fit(S / 2 + 1)) {
+      pl = plan(S / 2 + 1, true, 2 * cus);
+      pl.l1 = S / 2 + 1;
+      pl.l2 = S - pl.l1;
+      pl.h = cus;
+    } else if (pl.wgs > cus * k && a.count > 1 && (total_tiles + t - 1) / t <= cus * k &&
+               runs_fit(t)) {
+      pl = plan(t, true);
+      pl.l2 = total_tiles / pl.wgs;
+      pl.l1 = pl.l2 + 1;
+      pl.h = total_tiles % pl.wgs;
     }
   }
   const int tpw = pl.tpw, wgs = pl.wgs;
@@ -1045,9 +1066,10 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     a.y[j] = a.y[0];
     a.acc[j] = a.acc[0];
   }
-  // per-matrix runs: the first workgroups of matrices 1 and 2; balanced: qt, rt
-  int s1 = pl.bal ? total_tiles / wgs : a.wg0[1];
-  int s2 = pl.bal ? total_tiles % wgs : a.wg0[2];
+  // per-matrix runs: the first workgroups of matrices 1 and 2; list runs:
+  // L1 | L2 << 8 and h
+  int s1 = pl.bal ? pl.l1 | (pl.l2 << 8) : a.wg0[1];
+  int s2 = pl.bal ? pl.h : a.wg0[2];
   uint32_t mtck = (uint32_t)a.M | ((uint32_t)tpw << 5) | ((uint32_t)a.count << 10) |
                   ((uint32_t)a.K << 13);
   void* args[] = {&xin, &wp0, &wp1, &wp2, &n0, &n1, &n2, &s1, &s2, &mtck, &a};
