@@ -977,10 +977,12 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     return w;
   };
   // fused input groups of 16 per thread: held in registers when they are more
-  // than kHold (and at most kHoldPlain)
+  // than kHold + 1 (and at most kHoldPlain); with kHold + 1, two are held and
+  // the third read twice, cheaper than issuing kHoldPlain hold loads (T1 input
+  // of 8192: 515 groups; 100B-class T1 stack 8.28 -> 7.87 ms per token)
   const int staged = fmt == kFmtT1 ? 5 * ((a.K + 79) / 80) : a.K / 16;
   const int per_thread = (staged + (256 >> ceil_log2_host(a.M)) - 1) / (256 >> ceil_log2_host(a.M));
-  const bool long_input = fused && per_thread > kHold;
+  const bool long_input = fused && per_thread > kHold + 1;
   struct Plan {
     int tpw, wgs;
     bool bal;

@@ -379,6 +379,7 @@ def test_ternary_linear_multi(m, k, ns):
                                        (1, 2560, (6912, 6912), "bf16"),
                                        (3, 512, (100, 37, 16, 64, 200), "f32"),
                                        (1, 28672, (40, 24), "f32"), (8, 256, (16, 20), "f32"),
+                                       (1, 10240, (40, 24), "f32"), (1, 12288, (17,), "bf16"),
                                        (600, 256, (300, 100, 700), "bf16")])
 def test_quant_linear_multi(m, k, ns, dt):
     mats = _group(ns, k, 950)

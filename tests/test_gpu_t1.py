@@ -84,7 +84,9 @@ def test_ternary_linear_t1(m, k, ns, ydt):
 @pytest.mark.parametrize("m,k,ns,dt,glu,norm", [
     (1, 2560, (2560, 640, 640), "bf16", False, False), (1, 6912, (2560,), "bf16", True, True),
     (2, 2560, (6912, 6912), "f32", False, True), (3, 100 * 16, (48,), "f32", True, False),
-    (5, 256, (64, 33), "bf16", True, True), (4, 28672, (40,), "f32", False, False)])
+    (5, 256, (64, 33), "bf16", True, True), (4, 28672, (40,), "f32", False, False),
+    # three input groups per thread at M = 1: two held, the third read again
+    (1, 8192, (48, 20), "f32", False, False), (1, 8192, (33,), "bf16", False, False)])
 def test_quant_linear_t1(m, k, ns, dt, glu, norm):
     mats = _t1_mats(ns, k, 1300 + m + k)
     xt, x = acts(m, k, 1400 + k, dt)
