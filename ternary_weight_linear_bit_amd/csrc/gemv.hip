@@ -999,6 +999,10 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     // four (2B gate+up, 2560 -> 13824: the chain 5.49 -> 5.34 us per launch);
     // longer streams lose with it (100B-class stack 16.3 -> 18.0 us)
     if (p.wgs > 256 && t >= 2 && t * per_tile <= 6) ring = 2;
+    // T1 weights: two loads ahead on every launch (its decode keeps each load's
+    // registers longer; 2B T1 stack 0.668 -> 0.647 ms per token, 100B-class
+    // 7.86 -> 7.78 ms; 8 and 16 slower)
+    if (fmt == kFmtT1) ring = 2;
     if (ring > t * per_tile) ring = t * per_tile;
     p.kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, long_input, bal)
                              : select_kernel<kFmt2>(xmode, ring, long_input, bal);
