@@ -368,15 +368,17 @@ bitnet_status bitnet_ternary_linear_lut(const uint8_t *w_packed, const float *w_
  * implementation, for callers and tests that need to know which kernel variant a
  * call uses): the tile of the prefill kernel (M > 16 tokens, K % 64 == 0) that
  * bitnet_ternary_linear_multi uses for M tokens over `count` matrices of N[j]
- * rows on the current device: *tokens_per_tile x *rows_per_tile per workgroup
- * (256 x 256, 128 x 256, 128 x 128 or 64 x 128).  If *first_launch_tokens > 0,
- * the first *first_launch_tokens tokens run as one launch with that tile and the
- * remaining tokens as a second launch with the tile this query returns for them.
- * Does not depend on K.  M in 1..2^31-1, count in 1..4, N[j] >= 1; asks the HIP
- * runtime for the compute unit count (1 if it cannot say).
+ * rows and inputs of K on the current device: *tokens_per_tile x *rows_per_tile
+ * per workgroup (256 x 256, 128 x 256, 128 x 128 or 64 x 128).  If
+ * *first_launch_tokens > 0, the first *first_launch_tokens tokens run as one
+ * launch with that tile and the remaining tokens as a second launch with the
+ * tile this query returns for them.  M in 1..2^31-1, count in 1..4, N[j] >= 1,
+ * K >= 1 (BITNET_ERR_SHAPE otherwise); asks the HIP runtime for the compute
+ * unit count (1 if it cannot say).
  */
-bitnet_status bitnet_prefill_tile(int64_t M, const int64_t *N, int count, int *tokens_per_tile,
-                                  int *rows_per_tile, int64_t *first_launch_tokens);
+bitnet_status bitnet_prefill_tile(int64_t M, const int64_t *N, int count, int64_t K,
+                                  int *tokens_per_tile, int *rows_per_tile,
+                                  int64_t *first_launch_tokens);
 
 /*
  * Decode chain: a sequence of fused act-quant + ternary linear stages (each one

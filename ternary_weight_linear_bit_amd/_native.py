@@ -551,7 +551,7 @@ class BitnetChain(ctypes.Structure):
                 ("ring", ctypes.c_int)]
 
 
-SIGNATURES["bitnet_prefill_tile"] = (_I, [_I64, ctypes.POINTER(_I64), _I,
+SIGNATURES["bitnet_prefill_tile"] = (_I, [_I64, ctypes.POINTER(_I64), _I, _I64,
                                           ctypes.POINTER(_I), ctypes.POINTER(_I),
                                           ctypes.POINTER(_I64)])
 SIGNATURES["bitnet_chain_plan_bytes"] = (_SZ, [_I])
@@ -616,11 +616,11 @@ def bitnet_chain_error(chain) -> int:
     return e.value
 
 
-def bitnet_prefill_tile(m, ns):
+def bitnet_prefill_tile(m, ns, k):
     """(tokens per tile, rows per tile, first launch tokens) of the prefill kernel for
-    M tokens over matrices with ns rows (bitnet_prefill_tile)."""
+    M tokens over matrices with ns rows and inputs of K (bitnet_prefill_tile)."""
     arr = (ctypes.c_int64 * len(ns))(*ns)
     bm, bn, first = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int64(0)
-    _check("bitnet_prefill_tile", lib().bitnet_prefill_tile(m, arr, len(ns), ctypes.byref(bm),
+    _check("bitnet_prefill_tile", lib().bitnet_prefill_tile(m, arr, len(ns), k, ctypes.byref(bm),
                                                             ctypes.byref(bn), ctypes.byref(first)))
     return bm.value, bn.value, first.value

@@ -495,16 +495,18 @@ bitnet_status bitnet_quant_linear(const uint8_t* w_packed, const float* w_scale,
   return bitnet_quant_linear_multi(&m, 1, x, x_dtype, M, K, x_q, x_scale, y_dtype, stream);
 }
 
-bitnet_status bitnet_prefill_tile(int64_t M, const int64_t* N, int count, int* tokens_per_tile,
-                                 int* rows_per_tile, int64_t* first_launch_tokens) {
+bitnet_status bitnet_prefill_tile(int64_t M, const int64_t* N, int count, int64_t K,
+                                 int* tokens_per_tile, int* rows_per_tile,
+                                 int64_t* first_launch_tokens) {
   if (!N || !tokens_per_tile || !rows_per_tile || !first_launch_tokens) return BITNET_ERR_NULL;
-  if (M < 1 || M > kInt32Max || count < 1 || count > bitnet::kMaxGroup) return BITNET_ERR_SHAPE;
+  if (M < 1 || M > kInt32Max || count < 1 || count > bitnet::kMaxGroup || K < 1)
+    return BITNET_ERR_SHAPE;
   int n[bitnet::kMaxGroup] = {0, 0, 0, 0};
   for (int j = 0; j < count; ++j) {
     if (N[j] < 1 || N[j] > kInt32Max) return BITNET_ERR_SHAPE;
     n[j] = (int)N[j];
   }
-  const bitnet::GemmPlan p = bitnet::gemm_plan(M, n, count, bitnet::device_cus());
+  const bitnet::GemmPlan p = bitnet::gemm_plan(M, n, count, K, bitnet::device_cus());
   *tokens_per_tile = p.bm;
   *rows_per_tile = p.bn;
   *first_launch_tokens = p.first_tokens;

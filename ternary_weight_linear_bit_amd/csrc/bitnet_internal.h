@@ -470,7 +470,7 @@ struct GemmPlan {
   int bm, bn;
   int64_t first_tokens;
 };
-GemmPlan gemm_plan(int64_t M, const int* n, int count, int cus);
+GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus);
 // Lookup-table decode: workspace bytes (tables 16 K + accumulators 4 N, each
 // rounded up to 256) and the launches (three per token).  K % 64 == 0, 16-byte
 // aligned packed weights and workspace.

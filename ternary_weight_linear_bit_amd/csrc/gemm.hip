@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 
 }  // namespace
 
-GemmPlan gemm_plan(int64_t M, const int* n, int count, int cus) {
+GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
   // Four tile shapes:
   //  * 256 tokens x 256 rows (8 waves of 128 x 64; one workgroup per compute
   //    unit, two waves per SIMD): a wave's weight expansion serves twice the
@@ -457,7 +457,10 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int cus) {
   //    instructions per matrix instruction instead of 8 (vector and matrix
   //    instructions of one SIMD largely take turns, so this is the main cost
   //    besides the products).  Chosen when its tiles fill at least 80% of the
-  //    compute units over the launch's rounds;
+  //    compute units over the launch's rounds, or, at K >= 4096, at least 60%
+  //    of them in a single round (its cheaper steps then outweigh the idle
+  //    units: 2B down at 4096 tokens, 6912 -> 2560, 82 -> 76 us; 8B q+k+v at
+  //    2048 tokens 54 -> 52 us; at K = 2560 the 2B o projection was slower);
   //  * 128 x 256 (8 waves of 64 x 64; one per compute unit), when its tiles fill
   //    80-100% of one round (from 90%: 2B gate+up at M = 512 went to these tiles,
   //    the layer 100.7 -> 98.7 us);
@@ -478,7 +481,8 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int cus) {
   };
   const int64_t big_tiles = ((M + 255) / 256) * row_tiles(256);
   const int64_t big_rounds = (big_tiles + cus - 1) / cus;
-  const bool big = big_tiles > 0 && 5 * big_tiles >= 4 * big_rounds * (int64_t)cus;
+  const bool big = big_tiles > 0 && (5 * big_tiles >= 4 * big_rounds * (int64_t)cus ||
+                                     (K >= 4096 && big_rounds == 1 && 5 * big_tiles >= 3 * (int64_t)cus));
   // A last round of 256 x 256 tiles that fills under 40% of the compute units
   // idles most of the chip for a whole tile time: the token tiles that fit in the
   // full rounds run as one launch, and the remaining tokens as a second launch
@@ -498,7 +502,7 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int cus) {
 
 hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (a.K % 64 != 0 || a.count < 1 || a.count > kMaxGroup) return hipErrorInvalidValue;
-  const GemmPlan pl = gemm_plan(a.M, a.n, a.count, device_cus());
+  const GemmPlan pl = gemm_plan(a.M, a.n, a.count, a.K, device_cus());
   if (pl.first_tokens > 0 && pl.first_tokens < a.M) {
     const int64_t m1 = pl.first_tokens;
     GemmArgs rest = a;

@@ -25,6 +25,8 @@ pytestmark = pytest.mark.gpu
 CASES = {
     # name: (M, rows of each matrix, K, tile expected on 256 CUs, first launch tokens)
     "256x256": (4096, (4096,), 2560, (256, 256), 0),
+    # one round of 256 x 256 tiles filling 60% of the compute units, taken at K >= 4096
+    "256x256 one round": (2816, (3584,), 4096, (256, 256), 0),
     "128x256": (512, (6912, 6912), 2560, (128, 256), 0),
     "128x128": (1536, (6912,), 2560, (128, 128), 0),
     "64x128": (512, (2560,), 6912, (64, 128), 0),
@@ -43,12 +45,12 @@ def _gpu():
 def test_prefill_long_k_every_output(name):
     m, ns, k, tile, first = CASES[name]
     print(f"prefill long-K case {name}: M={m} N={ns} K={k}", flush=True)
-    bm, bn, f = N.bitnet_prefill_tile(m, ns)
+    bm, bn, f = N.bitnet_prefill_tile(m, ns, k)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert (bm, bn, f) == (*tile, first), (name, bm, bn, f)
         if first:
             # the rest of the tokens: a second launch with its own tile
-            assert N.bitnet_prefill_tile(m - first, ns) == (128, 256, 0)
+            assert N.bitnet_prefill_tile(m - first, ns, k) == (128, 256, 0)
     xt, x = acts(m, k, 90 + m, "f32")
     xq_t, xs_t = N.bitnet_quantize_acts(xt)
     want_q, want_d = O.quantize_acts(x)
