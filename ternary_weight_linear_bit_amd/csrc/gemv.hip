@@ -329,6 +329,11 @@ constexpr int kArgsAt =
 // takes L1 consecutive tiles if b < h, else L2 (a run may cross into the next
 // matrix); launch_gemv picks the lengths (this code's extra scalar work measured
 // 0.1-0.2 us per launch, so it is not the default).
+// With a prologue (PRO) the weights are loaded non-temporal: they are read once,
+// and the loads then leave the prologue's inputs (the up projection, the norm
+// weight) in L2 for the other workgroups (2B stack with the fused norms and
+// gating 0.821 -> 0.778 ms per token; without a prologue the same loads lost 2%
+// on the 100B-class stack and nothing was gained on the 2B one).
 template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const uint8_t* wp0,
                                                         const uint8_t* wp1, const uint8_t* wp2,
@@ -487,9 +492,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   };
   auto next_load = [&]() -> uint4 {
     const int c = 4 * (wave + 4 * jp) + g;
-    const uint4 v = bload16(rs, (tp < ntiles && c < Cp)
-                                    ? (uint32_t)r * rowb + kb0p + 16u * (uint32_t)c
-                                    : kOob);
+    const uint32_t off = (tp < ntiles && c < Cp) ? (uint32_t)r * rowb + kb0p + 16u * (uint32_t)c
+                                                 : kOob;
+    const uint4 v = PRO ? bload16_nt(rs, off) : bload16(rs, off);
     if (++jp == Jp) {
       jp = 0;
       ++tp;
@@ -909,9 +914,11 @@ const void* select_kernel(int xmode, int R, bool long_input, bool bal) {
   switch (xmode) {
     case 0: return ring_kernel<0, FMT, kHold>(R, bal);
     case 1:
-      return long_input ? ring_kernel<1, FMT, kHoldPlain>(R, bal) : ring_kernel<1, FMT, kHold>(R, bal);
+      return long_input ? ring_kernel<1, FMT, kHoldPlain>(R, bal)
+                        : ring_kernel<1, FMT, kHold>(R, bal);
     case 2:
-      return long_input ? ring_kernel<2, FMT, kHoldPlain>(R, bal) : ring_kernel<2, FMT, kHold>(R, bal);
+      return long_input ? ring_kernel<2, FMT, kHoldPlain>(R, bal)
+                        : ring_kernel<2, FMT, kHold>(R, bal);
     case 3: return ring_kernel<3, FMT, kHold>(R, bal);
     case 4: return ring_kernel<4, FMT, kHold>(R, bal);
     case 5: return ring_kernel<5, FMT, kHold>(R, bal);
@@ -990,6 +997,8 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     size_t lds;
     int l1, l2, h;   // list runs: L1 tiles for workgroups b < h, else L2
   };
+  // latency regime: at most kLatencyBytes of packed weights
+  const bool latency = (int64_t)total_tiles * 16 * row_bytes <= kLatencyBytes;
   auto plan = [&](int t, bool bal, int wgs = 0) {
     Plan p{t, wgs ? wgs : bal ? (total_tiles + t - 1) / t : count_wgs(t), bal, nullptr, 0, 0, 0, 0};
     int ring = 4;
@@ -1010,7 +1019,7 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     return p;
   };
   Plan pl = plan(1, false);
-  if ((int64_t)total_tiles * 16 * row_bytes > kLatencyBytes) {
+  if (!latency) {
     int k = kWgsPerCu;
     for (;; ++k)
       if ((total_tiles + cus * k - 1) / (cus * k) <= kMaxTiles) break;
