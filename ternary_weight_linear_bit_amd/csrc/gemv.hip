@@ -9,9 +9,13 @@
 // the int8 value q in registers, so the matrix cores contract q with x directly.
 //
 // Design for gfx950 (the pages' kernels are CPU SIMD and lookup-table code):
-//  * Workgroup = 4 waves; it owns T consecutive 16-row tiles of one matrix (of up
-//    to kMaxGroup matrices that share the activations).  T = 1 for small launches;
-//    large ones spread equal tile counts over two workgroups per CU.  K is cut into
+//  * Workgroup = 4 waves; it owns a run of consecutive 16-row tiles (of up to
+//    kMaxGroup matrices that share the activations).  One tile per workgroup for
+//    small launches; large ones spread the tiles over two workgroups per CU, each
+//    matrix split on its own or, for some launches, all matrices' tiles as one
+//    list in runs that may cross into the next matrix (launch_gemv: balanced
+//    runs, or skewed runs where the first-dispatched workgroup of each CU takes
+//    more).  K is cut into
 //    256-k super-chunks; wave w takes super-chunks w, w + 4, ..., so one wave load
 //    instruction covers 16 rows x 64 contiguous bytes and the four waves read 256
 //    contiguous bytes of each row per step.
@@ -36,8 +40,10 @@
 // M <= kMaxFusedM, one phase): the workgroup quantises the activations with the
 // same arithmetic as the standalone kernel while staging them (one read of the
 // input: each thread's first groups of 16, eight without a prologue and two with
-// one, stay in registers between the absmax and the quantise pass), and
-// workgroup 0 also writes x_q and x_scale.
+// one, stay in registers between the absmax and the quantise pass; more than
+// three groups per thread without a prologue take the eight-group variant), and
+// workgroup 0 also writes x_q and x_scale.  With a prologue the weight loads are
+// non-temporal, so that the prologue's inputs stay in L2.
 // XMODE 3-8 add the layer's input prologue (communeify.com page on BitNet b1.58
 // 2B4T, architecture item: squared-ReLU activation, subln norm, no biases): the
 // input may be the gate projection, gated as RN32(RN32(relu(x)^2) * up), and / or
