@@ -127,7 +127,11 @@ __device__ __forceinline__ void store_tile_impl(void* y, const v16i (&acc)[BM / 
       if (m < M) {
         char* dst = static_cast<char*>(y) + ((size_t)m * N + n) * E;
         if (n + 16 / E <= N) {
-          *reinterpret_cast<uint4*>(dst) = val;
+          // (non-temporal: the outputs are not read again by this launch, and
+          // leaving L2 to the weight and activation tiles measured 1-2% faster)
+          typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+          __builtin_nontemporal_store(*reinterpret_cast<const u4v*>(&val),
+                                      reinterpret_cast<u4v*>(dst));
         } else {
           const uint32_t w[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
