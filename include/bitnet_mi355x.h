@@ -369,7 +369,7 @@ bitnet_status bitnet_ternary_linear_lut(const uint8_t *w_packed, const float *w_
  * call uses): the tile of the prefill kernel (M > 16 tokens, K % 64 == 0) that
  * bitnet_ternary_linear_multi uses for M tokens over `count` matrices of N[j]
  * rows and inputs of K on the current device: *tokens_per_tile x *rows_per_tile
- * per workgroup (256 x 256, 128 x 256, 128 x 128 or 64 x 128).  If
+ * per workgroup (256 x 256, 192 x 256, 128 x 256, 128 x 128 or 64 x 128).  If
  * *first_launch_tokens > 0, the first *first_launch_tokens tokens run as one
  * launch with that tile and the remaining tokens as a second launch with the
  * tile this query returns for them.  M in 1..2^31-1, count in 1..4, N[j] >= 1,

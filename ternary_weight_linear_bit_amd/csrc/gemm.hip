@@ -46,6 +46,10 @@ __device__ __forceinline__ int lds_group(int t, int kg) {
   return t * kStride + 16 * (kg ^ (t & 7));
 }
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, each with its own L2
+#ifndef BITNET_TALL_TILES
+#define BITNET_TALL_TILES 1
+#endif
+constexpr bool kTallTiles = BITNET_TALL_TILES;   // 192 x 256 tiles in the planner
 constexpr int kDepth = 2;         // steps of global loads in flight (default)
 
 // Packed dword (16 codes) -> the codes c = q + 1 in {0, 1, 2} as an int8 operand
@@ -310,8 +314,12 @@ __global__ __launch_bounds__(128 * WN, LAYOUT == 1 ? 2 : 1) void gemm_kernel(
 #pragma unroll
         for (int i = 0; i < TB; ++i) an[i] = aread(cur, i, j + 1);
       }
-      static_assert(4 % XG == 0, "staged groups spread over the k-slices");
-      if (j % (4 / XG) == 0) stage(xv[j / (4 / XG)], j / (4 / XG), nxt);
+      static_assert(XG == 3 || 4 % XG == 0, "staged groups spread over the k-slices");
+      if constexpr (XG == 3) {
+        if (j < 3) stage(xv[j], j, nxt);
+      } else if (j % (4 / XG) == 0) {
+        stage(xv[j / (4 / XG)], j / (4 / XG), nxt);
+      }
       if (j == 3) {
         // every use of xv and wv is above this point (the asm takes the last
         // expansion and the token sums), so the refills below reuse their
@@ -454,7 +462,7 @@ __global__ __launch_bounds__(256) void generic_linear_kernel(
 }  // namespace
 
 GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
-  // Four tile shapes:
+  // Five tile shapes:
   //  * 256 tokens x 256 rows (8 waves of 128 x 64; one workgroup per compute
   //    unit, two waves per SIMD): a wave's weight expansion serves twice the
   //    tokens and the staging of the activations twice the rows, about 5 vector
@@ -465,6 +473,12 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
   //    of them in a single round (its cheaper steps then outweigh the idle
   //    units: 2B down at 4096 tokens, 6912 -> 2560, 82 -> 76 us; 8B q+k+v at
   //    2048 tokens 54 -> 52 us; at K = 2560 the 2B o projection was slower);
+  //  * 192 x 256 (8 waves of 96 x 64, three 32-token blocks each) when they run
+  //    in a single round filling at least 80% of the compute units and 256 x 256
+  //    tiles fill less than 80% (2B o and down projections at 4096 tokens: 160
+  //    tiles of 256 x 256 on 256 compute units, 220 of 192 x 256: 35.9 -> 29.9 us
+  //    and 78.9 -> 66 us; the per-step work is 3/4, the weight loads and their
+  //    expansion the same);
   //  * 128 x 256 (8 waves of 64 x 64; one per compute unit), when its tiles fill
   //    80-100% of one round (from 90%: 2B gate+up at M = 512 went to these tiles,
   //    the layer 100.7 -> 98.7 us);
@@ -485,8 +499,13 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
   };
   const int64_t big_tiles = ((M + 255) / 256) * row_tiles(256);
   const int64_t big_rounds = (big_tiles + cus - 1) / cus;
-  const bool big = big_tiles > 0 && (5 * big_tiles >= 4 * big_rounds * (int64_t)cus ||
-                                     (K >= 4096 && big_rounds == 1 && 5 * big_tiles >= 3 * (int64_t)cus));
+  const bool big_full = big_tiles > 0 && 5 * big_tiles >= 4 * big_rounds * (int64_t)cus;
+  // 192 x 256 tiles in a single round filling at least 80% of the compute units,
+  // where 256 x 256 tiles fill less
+  const int64_t tall_tiles = ((M + 191) / 192) * row_tiles(256);
+  const bool tall = kTallTiles && !big_full && tall_tiles <= cus && 5 * tall_tiles >= 4 * (int64_t)cus;
+  const bool big = !tall && big_tiles > 0 &&
+                   (big_full || (K >= 4096 && big_rounds == 1 && 5 * big_tiles >= 3 * (int64_t)cus));
   // A last round of 256 x 256 tiles that fills under 40% of the compute units
   // idles most of the chip for a whole tile time: the token tiles that fit in the
   // full rounds run as one launch, and the remaining tokens as a second launch
@@ -497,10 +516,10 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
   }
   const int64_t mt = (M + 127) / 128;
   const int64_t rows4 = row_tiles(256);
-  const bool wide = !big && rows4 * mt <= cus && 10 * rows4 * mt >= 8 * (int64_t)cus;
-  const bool small = !big && !wide && mt * row_tiles(128) <= cus;
-  p.bm = big ? 256 : small ? 64 : 128;
-  p.bn = big || wide ? 256 : 128;
+  const bool wide = !big && !tall && rows4 * mt <= cus && 10 * rows4 * mt >= 8 * (int64_t)cus;
+  const bool small = !big && !tall && !wide && mt * row_tiles(128) <= cus;
+  p.bm = tall ? 192 : big ? 256 : small ? 64 : 128;
+  p.bn = big || wide || tall ? 256 : 128;
   return p;
 }
 
@@ -523,7 +542,7 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
     return e != hipSuccess ? e : launch_gemm(rest, s);
   }
   const int bm = pl.bm, bn = pl.bn;
-  const bool big = bm == 256, small = bm == 64, wide = bm == 128 && bn == 256;
+  const bool big = bm == 256, small = bm == 64, wide = bm == 128 && bn == 256, tall = bm == 192;
   int64_t nbt = 0;
   for (int j = 0; j < kMaxGroup; ++j) {
     a.nb0[j] = (int)nbt;
@@ -538,6 +557,8 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (a.layout == 1) {
     if (big)
       hipLaunchKernelGGL((gemm_kernel<256, 4, kDepth, 1>), grid, dim3(512), 0, s, a);
+    else if (tall)
+      hipLaunchKernelGGL((gemm_kernel<192, 4, kDepth, 1>), grid, dim3(512), 0, s, a);
     else if (small)
       hipLaunchKernelGGL((gemm_kernel<64, 2, 4, 1>), grid, dim3(256), 0, s, a);
     else if (wide)
@@ -547,6 +568,8 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   } else {
     if (big)
       hipLaunchKernelGGL((gemm_kernel<256, 4, kDepth, 0>), grid, dim3(512), 0, s, a);
+    else if (tall)
+      hipLaunchKernelGGL((gemm_kernel<192, 4, kDepth, 0>), grid, dim3(512), 0, s, a);
     else if (small)
       hipLaunchKernelGGL((gemm_kernel<64, 2, 4, 0>), grid, dim3(256), 0, s, a);
     else if (wide)

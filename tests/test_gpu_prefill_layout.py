@@ -43,6 +43,7 @@ CASES = [
     (300, (257,), 192), (513, (640,), 512), (1000, (5000,), 192), (2000, (4000,), 64),
     (1920, (3900,), 320), (2000, (6600,), 64), (1100, (10400,), 192),
     (4096, (2560, 640, 640), 2560), (512, (6912, 6912), 2560), (256, (2560,), 6912),
+    (4000, (2500,), 192),
 ]
 
 

@@ -1,7 +1,7 @@
 """Prefill kernel at long K, every tile shape, every output compared.
 
-For each of the prefill kernel's tile shapes (256 x 256, 128 x 256, 128 x 128,
-64 x 128 tokens x rows) and for the split launch (the tokens that fill whole
+For each of the prefill kernel's tile shapes (256 x 256, 192 x 256, 128 x 256,
+128 x 128, 64 x 128 tokens x rows) and for the split launch (the tokens that fill whole
 rounds of 256 x 256 tiles, then the rest with their own tile), one shape at
 K >= 2560 (at least 20 steps of 128 k, so the loads issued ahead run in their
 steady state), with the tile the library picks asserted on a 256-CU MI355X, and
@@ -25,10 +25,14 @@ pytestmark = pytest.mark.gpu
 CASES = {
     # name: (M, rows of each matrix, K, tile expected on 256 CUs, first launch tokens)
     "256x256": (4096, (4096,), 2560, (256, 256), 0),
-    # one round of 256 x 256 tiles filling 60% of the compute units, taken at K >= 4096
-    "256x256 one round": (2816, (3584,), 4096, (256, 256), 0),
+    # one round of 256 x 256 tiles filling 75% of the compute units, taken at K >= 4096
+    # (192 x 256 tiles would need a second round)
+    "256x256 one round": (2048, (4096, 1024, 1024), 4096, (256, 256), 0),
+    # one round of 192 x 256 tiles (210 of 256 compute units; the last token tile
+    # holds 160 tokens)
+    "192x256": (4000, (2560,), 2560, (192, 256), 0),
     "128x256": (512, (6912, 6912), 2560, (128, 256), 0),
-    "128x128": (1536, (6912,), 2560, (128, 128), 0),
+    "128x128": (1280, (6912,), 2560, (128, 128), 0),
     "64x128": (512, (2560,), 6912, (64, 128), 0),
     "split": (4096, (6912, 6912), 2560, (256, 256), 3584),
 }
