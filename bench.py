@@ -3,7 +3,7 @@
 
 Default workload (`ternary100b-decode-m1-96L`): the ~100B-class ternary decode
 stack, one token (M = 1) streamed through 96 layers of {q, k, v, o: 8192->8192,
-gate, up: 8192->28672, down: 28672->8192} with fp32 activations between layers
+gate, up: 8192->28672, down: 28672->8192} with bf16 activations between layers
 and the per-token int8 activation quantisation fused into every layer (23.35 GB
 of packed weights per token, resident in HBM).  Chain per layer: q, k, v from
 the layer input (one launch); o from q (attention is out of scope); gate and up
@@ -24,7 +24,8 @@ kernel's int8 TOPS on the 2B shapes at M = 512 and 4096 and on the 8B shapes at
 M = 2048 (with its own roofline block), single matrices at M = 1 through the
 matrix-core kernel, T1 and the lookup-table path, the standalone quantisers
 against HBM, and the CPU oracle timed on bounded samples of the decode and
-prefill workloads (one core and all cores).
+prefill workloads (one core and all cores); the 100B-class stack again with fp32
+activations between layers.
 """
 
 from __future__ import annotations
@@ -50,9 +51,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def recorded_traffic(profile="gemv_100b_decode_stack.md"):
+def recorded_traffic(profile="gemv_100b_decode_stack.md", workload=None):
     """HBM bytes per decode launch from the committed PMC summary, or None when the
-    decode kernel's sources differ from the ones the counters were taken on."""
+    decode kernel's sources differ from the ones the counters were taken on, or the
+    record names another workload than `workload`."""
     import hashlib
     path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
@@ -64,6 +66,9 @@ def recorded_traffic(profile="gemv_100b_decode_stack.md"):
                 data = open(os.path.join(csrc, name), "rb").read()
                 if hashlib.sha256(data).hexdigest() != digest:
                     return None
+            wl = re.search(r"workload=(\S+)", line)
+            if workload is not None and wl is not None and wl.group(1) != workload:
+                return None
             return int(re.search(r"bytes_per_launch=(\d+)", line).group(1))
     return None
 
@@ -803,7 +808,7 @@ def main():
         "tokens_per_s": round(1e3 / d["ms"], 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(),
+                     "traffic": recorded_traffic(workload=args.workload),
                      "kernel": "gemv_kernel (decode, fused int8 activation quantisation)",
                      "avg_launch_us": round(avg_launch * 1e6, 3),
                      "avg_bytes_per_launch": int(avg_bytes),
@@ -815,13 +820,18 @@ def main():
         d2 = decode_leg(torch, N, I, two_b, args.steps, args.warmup)
         result["decode_2b"] = dict(workload=two_b, **leg_summary(d2, 1),
                                    traffic_per_launch=recorded_traffic(
-                                       "gemv_bitnet2b_decode_chain.md"))
+                                       "gemv_bitnet2b_decode_chain.md", two_b))
     if not args.no_extra:
         if not args.no_2b:
             df = decode_leg(torch, N, I, two_b, args.steps, args.warmup, full_layer=True)
             result["decode_2b_full_layer"] = dict(
                 workload=two_b + " with RMS norms and squared-ReLU gating fused in",
                 **leg_summary(df, 1))
+        if args.workload == "ternary100b-decode-m1-96L":
+            f32 = args.workload + "-f32"
+            d32 = decode_leg(torch, N, I, f32, max(5, args.steps // 3), 2)
+            result["decode_100b_f32"] = dict(
+                workload=f32 + " (fp32 activations between layers)", **leg_summary(d32, 1))
         for m in (1, 16):
             d8 = decode_leg(torch, N, I, "llama8b-ternary", max(5, args.steps // 3), 2, m=m)
             result[f"decode_8b_m{m}"] = dict(workload="llama8b-ternary (32 layers)",
