@@ -9,16 +9,17 @@
 // the int8 value q in registers, so the matrix cores contract q with x directly.
 //
 // Design for gfx950 (the pages' kernels are CPU SIMD and lookup-table code):
-//  * Workgroup = 4 waves; it owns a run of consecutive 16-row tiles (of up to
-//    kMaxGroup matrices that share the activations).  One tile per workgroup for
-//    small launches; large ones spread the tiles over two workgroups per CU, each
-//    matrix split on its own or, for some launches, all matrices' tiles as one
-//    list in runs that may cross into the next matrix (launch_gemv: balanced
-//    runs, or skewed runs where the first-dispatched workgroup of each CU takes
-//    more).  K is cut into
-//    256-k super-chunks; wave w takes super-chunks w, w + 4, ..., so one wave load
-//    instruction covers 16 rows x 64 contiguous bytes and the four waves read 256
-//    contiguous bytes of each row per step.
+//  * Workgroup = NW = 4 waves (8 where a launch has at most one tile per compute
+//    unit, so that each unit still runs 8 waves); it owns a run of consecutive
+//    16-row tiles (of up to kMaxGroup matrices that share the activations).  One
+//    tile per workgroup for small launches; large ones spread the tiles over two
+//    workgroups per CU, each matrix split on its own or, for some launches, all
+//    matrices' tiles as one list in runs that may cross into the next matrix
+//    (launch_gemv: balanced runs, or skewed runs where the first-dispatched
+//    workgroup of each CU takes more).  K is cut into 256-k super-chunks; wave w
+//    takes super-chunks w, w + NW, ..., so one wave load instruction covers 16
+//    rows x 64 contiguous bytes and the waves read 64 NW contiguous bytes of each
+//    row per step.
 //  * The activations are staged once per workgroup into LDS, byte-transposed
 //    within each 16-byte group; this is the order in which a shift, a mask and a
 //    byte lookup per field, (w >> 2i) & 0x03030303, unpack the weights, so no
@@ -108,10 +109,10 @@ constexpr int phase_k(int M, int K, int fmt, int budget = kXBudget) {
   return kx >= K ? K : kx;
 }
 
-// LDS: X [M][stride] | zero | part[T][16][16] int | dsc[16] | wred[16] | wss[4] double
+// LDS: X [M][stride] | zero | part[T][16][16] int | dsc[16] | wred[16] | wss[8] double
 int lds_bytes(int tiles, int M, int K, int fmt) {
   return M * stage_stride(phase_k(M, K, fmt), fmt) + zero_bytes(fmt) + tiles * 1024 + 64 + 64 +
-         32;
+         64;
 }
 
 // The launch's scalars.  The ones the first loads depend on (activations, the
@@ -340,8 +341,8 @@ constexpr int kArgsAt =
 // weight) in L2 for the other workgroups (2B stack with the fused norms and
 // gating 0.821 -> 0.778 ms per token; without a prologue the same loads lost 2%
 // on the 100B-class stack and nothing was gained on the 2B one).
-template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const uint8_t* wp0,
+template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const uint8_t* wp0,
                                                         const uint8_t* wp1, const uint8_t* wp2,
                                                         int n0, int n1, int n2, int s1, int s2,
                                                         uint32_t mtck, const GemvArgs a) {
@@ -355,6 +356,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   constexpr int HOLD = PRO ? kHold : H;       // fused: groups held per thread
   constexpr uint32_t ES = BF ? 2u : 4u;      // fused: input element size
   constexpr int ZB = FMT == kFmtT1 ? 96 : 64;  // zero slot bytes (zero_bytes)
+  constexpr int kT = 64 * NW;                // threads
+  static_assert(NW == 4 || (NW == 8 && XMODE > 0), "eight waves: fused activations only");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   int* part = reinterpret_cast<int*>(zero + ZB);         // [T][16 rows][16 tokens]
   float* dsc = reinterpret_cast<float*>(part + T * 256);  // [16]
   float* wred = dsc + 16;                                // [16]
-  double* wss = reinterpret_cast<double*>(wred + 16);    // [4]
+  double* wss = reinterpret_cast<double*>(wred + 16);    // [NW]
 
   // Buffer descriptor of local tile tl (wave-uniform; readfirstlane keeps it in
   // scalar registers so the loads need no per-lane legalisation loop).
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   };
 
   // clear the partial tiles and the zero slot
-  for (int i = tid; i < T * 64; i += kThreads) reinterpret_cast<uint4*>(part)[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < T * 64; i += kT) reinterpret_cast<uint4*>(part)[i] = make_uint4(0, 0, 0, 0);
   if (tid < ZB / 4) reinterpret_cast<uint32_t*>(zero)[tid] = 0u;
   // the rest of the arguments and the epilogue's scalars, fetched once the first
   // activation and weight loads are in flight (phase 0 below)
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
 
   // token groups: G consecutive threads per token (G = 256 / 2^ceil(log2 M));
   // threads of tokens >= M idle in the per-token passes
-  const int lgG = 8 - ceil_log2(M);
+  const int lgG = (NW == 8 ? 9 : 8) - ceil_log2(M);
   const int G = 1 << lgG;
   const int tk = tid >> lgG;
   const int jg = tid & (G - 1);
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     const int k0p = ph * kx, klenp = min(kx, K - k0p);
     Cp = FMT == kFmtT1 ? (klenp + 79) / 80 : klenp >> 6;
     const int Sp = (Cp + 3) >> 2;
-    Jp = Sp > wave ? (Sp - wave + 3) >> 2 : 0;
+    Jp = Sp > wave ? (Sp - wave + NW - 1) / NW : 0;
     kb0p = FMT == kFmtT1 ? (uint32_t)k0p / 5u : (uint32_t)k0p >> 2;
     pp = ph;
     tp = 0;
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     rs = tile_rsrc(0);
   };
   auto next_load = [&]() -> uint4 {
-    const int c = 4 * (wave + 4 * jp) + g;
+    const int c = 4 * (wave + NW * jp) + g;
     const uint32_t off = (tp < ntiles && c < Cp) ? (uint32_t)r * rowb + kb0p + 16u * (uint32_t)c
                                                  : kOob;
     const uint4 v = PRO ? bload16_nt(rs, off) : bload16(rs, off);
@@ -517,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
     // chunks (16 packed bytes of a row: 64 k, T1 80 k) in this phase
     const int C = FMT == kFmtT1 ? (klen + 79) / 80 : klen >> 6;
     const int S = (C + 3) >> 2;                    // 256-k super-chunks
-    const int J = S > wave ? (S - wave + 3) >> 2 : 0;
+    const int J = S > wave ? (S - wave + NW - 1) / NW : 0;
     const int Q = ntiles * J;                      // loads per lane in this phase
     const int K16 = klen >> 4;                     // 16-k groups of activations
     const int K16s = FMT == kFmtT1 ? 5 * C : K16;  // groups staged (T1: zeros past klen)
@@ -695,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
         bool fast = true;
         for (int t = 0; t < M; ++t) {
           double st = 0.0;
-          for (int i = 0; i < nw; ++i) st += wss[(t * nw + i) & 3];
+          for (int i = 0; i < nw; ++i) st += wss[(t * nw + i) & (NW - 1)];
           float mt;
           fast = mean_sq_fast(st, K, mt) && fast;
           if (t == tk) ms = mt;
@@ -726,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
             for (int t = 0; t < M; ++t) dsc[t] = sq_limbs_mean(limbs + t * kSqLimbs, K, sqwork);
           lds_barrier();
           if (tk < M) ms = dsc[tk];
-          for (int i = tid; i < T * 64; i += kThreads)
+          for (int i = tid; i < T * 64; i += kT)
             reinterpret_cast<uint4*>(part)[i] = make_uint4(0, 0, 0, 0);
         }
         r = rms_factor_of_mean(ms, a.eps);
@@ -749,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
       if (lane == 0) wred[wave] = amax;
       lds_barrier();
       float tmax = 0.0f;
-      for (int i = 0; i < nw; ++i) tmax = fmaxf(tmax, wred[(tk * nw + i) & 3]);
+      for (int i = 0; i < nw; ++i) tmax = fmaxf(tmax, wred[(tk * nw + i) & (NW - 1)]);
       const float astar = fmaxf(tmax, kEps);
       const float s_t = kQb / astar;
       if (jg == 0 && tk < M) {
@@ -788,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
       }
 #pragma unroll
       for (int u = 0; u < R; ++u) {
-        const int c = 4 * (wave + 4 * jc) + g;
+        const int c = 4 * (wave + NW * jc) + g;
         if constexpr (FMT == kFmtT1) {
           v4i t[5];
           unpack_t1(ring[u], t);
@@ -847,7 +850,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
   if constexpr (!BAL) {
     int32_t* accp = pro.acc;
     void* yp = pro.y;
-    for (int i = tid; i < ntiles * M * 16; i += kThreads) {
+    for (int i = tid; i < ntiles * M * 16; i += kT) {
       const int row = i & 15;
       const int tt = i >> 4;
       const int tl = (int)(((uint32_t)tt * (uint32_t)pro.mdiv) >> 16);  // tt / M
@@ -878,7 +881,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
       void* yp = h2 == 0 ? rpro.yA : rpro.yB;
       int32_t* accp = h2 == 0 ? rpro.accA : rpro.accB;
       const float gm = h2 == 0 ? gamma : gamB;
-      for (int i = tid; i < (hi - lo) * M * 16; i += kThreads) {
+      for (int i = tid; i < (hi - lo) * M * 16; i += kT) {
         const int row = i & 15;
         const int tt = i >> 4;
         const int tq = (int)(((uint32_t)tt * (uint32_t)rpro.mdiv) >> 16);  // tt / M
@@ -905,7 +908,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const void* xin, const u
 // (balanced runs come only with more than 256 workgroups, where the ring is at
 // most 4 deep: built for depths 2 and 4)
 template <int XMODE, int FMT, int H>
-const void* ring_kernel(int R, bool bal) {
+const void* ring_kernel(int R, bool bal, bool wide) {
+  if constexpr ((XMODE == 1 || XMODE == 2) && FMT == kFmt2) {
+    // eight-wave workgroups of one tile (per-matrix runs, ring depth 2 or 4)
+    if (wide && !bal)
+      return R <= 2 ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H, false, 8>)
+                    : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, false, 8>);
+  }
   if (bal)
     return R <= 2 ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H, true>)
                   : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, true>);
@@ -916,21 +925,21 @@ const void* ring_kernel(int R, bool bal) {
 }
 
 template <int FMT>
-const void* select_kernel(int xmode, int R, bool long_input, bool bal) {
+const void* select_kernel(int xmode, int R, bool long_input, bool bal, bool wide) {
   switch (xmode) {
-    case 0: return ring_kernel<0, FMT, kHold>(R, bal);
+    case 0: return ring_kernel<0, FMT, kHold>(R, bal, wide);
     case 1:
-      return long_input ? ring_kernel<1, FMT, kHoldPlain>(R, bal)
-                        : ring_kernel<1, FMT, kHold>(R, bal);
+      return long_input ? ring_kernel<1, FMT, kHoldPlain>(R, bal, wide)
+                        : ring_kernel<1, FMT, kHold>(R, bal, wide);
     case 2:
-      return long_input ? ring_kernel<2, FMT, kHoldPlain>(R, bal)
-                        : ring_kernel<2, FMT, kHold>(R, bal);
-    case 3: return ring_kernel<3, FMT, kHold>(R, bal);
-    case 4: return ring_kernel<4, FMT, kHold>(R, bal);
-    case 5: return ring_kernel<5, FMT, kHold>(R, bal);
-    case 6: return ring_kernel<6, FMT, kHold>(R, bal);
-    case 7: return ring_kernel<7, FMT, kHold>(R, bal);
-    default: return ring_kernel<8, FMT, kHold>(R, bal);
+      return long_input ? ring_kernel<2, FMT, kHoldPlain>(R, bal, wide)
+                        : ring_kernel<2, FMT, kHold>(R, bal, wide);
+    case 3: return ring_kernel<3, FMT, kHold>(R, bal, wide);
+    case 4: return ring_kernel<4, FMT, kHold>(R, bal, wide);
+    case 5: return ring_kernel<5, FMT, kHold>(R, bal, wide);
+    case 6: return ring_kernel<6, FMT, kHold>(R, bal, wide);
+    case 7: return ring_kernel<7, FMT, kHold>(R, bal, wide);
+    default: return ring_kernel<8, FMT, kHold>(R, bal, wide);
   }
 }
 
@@ -994,21 +1003,27 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
   // the third read twice, cheaper than issuing kHoldPlain hold loads (T1 input
   // of 8192: 515 groups; 100B-class T1 stack 8.28 -> 7.87 ms per token)
   const int staged = fmt == kFmtT1 ? 5 * ((a.K + 79) / 80) : a.K / 16;
-  const int per_thread = (staged + (256 >> ceil_log2_host(a.M)) - 1) / (256 >> ceil_log2_host(a.M));
-  const bool long_input = fused && per_thread > kHold + 1;
+  auto long_input = [&](int threads) {
+    const int g = threads >> ceil_log2_host(a.M);   // threads per token
+    return fused && (staged + g - 1) / g > kHold + 1;
+  };
   struct Plan {
     int tpw, wgs;
     bool bal;
     const void* kernel;
     size_t lds;
     int l1, l2, h;   // list runs: L1 tiles for workgroups b < h, else L2
+    bool wide;       // eight-wave workgroups
   };
   // latency regime: at most kLatencyBytes of packed weights
   const bool latency = (int64_t)total_tiles * 16 * row_bytes <= kLatencyBytes;
-  auto plan = [&](int t, bool bal, int wgs = 0) {
-    Plan p{t, wgs ? wgs : bal ? (total_tiles + t - 1) / t : count_wgs(t), bal, nullptr, 0, 0, 0, 0};
+  auto plan = [&](int t, bool bal, int wgs = 0, bool wide = false) {
+    Plan p{t, wgs ? wgs : bal ? (total_tiles + t - 1) / t : count_wgs(t), bal, nullptr, 0, 0, 0, 0,
+           wide};
+    const int nw = wide ? 8 : 4;
+    const int per_tile_w = ((chunks + 3) / 4 + nw - 1) / nw;   // loads per lane of a tile
     int ring = 4;
-    while (ring < 16 && 2 * ring * 4 * p.wgs <= kFlightLoads) ring *= 2;
+    while (!wide && ring < 16 && 2 * ring * nw * p.wgs <= kFlightLoads) ring *= 2;
     // several tiles per workgroup but short rows (at most 6 loads per wave in
     // all, over more than 256 workgroups): two loads ahead measured faster than
     // four (2B gate+up, 2560 -> 13824: the chain 5.49 -> 5.34 us per launch);
@@ -1018,9 +1033,10 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     // registers longer; 2B T1 stack 0.668 -> 0.647 ms per token, 100B-class
     // 7.86 -> 7.78 ms; 8 and 16 slower)
     if (fmt == kFmtT1) ring = 2;
-    if (ring > t * per_tile) ring = t * per_tile;
-    p.kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, long_input, bal)
-                             : select_kernel<kFmt2>(xmode, ring, long_input, bal);
+    if (ring > t * per_tile_w) ring = t * per_tile_w;
+    const bool li = long_input(64 * nw);
+    p.kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, li, bal, wide)
+                             : select_kernel<kFmt2>(xmode, ring, li, bal, wide);
     p.lds = (size_t)lds_bytes(t, a.M, a.K, fmt);
     return p;
   };
@@ -1065,6 +1081,15 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
       pl.l1 = pl.l2 + 1;
       pl.h = total_tiles % pl.wgs;
     }
+    // At most one tile per compute unit (the 8B-class down projection, 14336 ->
+    // 4096: 256 tiles): four-wave workgroups would leave each compute unit one
+    // workgroup, half its wave slots; eight-wave workgroups split each tile's K
+    // over twice the waves (fused 2-bit launches; 9.0 -> 7.1 us).  With more
+    // tiles than compute units, two four-wave workgroups per compute unit
+    // measured faster (eight-wave workgroups of 2-14 tiles: 8B-class q+k+v 5.66
+    // -> 5.77 us, gate+up 8.85 -> 10.2; 100B-class launches +0.3-4%)
+    if ((xmode == 1 || xmode == 2) && fmt == kFmt2 && total_tiles <= cus)
+      pl = plan(1, false, 0, true);
   }
   const int tpw = pl.tpw, wgs = pl.wgs;
   const void* kernel = pl.kernel;
@@ -1094,7 +1119,8 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
   uint32_t mtck = (uint32_t)a.M | ((uint32_t)tpw << 5) | ((uint32_t)a.count << 10) |
                   ((uint32_t)a.K << 13);
   void* args[] = {&xin, &wp0, &wp1, &wp2, &n0, &n1, &n2, &s1, &s2, &mtck, &a};
-  return hipLaunchKernel(kernel, dim3((unsigned)wgs), dim3(kThreads), args, lds, s);
+  return hipLaunchKernel(kernel, dim3((unsigned)wgs), dim3(pl.wide ? 512 : kThreads), args, lds,
+                         s);
 }
 
 }  // namespace bitnet

@@ -32,6 +32,14 @@ def master_weights(n: int, k: int, seed: int, sigma: float = WEIGHT_SIGMA) -> np
     return rng.standard_normal((n, k), dtype=np.float32) * np.float32(sigma)
 
 
+def ternary_codes(n: int, k: int, seed: int) -> np.ndarray:
+    """int8 [N, K] in {-1, 0, +1} with the mix of absmean-ternarised N(0, sigma)
+    weights, P(0) = 0.31 and P(+1) = P(-1) = 0.345 (numpy PCG64, seeded): ready-made
+    ternary weights for shapes too large to ternarise master weights on the host."""
+    u = np.random.Generator(np.random.PCG64(seed)).random((n, k), dtype=np.float32)
+    return (u > np.float32(0.655)).astype(np.int8) - (u < np.float32(0.345)).astype(np.int8)
+
+
 def activations(m: int, k: int, seed: int = ACT_SEED) -> np.ndarray:
     """fp32 [M, K] ~ N(0, 1) from numpy's PCG64 with the given seed."""
     rng = np.random.Generator(np.random.PCG64(seed))
