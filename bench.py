@@ -829,7 +829,7 @@ def main():
                 **leg_summary(df, 1))
         if args.workload == "ternary100b-decode-m1-96L":
             f32 = args.workload + "-f32"
-            d32 = decode_leg(torch, N, I, f32, max(5, args.steps // 3), 2)
+            d32 = decode_leg(torch, N, I, f32, max(10, args.steps // 2), 5)
             result["decode_100b_f32"] = dict(
                 workload=f32 + " (fp32 activations between layers)", **leg_summary(d32, 1))
         for m in (1, 16):
