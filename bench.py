@@ -93,6 +93,9 @@ def parse():
     p.add_argument("--no-compare", action="store_true",
                    help="skip the single-matrix comparison of the decode kernels")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--sustain-seconds", type=float, default=8.0,
+                   help="after the timed steps, run the headline stack on for this long "
+                        "(reported as decode_sustained; 0: skip)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this size (PMC calibration)")
     return p.parse_args()
@@ -165,8 +168,10 @@ def chain_fn(torch, N, layers_mats, h0, bufs, norms=None, eps=1e-5, fmt="2bit"):
 
 
 def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycle=None,
-               fmt="2bit"):
-    """M tokens at a time through a whole layer stack, replayed from HIP graphs."""
+               fmt="2bit", sustain_s=0.0):
+    """M tokens at a time through a whole layer stack, replayed from HIP graphs.
+    With sustain_s > 0, the stack then runs on for about that many seconds, timed
+    on its own (the sustained rate: clocks and temperature under continuous load)."""
     wl = I.WORKLOADS[name]
     shapes, layers = wl["layer"], wl["layers"]
     per_stack = I.packed_bytes(shapes, fmt) * layers
@@ -222,6 +227,19 @@ def decode_leg(torch, N, I, name, steps, warmup, m=1, full_layer=False, min_cycl
                weights=sum(n * k for _, k, n in shapes) * layers,
                layers=layers, shapes=shapes, act=wl["act"],
                ms_p10=pct[10], ms_median=pct[50], ms_p90=pct[90])
+    if sustain_s > 0:
+        n_sus = max(1, int(sustain_s * 1e3 / ms))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_sus):
+            graphs[i % replicas].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_sus = e0.elapsed_time(e1) / n_sus
+        res["sustained"] = {"steps": n_sus, "seconds": round(ms_sus * n_sus * 1e-3, 2),
+                            "ms_per_step": round(ms_sus, 5),
+                            "gbs": round(per_stack / (ms_sus * 1e-3) / 1e9, 1)}
+        log(f"{name}: sustained {n_sus} steps, {ms_sus * 1e3:.1f} us/step")
     del graphs, stack
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -782,7 +800,8 @@ def main():
         log(f"cpu baseline: {cpu}")
     torch.cuda.set_device(0)
     N.lib()
-    d = decode_leg(torch, N, I, args.workload, args.steps, args.warmup)
+    d = decode_leg(torch, N, I, args.workload, args.steps, args.warmup,
+                   sustain_s=args.sustain_seconds)
     avg_launch = d["ms"] * 1e-3 / d["launches"]
     avg_bytes = d["per_stack"] / d["launches"]
     achieved = avg_bytes / avg_launch / 1e9
@@ -806,6 +825,7 @@ def main():
         "ms_per_step_p10_median_p90": [round(d["ms_p10"], 5), round(d["ms_median"], 5),
                                        round(d["ms_p90"], 5)],
         "tokens_per_s": round(1e3 / d["ms"], 1),
+        "decode_sustained": d.get("sustained"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(workload=args.workload),
