@@ -1,10 +1,13 @@
-"""The four launches of a 100B-class layer at M <= 4 through the fused act-quant
-call (the decode path the bench times), every output compared with the oracle.
+"""Decode launches of the bench's stacks at M <= 4 through the fused act-quant call
+(the decode path the bench times), every output compared with the oracle.
 
-q+k+v (3 x 8192 -> 8192), o (8192 -> 8192), gate+up (2 x 8192 -> 28672) and down
-(28672 -> 8192), each with its own seeded input, bf16 and fp32 inputs: these
-launches take the bandwidth-regime plans (several 16-row tiles per workgroup,
-list runs) that the small parity shapes do not reach.  Weights are seeded
+The four launches of a 100B-class layer, q+k+v (3 x 8192 -> 8192), o (8192 ->
+8192), gate+up (2 x 8192 -> 28672) and down (28672 -> 8192), take the
+bandwidth-regime plans with several 16-row tiles per workgroup (list runs); the
+8B-class down projection (14336 -> 4096, 256 tiles) and a ragged 12800 -> 3000
+(188 tiles) take eight-wave workgroups of one tile each.  Each launch has its own
+seeded input, bf16 and fp32 inputs; the small parity shapes reach none of these
+plans.  Weights are seeded
 ternary codes packed by the oracle (ternarising 235 M master weights on the host
 would take minutes; the weight quantiser is checked at these sizes in
 test_gpu_full_size.py).  Bar: bit-exact x_q, token scales and outputs.  The
@@ -27,7 +30,8 @@ pytestmark = pytest.mark.gpu
 
 GAMMA = np.float32(0.0159)
 LAUNCHES = {"qkv": (8192, (8192, 8192, 8192)), "o": (8192, (8192,)),
-            "gate+up": (8192, (28672, 28672)), "down": (28672, (8192,))}
+            "gate+up": (8192, (28672, 28672)), "down": (28672, (8192,)),
+            "8B down": (14336, (4096,)), "ragged": (12800, (3000,))}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -50,7 +54,7 @@ def weights():
 @pytest.mark.parametrize("name", list(LAUNCHES))
 def test_100b_launch_every_output(weights, name, dt, m):
     k, ns = LAUNCHES[name]
-    print(f"100B-class launch {name}: K={k} N={ns} M={m} input {dt}", flush=True)
+    print(f"decode launch {name}: K={k} N={ns} M={m} input {dt}", flush=True)
     xt, x = acts(m, k, 9200 + m + k, dt)
     g_d = dev(np.array([GAMMA], np.float32))
     mats = [(dev(p), g_d) for p in weights[name]]
