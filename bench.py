@@ -3,7 +3,7 @@
 
 Default workload (`ternary100b-decode-m1-96L`): the ~100B-class ternary decode
 stack, one token (M = 1) streamed through 96 layers of {q, k, v, o: 8192->8192,
-gate, up: 8192->28672, down: 28672->8192} with bf16 activations between layers
+gate, up: 8192->28672, down: 28672->8192} with fp32 activations between layers
 and the per-token int8 activation quantisation fused into every layer (23.35 GB
 of packed weights per token, resident in HBM).  Chain per layer: q, k, v from
 the layer input (one launch); o from q (attention is out of scope); gate and up
@@ -24,7 +24,7 @@ kernel's int8 TOPS on the 2B shapes at M = 512 and 4096 and on the 8B shapes at
 M = 2048 (with its own roofline block), single matrices at M = 1 through the
 matrix-core kernel, T1 and the lookup-table path, the standalone quantisers
 against HBM, and the CPU oracle timed on bounded samples of the decode and
-prefill workloads (one core and all cores); the 100B-class stack again with fp32
+prefill workloads (one core and all cores); the 100B-class stack again with bf16
 activations between layers.
 """
 
@@ -848,10 +848,10 @@ def main():
                 workload=two_b + " with RMS norms and squared-ReLU gating fused in",
                 **leg_summary(df, 1))
         if args.workload == "ternary100b-decode-m1-96L":
-            f32 = args.workload + "-f32"
-            d32 = decode_leg(torch, N, I, f32, max(10, args.steps // 2), 5)
-            result["decode_100b_f32"] = dict(
-                workload=f32 + " (fp32 activations between layers)", **leg_summary(d32, 1))
+            b16 = args.workload + "-bf16"
+            d16 = decode_leg(torch, N, I, b16, max(10, args.steps // 2), 5)
+            result["decode_100b_bf16"] = dict(
+                workload=b16 + " (bf16 activations between layers)", **leg_summary(d16, 1))
         for m in (1, 16):
             d8 = decode_leg(torch, N, I, "llama8b-ternary", max(5, args.steps // 3), 2, m=m)
             result[f"decode_8b_m{m}"] = dict(workload="llama8b-ternary (32 layers)",

@@ -72,8 +72,8 @@ WORKLOADS = {
     "bitnet2b-decode-m1-30L": dict(layer=LAYER_2B, layers=30, m=(1,), act="bf16"),
     "bitnet2b-prefill": dict(layer=LAYER_2B, layers=1, m=(512, 4096), act="bf16"),
     "llama8b-ternary": dict(layer=LAYER_8B, layers=32, m=(1, 16, 2048), act="bf16"),
-    "ternary100b-decode-m1-96L": dict(layer=LAYER_100B, layers=96, m=(1,), act="bf16"),
-    "ternary100b-decode-m1-96L-f32": dict(layer=LAYER_100B, layers=96, m=(1,), act="f32"),
+    "ternary100b-decode-m1-96L": dict(layer=LAYER_100B, layers=96, m=(1,), act="f32"),
+    "ternary100b-decode-m1-96L-bf16": dict(layer=LAYER_100B, layers=96, m=(1,), act="bf16"),
 }
 
 
