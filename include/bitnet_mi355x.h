@@ -372,13 +372,18 @@ bitnet_status bitnet_ternary_linear_lut(const uint8_t *w_packed, const float *w_
  * per workgroup (256 x 256, 192 x 256, 128 x 256, 128 x 128 or 64 x 128).  If
  * *first_launch_tokens > 0, the first *first_launch_tokens tokens run as one
  * launch with that tile and the remaining tokens as a second launch with the
- * tile this query returns for them.  M in 1..2^31-1, count in 1..4, N[j] >= 1,
- * K >= 1 (BITNET_ERR_SHAPE otherwise); asks the HIP runtime for the compute
- * unit count (1 if it cannot say).
+ * tile this query returns for them.  If *first_launch_rows > 0 (a multiple of
+ * 256), the matrices' rows are taken in order, each matrix's row count rounded
+ * up to a multiple of 256, and the first *first_launch_rows of them run as one
+ * launch with that tile, the remaining rows (the rest of the matrix the cut
+ * falls in, then the following matrices) as a second launch with the tile this
+ * query returns for those row counts.  M in 1..2^31-1, count in 1..4, N[j] >= 1,
+ * K >= 1 (BITNET_ERR_SHAPE otherwise); asks the HIP runtime for the compute unit
+ * count (1 if it cannot say).
  */
 bitnet_status bitnet_prefill_tile(int64_t M, const int64_t *N, int count, int64_t K,
                                   int *tokens_per_tile, int *rows_per_tile,
-                                  int64_t *first_launch_tokens);
+                                  int64_t *first_launch_tokens, int64_t *first_launch_rows);
 
 /*
  * Decode chain: a sequence of fused act-quant + ternary linear stages (each one

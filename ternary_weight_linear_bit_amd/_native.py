@@ -553,7 +553,7 @@ class BitnetChain(ctypes.Structure):
 
 SIGNATURES["bitnet_prefill_tile"] = (_I, [_I64, ctypes.POINTER(_I64), _I, _I64,
                                           ctypes.POINTER(_I), ctypes.POINTER(_I),
-                                          ctypes.POINTER(_I64)])
+                                          ctypes.POINTER(_I64), ctypes.POINTER(_I64)])
 SIGNATURES["bitnet_chain_plan_bytes"] = (_SZ, [_I])
 SIGNATURES["bitnet_chain_plan"] = (_I, [ctypes.POINTER(BitnetChainStage), _I, _I64, _P, _SZ,
                                         ctypes.POINTER(BitnetChain)])
@@ -617,10 +617,13 @@ def bitnet_chain_error(chain) -> int:
 
 
 def bitnet_prefill_tile(m, ns, k):
-    """(tokens per tile, rows per tile, first launch tokens) of the prefill kernel for
-    M tokens over matrices with ns rows and inputs of K (bitnet_prefill_tile)."""
+    """(tokens per tile, rows per tile, first launch tokens, first launch rows) of the
+    prefill kernel for M tokens over matrices with ns rows and inputs of K
+    (bitnet_prefill_tile)."""
     arr = (ctypes.c_int64 * len(ns))(*ns)
-    bm, bn, first = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int64(0)
+    bm, bn = ctypes.c_int(0), ctypes.c_int(0)
+    first, rows = ctypes.c_int64(0), ctypes.c_int64(0)
     _check("bitnet_prefill_tile", lib().bitnet_prefill_tile(m, arr, len(ns), k, ctypes.byref(bm),
-                                                            ctypes.byref(bn), ctypes.byref(first)))
-    return bm.value, bn.value, first.value
+                                                            ctypes.byref(bn), ctypes.byref(first),
+                                                            ctypes.byref(rows)))
+    return bm.value, bn.value, first.value, rows.value

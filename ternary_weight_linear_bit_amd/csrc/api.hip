@@ -497,8 +497,9 @@ bitnet_status bitnet_quant_linear(const uint8_t* w_packed, const float* w_scale,
 
 bitnet_status bitnet_prefill_tile(int64_t M, const int64_t* N, int count, int64_t K,
                                  int* tokens_per_tile, int* rows_per_tile,
-                                 int64_t* first_launch_tokens) {
-  if (!N || !tokens_per_tile || !rows_per_tile || !first_launch_tokens) return BITNET_ERR_NULL;
+                                 int64_t* first_launch_tokens, int64_t* first_launch_rows) {
+  if (!N || !tokens_per_tile || !rows_per_tile || !first_launch_tokens || !first_launch_rows)
+    return BITNET_ERR_NULL;
   if (M < 1 || M > kInt32Max || count < 1 || count > bitnet::kMaxGroup || K < 1)
     return BITNET_ERR_SHAPE;
   int n[bitnet::kMaxGroup] = {0, 0, 0, 0};
@@ -510,6 +511,7 @@ bitnet_status bitnet_prefill_tile(int64_t M, const int64_t* N, int count, int64_
   *tokens_per_tile = p.bm;
   *rows_per_tile = p.bn;
   *first_launch_tokens = p.first_tokens;
+  *first_launch_rows = p.first_rows;
   return BITNET_OK;
 }
 

@@ -454,6 +454,7 @@ struct GemmArgs {
   void* y[kMaxGroup];
   int32_t* acc[kMaxGroup];
   int n[kMaxGroup];
+  int ld[kMaxGroup];         // row stride of y and acc in elements (0: n)
   int nb0[kMaxGroup + 1];    // first row tile of each matrix; nb0[count] = all row tiles
   const int8_t* xq;          // int8 activations [M][K]
   const float* xs;           // their token scales
@@ -470,10 +471,14 @@ hipError_t launch_repack_prefill(const uint8_t* w, int64_t N, int64_t K, uint8_t
 // The prefill launch's tile for M tokens over `count` matrices of n[j] rows on a
 // device with `cus` compute units: bm tokens x bn rows per workgroup; when
 // first_tokens > 0 the first first_tokens tokens run as one launch with this tile
-// and the rest as a second launch planned on its own.
+// and the rest as a second launch planned on its own; when first_rows > 0, the
+// first first_rows rows of the matrices taken in order (a multiple of bn) run as
+// one launch with this tile and the remaining rows as a second launch planned on
+// its own.
 struct GemmPlan {
   int bm, bn;
   int64_t first_tokens;
+  int64_t first_rows;
 };
 GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus);
 // Lookup-table decode: workspace bytes (tables 16 K + accumulators 4 N, each

@@ -78,7 +78,8 @@ __device__ __forceinline__ v4i expand_codes(uint32_t w) {
 template <int E, int BM, int WN>
 __device__ __forceinline__ void store_tile_impl(void* y, const v16i (&acc)[BM / 64][NBW],
                                                 const int* xsum, const float* xsc, float gamma,
-                                                uint8_t* lds, int m0, int wrow0, int M, int N) {
+                                                uint8_t* lds, int m0, int wrow0, int M, int N,
+                                                int ldy) {
   constexpr int TB = BM / 64;
   constexpr int RB = 64 * E;                       // bytes per token row of the slice
   constexpr int U = 16 * RB;                       // bytes per unit of 16 tokens
@@ -129,7 +130,7 @@ __device__ __forceinline__ void store_tile_impl(void* y, const v16i (&acc)[BM / 
       const int m = m0 + wt * (BM / 2) + 32 * i + 16 * hq + tl;
       const int n = wrow0 + c16 / E;
       if (m < M) {
-        char* dst = static_cast<char*>(y) + ((size_t)m * N + n) * E;
+        char* dst = static_cast<char*>(y) + ((size_t)m * ldy + n) * E;
         if (n + 16 / E <= N) {
           // (non-temporal: the outputs are not read again by this launch, and
           // leaving L2 to the weight and activation tiles measured 1-2% faster)
@@ -189,10 +190,10 @@ __global__ __launch_bounds__(128 * WN, LAYOUT == 1 ? 2 : 1) void gemm_kernel(
   const float* w_scale = args.ws[0];
   void* y = args.y[0];
   int32_t* acc_out = args.acc[0];
-  int N = args.n[0], nbase = 0;
-  if (jm >= 1) { wp = args.wp[1]; w_scale = args.ws[1]; y = args.y[1]; acc_out = args.acc[1]; N = args.n[1]; nbase = args.nb0[1]; }
-  if (jm >= 2) { wp = args.wp[2]; w_scale = args.ws[2]; y = args.y[2]; acc_out = args.acc[2]; N = args.n[2]; nbase = args.nb0[2]; }
-  if (jm >= 3) { wp = args.wp[3]; w_scale = args.ws[3]; y = args.y[3]; acc_out = args.acc[3]; N = args.n[3]; nbase = args.nb0[3]; }
+  int N = args.n[0], nbase = 0, ldy = args.ld[0];
+  if (jm >= 1) { wp = args.wp[1]; w_scale = args.ws[1]; y = args.y[1]; acc_out = args.acc[1]; N = args.n[1]; nbase = args.nb0[1]; ldy = args.ld[1]; }
+  if (jm >= 2) { wp = args.wp[2]; w_scale = args.ws[2]; y = args.y[2]; acc_out = args.acc[2]; N = args.n[2]; nbase = args.nb0[2]; ldy = args.ld[2]; }
+  if (jm >= 3) { wp = args.wp[3]; w_scale = args.ws[3]; y = args.y[3]; acc_out = args.acc[3]; N = args.n[3]; nbase = args.nb0[3]; ldy = args.ld[3]; }
   const int8_t* xq = args.xq;
   const float* x_scale = args.xs;
   const int y_bf16 = args.y_bf16;
@@ -389,17 +390,17 @@ __global__ __launch_bounds__(128 * WN, LAYOUT == 1 ? 2 : 1) void gemm_kernel(
 #pragma unroll
           for (int b = 0; b < NBW; ++b) {
             const int n = wrow0 + 32 * b + r;
-            if (n < N) acc_out[(size_t)m * N + n] = acc[i][b][v] - xsum[ml];   // sum (c - 1) x
+            if (n < N) acc_out[(size_t)m * ldy + n] = acc[i][b][v] - xsum[ml];   // sum (c - 1) x
           }
         }
       }
   }
   const int es = y_bf16 ? 2 : 4;
-  if ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ((N * es) & 15) == 0) {
+  if ((reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ((ldy * es) & 15) == 0) {
     if (y_bf16)
-      store_tile_impl<2, BM, WN>(y, acc, xsum, xsc, gamma, &xs[0][0], m0, wrow0, M, N);
+      store_tile_impl<2, BM, WN>(y, acc, xsum, xsc, gamma, &xs[0][0], m0, wrow0, M, N, ldy);
     else
-      store_tile_impl<4, BM, WN>(y, acc, xsum, xsc, gamma, &xs[0][0], m0, wrow0, M, N);
+      store_tile_impl<4, BM, WN>(y, acc, xsum, xsc, gamma, &xs[0][0], m0, wrow0, M, N, ldy);
     return;
   }
   // y not 16-byte aligned or rows not a whole number of 16 bytes: one store per value
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(128 * WN, LAYOUT == 1 ? 2 : 1) void gemm_kernel(
         for (int b = 0; b < NBW; ++b) {
           const int n = wrow0 + 32 * b + r;
           if (n < N) {
-            const size_t o = (size_t)m * N + n;
+            const size_t o = (size_t)m * ldy + n;
             if (y_bf16)
               reinterpret_cast<uint16_t*>(y)[o] = (uint16_t)(pk >> (16 * b));
             else
@@ -491,7 +492,7 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
   //    deeper loads on the other shapes, measured no better).
   // Measured on the prefill shapes; 4 x 32-row blocks per wave measured slower
   // everywhere (registers: one wave per SIMD).
-  GemmPlan p{128, 128, 0};
+  GemmPlan p{128, 128, 0, 0};
   auto row_tiles = [&](int bn) {
     int64_t t = 0;
     for (int j = 0; j < count; ++j) t += (n[j] + bn - 1) / bn;
@@ -514,6 +515,29 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
     const int64_t m1 = (big_rounds - 1) * cus / row_tiles(256) * 256;   // tokens
     if (m1 > 0 && m1 < M) p.first_tokens = m1;
   }
+  // A last round left partly empty where the full rounds hold whole token tiles'
+  // worth of row tiles (with more row tiles per token tile than divide the
+  // compute units, the token split above cannot fill whole rounds): the row tiles
+  // of the full rounds, the matrices taken in order, run as one launch, and the
+  // remaining rows as a second launch with its own tile, when that tile is
+  // smaller (8B gate+up at 2048 tokens: 896 tiles of 256 x 256 in 3.5 rounds ->
+  // 768 in 3 rounds, then the last 4096 rows of up in one round of 128 x 256).
+  if (big && big_rounds > 1 && p.first_tokens == 0 && big_tiles % cus != 0) {
+    const int64_t tt = (M + 255) / 256;                  // token tiles
+    const int64_t full = (big_rounds - 1) * (int64_t)cus;
+    if (full % tt == 0) {
+      const int64_t r1 = full / tt;                      // row tiles in the first launch
+      int rest[kMaxGroup];
+      int rc = 0;
+      int64_t t0 = 0;
+      for (int j = 0; j < count; ++j) {
+        const int64_t tj = (n[j] + 255) / 256;
+        if (t0 + tj > r1) rest[rc++] = (int)(n[j] - (t0 < r1 ? (r1 - t0) * 256 : 0));
+        t0 += tj;
+      }
+      if (rc > 0 && gemm_plan(M, rest, rc, K, cus).bm != 256) p.first_rows = r1 * 256;
+    }
+  }
   const int64_t mt = (M + 127) / 128;
   const int64_t rows4 = row_tiles(256);
   const bool wide = !big && !tall && rows4 * mt <= cus && 10 * rows4 * mt >= 8 * (int64_t)cus;
@@ -525,20 +549,57 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
 
 hipError_t launch_gemm(GemmArgs a, hipStream_t s) {
   if (a.K % 64 != 0 || a.count < 1 || a.count > kMaxGroup) return hipErrorInvalidValue;
+  for (int j = 0; j < a.count; ++j)
+    if (a.ld[j] == 0) a.ld[j] = a.n[j];
   const GemmPlan pl = gemm_plan(a.M, a.n, a.count, a.K, device_cus());
+  const size_t es = a.y_bf16 ? 2 : 4;
   if (pl.first_tokens > 0 && pl.first_tokens < a.M) {
     const int64_t m1 = pl.first_tokens;
     GemmArgs rest = a;
     rest.M = (int)(a.M - m1);
     rest.xq = a.xq + m1 * a.K;
     rest.xs = a.xs + m1;
-    const size_t es = a.y_bf16 ? 2 : 4;
     for (int j = 0; j < a.count; ++j) {
-      rest.y[j] = static_cast<char*>(a.y[j]) + (size_t)m1 * a.n[j] * es;
-      if (a.acc[j]) rest.acc[j] = a.acc[j] + (size_t)m1 * a.n[j];
+      rest.y[j] = static_cast<char*>(a.y[j]) + (size_t)m1 * a.ld[j] * es;
+      if (a.acc[j]) rest.acc[j] = a.acc[j] + (size_t)m1 * a.ld[j];
     }
     a.M = (int)m1;
     const hipError_t e = launch_gemm(a, s);
+    return e != hipSuccess ? e : launch_gemm(rest, s);
+  }
+  if (pl.first_rows > 0) {
+    // rows [0, h) of each matrix in the first launch, [h, n) in the second: the
+    // weights from row h on (prefill layout: 32-row blocks of ceil(K / 128) KiB),
+    // the outputs from column h on with the matrix's own row stride
+    const int64_t r1 = pl.first_rows / 256;
+    GemmArgs head = a, rest = a;
+    head.count = rest.count = 0;
+    const int64_t blk = (int64_t)((a.K + 127) / 128) * 1024;
+    int64_t t0 = 0;
+    for (int j = 0; j < a.count; ++j) {
+      const int64_t tj = (a.n[j] + 255) / 256;
+      const int64_t h = t0 >= r1 ? 0 : t0 + tj <= r1 ? a.n[j] : (r1 - t0) * 256;
+      if (h > 0) {
+        const int k = head.count++;
+        head.wp[k] = a.wp[j];
+        head.ws[k] = a.ws[j];
+        head.y[k] = a.y[j];
+        head.acc[k] = a.acc[j];
+        head.n[k] = (int)h;
+        head.ld[k] = a.ld[j];
+      }
+      if (h < a.n[j]) {
+        const int k = rest.count++;
+        rest.wp[k] = a.wp[j] + (a.layout == 1 ? h / 32 * blk : h * (a.K / 4));
+        rest.ws[k] = a.ws[j];
+        rest.y[k] = static_cast<char*>(a.y[j]) + (size_t)h * es;
+        rest.acc[k] = a.acc[j] ? a.acc[j] + h : nullptr;
+        rest.n[k] = (int)(a.n[j] - h);
+        rest.ld[k] = a.ld[j];
+      }
+      t0 += tj;
+    }
+    const hipError_t e = launch_gemm(head, s);
     return e != hipSuccess ? e : launch_gemm(rest, s);
   }
   const int bm = pl.bm, bn = pl.bn;
