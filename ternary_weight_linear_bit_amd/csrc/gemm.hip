@@ -46,10 +46,6 @@ __device__ __forceinline__ int lds_group(int t, int kg) {
   return t * kStride + 16 * (kg ^ (t & 7));
 }
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, each with its own L2
-#ifndef BITNET_TALL_TILES
-#define BITNET_TALL_TILES 1
-#endif
-constexpr bool kTallTiles = BITNET_TALL_TILES;   // 192 x 256 tiles in the planner
 constexpr int kDepth = 2;         // steps of global loads in flight (default)
 
 // Packed dword (16 codes) -> the codes c = q + 1 in {0, 1, 2} as an int8 operand
@@ -504,7 +500,7 @@ GemmPlan gemm_plan(int64_t M, const int* n, int count, int64_t K, int cus) {
   // 192 x 256 tiles in a single round filling at least 80% of the compute units,
   // where 256 x 256 tiles fill less
   const int64_t tall_tiles = ((M + 191) / 192) * row_tiles(256);
-  const bool tall = kTallTiles && !big_full && tall_tiles <= cus && 5 * tall_tiles >= 4 * (int64_t)cus;
+  const bool tall = !big_full && tall_tiles <= cus && 5 * tall_tiles >= 4 * (int64_t)cus;
   const bool big = !tall && big_tiles > 0 &&
                    (big_full || (K >= 4096 && big_rounds == 1 && 5 * big_tiles >= 3 * (int64_t)cus));
   // A last round of 256 x 256 tiles that fills under 40% of the compute units

@@ -65,7 +65,7 @@
 namespace bitnet {
 namespace {
 
-constexpr int kThreads = 256;              // 4 waves
+constexpr int kThreads = 256;              // 4 waves (eight-wave launches: 512)
 constexpr int kMaxTiles = 16;              // row tiles per workgroup
 constexpr int kMaxM = 16;
 constexpr int kMaxFusedM = 4;
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const ui
   float xs_t = 0.0f, gamma = 0.0f;
   float gamB = 0.0f;    // balanced runs: gamma* of matrix B (gamma: of A)
 
-  // token groups: G consecutive threads per token (G = 256 / 2^ceil(log2 M));
+  // token groups: G consecutive threads per token (G = 64 NW / 2^ceil(log2 M));
   // threads of tokens >= M idle in the per-token passes
   const int lgG = (NW == 8 ? 9 : 8) - ceil_log2(M);
   const int G = 1 << lgG;
