@@ -120,17 +120,30 @@ __device__ __forceinline__ void store_transposed(uint8_t* dst, uint4 v) {
   *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Quantise four activations with the token's factor s = RN32(127 / a*):
-// clip(rne(RN32(x * s)), -128, 127), packed little-endian into one dword.
+// The code clip(rne(RN32(x * s)), -128, 127) of activation x with the token's
+// factor s = RN32(127 / a*), in the low byte of the bits of RN32(t + 1.5 * 2^23),
+// t = RN32(x * s): the sum lies in [2^23, 2^24), where the floats are the
+// integers, so the addition rounds t to the nearest integer, ties to even
+// (1.5 * 2^23 is even), and the low mantissa byte is that integer mod 256, its
+// int8 bit pattern.  For finite inputs |x| <= a*, so |t| <= 127 (1 + 2^-24)
+// and the clip never acts.  (Two instructions per value; rounding, clamping
+// and converting took four, and the packing two more.)
+constexpr float kRneMagic = 12582912.0f;   // 1.5 * 2^23
+__device__ __forceinline__ uint32_t rne_bits(float x, float s) {
+  const float t = x * s;
+  return __float_as_uint(t + kRneMagic);
+}
+
+// The low bytes of four dwords, a first, as one dword (three byte permutes)
+__device__ __forceinline__ uint32_t low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);   // a.b0 b.b0 0 0
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);   // c.b0 d.b0 0 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Quantise four activations (rne_bits), packed little-endian into one dword.
 __device__ __forceinline__ uint32_t quant4(const float* v, float s) {
-  uint32_t out = 0u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float q = rintf(v[i] * s);
-    q = fminf(fmaxf(q, -128.0f), 127.0f);
-    out |= ((uint32_t)(int32_t)q & 0xffu) << (8 * i);
-  }
-  return out;
+  return low_bytes(rne_bits(v[0], s), rne_bits(v[1], s), rne_bits(v[2], s), rne_bits(v[3], s));
 }
 
 // 16 consecutive fp32 or bf16 activations from a 16-byte aligned address
