@@ -83,6 +83,7 @@ constexpr int kHoldPlain = 8;              // fused, no prologue: K <= 32768 at 
 constexpr int64_t kLatencyBytes = 6000000; // launches above this use the bandwidth regime
 constexpr int kWgsPerCu = 2;               // bandwidth regime: workgroups per compute unit
 constexpr int kFlightLoads = 4096;         // target 1 KiB loads in flight over the chip
+constexpr int kPrioSplit = 256;            // MI355X compute units (gemv_kernel PRIO)
 
 // zero slot: one B operand set read for tokens >= M and chunks past the end
 constexpr int zero_bytes(int fmt) { return fmt ? 96 : 64; }
@@ -341,7 +342,15 @@ constexpr int kArgsAt =
 // weight) in L2 for the other workgroups (2B stack with the fused norms and
 // gating 0.821 -> 0.778 ms per token; without a prologue the same loads lost 2%
 // on the 100B-class stack and nothing was gained on the 2B one).
-template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false, int NW = 4>
+// PRIO: launches of one tile per workgroup and two workgroups per compute unit
+// on a chip of kPrioSplit compute units: the second-dispatched workgroup of each
+// unit (b >= kPrioSplit) stages its input at wave priority 1.  Issue
+// arbitration otherwise favours the older waves, so that workgroup waited behind
+// the first one's staging and ran 1.6-1.9x longer; raising it for the whole
+// launch measured slower, for the staging alone faster (100B-class stack, o and
+// down projections: 5.646 -> 5.579 ms per token).
+template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false, int NW = 4,
+          bool PRIO = false>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const uint8_t* wp0,
                                                         const uint8_t* wp1, const uint8_t* wp2,
                                                         int n0, int n1, int n2, int s1, int s2,
@@ -358,6 +367,10 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const ui
   constexpr int ZB = FMT == kFmtT1 ? 96 : 64;  // zero slot bytes (zero_bytes)
   constexpr int kT = 64 * NW;                // threads
   static_assert(NW == 4 || (NW == 8 && XMODE > 0), "eight waves: fused activations only");
+  static_assert(!PRIO || (!BAL && NW == 4), "staging priority: per-matrix runs of four waves");
+  if constexpr (PRIO) {
+    if (blockIdx.x >= kPrioSplit) __builtin_amdgcn_s_setprio(1);
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
@@ -796,6 +809,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const ui
     }
     lds_barrier();
 
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);   // staged: back to age order
     // 3. stream: consumer position (tc, jc); flush a tile's partial when it ends
     const int bt = r < M ? r * stride : -1;
     int tc = 0, jc = 0;
@@ -925,7 +939,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const ui
 // (balanced runs come only with more than 256 workgroups, where the ring is at
 // most 4 deep: built for depths 2 and 4)
 template <int XMODE, int FMT, int H>
-const void* ring_kernel(int R, bool bal, bool wide) {
+const void* ring_kernel(int R, bool bal, bool wide, bool prio) {
   if constexpr ((XMODE == 1 || XMODE == 2) && FMT == kFmt2) {
     // eight-wave workgroups of one tile (per-matrix runs, ring depth 2 or 4)
     if (wide && !bal)
@@ -935,6 +949,11 @@ const void* ring_kernel(int R, bool bal, bool wide) {
   if (bal)
     return R <= 2 ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H, true>)
                   : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, true>);
+  if constexpr ((XMODE == 1 || XMODE == 2) && FMT == kFmt2) {
+    // staging priority for the second workgroup of each compute unit (ring depth 4)
+    if (prio && R > 2 && R <= 4)
+      return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, false, 4, true>);
+  }
   if (R <= 2) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H>);
   if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H>);
   if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8, FMT, H>);
@@ -942,21 +961,21 @@ const void* ring_kernel(int R, bool bal, bool wide) {
 }
 
 template <int FMT>
-const void* select_kernel(int xmode, int R, bool long_input, bool bal, bool wide) {
+const void* select_kernel(int xmode, int R, bool long_input, bool bal, bool wide, bool prio) {
   switch (xmode) {
-    case 0: return ring_kernel<0, FMT, kHold>(R, bal, wide);
+    case 0: return ring_kernel<0, FMT, kHold>(R, bal, wide, prio);
     case 1:
-      return long_input ? ring_kernel<1, FMT, kHoldPlain>(R, bal, wide)
-                        : ring_kernel<1, FMT, kHold>(R, bal, wide);
+      return long_input ? ring_kernel<1, FMT, kHoldPlain>(R, bal, wide, prio)
+                        : ring_kernel<1, FMT, kHold>(R, bal, wide, prio);
     case 2:
-      return long_input ? ring_kernel<2, FMT, kHoldPlain>(R, bal, wide)
-                        : ring_kernel<2, FMT, kHold>(R, bal, wide);
-    case 3: return ring_kernel<3, FMT, kHold>(R, bal, wide);
-    case 4: return ring_kernel<4, FMT, kHold>(R, bal, wide);
-    case 5: return ring_kernel<5, FMT, kHold>(R, bal, wide);
-    case 6: return ring_kernel<6, FMT, kHold>(R, bal, wide);
-    case 7: return ring_kernel<7, FMT, kHold>(R, bal, wide);
-    default: return ring_kernel<8, FMT, kHold>(R, bal, wide);
+      return long_input ? ring_kernel<2, FMT, kHoldPlain>(R, bal, wide, prio)
+                        : ring_kernel<2, FMT, kHold>(R, bal, wide, prio);
+    case 3: return ring_kernel<3, FMT, kHold>(R, bal, wide, prio);
+    case 4: return ring_kernel<4, FMT, kHold>(R, bal, wide, prio);
+    case 5: return ring_kernel<5, FMT, kHold>(R, bal, wide, prio);
+    case 6: return ring_kernel<6, FMT, kHold>(R, bal, wide, prio);
+    case 7: return ring_kernel<7, FMT, kHold>(R, bal, wide, prio);
+    default: return ring_kernel<8, FMT, kHold>(R, bal, wide, prio);
   }
 }
 
@@ -1031,12 +1050,13 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     size_t lds;
     int l1, l2, h;   // list runs: L1 tiles for workgroups b < h, else L2
     bool wide;       // eight-wave workgroups
+    bool prio;       // staging priority for the second workgroup of each CU
   };
   // latency regime: at most kLatencyBytes of packed weights
   const bool latency = (int64_t)total_tiles * 16 * row_bytes <= kLatencyBytes;
-  auto plan = [&](int t, bool bal, int wgs = 0, bool wide = false) {
+  auto plan = [&](int t, bool bal, int wgs = 0, bool wide = false, bool prio = false) {
     Plan p{t, wgs ? wgs : bal ? (total_tiles + t - 1) / t : count_wgs(t), bal, nullptr, 0, 0, 0, 0,
-           wide};
+           wide, prio};
     const int nw = wide ? 8 : 4;
     const int per_tile_w = ((chunks + 3) / 4 + nw - 1) / nw;   // loads per lane of a tile
     int ring = 4;
@@ -1052,8 +1072,8 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     if (fmt == kFmtT1) ring = 2;
     if (ring > t * per_tile_w) ring = t * per_tile_w;
     const bool li = long_input(64 * nw);
-    p.kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, li, bal, wide)
-                             : select_kernel<kFmt2>(xmode, ring, li, bal, wide);
+    p.kernel = fmt == kFmtT1 ? select_kernel<kFmtT1>(xmode, ring, li, bal, wide, prio)
+                             : select_kernel<kFmt2>(xmode, ring, li, bal, wide, prio);
     p.lds = (size_t)lds_bytes(t, a.M, a.K, fmt);
     return p;
   };
@@ -1107,6 +1127,11 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     // -> 5.77 us, gate+up 8.85 -> 10.2; 100B-class launches +0.3-4%)
     if ((xmode == 1 || xmode == 2) && fmt == kFmt2 && total_tiles <= cus)
       pl = plan(1, false, 0, true);
+    // one tile per workgroup, two workgroups on every compute unit: the second
+    // one stages at a raised wave priority (gemv_kernel PRIO; ring depth 4 only)
+    else if ((xmode == 1 || xmode == 2) && fmt == kFmt2 && cus == kPrioSplit && !pl.bal &&
+             pl.tpw == 1 && pl.wgs == kWgsPerCu * cus)
+      pl = plan(1, false, 0, false, true);
   }
   const int tpw = pl.tpw, wgs = pl.wgs;
   const void* kernel = pl.kernel;
