@@ -16,7 +16,8 @@
 //    workgroups per CU, each matrix split on its own or, for some launches, all
 //    matrices' tiles as one list in runs that may cross into the next matrix
 //    (launch_gemv: balanced runs, or skewed runs where the first-dispatched
-//    workgroup of each CU takes more).  K is cut into 256-k super-chunks; wave w
+//    workgroup of each CU takes more, or equal runs where the second one stages
+//    its input at a raised wave priority, PRIO).  K is cut into 256-k super-chunks; wave w
 //    takes super-chunks w, w + NW, ..., so one wave load instruction covers 16
 //    rows x 64 contiguous bytes and the waves read 64 NW contiguous bytes of each
 //    row per step.
@@ -342,13 +343,14 @@ constexpr int kArgsAt =
 // weight) in L2 for the other workgroups (2B stack with the fused norms and
 // gating 0.821 -> 0.778 ms per token; without a prologue the same loads lost 2%
 // on the 100B-class stack and nothing was gained on the 2B one).
-// PRIO: launches of one tile per workgroup and two workgroups per compute unit
-// on a chip of kPrioSplit compute units: the second-dispatched workgroup of each
-// unit (b >= kPrioSplit) stages its input at wave priority 1.  Issue
-// arbitration otherwise favours the older waves, so that workgroup waited behind
-// the first one's staging and ran 1.6-1.9x longer; raising it for the whole
-// launch measured slower, for the staging alone faster (100B-class stack, o and
-// down projections: 5.646 -> 5.579 ms per token).
+// PRIO: launches of two workgroups per compute unit with equal tile counts on a
+// chip of kPrioSplit compute units: the second-dispatched workgroup of each unit
+// (b >= kPrioSplit) stages its input at wave priority 1.  Issue arbitration
+// otherwise favours the older waves, so that workgroup waited behind the first
+// one's staging and ran 1.6-1.9x longer; raising it for the whole launch
+// measured slower, for the staging alone faster (100B-class stack, o and down
+// projections of one tile per workgroup: 5.646 -> 5.579 ms per token; q+k+v and
+// gate+up in equal list runs instead of skewed ones: 5.64 -> 5.60).
 template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false, int NW = 4,
           bool PRIO = false>
 __global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const uint8_t* wp0,
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) void gemv_kernel(const void* xin, const ui
   constexpr int ZB = FMT == kFmtT1 ? 96 : 64;  // zero slot bytes (zero_bytes)
   constexpr int kT = 64 * NW;                // threads
   static_assert(NW == 4 || (NW == 8 && XMODE > 0), "eight waves: fused activations only");
-  static_assert(!PRIO || (!BAL && NW == 4), "staging priority: per-matrix runs of four waves");
+  static_assert(!PRIO || NW == 4, "staging priority: four-wave workgroups");
   if constexpr (PRIO) {
     if (blockIdx.x >= kPrioSplit) __builtin_amdgcn_s_setprio(1);
   }
@@ -946,14 +948,15 @@ const void* ring_kernel(int R, bool bal, bool wide, bool prio) {
       return R <= 2 ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H, false, 8>)
                     : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, false, 8>);
   }
-  if (bal)
-    return R <= 2 ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H, true>)
-                  : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, true>);
   if constexpr ((XMODE == 1 || XMODE == 2) && FMT == kFmt2) {
     // staging priority for the second workgroup of each compute unit (ring depth 4)
     if (prio && R > 2 && R <= 4)
-      return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, false, 4, true>);
+      return bal ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, true, 4, true>)
+                 : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, false, 4, true>);
   }
+  if (bal)
+    return R <= 2 ? reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H, true>)
+                  : reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H, true>);
   if (R <= 2) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 2, FMT, H>);
   if (R <= 4) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 4, FMT, H>);
   if (R <= 8) return reinterpret_cast<const void*>(gemv_kernel<XMODE, 8, FMT, H>);
@@ -1095,7 +1098,8 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     //    gate+up, two 28672-row matrices: 8 + 6, 24.0 -> 23.3 us, where 9 + 5
     //    and the equal split were slower; the 8B-class gate+up, two 14336-row
     //    matrices, 4 + 3 in 512 workgroups instead of 448 runs of 4: 8B-class
-    //    stack 0.921 -> 0.897 ms per token);
+    //    stack 0.921 -> 0.897 ms per token), or, where the second one stages at
+    //    a raised priority (below), S / 2 each;
     //  * else, where each matrix's split rounded up needs more workgroups than
     //    the compute units hold two at a time (three 8192-row matrices in runs of
     //    3: 513), runs of qt + 1 for the first rt workgroups and qt for the rest
@@ -1106,9 +1110,16 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
       return true;
     };
     const int S = total_tiles % cus == 0 ? total_tiles / cus : 0;
-    if (k == kWgsPerCu && S >= 5 && S / 2 + 1 <= kMaxTiles && runs_fit(S / 2 + 1)) {
-      pl = plan(S / 2 + 1, true, 2 * cus);
-      pl.l1 = S / 2 + 1;
+    // With the staging priority (even S on a chip of kPrioSplit compute units,
+    // fused 2-bit launches) the two workgroups take S / 2 tiles each: 100B-class
+    // q+k+v 3 + 3, gate+up 7 + 7, stack 5.64 -> 5.60 ms per token (for odd S, the
+    // 8B-class gate+up 3 + 4 with it was 2% slower than 4 + 3 without).
+    const bool even_prio = (xmode == 1 || xmode == 2) && fmt == kFmt2 && cus == kPrioSplit &&
+                           S % 2 == 0;
+    const int L1 = even_prio ? S / 2 : S / 2 + 1;
+    if (k == kWgsPerCu && S >= 5 && L1 <= kMaxTiles && runs_fit(L1)) {
+      pl = plan(L1, true, 2 * cus, false, even_prio);
+      pl.l1 = L1;
       pl.l2 = S - pl.l1;
       pl.h = cus;
     } else if (pl.wgs > cus * k && a.count > 1 && (total_tiles + t - 1) / t <= cus * k &&

@@ -5,7 +5,9 @@ element by element, through the C ABI.
 The library takes list runs in two cases of a launch spread two workgroups per
 compute unit (over 6 MB of packed weights; K = 1024 here): when the tiles come
 to S = total / CUs per compute unit with S >= 5, the workgroups dispatched first
-(b < CUs) take S / 2 + 1 tiles and the others the rest (skewed runs); else, when
+(b < CUs) take S / 2 + 1 tiles and the others the rest (skewed runs; fused 2-bit
+launches with an even S on a 256-CU device take S / 2 each instead, the second
+workgroup of each compute unit staging its input at a raised priority); else, when
 splitting each matrix on its own would leave more workgroups than the compute
 units hold two at a time, runs of equal length to within one tile (with 3
 tiles per run, 513 per-matrix workgroups against 511 or 512).  The shapes cover
