@@ -343,9 +343,9 @@ constexpr int kArgsAt =
 // weight) in L2 for the other workgroups (2B stack with the fused norms and
 // gating 0.821 -> 0.778 ms per token; without a prologue the same loads lost 2%
 // on the 100B-class stack and nothing was gained on the 2B one).
-// PRIO: launches of two workgroups per compute unit with equal tile counts on a
-// chip of kPrioSplit compute units: the second-dispatched workgroup of each unit
-// (b >= kPrioSplit) stages its input at wave priority 1.  Issue arbitration
+// PRIO: launches of two workgroups per compute unit (on some or all units) with
+// equal tile counts on a chip of kPrioSplit compute units: the second-dispatched
+// workgroup of a unit (b >= kPrioSplit) stages its input at wave priority 1.  Issue arbitration
 // otherwise favours the older waves, so that workgroup waited behind the first
 // one's staging and ran 1.6-1.9x longer; raising it for the whole launch
 // measured slower, for the staging alone faster (100B-class stack, o and down
@@ -1138,10 +1138,11 @@ hipError_t launch_gemv(GemvArgs a, int xf_dtype, int fmt, hipStream_t s) {
     // -> 5.77 us, gate+up 8.85 -> 10.2; 100B-class launches +0.3-4%)
     if ((xmode == 1 || xmode == 2) && fmt == kFmt2 && total_tiles <= cus)
       pl = plan(1, false, 0, true);
-    // one tile per workgroup, two workgroups on every compute unit: the second
-    // one stages at a raised wave priority (gemv_kernel PRIO; ring depth 4 only)
+    // one tile per workgroup, two workgroups on some or every compute unit: the
+    // second one stages at a raised wave priority (gemv_kernel PRIO; ring depth 4
+    // only; the 8B-class q+k+v, 384 workgroups: stack 0.795 -> 0.790 ms per token)
     else if ((xmode == 1 || xmode == 2) && fmt == kFmt2 && cus == kPrioSplit && !pl.bal &&
-             pl.tpw == 1 && pl.wgs == kWgsPerCu * cus)
+             pl.tpw == 1 && pl.wgs > cus && pl.wgs <= kWgsPerCu * cus)
       pl = plan(1, false, 0, false, true);
   }
   const int tpw = pl.tpw, wgs = pl.wgs;

@@ -5,7 +5,9 @@ The four launches of a 100B-class layer, q+k+v (3 x 8192 -> 8192), o (8192 ->
 8192), gate+up (2 x 8192 -> 28672) and down (28672 -> 8192), take the
 bandwidth-regime plans with several 16-row tiles per workgroup (list runs); the
 8B-class down projection (14336 -> 4096, 256 tiles) and a ragged 12800 -> 3000
-(188 tiles) take eight-wave workgroups of one tile each.  Each launch has its own
+(188 tiles) take eight-wave workgroups of one tile each, and the 8B-class q+k+v
+(4096 -> 4096 + 1024 + 1024, 384 tiles) one tile in each of 384 four-wave
+workgroups, the second workgroup on a compute unit staging at a raised priority.  Each launch has its own
 seeded input, bf16 and fp32 inputs; the small parity shapes reach none of these
 plans.  Weights are seeded
 ternary codes packed by the oracle (ternarising 235 M master weights on the host
@@ -31,7 +33,8 @@ pytestmark = pytest.mark.gpu
 GAMMA = np.float32(0.0159)
 LAUNCHES = {"qkv": (8192, (8192, 8192, 8192)), "o": (8192, (8192,)),
             "gate+up": (8192, (28672, 28672)), "down": (28672, (8192,)),
-            "8B down": (14336, (4096,)), "ragged": (12800, (3000,))}
+            "8B down": (14336, (4096,)), "ragged": (12800, (3000,)),
+            "8B qkv": (4096, (4096, 1024, 1024))}
 
 
 @pytest.fixture(scope="module", autouse=True)
