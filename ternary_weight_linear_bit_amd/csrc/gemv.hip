@@ -17,10 +17,10 @@
 //    matrices' tiles as one list in runs that may cross into the next matrix
 //    (launch_gemv: balanced runs, or skewed runs where the first-dispatched
 //    workgroup of each CU takes more, or equal runs where the second one stages
-//    its input at a raised wave priority, PRIO).  K is cut into 256-k super-chunks; wave w
-//    takes super-chunks w, w + NW, ..., so one wave load instruction covers 16
-//    rows x 64 contiguous bytes and the waves read 64 NW contiguous bytes of each
-//    row per step.
+//    its input at a raised wave priority, PRIO).  K is cut into 256-k
+//    super-chunks; wave w takes super-chunks w, w + NW, ..., so one wave load
+//    instruction covers 16 rows x 64 contiguous bytes and the waves read 64 NW
+//    contiguous bytes of each row per step.
 //  * The activations are staged once per workgroup into LDS, byte-transposed
 //    within each 16-byte group; this is the order in which a shift, a mask and a
 //    byte lookup per field, (w >> 2i) & 0x03030303, unpack the weights, so no
@@ -345,10 +345,10 @@ constexpr int kArgsAt =
 // on the 100B-class stack and nothing was gained on the 2B one).
 // PRIO: launches of two workgroups per compute unit (on some or all units) with
 // equal tile counts on a chip of kPrioSplit compute units: the second-dispatched
-// workgroup of a unit (b >= kPrioSplit) stages its input at wave priority 1.  Issue arbitration
-// otherwise favours the older waves, so that workgroup waited behind the first
-// one's staging and ran 1.6-1.9x longer; raising it for the whole launch
-// measured slower, for the staging alone faster (100B-class stack, o and down
+// workgroup of a unit (b >= kPrioSplit) stages its input at wave priority 1.
+// Issue arbitration otherwise favours the older waves, so that workgroup waited
+// behind the first one's staging and ran 1.6-1.9x longer; raising it for the
+// whole launch measured slower, for the staging alone faster (100B-class stack, o and down
 // projections of one tile per workgroup: 5.646 -> 5.579 ms per token; q+k+v and
 // gate+up in equal list runs instead of skewed ones: 5.64 -> 5.60).
 template <int XMODE, int R, int FMT, int H = kHold, bool BAL = false, int NW = 4,
